@@ -17,8 +17,10 @@
  *     produced by the activation's producer (minfer Features, "GPU — CUDA").
  *     They do not give the rounding rule. Reading taken:
  *         amax = max |x_i|,  d = amax / 127 (f32 division),
- *         q_i  = 0 if amax == 0 else clamp(roundf(x_i / d), -127, 127),
+ *         q_i  = 0 if d == 0 else clamp(roundf(x_i / d), -127, 127),
  *         s    = d * (float)(sum of q_i)        (one f32 rounding).
+ *     d == 0 covers amax == 0 and an amax below 127 * 2^-150, whose
+ *     quotient underflows to zero.
  *
  *  2. The matmul. out[t][n] = sum_k w[n][k] * d[t][k/32] * q[t][k], with w
  *     the dequantized weight of GGML's Q4_K or Q6_K 256-value super-block
@@ -86,7 +88,7 @@ void oracle_quantize_act(const float *x, int64_t M, int64_t K, int64_t ldx,
             int sum = 0;
             for (int i = 0; i < 32; ++i) {
                 int qi = 0;
-                if (amax != 0.0f) {
+                if (db != 0.0f) {
                     float r = roundf(xb[i] / db);
                     if (r > 127.0f)
                         r = 127.0f;

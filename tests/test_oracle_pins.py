@@ -365,3 +365,19 @@ def test_generator_outliers_and_determinism():
     assert np.array_equal(a, b)
     big_cols = np.flatnonzero(np.abs(a).max(axis=0) > 6.0)
     assert 30 <= big_cols.size <= 36
+
+
+def test_quantizer_underflowing_scale():
+    """amax / 127 underflowing to 0 gives d = 0 and an all-zero block; a subnormal
+    d that does not underflow still quantizes the block's amax to 127."""
+    x = np.zeros((2, 32), np.float32)
+    x[0, 3] = np.float32(1e-45)          # smallest subnormal: 1e-45 / 127 -> 0
+    x[1, 3] = np.float32(2e-43)          # 2e-43 / 127 is a nonzero subnormal
+    x[1, 4] = np.float32(-1e-43)
+    q, d, s = oracle.quantize_act(x)
+    assert d[0, 0] == 0.0 and not q[0].any() and s[0, 0] == 0.0
+    # f32(2e-43) = 143 * 2^-149, so d = 143/127 * 2^-149 rounds to 2^-149;
+    # 143 clamps to 127. f32(-1e-43) = -71 * 2^-149 -> q = -71.
+    assert d[1, 0] == np.float32(2.0 ** -149)
+    assert q[1, 3] == 127 and q[1, 4] == -71
+    assert s[1, 0] == np.float32(2.0 ** -149) * np.float32(127 - 71)
