@@ -1,0 +1,308 @@
+"""Benchmark of the k-quant weight matmul hot path on one MI355X.
+
+One step is one pass of the whole hot path over one batch of synthetic input:
+  1. quantize the prefill activations  (M=3314, K=3584, f32 -> int8 plane)
+  2. Q4_K prefill GEMM                 (M=3314, N=18944, K=3584; int8 MFMA)
+  3. quantize the decode activation    (M=1, K=3584)
+  4. Q4_K decode GEMV                  (M=1, N=18944, K=3584)
+The inputs are the seeded 7B-class FFN up-projection workloads (prefill of a
+3314-token prompt and one decode token), resident in HBM before timing. The
+decode GEMV rotates through enough weight copies (>= 1 GiB) that the 256 MB
+last-level cache cannot hold them, so its weight bytes come from HBM.
+
+Prints one JSON line: value = int8 ops of the whole step (2*M*N*K of both
+matmuls) per second, in TOPS; "roofline" for the dominant kernel (the GEMM,
+MFMA-bound) and "decode_roofline" for the GEMV (HBM-bound), both from
+per-kernel HIP events over the timed region; "cpu_baseline" = the CPU oracle
+timed on a bounded sample of the same GEMM.
+
+  python bench.py [--steps K] [--warmup W] [--no-cpu]
+  python bench.py --all                  # per-matrix table of every workload
+  python bench.py --copy-calibration     # plain copy kernel (counter scale)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+INT8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA, published
+ROTATE_BYTES = 1 << 30       # weight copies for HBM-bound kernels
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = {
+    "gemm_q4k": "quant_gemm_amd/csrc/gemm.hip",
+    "gemm_q6k": "quant_gemm_amd/csrc/gemm.hip",
+    "gemv_q4k": "quant_gemm_amd/csrc/gemv.hip",
+    "gemv_q6k": "quant_gemm_amd/csrc/gemv.hip",
+    "quantize": "quant_gemm_amd/csrc/quantize.hip",
+}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def source_hash(kernel: str) -> str:
+    h = hashlib.sha256()
+    for rel in sorted({KERNEL_SOURCES[kernel], "quant_gemm_amd/csrc/mq_device.h"}):
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from committed counter runs, if the kernel source
+    is unchanged since they were taken; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get(kernel, {}).get(workload)
+    if not e or e.get("source_hash") != source_hash(kernel):
+        return None
+    return e.get("bytes_per_launch")
+
+
+def q4k_gemv_bytes(M, N, K):
+    return N * (K // 256) * 144 + M * (K + 2 * 4 * (K // 32)) + 4 * M * N
+
+
+def q6k_gemv_bytes(M, N, K):
+    return N * (K // 256) * 210 + M * (K + 4 * (K // 32)) + 4 * M * N
+
+
+def cpu_baseline(W, x, case, target_s):
+    """The oracle, as it is, on the first tokens of the prefill GEMM."""
+    import numpy as np
+    import oracle
+    oracle.lib()
+    threads = oracle.max_threads()
+    q, d, _ = oracle.quantize_act(x)
+    ntok = 2
+    t0 = time.perf_counter()
+    oracle.matmul_q4k(W, q, d, case.N, case.K, tokens=np.arange(ntok))
+    t = time.perf_counter() - t0
+    ntok = int(max(2, min(case.M, ntok * target_s / max(t, 1e-6))))
+    t0 = time.perf_counter()
+    oracle.matmul_q4k(W, q, d, case.N, case.K, tokens=np.arange(ntok))
+    t = time.perf_counter() - t0
+    macs = ntok * case.N * case.K
+    return {
+        "value": 2 * macs / t / 1e12, "unit": "TOPS", "cores": threads, "kind": "oracle",
+        "sample": (f"Q4_K matmul of tokens 0..{ntok - 1} of the M={case.M} prefill "
+                   f"(N={case.N}, K={case.K}): {macs:.3g} MACs in {t:.2f} s on {threads} "
+                   "OpenMP threads (plain C, integer group dots, f64 combination)"),
+    }
+
+
+def run_contract(args):
+    import numpy as np
+    import torch
+
+    import quant_gemm_amd as mq
+    from quant_gemm_amd import synth
+
+    mq.load()
+    dev = torch.device("cuda:0")
+    pre = synth.case_by_name("q4k_prefill_ffn_up")
+    dec = synth.case_by_name("q4k_decode_ffn_up")
+    log(f"[bench] generating inputs: {pre.name} and {dec.name}")
+    Wp_np = pre.make_weights()
+    xp_np = pre.make_activations()
+    Wd_np = dec.make_weights()
+    xd_np = dec.make_activations()
+
+    Wp = torch.from_numpy(Wp_np.reshape(-1)).to(dev)
+    xp = torch.from_numpy(xp_np).to(dev)
+    xd = torch.from_numpy(xd_np).to(dev)
+    Wd0 = torch.from_numpy(Wd_np.reshape(-1)).to(dev)
+    copies = max(1, -(-ROTATE_BYTES // Wd0.numel()))
+    Wd = [Wd0] + [Wd0.clone() for _ in range(copies - 1)]
+    qp = torch.empty((pre.M, pre.K), dtype=torch.int8, device=dev)
+    dp = torch.empty((pre.M, pre.K // 32), dtype=torch.float32, device=dev)
+    sp = torch.empty_like(dp)
+    qd = torch.empty((dec.M, dec.K), dtype=torch.int8, device=dev)
+    dd = torch.empty((dec.M, dec.K // 32), dtype=torch.float32, device=dev)
+    sd = torch.empty_like(dd)
+    outp = torch.empty((pre.M, pre.N), dtype=torch.float32, device=dev)
+    outd = torch.empty((dec.M, dec.N), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    names = ["quantize_prefill", "gemm_q4k", "quantize_decode", "gemv_q4k"]
+
+    def step(i, ev=None):
+        if ev: ev[0].record()
+        mq.quantize_act(xp, qp, dp, sp)
+        if ev: ev[1].record()
+        mq.matmul_q4k(Wp, qp, dp, sp, pre.N, pre.K, out=outp)
+        if ev: ev[2].record()
+        mq.quantize_act(xd, qd, dd, sd)
+        if ev: ev[3].record()
+        mq.matmul_q4k(Wd[i % copies], qd, dd, sd, dec.N, dec.K, out=outd)
+        if ev: ev[4].record()
+
+    log(f"[bench] warmup {args.warmup} steps")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    log(f"[bench] timing {args.steps} steps")
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(args.steps):
+        step(i, evs[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    per = {n: np.array([evs[i][k].elapsed_time(evs[i][k + 1]) for i in range(args.steps)])
+           for k, n in enumerate(names)}
+    avg_us = {n: float(v.mean() * 1e3) for n, v in per.items()}
+    med_us = {n: float(np.median(v) * 1e3) for n, v in per.items()}
+
+    ops_pre = pre.ops
+    ops_dec = dec.ops
+    ms_step = total_ms / args.steps
+    value = (ops_pre + ops_dec) / (ms_step * 1e-3) / 1e12
+
+    gemm_tops = ops_pre / (avg_us["gemm_q4k"] * 1e-6) / 1e12
+    gemv_bytes = q4k_gemv_bytes(dec.M, dec.N, dec.K)
+    gemv_gbs = gemv_bytes / (avg_us["gemv_q4k"] * 1e-6) / 1e9
+    qbytes = pre.M * pre.K * 4 + pre.M * pre.K + 2 * 4 * pre.M * (pre.K // 32)
+
+    res = {
+        "metric": "int8 TOPS + % MFMA peak (M=3314 GEMM); GB/s + % HBM peak (M=1 GEMV)",
+        "value": round(value, 3),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic (seeded Q4_K blocks and N(0,1) activations with 1% x20 outlier columns)",
+        "config": {
+            "workload": ("q4k ffn_up prefill M=3314 N=18944 K=3584 (quantize + GEMM) + "
+                         "q4k ffn_up decode M=1 N=18944 K=3584 (quantize + GEMV)"),
+            "prefill_tokens": pre.M, "decode_tokens": dec.M, "N": pre.N, "K": pre.K,
+            "decode_weight_copies": copies, "parallelism": "none (1 GPU)",
+        },
+        "roofline": {
+            "kernel": "gemm_q4k", "bound": "mfma", "achieved": round(gemm_tops, 2),
+            "peak": INT8_PEAK_TOPS, "unit": "TOPS", "frac": round(gemm_tops / INT8_PEAK_TOPS, 4),
+            "traffic": measured_traffic("gemm_q4k", "prefill_ffn_up"),
+            "work_per_launch": f"{ops_pre:.4g} int8 ops (2*M*N*K)",
+            "avg_us": round(avg_us["gemm_q4k"], 2),
+        },
+        "decode_roofline": {
+            "kernel": "gemv_q4k", "bound": "hbm", "achieved": round(gemv_gbs, 1),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gemv_gbs / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic("gemv_q4k", "decode_ffn_up"),
+            "work_per_launch": f"{gemv_bytes} bytes (weights + int8 plane + output)",
+            "avg_us": round(avg_us["gemv_q4k"], 3), "median_us": round(med_us["gemv_q4k"], 3),
+        },
+        "kernels_avg_us": {n: round(v, 3) for n, v in avg_us.items()},
+        "quantize_prefill_GBs": round(qbytes / (avg_us["quantize_prefill"] * 1e-6) / 1e9, 1),
+    }
+    if not args.no_cpu:
+        log("[bench] CPU oracle baseline")
+        res["cpu_baseline"] = cpu_baseline(Wp_np, xp_np, pre, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+def run_all(args):
+    """Per-matrix kernel times for every workload (a table, not the contract line)."""
+    import numpy as np
+    import torch
+
+    import quant_gemm_amd as mq
+    from quant_gemm_amd import synth
+
+    mq.load()
+    dev = torch.device("cuda:0")
+    rows = []
+    for cfg, case in synth.all_cases():
+        log(f"[bench --all] {case.name}")
+        W_np = case.make_weights()
+        x = torch.from_numpy(case.make_activations()).to(dev)
+        W0 = torch.from_numpy(W_np.reshape(-1)).to(dev)
+        hbm = case.M <= mq.gemv_max_m()
+        copies = max(1, -(-ROTATE_BYTES // W0.numel())) if hbm else 1
+        Ws = [W0] + [W0.clone() for _ in range(copies - 1)]
+        q, d, s = mq.quantize_act(x)
+        mm = mq.matmul_q4k if case.fmt == "q4k" else mq.matmul_q6k
+        out = torch.empty((case.M, case.N), dtype=torch.float32, device=dev)
+        for i in range(3):
+            mm(Ws[i % copies], q, d, s, case.N, case.K, out=out)
+        torch.cuda.synchronize()
+        reps = max(copies, 20 if not hbm else 2 * copies)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(reps):
+            mm(Ws[i % copies], q, d, s, case.N, case.K, out=out)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        row = {"config": cfg, "case": case.name, "fmt": case.fmt, "M": case.M, "N": case.N,
+               "K": case.K, "us": round(us, 2), "TOPS": round(case.ops / (us * 1e-6) / 1e12, 2)}
+        if hbm:
+            b = (q4k_gemv_bytes if case.fmt == "q4k" else q6k_gemv_bytes)(case.M, case.N, case.K)
+            row["GBs"] = round(b / (us * 1e-6) / 1e9, 1)
+            row["frac_hbm"] = round(row["GBs"] / HBM_PEAK_GBS, 3)
+        else:
+            row["frac_int8_peak"] = round(row["TOPS"] / INT8_PEAK_TOPS, 4)
+        rows.append(row)
+        print(json.dumps(row), flush=True)
+        del Ws, W0, out, q, d, s, x
+        torch.cuda.empty_cache()
+
+
+def run_copy_calibration(args):
+    """A plain device copy of known size, to scale FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    n = 256 << 20
+    a = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(args.steps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": args.steps}))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--all", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus}: this build measures one GPU only; the multi-GPU "
+              "path is a design (N-sharded weights), not an implementation", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        run_copy_calibration(args)
+    elif args.all:
+        run_all(args)
+    else:
+        run_contract(args)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,139 @@
+/*
+ * mq.h - k-quant weight matmul on AMD MI355X (gfx950): the C ABI.
+ *
+ * The operation is the quantized matmul of the CUDA prefill/decode path of
+ * the minfer pages: GGML Q4_K / Q6_K weight super-blocks multiplied against
+ * f32 activations that are first quantized to a per-32 int8 plane
+ * (minfer Features, "GPU — CUDA": int8 MMQ GEMMs for q4_K and q6_K fed by an
+ * int8 activation plane; decode by the MMVQ weight-streaming path.
+ * minfer Compute Graph Design, §9.3 Execution dispatch: the activation is
+ * quantized once and that plane serves every matmul that reads it.)
+ *
+ * Conventions for every entry point
+ *   - Pointers are device pointers owned by the caller. The library never
+ *     allocates, frees or synchronizes inside these calls; it enqueues kernels
+ *     on `stream` (a hipStream_t passed as void*, NULL = the null stream) and
+ *     returns. Inputs are read-only; outputs are overwritten.
+ *   - Arguments are validated on the host before any HIP call. A failed
+ *     check returns a nonzero mq_status and nothing is launched; the
+ *     calling thread's mq_last_error() then names the argument and its value.
+ *     Errors are never turned into a silent fallback (minfer Compute Graph
+ *     Design, §7.4 Error contract).
+ *   - After the checks the current device must be gfx950 (queried at run
+ *     time, minfer Architecture, §5.3 GPU safety), else MQ_ERR_UNSUPPORTED.
+ *   - Sizes are element counts. K must be a positive multiple of 256 (one
+ *     super-block); M and N may be any positive value up to 2^31-1.
+ *   - There is no device-side validation of data. Non-finite activations are
+ *     a precondition violation with unspecified output.
+ *   - Calls are thread-safe. Calls that overlap in time on the same output
+ *     buffers race, as for any kernel.
+ *
+ * Data layout in device memory
+ *   x    f32  [M][ldx]   activations, token-major (row t = one token)
+ *   q    int8 [M][K]     quantized activations, token-major
+ *   d    f32  [M][K/32]  per-block activation scale
+ *   s    f32  [M][K/32]  per-block d * (sum of the block's q)
+ *   W    N rows, each K/256 consecutive super-blocks, rows back to back:
+ *          Q4_K: 144-byte blocks  (f16 d, f16 dmin, 12 B of 6-bit scale and
+ *                min codes, 128 B of 4-bit quants); row = K/256*144 bytes
+ *          Q6_K: 210-byte blocks  (128 B low nibbles, 64 B high bit pairs,
+ *                16 int8 scales, f16 d); row = K/256*210 bytes
+ *        (GGML's layouts: minfer Architecture, §6 Quantization & Tensor
+ *        Layout; weights are [out][in] row-major, §4.5 Core invariants.)
+ *   out  f32  [M][N]     token-major output (minfer Compute Graph Design,
+ *                        §7.1: activations and outputs are token-major)
+ *
+ * Alignment: W, q, d and s must be 16-byte aligned; x and out 4-byte aligned.
+ */
+#ifndef MQ_H
+#define MQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MQ_ABI_VERSION 1
+
+typedef enum {
+    MQ_OK = 0,
+    MQ_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, unknown path */
+    MQ_ERR_SHAPE = 2,       /* K not a positive multiple of 256, ldx < K, too large */
+    MQ_ERR_ALIGN = 3,       /* a pointer is not aligned as required */
+    MQ_ERR_UNSUPPORTED = 4, /* the current device is not gfx950 */
+    MQ_ERR_DEVICE = 5,      /* a HIP runtime query failed */
+    MQ_ERR_LAUNCH = 6       /* the kernel launch failed */
+} mq_status;
+
+/* Kernel path selectors for the *_ex entry points. */
+enum { MQ_PATH_AUTO = 0, MQ_PATH_GEMV = 1, MQ_PATH_GEMM = 2 };
+
+/*
+ * Per-32 int8 activation quantization.
+ * For each token t and block b of 32 consecutive values x[t][32b .. 32b+31]:
+ *   amax = max |x|;  d[t][b] = amax / 127 (IEEE f32 division);
+ *   q[t][32b+i] = d[t][b] == 0 ? 0 : clamp(roundf(x[t][32b+i] / d[t][b]), -127, 127)
+ *                 (roundf rounds halves away from zero; d == 0 when amax == 0
+ *                 or when amax / 127 underflows);
+ *   s[t][b] = d[t][b] * (float)(sum_i q[t][32b+i]).
+ * The pages require an on-the-fly activation quantization with per-subblock
+ * sums (minfer Support Matrix, "Supported Quantization Formats") but do not
+ * give the rounding rule; this is the reading taken, and the result is
+ * bit-exact against it. x has row stride ldx >= K (elements).
+ * Outputs q [M][K], d and s [M][K/32] are written in full.
+ */
+int mq_quantize_act(const float *x, int64_t M, int64_t K, int64_t ldx,
+                    int8_t *q, float *d, float *s, void *stream);
+
+/*
+ * Q4_K matmul: out[t][n] = sum_k w[n][k] * d[t][k/32] * q[t][k], where
+ * w[n][k] = d_blk * sc_j * q4 - dmin_blk * m_j for the weight's super-block
+ * and 32-value sub-block j. The int8 dot of each 32-value sub-block is exact
+ * (int32); scales, mins and the min term (which uses s) are applied in f32.
+ * Result within 1e-4 * max|out| of the exact value for the workloads tested.
+ * M <= mq_gemv_max_m() runs the weight-streaming GEMV, larger M the int8
+ * MFMA GEMM (the CUDA dispatch splits decode from prefill by token count:
+ * minfer Support Matrix, "CUDA notes").
+ * W as described above; q, d, s from mq_quantize_act (s is required).
+ */
+int mq_matmul_q4k(const void *W, const int8_t *q, const float *d,
+                  const float *s, int64_t M, int64_t N, int64_t K,
+                  float *out, void *stream);
+
+/*
+ * Q6_K matmul: as mq_matmul_q4k with w[n][k] = d_blk * scales[j] * (q6 - 32)
+ * for the weight's 16-value group j. s is not used and may be NULL.
+ */
+int mq_matmul_q6k(const void *W, const int8_t *q, const float *d,
+                  const float *s, int64_t M, int64_t N, int64_t K,
+                  float *out, void *stream);
+
+/*
+ * As mq_matmul_q4k / mq_matmul_q6k with the kernel chosen by `path`
+ * (MQ_PATH_AUTO, MQ_PATH_GEMV, MQ_PATH_GEMM). MQ_PATH_GEMV requires
+ * M <= mq_gemv_max_m(). Both paths meet the same contract; tests use this
+ * to check each path on the same inputs.
+ */
+int mq_matmul_q4k_ex(const void *W, const int8_t *q, const float *d,
+                     const float *s, int64_t M, int64_t N, int64_t K,
+                     float *out, void *stream, int path);
+int mq_matmul_q6k_ex(const void *W, const int8_t *q, const float *d,
+                     const float *s, int64_t M, int64_t N, int64_t K,
+                     float *out, void *stream, int path);
+
+/* Largest M served by the GEMV path under MQ_PATH_AUTO. */
+int64_t mq_gemv_max_m(void);
+
+/* Message for the calling thread's last failed call ("" if none). The
+ * pointer stays valid until the thread's next mq_* call. */
+const char *mq_last_error(void);
+
+/* MQ_ABI_VERSION of the loaded library. */
+int mq_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MQ_H */

@@ -1,0 +1,187 @@
+// C ABI of libmq: argument validation, device check and kernel dispatch.
+//
+// Every check runs on the host before the first HIP call, so each failure
+// can be exercised without a GPU. Failures return a status and leave a
+// message naming the argument and its value (minfer Compute Graph Design,
+// §7.4 Error contract: errors name the actual values and never fall back).
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/mq.h"
+#include "mq_launch.h"
+
+namespace {
+
+thread_local char g_err[512];
+
+int fail(int status, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+constexpr int64_t kMaxDim = 0x7fffffff;
+
+// Per-device result of the architecture query: 0 unknown, 1 gfx950, 2 other.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_ok[kMaxDevices];
+
+int check_device()
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return fail(MQ_ERR_DEVICE, "hipGetDevice failed: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(MQ_ERR_DEVICE, "device ordinal %d out of range", dev);
+    int state = g_arch_ok[dev].load(std::memory_order_relaxed);
+    if (state == 0) {
+        hipDeviceProp_t prop;
+        e = hipGetDeviceProperties(&prop, dev);
+        if (e != hipSuccess)
+            return fail(MQ_ERR_DEVICE, "hipGetDeviceProperties(%d) failed: %s", dev,
+                        hipGetErrorString(e));
+        state = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        g_arch_ok[dev].store(state, std::memory_order_relaxed);
+        if (state == 2)
+            return fail(MQ_ERR_UNSUPPORTED, "device %d is %s; this library is built for gfx950",
+                        dev, prop.gcnArchName);
+    }
+    if (state == 2)
+        return fail(MQ_ERR_UNSUPPORTED, "device %d is not gfx950", dev);
+    return MQ_OK;
+}
+
+int launched(hipError_t e, const char *what)
+{
+    if (e != hipSuccess)
+        return fail(MQ_ERR_LAUNCH, "%s: kernel launch failed: %s", what, hipGetErrorString(e));
+    return MQ_OK;
+}
+
+int check_K(int64_t K, const char *fn)
+{
+    if (K < 256 || K % 256 != 0)
+        return fail(MQ_ERR_SHAPE, "%s: K=%lld must be a positive multiple of 256", fn, (long long)K);
+    if (K > kMaxDim)
+        return fail(MQ_ERR_SHAPE, "%s: K=%lld exceeds %lld", fn, (long long)K, (long long)kMaxDim);
+    return MQ_OK;
+}
+
+int matmul(bool q6, const void *W, const int8_t *q, const float *d, const float *s,
+           int64_t M, int64_t N, int64_t K, float *out, void *stream, int path)
+{
+    const char *fn = q6 ? "mq_matmul_q6k" : "mq_matmul_q4k";
+    if (!W) return fail(MQ_ERR_INVALID_ARG, "%s: W is NULL", fn);
+    if (!q) return fail(MQ_ERR_INVALID_ARG, "%s: q is NULL", fn);
+    if (!d) return fail(MQ_ERR_INVALID_ARG, "%s: d is NULL", fn);
+    if (!q6 && !s) return fail(MQ_ERR_INVALID_ARG, "%s: s is NULL (the Q4_K min term needs it)", fn);
+    if (!out) return fail(MQ_ERR_INVALID_ARG, "%s: out is NULL", fn);
+    if (M <= 0) return fail(MQ_ERR_INVALID_ARG, "%s: M=%lld must be positive", fn, (long long)M);
+    if (N <= 0) return fail(MQ_ERR_INVALID_ARG, "%s: N=%lld must be positive", fn, (long long)N);
+    if (int rc = check_K(K, fn)) return rc;
+    if (M > kMaxDim || N > kMaxDim)
+        return fail(MQ_ERR_SHAPE, "%s: M=%lld, N=%lld: each must be at most %lld", fn,
+                    (long long)M, (long long)N, (long long)kMaxDim);
+    if (path != MQ_PATH_AUTO && path != MQ_PATH_GEMV && path != MQ_PATH_GEMM)
+        return fail(MQ_ERR_INVALID_ARG, "%s: path=%d is not MQ_PATH_AUTO/GEMV/GEMM", fn, path);
+    if (path == MQ_PATH_GEMV && M > mq::GEMV_MAX_M)
+        return fail(MQ_ERR_INVALID_ARG, "%s: path=MQ_PATH_GEMV needs M <= %d, got M=%lld", fn,
+                    mq::GEMV_MAX_M, (long long)M);
+    if (!aligned(W, 16)) return fail(MQ_ERR_ALIGN, "%s: W=%p is not 16-byte aligned", fn, W);
+    if (!aligned(q, 16)) return fail(MQ_ERR_ALIGN, "%s: q=%p is not 16-byte aligned", fn, (const void *)q);
+    if (!aligned(d, 16)) return fail(MQ_ERR_ALIGN, "%s: d=%p is not 16-byte aligned", fn, (const void *)d);
+    if (s && !aligned(s, 16)) return fail(MQ_ERR_ALIGN, "%s: s=%p is not 16-byte aligned", fn, (const void *)s);
+    if (!aligned(out, 4)) return fail(MQ_ERR_ALIGN, "%s: out=%p is not 4-byte aligned", fn, (const void *)out);
+    // grid sizes must fit the launch limits
+    const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
+    if (tiles > kMaxDim)
+        return fail(MQ_ERR_SHAPE, "%s: M=%lld x N=%lld needs too many tiles", fn, (long long)M, (long long)N);
+    if (int rc = check_device()) return rc;
+
+    const bool gemv = path == MQ_PATH_GEMV || (path == MQ_PATH_AUTO && M <= mq::GEMV_MAX_M);
+    const auto *Wb = static_cast<const uint8_t *>(W);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int m = (int)M, n = (int)N, k = (int)K;
+    hipError_t e;
+    if (q6)
+        e = gemv ? mq::launch_gemv_q6k(Wb, q, d, m, n, k, out, st)
+                 : mq::launch_gemm_q6k(Wb, q, d, m, n, k, out, st);
+    else
+        e = gemv ? mq::launch_gemv_q4k(Wb, q, d, s, m, n, k, out, st)
+                 : mq::launch_gemm_q4k(Wb, q, d, s, m, n, k, out, st);
+    return launched(e, fn);
+}
+
+} // namespace
+
+extern "C" {
+
+int mq_quantize_act(const float *x, int64_t M, int64_t K, int64_t ldx, int8_t *q,
+                    float *d, float *s, void *stream)
+{
+    g_err[0] = '\0';
+    const char *fn = "mq_quantize_act";
+    if (!x) return fail(MQ_ERR_INVALID_ARG, "%s: x is NULL", fn);
+    if (!q) return fail(MQ_ERR_INVALID_ARG, "%s: q is NULL", fn);
+    if (!d) return fail(MQ_ERR_INVALID_ARG, "%s: d is NULL", fn);
+    if (!s) return fail(MQ_ERR_INVALID_ARG, "%s: s is NULL", fn);
+    if (M <= 0) return fail(MQ_ERR_INVALID_ARG, "%s: M=%lld must be positive", fn, (long long)M);
+    if (int rc = check_K(K, fn)) return rc;
+    if (ldx < K) return fail(MQ_ERR_SHAPE, "%s: ldx=%lld is smaller than K=%lld", fn, (long long)ldx, (long long)K);
+    if (M > kMaxDim) return fail(MQ_ERR_SHAPE, "%s: M=%lld exceeds %lld", fn, (long long)M, (long long)kMaxDim);
+    // the scalar path uses 32 threads per block: the grid must fit in 2^31-1 workgroups
+    if (M > (kMaxDim * 256 / 32) / (K / 32))
+        return fail(MQ_ERR_SHAPE, "%s: M=%lld x K=%lld is too large for one launch", fn, (long long)M, (long long)K);
+    if (!aligned(x, 4)) return fail(MQ_ERR_ALIGN, "%s: x=%p is not 4-byte aligned", fn, (const void *)x);
+    if (!aligned(q, 16)) return fail(MQ_ERR_ALIGN, "%s: q=%p is not 16-byte aligned", fn, (const void *)q);
+    if (!aligned(d, 16)) return fail(MQ_ERR_ALIGN, "%s: d=%p is not 16-byte aligned", fn, (const void *)d);
+    if (!aligned(s, 16)) return fail(MQ_ERR_ALIGN, "%s: s=%p is not 16-byte aligned", fn, (const void *)s);
+    if (int rc = check_device()) return rc;
+    return launched(mq::launch_quantize(x, M, K, ldx, q, d, s, static_cast<hipStream_t>(stream)), fn);
+}
+
+int mq_matmul_q4k(const void *W, const int8_t *q, const float *d, const float *s, int64_t M,
+                  int64_t N, int64_t K, float *out, void *stream)
+{
+    g_err[0] = '\0';
+    return matmul(false, W, q, d, s, M, N, K, out, stream, MQ_PATH_AUTO);
+}
+
+int mq_matmul_q6k(const void *W, const int8_t *q, const float *d, const float *s, int64_t M,
+                  int64_t N, int64_t K, float *out, void *stream)
+{
+    g_err[0] = '\0';
+    return matmul(true, W, q, d, s, M, N, K, out, stream, MQ_PATH_AUTO);
+}
+
+int mq_matmul_q4k_ex(const void *W, const int8_t *q, const float *d, const float *s, int64_t M,
+                     int64_t N, int64_t K, float *out, void *stream, int path)
+{
+    g_err[0] = '\0';
+    return matmul(false, W, q, d, s, M, N, K, out, stream, path);
+}
+
+int mq_matmul_q6k_ex(const void *W, const int8_t *q, const float *d, const float *s, int64_t M,
+                     int64_t N, int64_t K, float *out, void *stream, int path)
+{
+    g_err[0] = '\0';
+    return matmul(true, W, q, d, s, M, N, K, out, stream, path);
+}
+
+int64_t mq_gemv_max_m(void) { return mq::GEMV_MAX_M; }
+
+const char *mq_last_error(void) { return g_err; }
+
+int mq_abi_version(void) { return MQ_ABI_VERSION; }
+
+} // extern "C"

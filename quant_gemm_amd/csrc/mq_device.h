@@ -1,0 +1,57 @@
+// Device-side helpers shared by the gfx950 kernels of libmq.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mq {
+
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+// IEEE binary16 bits -> f32 (exact, subnormals included: f16 denormals are
+// kept on gfx9).
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t bits)
+{
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(bits & 0xffffu));
+}
+
+// Signed 4-way int8 dot product with int32 accumulate (v_dot4_i32_i8).
+__device__ __forceinline__ int dot4(int a, int b, int c)
+{
+    return __builtin_amdgcn_sdot4(a, b, c, false);
+}
+
+// Sum over the 64 lanes of a wavefront; every lane receives the total.
+__device__ __forceinline__ float wave_sum(float v)
+{
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+        v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+// The 4*n bytes at a 2-byte aligned address p, as n dwords, using only
+// aligned dword loads. When p is 2 mod 4 the loads also cover the 2 bytes
+// before p and the 2 bytes after p + 4n: callers keep [p - 2, p + 4n + 2)
+// inside one allocation.
+template <int n>
+__device__ __forceinline__ void load_dwords_a2(const uint8_t *p, uint32_t (&out)[n])
+{
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    const uint32_t *base = reinterpret_cast<const uint32_t *>(a & ~uintptr_t(3));
+    const uint32_t sh = (uint32_t)(a & 3u);   // 0 or 2
+    uint32_t w[n + 1];
+#pragma unroll
+    for (int i = 0; i < n; ++i)
+        w[i] = base[i];
+    w[n] = sh ? base[n] : 0u;
+#pragma unroll
+    for (int i = 0; i < n; ++i)
+        out[i] = __builtin_amdgcn_alignbyte(w[i + 1], w[i], sh);
+}
+
+} // namespace mq

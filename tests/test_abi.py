@@ -1,0 +1,129 @@
+"""The C ABI on the host (no GPU needed).
+
+libmq.so must load, export every function include/mq.h declares, and reject
+every invalid argument with its documented status and a message naming the
+argument, before any HIP call. Every call here fails validation, so nothing
+reaches a device (fake pointers are never dereferenced).
+"""
+import os
+import re
+
+import pytest
+
+import quant_gemm_amd as mq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mq.h")
+
+OK, INVALID, SHAPE, ALIGN = 0, 1, 2, 3
+P = 0x7f0000000000          # a 256-byte aligned fake device address
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mq_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return mq.load()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("mq_quantize_act", "mq_matmul_q4k", "mq_matmul_q6k", "mq_last_error"):
+        assert n in names
+    assert set(names) == set(mq.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_abi_version_and_constants(L):
+    assert L.mq_abi_version() == mq.ABI_VERSION
+    assert L.mq_gemv_max_m() >= 1
+    hdr = open(HEADER).read()
+    assert f"#define MQ_ABI_VERSION {mq.ABI_VERSION}" in hdr
+
+
+def _q4k(L, W=P, q=P, d=P, s=P, M=4, N=8, K=256, out=P, path=0):
+    return L.mq_matmul_q4k_ex(W, q, d, s, M, N, K, out, None, path)
+
+
+def _q6k(L, W=P, q=P, d=P, s=None, M=4, N=8, K=256, out=P, path=0):
+    return L.mq_matmul_q6k_ex(W, q, d, s, M, N, K, out, None, path)
+
+
+def _quant(L, x=P, M=4, K=256, ldx=256, q=P, d=P, s=P):
+    return L.mq_quantize_act(x, M, K, ldx, q, d, s, None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(W=None), INVALID, "W is NULL"),
+    (dict(q=None), INVALID, "q is NULL"),
+    (dict(d=None), INVALID, "d is NULL"),
+    (dict(s=None), INVALID, "s is NULL"),
+    (dict(out=None), INVALID, "out is NULL"),
+    (dict(M=0), INVALID, "M=0"),
+    (dict(M=-3), INVALID, "M=-3"),
+    (dict(N=0), INVALID, "N=0"),
+    (dict(K=0), SHAPE, "K=0"),
+    (dict(K=100), SHAPE, "K=100"),
+    (dict(K=384), SHAPE, "K=384"),
+    (dict(M=2 ** 31), SHAPE, "M=2147483648"),
+    (dict(path=3), INVALID, "path=3"),
+    (dict(path=1, M=9), INVALID, "M=9"),
+    (dict(W=P + 4), ALIGN, "W="),
+    (dict(q=P + 8), ALIGN, "q="),
+    (dict(d=P + 4), ALIGN, "d="),
+    (dict(s=P + 12), ALIGN, "s="),
+    (dict(out=P + 2), ALIGN, "out="),
+])
+def test_q4k_validation(L, kw, status, needle):
+    rc = _q4k(L, **kw)
+    assert rc == status
+    msg = L.mq_last_error().decode()
+    assert "mq_matmul_q4k" in msg and needle in msg
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(W=None), INVALID, "W is NULL"),
+    (dict(K=512 + 128), SHAPE, "K=640"),
+    (dict(N=-1), INVALID, "N=-1"),
+    (dict(W=P + 2), ALIGN, "W="),
+    (dict(s=P + 4), ALIGN, "s="),
+])
+def test_q6k_validation(L, kw, status, needle):
+    rc = _q6k(L, **kw)
+    assert rc == status
+    msg = L.mq_last_error().decode()
+    assert "mq_matmul_q6k" in msg and needle in msg
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(x=None), INVALID, "x is NULL"),
+    (dict(q=None), INVALID, "q is NULL"),
+    (dict(d=None), INVALID, "d is NULL"),
+    (dict(s=None), INVALID, "s is NULL"),
+    (dict(M=0), INVALID, "M=0"),
+    (dict(K=96), SHAPE, "K=96"),
+    (dict(ldx=255), SHAPE, "ldx=255"),
+    (dict(x=P + 2), ALIGN, "x="),
+    (dict(q=P + 4), ALIGN, "q="),
+    (dict(M=2 ** 40), SHAPE, "M="),
+])
+def test_quantize_validation(L, kw, status, needle):
+    rc = _quant(L, **kw)
+    assert rc == status
+    msg = L.mq_last_error().decode()
+    assert "mq_quantize_act" in msg and needle in msg
+
+
+def test_error_is_cleared_by_next_call(L):
+    assert _q4k(L, W=None) == INVALID
+    assert L.mq_last_error().decode() != ""
+    assert _q6k(L, N=0) == INVALID
+    assert "N=0" in L.mq_last_error().decode()

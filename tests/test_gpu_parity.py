@@ -1,0 +1,281 @@
+"""GPU parity: libmq (HIP, gfx950) against the CPU oracle, through the C ABI.
+
+Bars:
+  * the int8 activation plane (q, d, s) is bit-identical to the oracle's;
+  * every matmul output matrix satisfies max|gpu - oracle| <= 1e-4 * max|oracle|
+    over the compared elements (the oracle is the exact result rounded once
+    to f32; the GPU accumulates in f32 in its own order).
+Full-size workloads compare sampled token rows (all N outputs of each
+sampled token, tile edges and the ragged tail included); small shapes compare
+everything.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import quant_gemm_amd as mq
+from blocks import q4k_pack, q6k_pack
+from quant_gemm_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-4
+
+
+def to_dev(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+
+def host(t):
+    import torch
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def gpu_plane(x_np):
+    q, d, s = mq.quantize_act(to_dev(x_np))
+    return q, d, s
+
+
+def check_close(got, ref, what):
+    ref = np.asarray(ref, dtype=np.float64)
+    got = np.asarray(got, dtype=np.float64)
+    assert got.shape == ref.shape, what
+    assert np.all(np.isfinite(got)), what
+    scale = np.abs(ref).max()
+    err = np.abs(got - ref).max()
+    assert err <= TOL * scale, f"{what}: max|d|={err:.3e} > {TOL}*{scale:.3e}"
+    return err / max(scale, 1e-300)
+
+
+def run_matmul(fmt, W_np, q, d, s, N, K, path=mq.MQ_PATH_AUTO):
+    W = to_dev(W_np.reshape(-1))
+    f = mq.matmul_q4k if fmt == "q4k" else mq.matmul_q6k
+    return f(W, q, d, s if fmt == "q4k" else None, N, K, path=path)
+
+
+def oracle_mm(fmt, W_np, q_np, d_np, N, K, tokens=None):
+    f = oracle.matmul_q4k if fmt == "q4k" else oracle.matmul_q6k
+    return f(W_np, q_np, d_np, N, K, tokens=tokens)
+
+
+# ---------------------------------------------------------------- quantizer
+
+_QSHAPES = [(8, 1024), (1, 3584), (3314, 3584), (1, 18944), (512, 18944), (3314, 18944), (7, 256)]
+
+
+@pytest.mark.parametrize("M,K", _QSHAPES)
+def test_quantizer_bit_exact(dev, M, K):
+    rng = np.random.default_rng(M * 7 + K)
+    x = synth.activations(rng, M, K, outliers=K >= 3584)
+    q, d, s = gpu_plane(x)
+    rq, rd, rs = oracle.quantize_act(x)
+    assert np.array_equal(host(q), rq)
+    assert np.array_equal(host(d).view(np.uint32), rd.view(np.uint32))
+    assert np.array_equal(host(s).view(np.uint32), rs.view(np.uint32))
+
+
+def test_quantizer_edge_values(dev):
+    rng = np.random.default_rng(5)
+    K = 512
+    x = rng.standard_normal((12, K)).astype(np.float32)
+    x[0] = 0.0                                          # all-zero rows
+    x[1, :32] = np.float32(127.0)
+    x[1, 32:64] = np.array([127.0] + [2.5, -2.5, 0.5, -0.5, 1.5, -1.5] * 5 + [126.5], np.float32)
+    x[2] *= np.float32(1e-30)                           # tiny amax
+    x[3] *= np.float32(1e-39)                           # subnormal inputs
+    x[4] *= np.float32(3e37)                            # near the top of the f32 range
+    x[5] = -x[6]                                        # sign symmetry
+    x[7] = 0.0
+    x[7, ::32] = np.float32(1e-45)                      # amax/127 underflows to 0
+    x[7, 64] = np.float32(2e-43)                        # amax/127 is a subnormal
+    x[8] = np.round(x[8] * 10) / 10                     # many ties after scaling
+    x[9, 5] = np.float32(-1000.0)                       # one outlier
+    q, d, s = gpu_plane(x)
+    rq, rd, rs = oracle.quantize_act(x)
+    assert np.array_equal(host(q), rq)
+    assert np.array_equal(host(d).view(np.uint32), rd.view(np.uint32))
+    assert np.array_equal(host(s).view(np.uint32), rs.view(np.uint32))
+
+
+def test_quantizer_strided_rows(dev):
+    """ldx > K, including a row stride that is not a multiple of 4 (scalar path)."""
+    import torch
+    rng = np.random.default_rng(6)
+    for ldx in (1024 + 4, 1024 + 3):
+        xw = rng.standard_normal((5, ldx)).astype(np.float32)
+        xt = to_dev(xw)[:, :1024]
+        assert xt.stride(0) == ldx
+        q, d, s = mq.quantize_act(xt)
+        rq, rd, rs = oracle.quantize_act(np.ascontiguousarray(xw[:, :1024]))
+        assert np.array_equal(host(q), rq)
+        assert np.array_equal(host(d), rd) and np.array_equal(host(s), rs)
+    del torch
+
+
+# ---------------------------------------------------------------- small shapes, full compare
+
+SMALL = [(1, 1, 256), (2, 7, 512), (3, 33, 256), (5, 129, 768), (8, 256, 1024),
+         (9, 31, 256), (31, 100, 512), (127, 129, 256), (129, 300, 1280), (200, 64, 2048)]
+
+
+@pytest.mark.parametrize("fmt", ["q4k", "q6k"])
+@pytest.mark.parametrize("M,N,K", SMALL)
+def test_small_shapes_all_paths(dev, fmt, M, N, K):
+    rng = np.random.default_rng(M * 10007 + N * 101 + K + (fmt == "q6k"))
+    W = synth.weights(fmt, rng, N, K)
+    x = synth.activations(rng, M, K, outliers=True)
+    q, d, s = gpu_plane(x)
+    rq, rd, _ = oracle.quantize_act(x)
+    ref = oracle_mm(fmt, W, rq, rd, N, K)
+    paths = [mq.MQ_PATH_AUTO, mq.MQ_PATH_GEMM]
+    if M <= mq.gemv_max_m():
+        paths.append(mq.MQ_PATH_GEMV)
+    for p in paths:
+        out = host(run_matmul(fmt, W, q, d, s, N, K, path=p))
+        check_close(out, ref, f"{fmt} M={M} N={N} K={K} path={p}")
+
+
+def test_config0_exact_workload(dev):
+    case = synth.CONFIGS[0][0]
+    W = case.make_weights()
+    x = case.make_activations()
+    q, d, s = gpu_plane(x)
+    rq, rd, _ = oracle.quantize_act(x)
+    ref = oracle.matmul_q4k(W, rq, rd, case.N, case.K)
+    for p in (mq.MQ_PATH_GEMV, mq.MQ_PATH_GEMM, mq.MQ_PATH_AUTO):
+        check_close(host(run_matmul("q4k", W, q, d, s, case.N, case.K, path=p)), ref, f"cfg0 path={p}")
+
+
+# ---------------------------------------------------------------- position probes
+
+@pytest.mark.parametrize("fmt", ["q4k", "q6k"])
+def test_one_hot_positions_gemm(dev, fmt):
+    """Row n holds one nonzero quant at position n; token t is 127 e_t.
+    out[t, n] != 0 exactly when t == n, for all 256 positions of a block."""
+    K = N = M = 256
+    rows = []
+    for p in range(256):
+        if fmt == "q4k":
+            qv = np.zeros(256, int)
+            qv[p] = 1 + p % 15
+            rows.append(q4k_pack(1.0, 0.0, [1] * 8, [0] * 8, qv))
+        else:
+            qv = np.full(256, 32)
+            qv[p] = 33 + p % 30
+            rows.append(q6k_pack(1.0, [1] * 16, qv))
+    W = np.stack(rows)
+    x = np.zeros((M, K), np.float32)
+    x[np.arange(256), np.arange(256)] = 127.0
+    q, d, s = gpu_plane(x)
+    out = host(run_matmul(fmt, W, q, d, s, N, K, path=mq.MQ_PATH_GEMM))
+    diag = np.diag(out).copy()
+    expect = 127.0 * (1 + np.arange(256) % 15) if fmt == "q4k" else 127.0 * (1 + np.arange(256) % 30)
+    assert np.array_equal(diag, expect)
+    off = out - np.diag(diag)
+    assert not off.any()
+
+
+@pytest.mark.parametrize("fmt", ["q4k", "q6k"])
+def test_one_hot_positions_gemv(dev, fmt):
+    K, N = 256, 256
+    rows = []
+    for p in range(256):
+        if fmt == "q4k":
+            qv = np.zeros(256, int)
+            qv[p] = 1 + p % 15
+            rows.append(q4k_pack(1.0, 0.0, [1] * 8, [0] * 8, qv))
+        else:
+            qv = np.full(256, 32)
+            qv[p] = 33 + p % 30
+            rows.append(q6k_pack(1.0, [1] * 16, qv))
+    W = np.stack(rows)
+    for t0 in range(0, 256, 8):
+        x = np.zeros((8, K), np.float32)
+        x[np.arange(8), t0 + np.arange(8)] = 127.0
+        q, d, s = gpu_plane(x)
+        out = host(run_matmul(fmt, W, q, d, s, N, K, path=mq.MQ_PATH_GEMV))
+        nz = np.argwhere(out != 0)
+        assert nz.tolist() == [[i, t0 + i] for i in range(8)]
+
+
+# ---------------------------------------------------------------- invariants
+
+def test_zero_quants_zero_dmin_give_zero(dev):
+    rng = np.random.default_rng(9)
+    N, K, M = 130, 512, 70
+    W = synth.q4k_weights(rng, N, K).reshape(N, K // 256, 144)
+    W[:, :, 16:] = 0
+    W[:, :, 2:4] = np.array([0.0], np.float16).view(np.uint8)
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    q, d, s = gpu_plane(x)
+    for p in (mq.MQ_PATH_GEMM, mq.MQ_PATH_AUTO):
+        assert not host(run_matmul("q4k", W.reshape(N, -1), q, d, s, N, K, path=p)).any()
+    q8, d8, s8 = gpu_plane(x[:8])
+    assert not host(run_matmul("q4k", W.reshape(N, -1), q8, d8, s8, N, K, path=mq.MQ_PATH_GEMV)).any()
+
+
+def test_determinism_and_streams(dev):
+    import torch
+    rng = np.random.default_rng(10)
+    N, K, M = 300, 1024, 200
+    W = synth.q4k_weights(rng, N, K)
+    x = synth.activations(rng, M, K, outliers=True)
+    q, d, s = gpu_plane(x)
+    Wd = to_dev(W.reshape(-1))
+    a = host(mq.matmul_q4k(Wd, q, d, s, N, K))
+    b = host(mq.matmul_q4k(Wd, q, d, s, N, K))
+    assert np.array_equal(a, b)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        c = mq.matmul_q4k(Wd, q, d, s, N, K, stream=side)
+    side.synchronize()
+    assert np.array_equal(a, c.cpu().numpy())
+
+
+def test_cross_path_rows(dev):
+    """Token rows computed alone (GEMV, M=1) agree with the same rows inside a large GEMM."""
+    rng = np.random.default_rng(11)
+    N, K, M = 500, 3584, 300
+    for fmt in ("q4k", "q6k"):
+        W = synth.weights(fmt, rng, N, K)
+        x = synth.activations(rng, M, K, outliers=True)
+        q, d, s = gpu_plane(x)
+        big = host(run_matmul(fmt, W, q, d, s, N, K))
+        rq, rd, _ = oracle.quantize_act(x)
+        for t in (0, 137, 299):
+            q1, d1, s1 = gpu_plane(x[t:t + 1])
+            one = host(run_matmul(fmt, W, q1, d1, s1, N, K))
+            ref = oracle_mm(fmt, W, rq, rd, N, K, tokens=np.array([t]))
+            check_close(one, ref, f"{fmt} single row {t}")
+            check_close(big[t:t + 1], ref, f"{fmt} row {t} of M={M}")
+
+
+# ---------------------------------------------------------------- full-size workloads
+
+_SAMPLE_TOKENS = [0, 1, 2, 63, 64, 127, 128, 129, 511, 1000, 2047, 2048, 3199, 3200, 3201, 3250, 3312, 3313]
+
+
+def _tokens_for(M):
+    t = sorted({x for x in _SAMPLE_TOKENS if x < M} | {M - 1})
+    return np.array(t, dtype=np.int64)
+
+
+@pytest.mark.parametrize("name", [c.name for _, c in synth.all_cases()])
+def test_full_size_workloads(dev, name):
+    case = synth.case_by_name(name)
+    print(f"[parity] {case.name} {case.fmt} M={case.M} N={case.N} K={case.K}", flush=True)
+    W = case.make_weights()
+    x = case.make_activations()
+    q, d, s = gpu_plane(x)
+    rq, rd, rs = oracle.quantize_act(x)
+    assert np.array_equal(host(q), rq) and np.array_equal(host(d), rd) and np.array_equal(host(s), rs)
+    out_t = run_matmul(case.fmt, W, q, d, s, case.N, case.K)
+    toks = None if case.M <= 8 else _tokens_for(case.M)
+    ref = oracle_mm(case.fmt, W, rq, rd, case.N, case.K, tokens=toks)
+    out = host(out_t)
+    got = out if toks is None else out[toks]
+    rel = check_close(got, ref, case.name)
+    print(f"[parity] {case.name}: max|d|/max|ref| = {rel:.2e}", flush=True)
