@@ -38,8 +38,8 @@ INT8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA, published
 ROTATE_BYTES = 1 << 30       # weight copies for HBM-bound kernels
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
-    "gemm_q4k": "quant_gemm_amd/csrc/gemm.hip",
-    "gemm_q6k": "quant_gemm_amd/csrc/gemm.hip",
+    "gemm_q4k": "quant_gemm_amd/csrc/gemm_q4k.hip",
+    "gemm_q6k": "quant_gemm_amd/csrc/gemm_q6k.hip",
     "gemv_q4k": "quant_gemm_amd/csrc/gemv.hip",
     "gemv_q6k": "quant_gemm_amd/csrc/gemv.hip",
     "quantize": "quant_gemm_amd/csrc/quantize.hip",

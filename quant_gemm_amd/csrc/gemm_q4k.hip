@@ -1,0 +1,316 @@
+// Prefill GEMM for Q4_K weights x per-32 int8 activations (gfx950).
+//
+// The pages' prefill runs an int8 tensor-core GEMM on the raw 4-bit quants
+// against the int8 activation plane, with the block scales applied after
+// each integer product (minfer Features, "GPU — CUDA": raw-nibble int8 GEMMs
+// for q4_K and q6_K). This is a CDNA4 design of that step.
+//
+// Tiling. A 256-thread workgroup computes 128 tokens x 128 weight rows as
+// 2 x 2 wavefronts of 64 x 64, each 2 x 2 MFMA tiles of 32 x 32. The K loop
+// moves in half super-blocks (128 values = 4 sub-blocks of 32).
+//
+// Staging. Each step's slice goes into one of two LDS buffers: the int8
+// activations and the weights' raw quant bytes (64 per row: one 16-byte
+// chunk holds positions 16h..16h+15 of two sub-blocks, as low and high
+// nibbles) by global->LDS DMA (no registers, no LDS store instructions); the
+// per-32 activation scales and sums and, per row and sub-block, the f32
+// factors d*sc and dmin*m decoded from the block header through registers.
+// The loads for step s+1 are issued before step s is computed and fill the
+// other buffer, so one barrier per step suffices.
+//
+// Arithmetic. Every 32-value sub-block is one v_mfma_i32_32x32x32_i8 (exact
+// int32 dot of the 4-bit quants with the int8 activations). The f32
+// epilogue then adds, per token t, row n and sub-block j,
+//     d_x[t,j] * (d*sc_j)[n] * I  -  s_x[t,j] * (dmin*m_j)[n]
+// (the min term uses the activation block sums). On gfx950 this epilogue, not
+// the MFMA, bounds the kernel: 4 VALU operations per token, row and
+// sub-block against 32 int8 MACs.
+//
+// MFMA operand layout (32x32x32): lane l supplies row (l % 32) of A and
+// column (l % 32) of B, 16 consecutive K values from 16 * (l / 32) each;
+// both operands split K alike, so products pair up whatever order the
+// hardware uses within a lane. The result gives lane l column (l % 32) and
+// rows 8*(v/4) + 4*(l/32) + (v%4), v = 0..15. A = activations (rows =
+// tokens), B = weights (columns = output rows).
+#include "mq_device.h"
+#include "mq_launch.h"
+
+namespace mq {
+namespace {
+
+constexpr int BM = 128;          // tokens per tile
+constexpr int BN = 128;          // weight rows per tile
+constexpr int BK = 128;          // K values per step
+constexpr int NTHR = 256;
+constexpr int NWAVES = NTHR / 64;
+constexpr int A_CHUNKS = BM * BK / 16;      // 16-byte activation chunks per step
+constexpr int Q_CHUNKS = BN * BK / 2 / 16;  // 16-byte raw quant chunks per step
+
+// LDS layout of one step. The activation and quant tiles are filled by
+// global->LDS DMA, 64 lanes x 16 bytes per instruction into consecutive
+// slots, so they hold 16-byte chunks in a permuted order instead of padded
+// rows: chunk c of row r sits in slot  r*8 + (c ^ (r & 7))  (activations,
+// 8 chunks per row) or  r*4 + (c ^ ((r >> 2) & 3))  (quants, 4 per row).
+// Eight consecutive rows reading the same chunk then hit eight different
+// bank groups.
+struct Stage {
+    int8_t a[A_CHUNKS * 16];
+    uint8_t qs[Q_CHUNKS * 16];
+    float dx[BK / 32][BM];
+    float sx[BK / 32][BM];
+    float fw[BK / 32][BN];
+    float fm[BK / 32][BN];
+};
+
+__device__ __forceinline__ int a_slot(int r, int c) { return r * 8 + (c ^ (r & 7)); }
+__device__ __forceinline__ int q_slot(int r, int c) { return r * 4 + (c ^ ((r >> 2) & 3)); }
+
+// One 16-byte global->LDS DMA per lane: lane L's chunk lands at LDS byte
+// address lds_base + 16 * L (lds_base wave-uniform). Issued as inline asm so
+// that the compiler does not serialize the LDS reads of the other buffer
+// behind it; completion is awaited explicitly (wait_dma) before the barrier
+// that publishes the buffer.
+__device__ __forceinline__ void dma16(const void *src, const void *lds_dst)
+{
+    const uint32_t base = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)lds_dst);
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(src), "s"(base)
+                 : "memory", "m0");
+}
+
+// Start the DMA of step st's activation and quant tiles into s. Rows past M
+// or N read the last valid row instead: their results are never stored.
+__device__ __forceinline__ void issue_tiles(Stage &s, const uint8_t *__restrict__ W,
+                                            const int8_t *__restrict__ q, int M, int N, int K,
+                                            int t0, int n0, int st, int wave, int lane)
+{
+    const int k0 = st * BK;
+    const int sb = st >> 1, hf = st & 1;
+    const int64_t rowb = (int64_t)(K >> 8) * 144;
+#pragma unroll
+    for (int ii = 0; ii < A_CHUNKS / 64 / NWAVES; ++ii) {
+        const int i = wave * (A_CHUNKS / 64 / NWAVES) + ii;
+        const int p = 64 * i + lane;
+        const int r = p >> 3;
+        const int c = (p & 7) ^ (r & 7);
+        const int t = min(t0 + r, M - 1);
+        dma16(q + (int64_t)t * K + k0 + 16 * c, s.a + 1024 * i);
+    }
+#pragma unroll
+    for (int ii = 0; ii < Q_CHUNKS / 64 / NWAVES; ++ii) {
+        const int i = wave * (Q_CHUNKS / 64 / NWAVES) + ii;
+        const int p = 64 * i + lane;
+        const int r = p >> 2;
+        const int c = (p & 3) ^ ((r >> 2) & 3);
+        const int n = min(n0 + r, N - 1);
+        dma16(W + (int64_t)n * rowb + (int64_t)sb * 144 + 16 + 64 * hf + 16 * c, s.qs + 1024 * i);
+    }
+}
+
+// The per-row block header and the per-token scales / sums of a step pass
+// through registers (they are decoded or transposed on the way into LDS).
+// Loads always read a valid row (clamped); rows past M or N are zeroed when
+// stored, so their contributions vanish.
+struct Side {
+    uint4 hdr;      // block header of row n0 + tid (tid < BN)
+    float4 ds;      // 4 scales (tid < BM) or 4 sums (tid >= BM) of token t0 + tid % BM
+};
+
+__device__ __forceinline__ void load_side(Side &p, const uint8_t *__restrict__ W,
+                                          const float *__restrict__ dx,
+                                          const float *__restrict__ sx, int M, int N, int K,
+                                          int t0, int n0, int st)
+{
+    const int tid = threadIdx.x;
+    const int k0 = st * BK;
+    const int64_t rowb = (int64_t)(K >> 8) * 144;
+    if (tid < BN) {
+        const int n = min(n0 + tid, N - 1);
+        p.hdr = *reinterpret_cast<const uint4 *>(W + (int64_t)n * rowb + (int64_t)(st >> 1) * 144);
+    }
+    const int t = min(t0 + (tid & (BM - 1)), M - 1);
+    const float *src = tid < BM ? dx : sx;
+    p.ds = *reinterpret_cast<const float4 *>(src + (int64_t)t * (K >> 5) + (k0 >> 5));
+}
+
+__device__ __forceinline__ void store_side(Stage &s, const Side &p, int st, int M, int N,
+                                           int t0, int n0)
+{
+    const int tid = threadIdx.x;
+    const int hf = st & 1;
+    const int row = tid & (BM - 1);
+    const bool tok = t0 + row < M;
+    float(*dst)[BM] = tid < BM ? s.dx : s.sx;
+    dst[0][row] = tok ? p.ds.x : 0.0f;
+    dst[1][row] = tok ? p.ds.y : 0.0f;
+    dst[2][row] = tok ? p.ds.z : 0.0f;
+    dst[3][row] = tok ? p.ds.w : 0.0f;
+    if (tid < BN) {
+        // header: f16 d | f16 dmin | 12 bytes of 6-bit codes. Codes j = 0..3
+        // are bytes 0..3 (scale) and 4..7 (min) masked to 6 bits; codes
+        // 4..7 take their low 4 bits from bytes 8..11 and their high 2 bits
+        // from the top of bytes 0..3 (scale) or 4..7 (min).
+        const uint4 h = n0 + tid < N ? p.hdr : make_uint4(0, 0, 0, 0);
+        const float dd = f16_bits_to_f32(h.x);
+        const float dm = f16_bits_to_f32(h.x >> 16);
+        const uint32_t scw = hf == 0 ? (h.y & 0x3f3f3f3fu)
+                                     : ((h.w & 0x0f0f0f0fu) | ((h.y >> 2) & 0x30303030u));
+        const uint32_t mw = hf == 0 ? (h.z & 0x3f3f3f3fu)
+                                    : (((h.w >> 4) & 0x0f0f0f0fu) | ((h.z >> 2) & 0x30303030u));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            s.fw[j][tid] = dd * (float)((scw >> (8 * j)) & 0xffu);
+            s.fm[j][tid] = dm * (float)((mw >> (8 * j)) & 0xffu);
+        }
+    }
+}
+
+__device__ __forceinline__ void compute_step(const Stage &s, v16f (&acc)[2][2], int wm, int wn,
+                                             int lr, int lh)
+{
+#pragma unroll 1
+    for (int cl = 0; cl < 2; ++cl) {
+        v4i raw[2];
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const int r = wn * 64 + b * 32 + lr;
+            raw[b] = *reinterpret_cast<const v4i *>(s.qs + 16 * q_slot(r, 2 * cl + lh));
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int j = 2 * cl + h;            // sub-block within the step
+            v4i bf[2], af[2];
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+                bf[b] = h ? ((raw[b] >> 4) & 0x0f0f0f0f) : (raw[b] & 0x0f0f0f0f);
+#pragma unroll
+            for (int a = 0; a < 2; ++a) {
+                const int r = wm * 64 + a * 32 + lr;
+                af[a] = *reinterpret_cast<const v4i *>(s.a + 16 * a_slot(r, 2 * j + lh));
+            }
+            v16i I[2][2];
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+#pragma unroll
+                for (int b = 0; b < 2; ++b)
+                    I[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[a], bf[b], v16i{}, 0, 0, 0);
+            float fw[2], fm[2];
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                fw[b] = s.fw[j][wn * 64 + b * 32 + lr];
+                fm[b] = -s.fm[j][wn * 64 + b * 32 + lr];
+            }
+#pragma unroll
+            for (int a = 0; a < 2; ++a) {
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int tl = wm * 64 + a * 32 + 8 * g4 + 4 * lh;
+                    const float4 d4 = *reinterpret_cast<const float4 *>(&s.dx[j][tl]);
+                    const float4 s4 = *reinterpret_cast<const float4 *>(&s.sx[j][tl]);
+                    const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+                    const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+                    for (int b = 0; b < 2; ++b) {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int v = 4 * g4 + r;
+                            const float t = fmaf((float)I[a][b][v], dv[r] * fw[b], acc[a][b][v]);
+                            acc[a][b][v] = fmaf(sv[r], fm[b], t);
+                        }
+                    }
+                }
+            }
+        }
+    }
+}
+
+__device__ __forceinline__ void wait_dma()
+{
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+__global__ __launch_bounds__(NTHR, 2) void gemm_q4k_kernel(
+    const uint8_t *__restrict__ W, const int8_t *__restrict__ q,
+    const float *__restrict__ dx, const float *__restrict__ sx, int M, int N,
+    int K, int tiles_m, float *__restrict__ out)
+{
+    __shared__ Stage S0, S1;
+    const int tile_m = blockIdx.x % tiles_m;
+    const int tile_n = blockIdx.x / tiles_m;
+    const int t0 = tile_m * BM;
+    const int n0 = tile_n * BN;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int wm = wave & 1, wn = wave >> 1;
+    const int lr = lane & 31, lh = lane >> 5;
+
+    v16f acc[2][2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                acc[a][b][v] = 0.0f;
+
+    // K / BK is even (K is a multiple of 256): steps alternate S0, S1.
+    const int nsteps = K / BK;
+    Side p;
+    issue_tiles(S0, W, q, M, N, K, t0, n0, 0, wave, lane);
+    load_side(p, W, dx, sx, M, N, K, t0, n0, 0);
+    wait_dma();
+    store_side(S0, p, 0, M, N, t0, n0);
+    __syncthreads();
+    for (int st = 0; st < nsteps; st += 2) {
+        issue_tiles(S1, W, q, M, N, K, t0, n0, st + 1, wave, lane);
+        load_side(p, W, dx, sx, M, N, K, t0, n0, st + 1);
+        compute_step(S0, acc, wm, wn, lr, lh);
+        wait_dma();
+        store_side(S1, p, st + 1, M, N, t0, n0);
+        __syncthreads();
+        const bool more = st + 2 < nsteps;
+        if (more) {
+            issue_tiles(S0, W, q, M, N, K, t0, n0, st + 2, wave, lane);
+            load_side(p, W, dx, sx, M, N, K, t0, n0, st + 2);
+        }
+        compute_step(S1, acc, wm, wn, lr, lh);
+        if (more) {
+            wait_dma();
+            store_side(S0, p, st + 2, M, N, t0, n0);
+        }
+        __syncthreads();
+    }
+
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const int n = n0 + wn * 64 + b * 32 + lr;
+            if (n < N) {
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int t = t0 + wm * 64 + a * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
+                    if (t < M)
+                        out[(int64_t)t * N + n] = acc[a][b][v];
+                }
+            }
+        }
+    }
+}
+
+} // namespace
+
+hipError_t launch_gemm_q4k(const uint8_t *W, const int8_t *q, const float *d,
+                           const float *s, int M, int N, int K, float *out,
+                           hipStream_t st)
+{
+    const int tiles_m = (M + BM - 1) / BM;
+    const int tiles_n = (N + BN - 1) / BN;
+    const int64_t grid = (int64_t)tiles_m * tiles_n;
+    gemm_q4k_kernel<<<dim3((unsigned)grid), dim3(NTHR), 0, st>>>(W, q, d, s, M, N, K, tiles_m, out);
+    return hipGetLastError();
+}
+
+} // namespace mq

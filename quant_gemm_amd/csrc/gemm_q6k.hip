@@ -1,4 +1,4 @@
-// Prefill GEMM for Q4_K / Q6_K weights x per-32 int8 activations (gfx950).
+// Prefill GEMM for Q6_K weights x per-32 int8 activations (gfx950).
 //
 // The pages' prefill runs an int8 tensor-core GEMM directly on the raw
 // 4-/6-bit quants against the int8 activation plane, with the block scales
@@ -353,13 +353,6 @@ hipError_t launch_gemm(const uint8_t *W, const int8_t *q, const float *d,
 }
 
 } // namespace
-
-hipError_t launch_gemm_q4k(const uint8_t *W, const int8_t *q, const float *d,
-                           const float *s, int M, int N, int K, float *out,
-                           hipStream_t st)
-{
-    return launch_gemm<false>(W, q, d, s, M, N, K, out, st);
-}
 
 hipError_t launch_gemm_q6k(const uint8_t *W, const int8_t *q, const float *d,
                            int M, int N, int K, float *out, hipStream_t st)
