@@ -6,8 +6,8 @@
 // for q4_K and q6_K). This is a CDNA4 design of that step.
 //
 // Tiling. A 256-thread workgroup computes 128 tokens x 128 weight rows as
-// 2 x 2 wavefronts of 64 x 64, each 2 x 2 MFMA tiles of 32 x 32. The K loop
-// moves in half super-blocks (128 values = 4 sub-blocks of 32).
+// 4 wavefronts of 32 tokens x 128 rows, each 1 x 4 MFMA tiles of 32 x 32.
+// The K loop moves in half super-blocks (128 values = 4 sub-blocks of 32).
 //
 // Staging. Each step's slice goes into one of two LDS buffers: the int8
 // activations and the weights' raw quant bytes (64 per row: one 16-byte
@@ -38,13 +38,30 @@
 namespace mq {
 namespace {
 
-constexpr int BM = 128;          // tokens per tile
-constexpr int BN = 128;          // weight rows per tile
-constexpr int BK = 128;          // K values per step
-constexpr int NTHR = 256;
-constexpr int NWAVES = NTHR / 64;
+// Workgroup tile: WM x WN wavefronts, each TM x TN MFMA tiles of 32 x 32.
+// One wavefront owns 32 tokens x 128 rows: each activation scale/sum read
+// from LDS then serves four row tiles (measured fastest on MI355X among
+// 64x64, 32x64 and 64x32 wave tiles).
+#ifndef MQ_Q4K_TM
+#define MQ_Q4K_TM 1
+#define MQ_Q4K_TN 4
+#define MQ_Q4K_WM 4
+#define MQ_Q4K_WN 1
+#define MQ_Q4K_OCC 2
+#endif
+constexpr int TM = MQ_Q4K_TM;             // 32-token tiles per wavefront
+constexpr int TN = MQ_Q4K_TN;             // 32-row tiles per wavefront
+constexpr int WM = MQ_Q4K_WM;             // wavefronts along tokens
+constexpr int WN = MQ_Q4K_WN;             // wavefronts along rows
+constexpr int BM = 32 * TM * WM;          // tokens per tile
+constexpr int BN = 32 * TN * WN;          // weight rows per tile
+constexpr int BK = 128;                   // K values per step
+constexpr int NWAVES = WM * WN;
+constexpr int NTHR = 64 * NWAVES;
 constexpr int A_CHUNKS = BM * BK / 16;      // 16-byte activation chunks per step
 constexpr int Q_CHUNKS = BN * BK / 2 / 16;  // 16-byte raw quant chunks per step
+static_assert(A_CHUNKS % (64 * NWAVES) == 0 && Q_CHUNKS % (64 * NWAVES) == 0, "DMA split");
+static_assert(NTHR >= 2 * BM && NTHR >= BN, "side loads need one thread per row");
 
 // LDS layout of one step. The activation and quant tiles are filled by
 // global->LDS DMA, 64 lanes x 16 bytes per instruction into consecutive
@@ -130,9 +147,11 @@ __device__ __forceinline__ void load_side(Side &p, const uint8_t *__restrict__ W
         const int n = min(n0 + tid, N - 1);
         p.hdr = *reinterpret_cast<const uint4 *>(W + (int64_t)n * rowb + (int64_t)(st >> 1) * 144);
     }
-    const int t = min(t0 + (tid & (BM - 1)), M - 1);
-    const float *src = tid < BM ? dx : sx;
-    p.ds = *reinterpret_cast<const float4 *>(src + (int64_t)t * (K >> 5) + (k0 >> 5));
+    if (tid < 2 * BM) {
+        const int t = min(t0 + (tid & (BM - 1)), M - 1);
+        const float *src = tid < BM ? dx : sx;
+        p.ds = *reinterpret_cast<const float4 *>(src + (int64_t)t * (K >> 5) + (k0 >> 5));
+    }
 }
 
 __device__ __forceinline__ void store_side(Stage &s, const Side &p, int st, int M, int N,
@@ -142,11 +161,13 @@ __device__ __forceinline__ void store_side(Stage &s, const Side &p, int st, int 
     const int hf = st & 1;
     const int row = tid & (BM - 1);
     const bool tok = t0 + row < M;
-    float(*dst)[BM] = tid < BM ? s.dx : s.sx;
-    dst[0][row] = tok ? p.ds.x : 0.0f;
-    dst[1][row] = tok ? p.ds.y : 0.0f;
-    dst[2][row] = tok ? p.ds.z : 0.0f;
-    dst[3][row] = tok ? p.ds.w : 0.0f;
+    if (tid < 2 * BM) {
+        float(*dst)[BM] = tid < BM ? s.dx : s.sx;
+        dst[0][row] = tok ? p.ds.x : 0.0f;
+        dst[1][row] = tok ? p.ds.y : 0.0f;
+        dst[2][row] = tok ? p.ds.z : 0.0f;
+        dst[3][row] = tok ? p.ds.w : 0.0f;
+    }
     if (tid < BN) {
         // header: f16 d | f16 dmin | 12 bytes of 6-bit codes. Codes j = 0..3
         // are bytes 0..3 (scale) and 4..7 (min) masked to 6 bits; codes
@@ -167,52 +188,52 @@ __device__ __forceinline__ void store_side(Stage &s, const Side &p, int st, int 
     }
 }
 
-__device__ __forceinline__ void compute_step(const Stage &s, v16f (&acc)[2][2], int wm, int wn,
+__device__ __forceinline__ void compute_step(const Stage &s, v16f (&acc)[TM][TN], int wm, int wn,
                                              int lr, int lh)
 {
 #pragma unroll 1
     for (int cl = 0; cl < 2; ++cl) {
-        v4i raw[2];
+        v4i raw[TN];
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            const int r = wn * 64 + b * 32 + lr;
+        for (int b = 0; b < TN; ++b) {
+            const int r = (wn * TN + b) * 32 + lr;
             raw[b] = *reinterpret_cast<const v4i *>(s.qs + 16 * q_slot(r, 2 * cl + lh));
         }
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int j = 2 * cl + h;            // sub-block within the step
-            v4i bf[2], af[2];
+            v4i bf[TN], af[TM];
 #pragma unroll
-            for (int b = 0; b < 2; ++b)
+            for (int b = 0; b < TN; ++b)
                 bf[b] = h ? ((raw[b] >> 4) & 0x0f0f0f0f) : (raw[b] & 0x0f0f0f0f);
 #pragma unroll
-            for (int a = 0; a < 2; ++a) {
-                const int r = wm * 64 + a * 32 + lr;
+            for (int a = 0; a < TM; ++a) {
+                const int r = (wm * TM + a) * 32 + lr;
                 af[a] = *reinterpret_cast<const v4i *>(s.a + 16 * a_slot(r, 2 * j + lh));
             }
-            v16i I[2][2];
+            v16i I[TM][TN];
 #pragma unroll
-            for (int a = 0; a < 2; ++a)
+            for (int a = 0; a < TM; ++a)
 #pragma unroll
-                for (int b = 0; b < 2; ++b)
+                for (int b = 0; b < TN; ++b)
                     I[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[a], bf[b], v16i{}, 0, 0, 0);
-            float fw[2], fm[2];
+            float fw[TN], fm[TN];
 #pragma unroll
-            for (int b = 0; b < 2; ++b) {
-                fw[b] = s.fw[j][wn * 64 + b * 32 + lr];
-                fm[b] = -s.fm[j][wn * 64 + b * 32 + lr];
+            for (int b = 0; b < TN; ++b) {
+                fw[b] = s.fw[j][(wn * TN + b) * 32 + lr];
+                fm[b] = -s.fm[j][(wn * TN + b) * 32 + lr];
             }
 #pragma unroll
-            for (int a = 0; a < 2; ++a) {
+            for (int a = 0; a < TM; ++a) {
 #pragma unroll
                 for (int g4 = 0; g4 < 4; ++g4) {
-                    const int tl = wm * 64 + a * 32 + 8 * g4 + 4 * lh;
+                    const int tl = (wm * TM + a) * 32 + 8 * g4 + 4 * lh;
                     const float4 d4 = *reinterpret_cast<const float4 *>(&s.dx[j][tl]);
                     const float4 s4 = *reinterpret_cast<const float4 *>(&s.sx[j][tl]);
                     const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
                     const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
 #pragma unroll
-                    for (int b = 0; b < 2; ++b) {
+                    for (int b = 0; b < TN; ++b) {
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
                             const int v = 4 * g4 + r;
@@ -231,7 +252,7 @@ __device__ __forceinline__ void wait_dma()
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-__global__ __launch_bounds__(NTHR, 2) void gemm_q4k_kernel(
+__global__ __launch_bounds__(NTHR, MQ_Q4K_OCC) void gemm_q4k_kernel(
     const uint8_t *__restrict__ W, const int8_t *__restrict__ q,
     const float *__restrict__ dx, const float *__restrict__ sx, int M, int N,
     int K, int tiles_m, float *__restrict__ out)
@@ -243,14 +264,14 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_q4k_kernel(
     const int n0 = tile_n * BN;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int wm = wave & 1, wn = wave >> 1;
+    const int wm = wave % WM, wn = wave / WM;
     const int lr = lane & 31, lh = lane >> 5;
 
-    v16f acc[2][2];
+    v16f acc[TM][TN];
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int a = 0; a < TM; ++a)
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+        for (int b = 0; b < TN; ++b)
 #pragma unroll
             for (int v = 0; v < 16; ++v)
                 acc[a][b][v] = 0.0f;
@@ -284,14 +305,14 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_q4k_kernel(
     }
 
 #pragma unroll
-    for (int a = 0; a < 2; ++a) {
+    for (int a = 0; a < TM; ++a) {
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            const int n = n0 + wn * 64 + b * 32 + lr;
+        for (int b = 0; b < TN; ++b) {
+            const int n = n0 + (wn * TN + b) * 32 + lr;
             if (n < N) {
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
-                    const int t = t0 + wm * 64 + a * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
+                    const int t = t0 + (wm * TM + a) * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
                     if (t < M)
                         out[(int64_t)t * N + n] = acc[a][b][v];
                 }

@@ -23,26 +23,86 @@ namespace mq {
 namespace {
 
 constexpr int GEMV_WAVES = 4;   // wavefronts per workgroup
+#ifndef GEMV_STREAM_WGS
+#define GEMV_STREAM_WGS 1024        // workgroups of the persistent stream kernel
+#define GEMV_STREAM_D 2             // rows in flight per wavefront
+#endif
 
 // ---------------------------------------------------------------- Q4_K
-// Row slice owned by one lane: one 16-byte chunk c (0..7) of a block's 128
-// quant bytes. Chunk c covers positions po..po+15 (po = 16*(c&1)) of the
-// sub-blocks j0 = 2*(c>>1) (low nibbles) and j0+1 (high nibbles).
-template <int MT, int R>
+// The R rows of a wavefront are consecutive, so their blocks form one
+// contiguous byte range of R * K/256 * 144 bytes. The wavefront streams it
+// as 16-byte chunks, 7 blocks (63 lanes) per pass: lane 9s + p holds chunk p
+// of block s of the pass. Chunk 0 is the block header (d, dmin, 6-bit
+// codes); chunk p = 1..8 holds quant bytes 16(p-1)..16(p-1)+15, i.e.
+// positions po..po+15 (po = 16*((p-1)&1)) of sub-blocks j0 = 2*((p-1)>>1)
+// (low nibbles) and j0+1 (high nibbles). The header reaches the other eight
+// lanes of its block through ds_bpermute. Every load of a lane is issued
+// before any of its arithmetic, so a wavefront waits on memory once.
+//
+// With ACT_LDS the workgroup first copies the whole activation plane
+// (M x K int8 plus the per-32 scales and sums, at most GEMV_ACT_LDS bytes)
+// into LDS; the loads for it are issued before the weight loads, so the copy
+// overlaps the weight stream, and the dot products then read activations
+// from LDS instead of making one cache round trip per pass.
+constexpr int GEMV_ACT_LDS = 16 * 1024;
+
+// Copy the activation plane (q, then d, then s: M*K + 2*M*K/8 bytes, a
+// multiple of 16) into LDS. Loads are issued here; the stores wait for them.
+struct ActCopy {
+    static constexpr int MAXC = GEMV_ACT_LDS / 16 / (64 * GEMV_WAVES);  // chunks per thread
+    v4i v[MAXC];
+};
+
+__device__ __forceinline__ void act_load(ActCopy &c, const int8_t *q, const float *d,
+                                         const float *s, int M, int K)
+{
+    const int qchunks = M * K / 16, dchunks = M * K / 128;
+#pragma unroll
+    for (int i = 0; i < ActCopy::MAXC; ++i) {
+        const int ch = threadIdx.x + i * 64 * GEMV_WAVES;
+        const v4i *src;
+        if (ch < qchunks)
+            src = reinterpret_cast<const v4i *>(q) + ch;
+        else if (ch < qchunks + dchunks)
+            src = reinterpret_cast<const v4i *>(d) + (ch - qchunks);
+        else
+            src = reinterpret_cast<const v4i *>(s) + min(ch - qchunks - dchunks, dchunks - 1);
+        c.v[i] = ch < qchunks + 2 * dchunks ? *src : v4i{0, 0, 0, 0};
+    }
+}
+
+__device__ __forceinline__ void act_store(const ActCopy &c, v4i *lds, int M, int K)
+{
+    const int nchunks = M * K / 16 + 2 * (M * K / 128);
+#pragma unroll
+    for (int i = 0; i < ActCopy::MAXC; ++i) {
+        const int ch = threadIdx.x + i * 64 * GEMV_WAVES;
+        if (ch < nchunks)
+            lds[ch] = c.v[i];
+    }
+}
+
+template <int MT, int R, int IT, bool ACT_LDS>
 __global__ __launch_bounds__(64 * GEMV_WAVES) void gemv_q4k_kernel(
     const uint8_t *__restrict__ W, const int8_t *__restrict__ q,
     const float *__restrict__ dx, const float *__restrict__ sx, int M, int N,
     int K, float *__restrict__ out)
 {
+    __shared__ v4i act[ACT_LDS ? GEMV_ACT_LDS / 16 : 1];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int row0 = (blockIdx.x * GEMV_WAVES + wave) * R;
-    if (row0 >= N)
-        return;
-    const int nsb = K >> 8;
-    const int nch = nsb * 8;
+    ActCopy ac;
+    if constexpr (ACT_LDS)
+        act_load(ac, q, dx, sx, M, K);
+    const int nb = K >> 8;                       // blocks per row
     const int nb32 = K >> 5;
-    const int64_t rowb = (int64_t)nsb * 144;
+    const int rows = max(0, min(R, N - row0));  // 0 for a wavefront past the last row
+    const int total = rows * nb;                 // blocks of this wavefront
+    const int slot = lane / 9;                   // block within a pass (7 = idle lane)
+    const int part = lane - 9 * slot;            // chunk within the block
+    const int hdr_lane = 9 * slot;
+    const uint8_t *base = W + (int64_t)row0 * nb * 144;
 
     float acc[R][MT];
 #pragma unroll
@@ -51,75 +111,86 @@ __global__ __launch_bounds__(64 * GEMV_WAVES) void gemv_q4k_kernel(
         for (int m = 0; m < MT; ++m)
             acc[r][m] = 0.0f;
 
-    for (int ch = lane; ch < nch; ch += 64) {
-        const int blk = ch >> 3;
-        const int c = ch & 7;
-        const int cc = c >> 1;
-        const int po = (c & 1) << 4;
-        const int k0 = (blk << 8) + (cc << 6) + po;     // sub-block j0, positions po..
-        const int b0 = (blk << 3) + (cc << 1);          // its 32-block index
-        // activation slices (shared by all R rows)
-        v4i xa[MT], xb[MT];
-        float da[MT], db[MT], sa[MT], sb[MT];
+    // this lane's (row, block) position, advanced by 7 blocks per pass
+    int rl = 0, blk = slot;
+    while (blk >= nb) { blk -= nb; ++rl; }
+
+    const int8_t *qa = q;                        // activation sources: global or LDS
+    const float *da = dx, *sa = sx;
+    if constexpr (ACT_LDS) {
+        qa = reinterpret_cast<const int8_t *>(act);
+        da = reinterpret_cast<const float *>(qa + M * K);
+        sa = da + M * nb32;
+    }
+    for (int it0 = 0; it0 < max(total, 1); it0 += 7 * IT) {
+        v4i v[IT];
 #pragma unroll
-        for (int m = 0; m < MT; ++m) {
-            if (m < M) {
-                xa[m] = *reinterpret_cast<const v4i *>(q + (int64_t)m * K + k0);
-                xb[m] = *reinterpret_cast<const v4i *>(q + (int64_t)m * K + k0 + 32);
-                da[m] = dx[(int64_t)m * nb32 + b0];
-                db[m] = dx[(int64_t)m * nb32 + b0 + 1];
-                sa[m] = sx[(int64_t)m * nb32 + b0];
-                sb[m] = sx[(int64_t)m * nb32 + b0 + 1];
-            } else {
-                xa[m] = xb[m] = v4i{0, 0, 0, 0};
-                da[m] = db[m] = sa[m] = sb[m] = 0.0f;
-            }
+        for (int i = 0; i < IT; ++i) {
+            const int fb = it0 + 7 * i + slot;
+            v[i] = (slot < 7 && fb < total)
+                       ? __builtin_nontemporal_load(reinterpret_cast<const v4i *>(base + (int64_t)fb * 144 + 16 * part))
+                       : v4i{0, 0, 0, 0};
         }
-        const float minw = po == 0 ? 1.0f : 0.0f;   // one of the two lanes adds the min term
+        if (ACT_LDS && it0 == 0) {
+            act_store(ac, act, M, K);
+            __syncthreads();
+        }
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const int n = row0 + r;
-            if (n < N) {
-                const uint8_t *bp = W + (int64_t)n * rowb + (int64_t)blk * 144;
-                const uint4 hdr = *reinterpret_cast<const uint4 *>(bp);
-                const uint4 qw = *reinterpret_cast<const uint4 *>(bp + 16 + 16 * c);
-                const float dd = f16_bits_to_f32(hdr.x);
-                const float dm = f16_bits_to_f32(hdr.x >> 16);
-                // 6-bit codes: bytes 0..3 of sc_lo/m_lo are j = 0..3, of
-                // sc_hi/m_hi j = 4..7.
-                const uint32_t sc_lo = hdr.y & 0x3f3f3f3fu;
-                const uint32_t m_lo = hdr.z & 0x3f3f3f3fu;
-                const uint32_t sc_hi = (hdr.w & 0x0f0f0f0fu) | ((hdr.y >> 2) & 0x30303030u);
-                const uint32_t m_hi = ((hdr.w >> 4) & 0x0f0f0f0fu) | ((hdr.z >> 2) & 0x30303030u);
-                const uint32_t scw = cc < 2 ? sc_lo : sc_hi;
-                const uint32_t mw = cc < 2 ? m_lo : m_hi;
-                const int sh = (cc & 1) << 4;               // byte 2*(cc&1)
+        for (int i = 0; i < IT; ++i) {
+            const int fb = it0 + 7 * i + slot;
+            // block header from lane 9*slot
+            const uint32_t h0 = __builtin_amdgcn_ds_bpermute(4 * hdr_lane, v[i].x);
+            const uint32_t h1 = __builtin_amdgcn_ds_bpermute(4 * hdr_lane, v[i].y);
+            const uint32_t h2 = __builtin_amdgcn_ds_bpermute(4 * hdr_lane, v[i].z);
+            const uint32_t h3 = __builtin_amdgcn_ds_bpermute(4 * hdr_lane, v[i].w);
+            if (slot < 7 && fb < total && part > 0) {
+                const int c = part - 1;
+                const int cc = c >> 1;
+                const int po = (c & 1) << 4;
+                const int k0 = (blk << 8) + (cc << 6) + po;   // sub-block j0, positions po..
+                const int b0 = (blk << 3) + (cc << 1);        // its 32-block index
+                const float dd = f16_bits_to_f32(h0);
+                const float dm = f16_bits_to_f32(h0 >> 16);
+                const uint32_t scw = cc < 2 ? (h1 & 0x3f3f3f3fu)
+                                            : ((h3 & 0x0f0f0f0fu) | ((h1 >> 2) & 0x30303030u));
+                const uint32_t mw = cc < 2 ? (h2 & 0x3f3f3f3fu)
+                                           : (((h3 >> 4) & 0x0f0f0f0fu) | ((h2 >> 2) & 0x30303030u));
+                const int sh = (cc & 1) << 4;
                 const float f0 = dd * (float)((scw >> sh) & 0xffu);
                 const float f1 = dd * (float)((scw >> (sh + 8)) & 0xffu);
-                const float g0 = dm * (float)((mw >> sh) & 0xffu);
-                const float g1 = dm * (float)((mw >> (sh + 8)) & 0xffu);
-                const int lo0 = qw.x & 0x0f0f0f0f, lo1 = qw.y & 0x0f0f0f0f;
-                const int lo2 = qw.z & 0x0f0f0f0f, lo3 = qw.w & 0x0f0f0f0f;
-                const int hi0 = (qw.x >> 4) & 0x0f0f0f0f, hi1 = (qw.y >> 4) & 0x0f0f0f0f;
-                const int hi2 = (qw.z >> 4) & 0x0f0f0f0f, hi3 = (qw.w >> 4) & 0x0f0f0f0f;
+                const float g0 = po == 0 ? dm * (float)((mw >> sh) & 0xffu) : 0.0f;
+                const float g1 = po == 0 ? dm * (float)((mw >> (sh + 8)) & 0xffu) : 0.0f;
+                const int lo0 = v[i].x & 0x0f0f0f0f, lo1 = v[i].y & 0x0f0f0f0f;
+                const int lo2 = v[i].z & 0x0f0f0f0f, lo3 = v[i].w & 0x0f0f0f0f;
+                const int hi0 = (v[i].x >> 4) & 0x0f0f0f0f, hi1 = (v[i].y >> 4) & 0x0f0f0f0f;
+                const int hi2 = (v[i].z >> 4) & 0x0f0f0f0f, hi3 = (v[i].w >> 4) & 0x0f0f0f0f;
 #pragma unroll
                 for (int m = 0; m < MT; ++m) {
-                    int i0 = dot4(lo0, xa[m].x, 0);
-                    i0 = dot4(lo1, xa[m].y, i0);
-                    i0 = dot4(lo2, xa[m].z, i0);
-                    i0 = dot4(lo3, xa[m].w, i0);
-                    int i1 = dot4(hi0, xb[m].x, 0);
-                    i1 = dot4(hi1, xb[m].y, i1);
-                    i1 = dot4(hi2, xb[m].z, i1);
-                    i1 = dot4(hi3, xb[m].w, i1);
-                    float a = acc[r][m];
-                    a = fmaf((float)i0, da[m] * f0, a);
-                    a = fmaf((float)i1, db[m] * f1, a);
-                    a = fmaf(-minw * g0, sa[m], a);
-                    a = fmaf(-minw * g1, sb[m], a);
-                    acc[r][m] = a;
+                    if (m < M) {
+                        const v4i xa = *reinterpret_cast<const v4i *>(qa + (int64_t)m * K + k0);
+                        const v4i xb = *reinterpret_cast<const v4i *>(qa + (int64_t)m * K + k0 + 32);
+                        const float2 dpair = *reinterpret_cast<const float2 *>(da + (int64_t)m * nb32 + b0);
+                        const float2 spair = *reinterpret_cast<const float2 *>(sa + (int64_t)m * nb32 + b0);
+                        int i0 = dot4(lo0, xa.x, 0);
+                        i0 = dot4(lo1, xa.y, i0);
+                        i0 = dot4(lo2, xa.z, i0);
+                        i0 = dot4(lo3, xa.w, i0);
+                        int i1 = dot4(hi0, xb.x, 0);
+                        i1 = dot4(hi1, xb.y, i1);
+                        i1 = dot4(hi2, xb.z, i1);
+                        i1 = dot4(hi3, xb.w, i1);
+                        float contrib = (float)i0 * (dpair.x * f0);
+                        contrib = fmaf((float)i1, dpair.y * f1, contrib);
+                        contrib = fmaf(-g0, spair.x, contrib);
+                        contrib = fmaf(-g1, spair.y, contrib);
+#pragma unroll
+                        for (int r = 0; r < R; ++r)
+                            acc[r][m] += rl == r ? contrib : 0.0f;
+                    }
                 }
             }
+            blk += 7;
+            while (blk >= nb) { blk -= nb; ++rl; }
         }
     }
 #pragma unroll
@@ -127,9 +198,143 @@ __global__ __launch_bounds__(64 * GEMV_WAVES) void gemv_q4k_kernel(
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
             const float v = wave_sum(acc[r][m]);
-            const int n = row0 + r;
-            if (lane == 0 && m < M && n < N)
-                out[(int64_t)m * N + n] = v;
+            if (lane == 0 && m < M && r < rows)
+                out[(int64_t)m * N + row0 + r] = v;
+        }
+    }
+}
+
+// Persistent, software-pipelined form of the same stream for short rows
+// (K <= NP * 7 * 256). A fixed grid of wavefronts walks the rows
+// n = w, w + NW, w + 2 NW, ... (NW wavefronts in all, so neighbouring
+// wavefronts read neighbouring rows). Each row is NP passes of 7 blocks; the
+// loads of the next D rows stay in flight while a row is reduced across the
+// wavefront and stored. Loads always use a valid address (the last row or
+// block) and are masked afterwards, so every wavefront issues the same
+// number of loads per row and the waits stay exact.
+template <int MT, int NP, int D>
+__global__ __launch_bounds__(64 * GEMV_WAVES) void gemv_q4k_stream_kernel(
+    const uint8_t *__restrict__ W, const int8_t *__restrict__ q,
+    const float *__restrict__ dx, const float *__restrict__ sx, int M, int N,
+    int K, float *__restrict__ out)
+{
+    __shared__ v4i act[GEMV_ACT_LDS / 16];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int nw = gridDim.x * GEMV_WAVES;
+    const int w = blockIdx.x * GEMV_WAVES + wave;
+    ActCopy ac;
+    act_load(ac, q, dx, sx, M, K);
+
+    const int nb = K >> 8;
+    const int nb32 = K >> 5;
+    const int64_t rowb = (int64_t)nb * 144;
+    const int slot = lane / 9;
+    const int part = lane - 9 * slot;
+    const int hdr_lane = 9 * slot;
+    const int nrows = w < N ? (N - 1 - w) / nw + 1 : 0;   // rows of this wavefront
+
+    // per pass p this lane owns block 7p + slot of the row
+    bool valid[NP];
+    int boff[NP];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        const int blk = 7 * p + slot;
+        valid[p] = slot < 7 && blk < nb;
+        boff[p] = min(blk, nb - 1) * 144 + 16 * part;
+    }
+
+    v4i ring[D][NP];
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+        const int n = min(w + d * nw, N - 1);
+#pragma unroll
+        for (int p = 0; p < NP; ++p)
+            ring[d][p] = __builtin_nontemporal_load(reinterpret_cast<const v4i *>(W + (int64_t)n * rowb + boff[p]));
+    }
+    act_store(ac, act, M, K);
+    __syncthreads();
+    const int8_t *qa = reinterpret_cast<const int8_t *>(act);
+    const float *da = reinterpret_cast<const float *>(qa + M * K);
+    const float *sa = da + M * nb32;
+
+    for (int i0 = 0; i0 < nrows; i0 += D) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            const int i = i0 + d;
+            if (i < nrows) {
+                float acc[MT];
+#pragma unroll
+                for (int m = 0; m < MT; ++m)
+                    acc[m] = 0.0f;
+#pragma unroll
+                for (int p = 0; p < NP; ++p) {
+                    const v4i v = ring[d][p];
+                    const uint32_t h0 = __builtin_amdgcn_ds_bpermute(4 * hdr_lane, v.x);
+                    const uint32_t h1 = __builtin_amdgcn_ds_bpermute(4 * hdr_lane, v.y);
+                    const uint32_t h2 = __builtin_amdgcn_ds_bpermute(4 * hdr_lane, v.z);
+                    const uint32_t h3 = __builtin_amdgcn_ds_bpermute(4 * hdr_lane, v.w);
+                    if (valid[p] && part > 0) {
+                        const int blk = 7 * p + slot;
+                        const int c = part - 1;
+                        const int cc = c >> 1;
+                        const int po = (c & 1) << 4;
+                        const int k0 = (blk << 8) + (cc << 6) + po;
+                        const int b0 = (blk << 3) + (cc << 1);
+                        const float dd = f16_bits_to_f32(h0);
+                        const float dm = f16_bits_to_f32(h0 >> 16);
+                        const uint32_t scw = cc < 2 ? (h1 & 0x3f3f3f3fu)
+                                                    : ((h3 & 0x0f0f0f0fu) | ((h1 >> 2) & 0x30303030u));
+                        const uint32_t mw = cc < 2 ? (h2 & 0x3f3f3f3fu)
+                                                   : (((h3 >> 4) & 0x0f0f0f0fu) | ((h2 >> 2) & 0x30303030u));
+                        const int sh = (cc & 1) << 4;
+                        const float f0 = dd * (float)((scw >> sh) & 0xffu);
+                        const float f1 = dd * (float)((scw >> (sh + 8)) & 0xffu);
+                        const float g0 = po == 0 ? dm * (float)((mw >> sh) & 0xffu) : 0.0f;
+                        const float g1 = po == 0 ? dm * (float)((mw >> (sh + 8)) & 0xffu) : 0.0f;
+                        const int lo0 = v.x & 0x0f0f0f0f, lo1 = v.y & 0x0f0f0f0f;
+                        const int lo2 = v.z & 0x0f0f0f0f, lo3 = v.w & 0x0f0f0f0f;
+                        const int hi0 = (v.x >> 4) & 0x0f0f0f0f, hi1 = (v.y >> 4) & 0x0f0f0f0f;
+                        const int hi2 = (v.z >> 4) & 0x0f0f0f0f, hi3 = (v.w >> 4) & 0x0f0f0f0f;
+#pragma unroll
+                        for (int m = 0; m < MT; ++m) {
+                            if (m < M) {
+                                const v4i xa = *reinterpret_cast<const v4i *>(qa + m * K + k0);
+                                const v4i xb = *reinterpret_cast<const v4i *>(qa + m * K + k0 + 32);
+                                const float2 dp = *reinterpret_cast<const float2 *>(da + m * nb32 + b0);
+                                const float2 sp = *reinterpret_cast<const float2 *>(sa + m * nb32 + b0);
+                                int i0v = dot4(lo0, xa.x, 0);
+                                i0v = dot4(lo1, xa.y, i0v);
+                                i0v = dot4(lo2, xa.z, i0v);
+                                i0v = dot4(lo3, xa.w, i0v);
+                                int i1v = dot4(hi0, xb.x, 0);
+                                i1v = dot4(hi1, xb.y, i1v);
+                                i1v = dot4(hi2, xb.z, i1v);
+                                i1v = dot4(hi3, xb.w, i1v);
+                                float a = fmaf((float)i0v, dp.x * f0, acc[m]);
+                                a = fmaf((float)i1v, dp.y * f1, a);
+                                a = fmaf(-g0, sp.x, a);
+                                acc[m] = fmaf(-g1, sp.y, a);
+                            }
+                        }
+                    }
+                }
+                // refill this ring slot with the row D ahead
+                {
+                    const int n = min(w + (i + D) * nw, N - 1);
+#pragma unroll
+                    for (int p = 0; p < NP; ++p)
+                        ring[d][p] = __builtin_nontemporal_load(
+                            reinterpret_cast<const v4i *>(W + (int64_t)n * rowb + boff[p]));
+                }
+                const int n = w + i * nw;
+#pragma unroll
+                for (int m = 0; m < MT; ++m) {
+                    const float v = wave_sum(acc[m]);
+                    if (lane == 0 && m < M)
+                        out[(int64_t)m * N + n] = v;
+                }
+            }
         }
     }
 }
@@ -252,10 +457,25 @@ hipError_t gemv_q4k_mt(const uint8_t *W, const int8_t *q, const float *d,
                        const float *s, int M, int N, int K, float *out,
                        hipStream_t st)
 {
-    constexpr int R = MT <= 2 ? 4 : 2;
+    constexpr int R = MT <= 2 ? 4 : 2;           // rows per wavefront
+    constexpr int IT = 8;                        // passes (of 7 blocks) in flight
     const int rows_per_wg = GEMV_WAVES * R;
     const int grid = (N + rows_per_wg - 1) / rows_per_wg;
-    gemv_q4k_kernel<MT, R><<<dim3(grid), dim3(64 * GEMV_WAVES), 0, st>>>(W, q, d, s, M, N, K, out);
+    const bool act_lds = (int64_t)M * K * 5 / 4 <= GEMV_ACT_LDS;
+    if (act_lds)
+        gemv_q4k_kernel<MT, R, IT, true><<<dim3(grid), dim3(64 * GEMV_WAVES), 0, st>>>(W, q, d, s, M, N, K, out);
+    else
+        gemv_q4k_kernel<MT, R, IT, false><<<dim3(grid), dim3(64 * GEMV_WAVES), 0, st>>>(W, q, d, s, M, N, K, out);
+    return hipGetLastError();
+}
+
+template <int MT, int R>
+hipError_t gemv_q6k_launch(const uint8_t *W, const int8_t *q, const float *d,
+                           int M, int N, int K, float *out, hipStream_t st)
+{
+    const int rows_per_wg = GEMV_WAVES * R;
+    const int grid = (N + rows_per_wg - 1) / rows_per_wg;
+    gemv_q6k_kernel<MT, R><<<dim3(grid), dim3(64 * GEMV_WAVES), 0, st>>>(W, q, d, M, N, K, out);
     return hipGetLastError();
 }
 
@@ -263,11 +483,10 @@ template <int MT>
 hipError_t gemv_q6k_mt(const uint8_t *W, const int8_t *q, const float *d,
                        int M, int N, int K, float *out, hipStream_t st)
 {
-    constexpr int R = MT <= 2 ? 4 : 2;
-    const int rows_per_wg = GEMV_WAVES * R;
-    const int grid = (N + rows_per_wg - 1) / rows_per_wg;
-    gemv_q6k_kernel<MT, R><<<dim3(grid), dim3(64 * GEMV_WAVES), 0, st>>>(W, q, d, M, N, K, out);
-    return hipGetLastError();
+    // long rows: one row per wavefront keeps enough wavefronts in flight
+    if (K >= 8192)
+        return gemv_q6k_launch<MT, 1>(W, q, d, M, N, K, out, st);
+    return gemv_q6k_launch<MT, MT <= 2 ? 4 : 2>(W, q, d, M, N, K, out, st);
 }
 
 } // namespace
@@ -276,6 +495,15 @@ hipError_t launch_gemv_q4k(const uint8_t *W, const int8_t *q, const float *d,
                            const float *s, int M, int N, int K, float *out,
                            hipStream_t st)
 {
+    if (M <= 2 && K <= 2 * 7 * 256 && (int64_t)M * K * 5 / 4 <= GEMV_ACT_LDS) {
+        // persistent stream: up to 8 wavefronts per CU, never more than one per row
+        const int nwg = max(1, min((N + GEMV_WAVES - 1) / GEMV_WAVES, GEMV_STREAM_WGS));
+        if (M == 1)
+            gemv_q4k_stream_kernel<1, 2, GEMV_STREAM_D><<<dim3(nwg), dim3(64 * GEMV_WAVES), 0, st>>>(W, q, d, s, M, N, K, out);
+        else
+            gemv_q4k_stream_kernel<2, 2, GEMV_STREAM_D><<<dim3(nwg), dim3(64 * GEMV_WAVES), 0, st>>>(W, q, d, s, M, N, K, out);
+        return hipGetLastError();
+    }
     if (M <= 1) return gemv_q4k_mt<1>(W, q, d, s, M, N, K, out, st);
     if (M <= 2) return gemv_q4k_mt<2>(W, q, d, s, M, N, K, out, st);
     if (M <= 4) return gemv_q4k_mt<4>(W, q, d, s, M, N, K, out, st);

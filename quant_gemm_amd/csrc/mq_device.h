@@ -25,13 +25,28 @@ __device__ __forceinline__ int dot4(int a, int b, int c)
     return __builtin_amdgcn_sdot4(a, b, c, false);
 }
 
-// Sum over the 64 lanes of a wavefront; every lane receives the total.
+// v from another lane, moved by a DPP pattern (lanes the pattern leaves
+// without a source, or whose row is masked off, receive 0).
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ float dpp_move(float v)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+        0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xf, true));
+}
+
+// Sum over the 64 lanes of a wavefront with DPP moves (no LDS crossbar);
+// every lane receives the total. Pairs, quads, half-rows and rows of 16 are
+// folded within each row, then rows 0+1 and 2+3 and finally all four rows
+// are combined through the row broadcasts, leaving the sum in lane 63.
 __device__ __forceinline__ float wave_sum(float v)
 {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1)
-        v += __shfl_xor(v, o, 64);
-    return v;
+    v += dpp_move<0xb1>(v);          // quad_perm [1,0,3,2]
+    v += dpp_move<0x4e>(v);          // quad_perm [2,3,0,1]
+    v += dpp_move<0x141>(v);         // row_half_mirror
+    v += dpp_move<0x140>(v);         // row_mirror
+    v += dpp_move<0x142, 0xa>(v);    // row_bcast:15 into rows 1 and 3
+    v += dpp_move<0x143, 0xc>(v);    // row_bcast:31 into rows 2 and 3
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
 // The 4*n bytes at a 2-byte aligned address p, as n dwords, using only
