@@ -233,7 +233,7 @@ def run_all(args):
     mq.load()
     dev = torch.device("cuda:0")
     rows = []
-    for cfg, case in synth.all_cases():
+    for grp, case in synth.all_cases():
         log(f"[bench --all] {case.name}")
         W_np = case.make_weights()
         x = torch.from_numpy(case.make_activations()).to(dev)
@@ -256,7 +256,7 @@ def run_all(args):
         e1.record()
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / reps
-        row = {"config": cfg, "case": case.name, "fmt": case.fmt, "M": case.M, "N": case.N,
+        row = {"group": grp, "case": case.name, "fmt": case.fmt, "M": case.M, "N": case.N,
                "K": case.K, "us": round(us, 2), "TOPS": round(case.ops / (us * 1e-6) / 1e12, 2)}
         if hbm:
             b = (q4k_gemv_bytes if case.fmt == "q4k" else q6k_gemv_bytes)(case.M, case.N, case.K)
@@ -293,7 +293,7 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: --gpus {args.gpus}: this build measures one GPU only; the multi-GPU "
+        print(f"bench.py: --gpus {args.gpus}: this benchmark measures one GPU only; the multi-GPU "
               "path is a design (N-sharded weights), not an implementation", file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:

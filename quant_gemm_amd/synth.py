@@ -119,7 +119,7 @@ def _c(name, fmt, M, N, K, outliers, seed, w_key, x_key):
 
 # The workloads: 7B-class shapes (hidden 3584, FFN 18944, fused QKV 4608,
 # vocabulary rows 152064, prompt of 3314 tokens).
-CONFIGS = {
+WORKLOAD_GROUPS = {
     0: [_c("tiny_q4k", "q4k", 8, 256, 1024, False, 1000, 0, 0)],
     1: [_c("q4k_decode_ffn_up", "q4k", 1, 18944, 3584, False, 1001, 0, 0)],
     2: [_c("q6k_ffn_down_m1", "q6k", 1, 3584, 18944, False, 1002, 0, 0),
@@ -136,9 +136,9 @@ CONFIGS = {
 
 
 def all_cases():
-    for cfg, cases in CONFIGS.items():
+    for grp, cases in WORKLOAD_GROUPS.items():
         for c in cases:
-            yield cfg, c
+            yield grp, c
 
 
 def case_by_name(name: str) -> Case:

@@ -138,7 +138,7 @@ def test_small_shapes_all_paths(dev, fmt, M, N, K):
 
 
 def test_config0_exact_workload(dev):
-    case = synth.CONFIGS[0][0]
+    case = synth.case_by_name("tiny_q4k")
     W = case.make_weights()
     x = case.make_activations()
     q, d, s = gpu_plane(x)

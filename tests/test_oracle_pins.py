@@ -40,7 +40,7 @@ def _rel_err(a, b):
 
 @pytest.mark.parametrize("fmt", ["q4k", "q6k"])
 def test_oracle_matches_bruteforce_config0_shape(fmt):
-    case = synth.CONFIGS[0][0]
+    case = synth.case_by_name("tiny_q4k")
     W = (case.make_weights() if fmt == "q4k"
          else synth.q6k_weights(np.random.default_rng(7), case.N, case.K))
     x = case.make_activations()
@@ -358,7 +358,7 @@ def test_generator_codes_are_uniform():
 
 
 def test_generator_outliers_and_determinism():
-    c = synth.CONFIGS[3][1]
+    c = synth.case_by_name("q4k_prefill_attn_o")
     small = synth.Case(c.name, c.fmt, 4, c.N, c.K, True, c.seed, c.w_key, c.x_key)
     a = small.make_activations()
     b = small.make_activations()
