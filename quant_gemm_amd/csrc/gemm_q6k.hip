@@ -1,355 +1,319 @@
 // Prefill GEMM for Q6_K weights x per-32 int8 activations (gfx950).
 //
-// The pages' prefill runs an int8 tensor-core GEMM directly on the raw
-// 4-/6-bit quants against the int8 activation plane, with the block scales
-// applied after each integer product (minfer Features, "GPU — CUDA": raw-
-// nibble int8 GEMMs for q4_K and q6_K). This is a CDNA4 design of that:
+// The pages' prefill runs an int8 tensor-core GEMM on the raw quants for
+// q6_K as for q4_K (minfer Features, "GPU — CUDA": raw-nibble int8 GEMMs
+// for q4_K and q6_K). Q6_K has an int8 scale per 16 values, so one int8
+// product per 32-value activation block would mix two scales. Here the scale
+// is folded into the weights exactly: each weight becomes
+//     p = sc * (q - 32)  in [-4096, 4064],  split as  p = 64 * hi + lo,
+// lo = p & 63 in [0, 63] and hi = p >> 6 in [-64, 63], both int8. Two
+// v_mfma_i32_32x32x32_i8 per 32-value block (one per limb) give
+//     J = 64 * I_hi + I_lo = sum_k sc_k * (q_k - 32) * x_k
+// exactly in int32 (|J| <= 32 * 4096 * 127 < 2^31), and the f32 epilogue
+// per token t, row n and block is  acc += d_x[t] * d[n] * J:  4 VALU
+// operations (combine, convert, scale, add) per 32 values instead of two
+// scaled groups of 16.
 //
-//   * a 256-thread workgroup computes a 128-token x 128-row output tile as
-//     2 x 2 wavefronts of 64 x 64, each 2 x 2 MFMA tiles of 32 x 32;
-//   * the K loop moves in half super-blocks (128 values). Each step stages
-//     the int8 activations, their per-32 scales and sums, and the weight
-//     quants unpacked to int8 (4-bit nibbles, or 6-bit values minus 32) in
-//     natural K order into LDS, together with the f32 per-group weight
-//     factors (d*sc, dmin*m for Q4_K; d*sc for Q6_K);
-//   * the integer dot of every scale group is one int8 MFMA, exact in int32:
-//     v_mfma_i32_32x32x32_i8 per 32-value Q4_K sub-block,
-//     v_mfma_i32_32x32x16_i8 per 16-value Q6_K group;
-//   * the f32 epilogue applies the activation scale times the weight factor
-//     (and the Q4_K min term, which uses the activation sums) per group.
+// Tiling and staging follow the Q4_K kernel: a 256-thread workgroup computes
+// 128 tokens x 128 rows as 4 wavefronts of 32 tokens x 128 rows (1 x 4 MFMA
+// tiles of 32 x 32); K moves in steps of 128 values (half a super-block:
+// weights 128g .. 128g+127). Activations arrive by global->LDS DMA into
+// XOR-swizzled double buffers. The weights are decoded to limbs on the way
+// into LDS (their 210-byte blocks are only 2-byte aligned, so they are read
+// with aligned dword loads realigned in registers): the limb planes use one
+// buffer, written between two barriers.
 //
-// MFMA operand layout (32x32xK): lane l supplies row (l % 32) of A and
-// column (l % 32) of B, each with K/2 consecutive values starting at
-// K/2 * (l / 32); since both operands split K the same way, the products pair
-// up whatever order the hardware uses inside a lane. The 32x32 result gives
-// lane l column (l % 32) and rows 8*(v/4) + 4*(l/32) + (v%4), v = 0..15.
-// Here A = activations (rows = tokens), B = weights (columns = output rows).
+// MFMA operand layout (32x32x32): lane l supplies row (l % 32) of A and
+// column (l % 32) of B, 16 consecutive K values from 16 * (l / 32) each;
+// both operands split K alike. The result gives lane l column (l % 32) and
+// rows 8*(v/4) + 4*(l/32) + (v%4). A = activations, B = weight limbs.
 #include "mq_device.h"
 #include "mq_launch.h"
 
 namespace mq {
 namespace {
 
-constexpr int BM = 128;        // tokens per tile
-constexpr int BN = 128;        // weight rows per tile
-constexpr int BK = 128;        // K values per step (half a super-block)
-constexpr int LDA = BK + 16;   // padded LDS row (bytes) against bank conflicts
-constexpr int NTHR = 256;
+constexpr int TM = 1, TN = 4, WM = 4, WN = 1;
+constexpr int BM = 32 * TM * WM;            // 128 tokens
+constexpr int BN = 32 * TN * WN;            // 128 rows
+constexpr int BK = 128;
+constexpr int NWAVES = WM * WN;
+constexpr int NTHR = 64 * NWAVES;
+constexpr int A_CHUNKS = BM * BK / 16;      // 16-byte activation chunks per step
+static_assert(A_CHUNKS % (64 * NWAVES) == 0, "DMA split");
+static_assert(NTHR == 2 * BN && NTHR >= BM, "one thread per (row, half) and per token");
 
-template <bool Q6>
-struct Smem {
-    int8_t a[BM][LDA];               // activations, int8
-    int8_t b[BN][LDA];               // weights, int8 (natural K order)
-    float dx[BK / 32][BM];           // activation scale per 32-block
-    float sx[BK / 32][BM];           // activation sum (Q4_K only)
-    float fw[Q6 ? BK / 16 : BK / 32][BN];   // d*sc per weight scale group
-    float fm[BK / 32][BN];           // dmin*m per sub-block (Q4_K only)
+// LDS. 16-byte chunk c of row r sits in slot r*8 + (c ^ (r & 7)) in the
+// activation tiles and in both limb planes.
+struct ActStage {
+    int8_t a[A_CHUNKS * 16];
+    float dx[BK / 32][BM];
+};
+struct WgtStage {
+    int8_t lo[BN * BK];
+    int8_t hi[BN * BK];
+    float dw[BN];                            // d of the row's super-block
 };
 
-__device__ __forceinline__ void zero16(int8_t *p)
+__device__ __forceinline__ int slot8(int r, int c) { return r * 8 + (c ^ (r & 7)); }
+
+__device__ __forceinline__ void dma16(const void *src, const void *lds_dst)
 {
-    *reinterpret_cast<v4i *>(p) = v4i{0, 0, 0, 0};
+    const uint32_t base = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)lds_dst);
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(src), "s"(base)
+                 : "memory", "m0");
 }
 
-// Stage the activation plane slice [t0, t0+BM) x [k0, k0+BK).
-template <bool Q6>
-__device__ __forceinline__ void stage_act(Smem<Q6> &sm, const int8_t *__restrict__ q,
-                                          const float *__restrict__ dx,
-                                          const float *__restrict__ sx, int M, int K,
-                                          int t0, int k0)
+__device__ __forceinline__ void wait_dma()
+{
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// Activation tile of step st by DMA; rows past M read the last valid row.
+__device__ __forceinline__ void issue_act(ActStage &s, const int8_t *__restrict__ q, int M,
+                                          int K, int t0, int st, int wave, int lane)
+{
+    const int k0 = st * BK;
+#pragma unroll
+    for (int ii = 0; ii < A_CHUNKS / 64 / NWAVES; ++ii) {
+        const int i = wave * (A_CHUNKS / 64 / NWAVES) + ii;
+        const int p = 64 * i + lane;
+        const int r = p >> 3;
+        const int c = (p & 7) ^ (r & 7);
+        const int t = min(t0 + r, M - 1);
+        dma16(q + (int64_t)t * K + k0 + 16 * c, s.a + 1024 * i);
+    }
+}
+
+// One thread's raw share of a step: row n0 + tid/2, half hh = tid & 1 of
+// the 128 weights (positions 32r + 16hh + i, r = 0..3, i = 0..15). The
+// fields start 2 bytes into a dword when the block does; the aligned dwords
+// covering them are kept as loaded and realigned only after the step's
+// compute, so the loads stay in flight during it.
+struct Raw {
+    uint32_t w0[5], w1[5], wh[5], ws[3];
+    uint32_t sh;                             // 0 or 2: byte offset of the fields in their dwords
+    uint32_t dbits;
+    float4 ds;                               // 4 activation scales of token tid (tid < BM)
+};
+
+template <int n>
+__device__ __forceinline__ void load_dw(const uint8_t *p, uint32_t (&w)[n + 1], uint32_t sh)
+{
+    const uint32_t *b = reinterpret_cast<const uint32_t *>(p - sh);   // stays a global pointer
+#pragma unroll
+    for (int i = 0; i < n; ++i)
+        w[i] = b[i];
+    // the dword past the field only when the field straddles one; otherwise a
+    // dword inside the field (ignored by realign), so no load leaves the block
+    w[n] = b[sh ? n : n - 1];
+}
+
+template <int n>
+__device__ __forceinline__ void realign(const uint32_t (&w)[n + 1], uint32_t sh, uint32_t (&o)[n])
+{
+#pragma unroll
+    for (int i = 0; i < n; ++i)
+        o[i] = __builtin_amdgcn_alignbyte(w[i + 1], w[i], sh);
+}
+
+__device__ __forceinline__ void load_raw(Raw &p, const uint8_t *__restrict__ W,
+                                         const float *__restrict__ dx, int M, int N, int K,
+                                         int t0, int n0, int st)
 {
     const int tid = threadIdx.x;
-    const int nb32 = K >> 5;
-#pragma unroll
-    for (int i = 0; i < (BM * BK / 16) / NTHR; ++i) {
-        const int c = tid + i * NTHR;
-        const int row = c >> 3;
-        const int col = (c & 7) << 4;
-        const int t = t0 + row;
-        if (t < M)
-            *reinterpret_cast<v4i *>(&sm.a[row][col]) =
-                *reinterpret_cast<const v4i *>(q + (int64_t)t * K + k0 + col);
-        else
-            zero16(&sm.a[row][col]);
-    }
-    // scales (threads 0..127) and sums (threads 128..255): 4 floats per token
-    {
-        const int row = tid & (BM - 1);
-        const int t = t0 + row;
-        const bool sums = tid >= BM;
-        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (t < M && (!Q6 || !sums))
-            v = *reinterpret_cast<const float4 *>((sums ? sx : dx) + (int64_t)t * nb32 + (k0 >> 5));
-        float(*dst)[BM] = sums ? sm.sx : sm.dx;
-        dst[0][row] = v.x;
-        dst[1][row] = v.y;
-        dst[2][row] = v.z;
-        dst[3][row] = v.w;
-    }
+    const int row = tid >> 1, hh = tid & 1;
+    const int g = st & 1;
+    const int n = min(n0 + row, N - 1);
+    // Fields start at block offset + an even number of bytes; the block
+    // offset is 0 or 2 mod 4, so all fields share the dword phase sh.
+    // Reads stay within [field - 2, field end + 2), inside the block.
+    const uint8_t *bp = W + (int64_t)n * ((K >> 8) * 210) + (int64_t)(st >> 1) * 210;
+    p.sh = (uint32_t)(reinterpret_cast<uintptr_t>(bp) & 3u);
+    load_dw<4>(bp + 64 * g + 16 * hh, p.w0, p.sh);
+    load_dw<4>(bp + 64 * g + 32 + 16 * hh, p.w1, p.sh);
+    load_dw<4>(bp + 128 + 32 * g + 16 * hh, p.wh, p.sh);
+    load_dw<2>(bp + 192 + 8 * g, p.ws, p.sh);
+    p.dbits = *reinterpret_cast<const uint16_t *>(bp + 208);
+    const int t = min(t0 + (tid & (BM - 1)), M - 1);
+    p.ds = *reinterpret_cast<const float4 *>(dx + (int64_t)t * (K >> 5) + (st * BK >> 5));
 }
 
-// Stage Q4_K weights for rows [n0, n0+BN), half hf of super-block sb.
-__device__ __forceinline__ void stage_w_q4k(Smem<false> &sm, const uint8_t *__restrict__ W,
-                                            int N, int K, int n0, int sb, int hf)
+typedef short v2s __attribute__((ext_vector_type(2)));
+
+// Four 6-bit quants (bytes of qv, 0..63) times the int8 scale s, split into
+// the low limb (p & 63) and the high limb (p >> 6), four bytes each.
+__device__ __forceinline__ void limbs4(uint32_t qv, int s, uint32_t &lo, uint32_t &hi)
+{
+    // bytes 0, 2 and bytes 1, 3 as 16-bit lanes
+    const uint32_t ea = __builtin_amdgcn_perm(0u, qv, 0x0c020c00u);
+    const uint32_t eb = __builtin_amdgcn_perm(0u, qv, 0x0c030c01u);
+    const v2s s2 = {(short)s, (short)s};
+    const v2s c32 = {32, 32};
+    const v2s pa = (__builtin_bit_cast(v2s, ea) - c32) * s2;
+    const v2s pb = (__builtin_bit_cast(v2s, eb) - c32) * s2;
+    const v2s m63 = {63, 63};
+    const uint32_t la = __builtin_bit_cast(uint32_t, (v2s)(pa & m63));
+    const uint32_t lb = __builtin_bit_cast(uint32_t, (v2s)(pb & m63));
+    const uint32_t ha = __builtin_bit_cast(uint32_t, (v2s)(pa >> (short)6));
+    const uint32_t hb = __builtin_bit_cast(uint32_t, (v2s)(pb >> (short)6));
+    // interleave back to byte order w0, w1, w2, w3
+    lo = __builtin_amdgcn_perm(lb, la, 0x06020400u);
+    hi = __builtin_amdgcn_perm(hb, ha, 0x06020400u);
+}
+
+__device__ __forceinline__ void store_raw(WgtStage &w, ActStage &a, const Raw &p, int M, int N,
+                                          int t0, int n0)
 {
     const int tid = threadIdx.x;
-    const int64_t rowb = (int64_t)(K >> 8) * 144;
-    // quants: per row 64 bytes = 4 chunks of 16 (sub-blocks 4hf..4hf+3)
-#pragma unroll
-    for (int i = 0; i < (BN * 4) / NTHR; ++i) {
-        const int c = tid + i * NTHR;
-        const int row = c >> 2;
-        const int part = c & 3;
-        const int cl = part >> 1;                 // chunk pair within the half
-        const int po = (part & 1) << 4;
-        const int n = n0 + row;
-        int8_t *lo = &sm.b[row][64 * cl + po];    // sub-block 2cl (local), low nibbles
-        int8_t *hi = lo + 32;                     // sub-block 2cl+1, high nibbles
-        if (n < N) {
-            const uint8_t *bp = W + (int64_t)n * rowb + (int64_t)sb * 144;
-            const v4i w = *reinterpret_cast<const v4i *>(bp + 16 + 64 * hf + 32 * cl + po);
-            *reinterpret_cast<v4i *>(lo) = w & 0x0f0f0f0f;
-            *reinterpret_cast<v4i *>(hi) = (w >> 4) & 0x0f0f0f0f;
-        } else {
-            zero16(lo);
-            zero16(hi);
-        }
-    }
-    // block header: d, dmin and the four scale/min codes of this half
-    if (tid < BN) {
-        const int n = n0 + tid;
-        float f[4] = {0.f, 0.f, 0.f, 0.f}, g[4] = {0.f, 0.f, 0.f, 0.f};
-        if (n < N) {
-            const uint4 hdr = *reinterpret_cast<const uint4 *>(W + (int64_t)n * rowb + (int64_t)sb * 144);
-            const float dd = f16_bits_to_f32(hdr.x);
-            const float dm = f16_bits_to_f32(hdr.x >> 16);
-            const uint32_t scw = hf == 0 ? (hdr.y & 0x3f3f3f3fu)
-                                         : ((hdr.w & 0x0f0f0f0fu) | ((hdr.y >> 2) & 0x30303030u));
-            const uint32_t mw = hf == 0 ? (hdr.z & 0x3f3f3f3fu)
-                                        : (((hdr.w >> 4) & 0x0f0f0f0fu) | ((hdr.z >> 2) & 0x30303030u));
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                f[j] = dd * (float)((scw >> (8 * j)) & 0xffu);
-                g[j] = dm * (float)((mw >> (8 * j)) & 0xffu);
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            sm.fw[j][tid] = f[j];
-            sm.fm[j][tid] = g[j];
-        }
-    }
-}
-
-// q (0..63 per byte) -> q - 32 as int8 per byte.
-__device__ __forceinline__ uint32_t q6_center(uint32_t qv)
-{
-    uint32_t v = qv ^ 0x20202020u;          // 6-bit two's complement of q - 32
-    const uint32_t sgn = v & 0x20202020u;
-    return v | (sgn << 1) | (sgn << 2);     // sign-extend bit 5 into bits 6, 7
-}
-
-// Stage Q6_K weights for rows [n0, n0+BN), half g of super-block sb
-// (weights 128g .. 128g+127 of the block).
-__device__ __forceinline__ void stage_w_q6k(Smem<true> &sm, const uint8_t *__restrict__ W,
-                                            int N, int K, int n0, int sb, int g)
-{
-    const int tid = threadIdx.x;
-    const int64_t rowb = (int64_t)(K >> 8) * 210;
-    const int row = tid >> 1;
-    const int hh = tid & 1;
-    const int n = n0 + row;
-    uint32_t qr[4][4];
-    float f[8];
-    if (n < N) {
-        const uint8_t *bp = W + (int64_t)n * rowb + (int64_t)sb * 210;
-        uint32_t l0[4], l1[4], h[4];
-        load_dwords_a2<4>(bp + 64 * g + 16 * hh, l0);
-        load_dwords_a2<4>(bp + 64 * g + 32 + 16 * hh, l1);
-        load_dwords_a2<4>(bp + 128 + 32 * g + 16 * hh, h);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            qr[0][i] = q6_center((l0[i] & 0x0f0f0f0fu) | ((h[i] << 4) & 0x30303030u));
-            qr[1][i] = q6_center((l1[i] & 0x0f0f0f0fu) | ((h[i] << 2) & 0x30303030u));
-            qr[2][i] = q6_center(((l0[i] >> 4) & 0x0f0f0f0fu) | (h[i] & 0x30303030u));
-            qr[3][i] = q6_center(((l1[i] >> 4) & 0x0f0f0f0fu) | ((h[i] >> 2) & 0x30303030u));
-        }
-        if (hh == 0) {
-            uint32_t sc[2];
-            load_dwords_a2<2>(bp + 192 + 8 * g, sc);
-            const float dd = f16_bits_to_f32(*reinterpret_cast<const uint16_t *>(bp + 208));
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                f[j] = dd * (float)(int)(int8_t)(sc[j >> 2] >> (8 * (j & 3)));
-        }
-    } else {
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                qr[r][i] = 0u;
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            f[j] = 0.0f;
-    }
+    const int row = tid >> 1, hh = tid & 1;
+    const bool rok = n0 + row < N;
+    uint32_t l0[4], l1[4], h[4], sc[2];
+    realign<4>(p.w0, p.sh, l0);
+    realign<4>(p.w1, p.sh, l1);
+    realign<4>(p.wh, p.sh, h);
+    realign<2>(p.ws, p.sh, sc);
+    // scales of the four 16-value groups 2r + hh, r = 0..3
+    int s[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-        *reinterpret_cast<v4i *>(&sm.b[row][32 * r + 16 * hh]) =
-            v4i{(int)qr[r][0], (int)qr[r][1], (int)qr[r][2], (int)qr[r][3]};
-    if (hh == 0) {
+        s[r] = rok ? (int)(int8_t)(sc[r >> 1] >> (16 * (r & 1) + 8 * hh)) : 0;
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            sm.fw[j][row] = f[j];
+    for (int r = 0; r < 4; ++r) {
+        uint32_t lo[4], hi[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t l = r & 1 ? l1[i] : l0[i];
+            const uint32_t nib = (r >> 1 ? (l >> 4) : l) & 0x0f0f0f0fu;
+            const uint32_t hb = ((r == 0 ? h[i] << 4 : r == 1 ? h[i] << 2 : r == 2 ? h[i] : h[i] >> 2)) &
+                                0x30303030u;
+            limbs4(nib | hb, s[r], lo[i], hi[i]);
+        }
+        const int c = 2 * r + hh;            // 16-byte chunk of the row
+        *reinterpret_cast<v4i *>(w.lo + 16 * slot8(row, c)) = v4i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3]};
+        *reinterpret_cast<v4i *>(w.hi + 16 * slot8(row, c)) = v4i{(int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    }
+    // every thread consumes its loaded values (only some store them), so no
+    // load into these registers is left pending into the next step
+    const float dwv = rok ? f16_bits_to_f32(p.dbits) : 0.0f;
+    const bool tok = t0 + (tid & (BM - 1)) < M;
+    const float4 ds = tok ? p.ds : make_float4(0.f, 0.f, 0.f, 0.f);
+    if (hh == 0)
+        w.dw[row] = dwv;
+    if (tid < BM) {
+        a.dx[0][tid] = ds.x;
+        a.dx[1][tid] = ds.y;
+        a.dx[2][tid] = ds.z;
+        a.dx[3][tid] = ds.w;
     }
 }
 
-template <bool Q6>
-__global__ __launch_bounds__(NTHR, 2) void gemm_kernel(
-    const uint8_t *__restrict__ W, const int8_t *__restrict__ q,
-    const float *__restrict__ dx, const float *__restrict__ sx, int M, int N,
-    int K, int tiles_m, float *__restrict__ out)
+__device__ __forceinline__ void compute_step(const ActStage &a, const WgtStage &w,
+                                             v16f (&acc)[TN], int wm, int lr, int lh)
 {
-    __shared__ Smem<Q6> sm;
+    float dwv[TN];
+#pragma unroll
+    for (int b = 0; b < TN; ++b)
+        dwv[b] = w.dw[b * 32 + lr];
+#pragma unroll 1
+    for (int j = 0; j < BK / 32; ++j) {
+        const int tr = wm * 32 + lr;
+        const v4i af = *reinterpret_cast<const v4i *>(a.a + 16 * slot8(tr, 2 * j + lh));
+        float dv[16];
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+            const float4 d4 = *reinterpret_cast<const float4 *>(&a.dx[j][wm * 32 + 8 * g4 + 4 * lh]);
+            dv[4 * g4 + 0] = d4.x;
+            dv[4 * g4 + 1] = d4.y;
+            dv[4 * g4 + 2] = d4.z;
+            dv[4 * g4 + 3] = d4.w;
+        }
+#pragma unroll
+        for (int b = 0; b < TN; ++b) {
+            const int r = b * 32 + lr;
+            const v4i blo = *reinterpret_cast<const v4i *>(w.lo + 16 * slot8(r, 2 * j + lh));
+            const v4i bhi = *reinterpret_cast<const v4i *>(w.hi + 16 * slot8(r, 2 * j + lh));
+            const v16i il = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, blo, v16i{}, 0, 0, 0);
+            const v16i ih = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, bhi, v16i{}, 0, 0, 0);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int J = (ih[v] << 6) + il[v];
+                acc[b][v] = fmaf((float)J, dv[v] * dwv[b], acc[b][v]);
+            }
+        }
+    }
+}
+
+__global__ __launch_bounds__(NTHR, 2) void gemm_q6k_kernel(
+    const uint8_t *__restrict__ W, const int8_t *__restrict__ q,
+    const float *__restrict__ dx, int M, int N, int K, int tiles_m,
+    float *__restrict__ out)
+{
+    __shared__ ActStage A0, A1;
+    __shared__ WgtStage B;
     const int tile_m = blockIdx.x % tiles_m;
     const int tile_n = blockIdx.x / tiles_m;
     const int t0 = tile_m * BM;
     const int n0 = tile_n * BN;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int wm = wave & 1;          // 64-token half of the tile
-    const int wn = wave >> 1;         // 64-row half of the tile
-    const int lr = lane & 31;         // operand row / result column
-    const int lh = lane >> 5;         // K half / result row group
+    const int wm = wave;                      // WN == 1
+    const int lr = lane & 31, lh = lane >> 5;
 
-    v16f acc[2][2];
+    v16f acc[TN];
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int b = 0; b < TN; ++b)
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-            for (int v = 0; v < 16; ++v)
-                acc[a][b][v] = 0.0f;
+        for (int v = 0; v < 16; ++v)
+            acc[b][v] = 0.0f;
 
+    // K / BK is even: steps alternate activation buffers A0, A1.
     const int nsteps = K / BK;
-    for (int st = 0; st < nsteps; ++st) {
-        const int k0 = st * BK;
-        __syncthreads();                       // previous step's reads done
-        stage_act<Q6>(sm, q, dx, sx, M, K, t0, k0);
-        if constexpr (Q6)
-            stage_w_q6k(sm, W, N, K, n0, st >> 1, st & 1);
-        else
-            stage_w_q4k(sm, W, N, K, n0, st >> 1, st & 1);
+    Raw p;
+    issue_act(A0, q, M, K, t0, 0, wave, lane);
+    load_raw(p, W, dx, M, N, K, t0, n0, 0);
+    wait_dma();
+    store_raw(B, A0, p, M, N, t0, n0);
+    __syncthreads();
+    for (int st = 0; st < nsteps; st += 2) {
+        // register loads before the DMA: any wait the compiler puts in front
+        // of them then has no DMA in flight to wait for
+        load_raw(p, W, dx, M, N, K, t0, n0, st + 1);
+        issue_act(A1, q, M, K, t0, st + 1, wave, lane);
+        compute_step(A0, B, acc, wm, lr, lh);
+        __syncthreads();                      // limb planes of step st consumed
+        wait_dma();
+        store_raw(B, A1, p, M, N, t0, n0);
         __syncthreads();
-
-        if constexpr (!Q6) {
-#pragma unroll
-            for (int j = 0; j < BK / 32; ++j) {
-                v4i af[2], bf[2];
-#pragma unroll
-                for (int a = 0; a < 2; ++a)
-                    af[a] = *reinterpret_cast<const v4i *>(&sm.a[wm * 64 + a * 32 + lr][32 * j + 16 * lh]);
-#pragma unroll
-                for (int b = 0; b < 2; ++b)
-                    bf[b] = *reinterpret_cast<const v4i *>(&sm.b[wn * 64 + b * 32 + lr][32 * j + 16 * lh]);
-                v16i I[2][2];
-#pragma unroll
-                for (int a = 0; a < 2; ++a)
-#pragma unroll
-                    for (int b = 0; b < 2; ++b)
-                        I[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[a], bf[b], v16i{}, 0, 0, 0);
-#pragma unroll
-                for (int a = 0; a < 2; ++a) {
-                    float dxv[16], sxv[16];
-#pragma unroll
-                    for (int g4 = 0; g4 < 4; ++g4) {
-                        const int tl = wm * 64 + a * 32 + 8 * g4 + 4 * lh;
-                        const float4 d4 = *reinterpret_cast<const float4 *>(&sm.dx[j][tl]);
-                        const float4 s4 = *reinterpret_cast<const float4 *>(&sm.sx[j][tl]);
-                        dxv[4 * g4 + 0] = d4.x; dxv[4 * g4 + 1] = d4.y;
-                        dxv[4 * g4 + 2] = d4.z; dxv[4 * g4 + 3] = d4.w;
-                        sxv[4 * g4 + 0] = s4.x; sxv[4 * g4 + 1] = s4.y;
-                        sxv[4 * g4 + 2] = s4.z; sxv[4 * g4 + 3] = s4.w;
-                    }
-#pragma unroll
-                    for (int b = 0; b < 2; ++b) {
-                        const int nl = wn * 64 + b * 32 + lr;
-                        const float fw = sm.fw[j][nl];
-                        const float fm = -sm.fm[j][nl];
-#pragma unroll
-                        for (int v = 0; v < 16; ++v) {
-                            float t = fmaf((float)I[a][b][v], dxv[v] * fw, acc[a][b][v]);
-                            acc[a][b][v] = fmaf(sxv[v], fm, t);
-                        }
-                    }
-                }
-            }
-        } else {
-#pragma unroll
-            for (int j = 0; j < BK / 16; ++j) {
-                long af[2], bf[2];
-#pragma unroll
-                for (int a = 0; a < 2; ++a)
-                    af[a] = *reinterpret_cast<const long *>(&sm.a[wm * 64 + a * 32 + lr][16 * j + 8 * lh]);
-#pragma unroll
-                for (int b = 0; b < 2; ++b)
-                    bf[b] = *reinterpret_cast<const long *>(&sm.b[wn * 64 + b * 32 + lr][16 * j + 8 * lh]);
-                v16i I[2][2];
-#pragma unroll
-                for (int a = 0; a < 2; ++a)
-#pragma unroll
-                    for (int b = 0; b < 2; ++b)
-                        I[a][b] = __builtin_amdgcn_mfma_i32_32x32x16_i8(af[a], bf[b], v16i{}, 0, 0, 0);
-#pragma unroll
-                for (int a = 0; a < 2; ++a) {
-                    float dxv[16];
-#pragma unroll
-                    for (int g4 = 0; g4 < 4; ++g4) {
-                        const int tl = wm * 64 + a * 32 + 8 * g4 + 4 * lh;
-                        const float4 d4 = *reinterpret_cast<const float4 *>(&sm.dx[j >> 1][tl]);
-                        dxv[4 * g4 + 0] = d4.x; dxv[4 * g4 + 1] = d4.y;
-                        dxv[4 * g4 + 2] = d4.z; dxv[4 * g4 + 3] = d4.w;
-                    }
-#pragma unroll
-                    for (int b = 0; b < 2; ++b) {
-                        const int nl = wn * 64 + b * 32 + lr;
-                        const float fw = sm.fw[j][nl];
-#pragma unroll
-                        for (int v = 0; v < 16; ++v)
-                            acc[a][b][v] = fmaf((float)I[a][b][v], dxv[v] * fw, acc[a][b][v]);
-                    }
-                }
-            }
+        const bool more = st + 2 < nsteps;
+        if (more) {
+            load_raw(p, W, dx, M, N, K, t0, n0, st + 2);
+            issue_act(A0, q, M, K, t0, st + 2, wave, lane);
+        }
+        compute_step(A1, B, acc, wm, lr, lh);
+        __syncthreads();
+        if (more) {
+            wait_dma();
+            store_raw(B, A0, p, M, N, t0, n0);
+            __syncthreads();
         }
     }
 
-    // store: lane owns column n0 + nl and rows t0 + tl (+ v layout)
 #pragma unroll
-    for (int a = 0; a < 2; ++a) {
+    for (int b = 0; b < TN; ++b) {
+        const int n = n0 + b * 32 + lr;
+        if (n < N) {
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            const int n = n0 + wn * 64 + b * 32 + lr;
-            if (n < N) {
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int t = t0 + wm * 64 + a * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
-                    if (t < M)
-                        out[(int64_t)t * N + n] = acc[a][b][v];
-                }
+            for (int v = 0; v < 16; ++v) {
+                const int t = t0 + wm * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
+                if (t < M)
+                    out[(int64_t)t * N + n] = acc[b][v];
             }
         }
     }
-}
-
-template <bool Q6>
-hipError_t launch_gemm(const uint8_t *W, const int8_t *q, const float *d,
-                       const float *s, int M, int N, int K, float *out,
-                       hipStream_t st)
-{
-    const int tiles_m = (M + BM - 1) / BM;
-    const int tiles_n = (N + BN - 1) / BN;
-    const int64_t grid = (int64_t)tiles_m * tiles_n;
-    gemm_kernel<Q6><<<dim3((unsigned)grid), dim3(NTHR), 0, st>>>(W, q, d, s, M, N, K, tiles_m, out);
-    return hipGetLastError();
 }
 
 } // namespace
@@ -357,7 +321,11 @@ hipError_t launch_gemm(const uint8_t *W, const int8_t *q, const float *d,
 hipError_t launch_gemm_q6k(const uint8_t *W, const int8_t *q, const float *d,
                            int M, int N, int K, float *out, hipStream_t st)
 {
-    return launch_gemm<true>(W, q, d, nullptr, M, N, K, out, st);
+    const int tiles_m = (M + BM - 1) / BM;
+    const int tiles_n = (N + BN - 1) / BN;
+    const int64_t grid = (int64_t)tiles_m * tiles_n;
+    gemm_q6k_kernel<<<dim3((unsigned)grid), dim3(NTHR), 0, st>>>(W, q, d, M, N, K, tiles_m, out);
+    return hipGetLastError();
 }
 
 } // namespace mq
