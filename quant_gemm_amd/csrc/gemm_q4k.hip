@@ -70,7 +70,7 @@ static_assert(NTHR >= 2 * BM && NTHR >= BN, "side loads need one thread per row"
 // 8 chunks per row) or  r*4 + (c ^ ((r >> 2) & 3))  (quants, 4 per row).
 // Eight consecutive rows reading the same chunk then hit eight different
 // bank groups.
-struct Stage {
+struct alignas(16) Stage {
     int8_t a[A_CHUNKS * 16];
     uint8_t qs[Q_CHUNKS * 16];
     float dx[BK / 32][BM];

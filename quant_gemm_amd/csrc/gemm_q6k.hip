@@ -45,11 +45,11 @@ static_assert(NTHR == 2 * BN && NTHR >= BM, "one thread per (row, half) and per 
 
 // LDS. 16-byte chunk c of row r sits in slot r*8 + (c ^ (r & 7)) in the
 // activation tiles and in both limb planes.
-struct ActStage {
+struct alignas(16) ActStage {
     int8_t a[A_CHUNKS * 16];
     float dx[BK / 32][BM];
 };
-struct WgtStage {
+struct alignas(16) WgtStage {
     int8_t lo[BN * BK];
     int8_t hi[BN * BK];
     float dw[BN];                            // d of the row's super-block
