@@ -22,9 +22,12 @@
 // int32 dot of the 4-bit quants with the int8 activations). The f32
 // epilogue then adds, per token t, row n and sub-block j,
 //     d_x[t,j] * (d*sc_j)[n] * I  -  s_x[t,j] * (dmin*m_j)[n]
-// (the min term uses the activation block sums). On gfx950 this epilogue, not
-// the MFMA, bounds the kernel: 4 VALU operations per token, row and
-// sub-block against 32 int8 MACs.
+// (the min term uses the activation block sums). The first term is a
+// per-element scaling (3 VALU operations: convert, scale product, fma); the
+// second is a rank-4 product per step, summed on the bf16 matrix cores from
+// three-limb splits of both f32 factors (f32 accuracy; see limbs4). On
+// gfx950 the VALU part, not the int8 MFMA, bounds the kernel: 3 VALU
+// operations per token, row and sub-block against 32 int8 MACs.
 //
 // MFMA operand layout (32x32x32): lane l supplies row (l % 32) of A and
 // column (l % 32) of B, 16 consecutive K values from 16 * (l / 32) each;
@@ -74,10 +77,38 @@ struct alignas(16) Stage {
     int8_t a[A_CHUNKS * 16];
     uint8_t qs[Q_CHUNKS * 16];
     float dx[BK / 32][BM];
-    float sx[BK / 32][BM];
     float fw[BK / 32][BN];
-    float fm[BK / 32][BN];
+    uint4 sxl[BM][2];       // bf16 limbs of s_x for the step's 4 sub-blocks (see Limbs)
+    uint4 fml[BN][2];       // bf16 limbs of -(dmin*m_j)
 };
+
+// The min term  -sum_j s_x[t,j] * (dmin*m_j)[n]  is a contraction over the
+// sub-blocks, so it runs on the bf16 matrix cores instead of the VALU. Each
+// f32 factor is split into three bf16 limbs, x = x1 + x2 + x3 up to 2^-27
+// relative (each limb the nearest bf16 of what the previous ones left), and
+// the eight limb products other than x3*y3 are summed with f32 accumulation:
+// the same accuracy as one f32 multiply-add per sub-block. A record holds,
+// for one token or row, the limbs of the step's 4 sub-blocks as bf16 pairs:
+// uint4 [0] = {x1 j0j1, x1 j2j3, x2 j0j1, x2 j2j3}, [1] = {x3 j0j1, x3 j2j3, 0, 0}.
+__device__ __forceinline__ uint32_t bf16_bits(float x)
+{
+    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x);
+}
+
+__device__ __forceinline__ void limbs4(const float (&x)[4], uint4 &r0, uint4 &r1)
+{
+    uint32_t h[4], m[4], l[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        h[j] = bf16_bits(x[j]);
+        const float r = x[j] - __builtin_bit_cast(float, h[j] << 16);
+        m[j] = bf16_bits(r);
+        const float rr = r - __builtin_bit_cast(float, m[j] << 16);
+        l[j] = bf16_bits(rr);
+    }
+    r0 = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), m[0] | (m[1] << 16), m[2] | (m[3] << 16));
+    r1 = make_uint4(l[0] | (l[1] << 16), l[2] | (l[3] << 16), 0u, 0u);
+}
 
 __device__ __forceinline__ int a_slot(int r, int c) { return r * 8 + (c ^ (r & 7)); }
 __device__ __forceinline__ int q_slot(int r, int c) { return r * 4 + (c ^ ((r >> 2) & 3)); }
@@ -161,12 +192,15 @@ __device__ __forceinline__ void store_side(Stage &s, const Side &p, int st, int 
     const int hf = st & 1;
     const int row = tid & (BM - 1);
     const bool tok = t0 + row < M;
-    if (tid < 2 * BM) {
-        float(*dst)[BM] = tid < BM ? s.dx : s.sx;
-        dst[0][row] = tok ? p.ds.x : 0.0f;
-        dst[1][row] = tok ? p.ds.y : 0.0f;
-        dst[2][row] = tok ? p.ds.z : 0.0f;
-        dst[3][row] = tok ? p.ds.w : 0.0f;
+    if (tid < BM) {
+        s.dx[0][row] = tok ? p.ds.x : 0.0f;
+        s.dx[1][row] = tok ? p.ds.y : 0.0f;
+        s.dx[2][row] = tok ? p.ds.z : 0.0f;
+        s.dx[3][row] = tok ? p.ds.w : 0.0f;
+    } else if (tid < 2 * BM) {
+        const float x[4] = {tok ? p.ds.x : 0.0f, tok ? p.ds.y : 0.0f, tok ? p.ds.z : 0.0f,
+                            tok ? p.ds.w : 0.0f};
+        limbs4(x, s.sxl[row][0], s.sxl[row][1]);
     }
     if (tid < BN) {
         // header: f16 d | f16 dmin | 12 bytes of 6-bit codes. Codes j = 0..3
@@ -180,17 +214,48 @@ __device__ __forceinline__ void store_side(Stage &s, const Side &p, int st, int 
                                      : ((h.w & 0x0f0f0f0fu) | ((h.y >> 2) & 0x30303030u));
         const uint32_t mw = hf == 0 ? (h.z & 0x3f3f3f3fu)
                                     : (((h.w >> 4) & 0x0f0f0f0fu) | ((h.z >> 2) & 0x30303030u));
+        float fm[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             s.fw[j][tid] = dd * (float)((scw >> (8 * j)) & 0xffu);
-            s.fm[j][tid] = dm * (float)((mw >> (8 * j)) & 0xffu);
+            fm[j] = -(dm * (float)((mw >> (8 * j)) & 0xffu));
         }
+        limbs4(fm, s.fml[tid][0], s.fml[tid][1]);
     }
 }
 
 __device__ __forceinline__ void compute_step(const Stage &s, v16f (&acc)[TM][TN], int wm, int wn,
                                              int lr, int lh)
 {
+    // Min term of the step's 4 sub-blocks: two 32x32x16 bf16 MFMAs per tile.
+    // K slot 8*lh + e pairs element e of the A and B operands; lane half 0
+    // carries x1*y1, x1*y2 (first MFMA) and x2*y2, x3*y1 (second), lane
+    // half 1 x2*y1, x1*y3 and x2*y3, x3*y2, for j = 0..3 each.
+    {
+        v4i A0[TM], A1[TM];
+#pragma unroll
+        for (int a = 0; a < TM; ++a) {
+            const int t = (wm * TM + a) * 32 + lr;
+            const uint4 r0 = s.sxl[t][0], r1 = s.sxl[t][1];
+            A0[a] = v4i{(int)(lh ? r0.z : r0.x), (int)(lh ? r0.w : r0.y), (int)r0.x, (int)r0.y};
+            A1[a] = v4i{(int)r0.z, (int)r0.w, (int)r1.x, (int)r1.y};
+        }
+#pragma unroll
+        for (int b = 0; b < TN; ++b) {
+            const int n = (wn * TN + b) * 32 + lr;
+            const uint4 q0 = s.fml[n][0], q1 = s.fml[n][1];
+            const uint32_t y2a = lh ? q1.x : q0.z, y2b = lh ? q1.y : q0.w;   // y2 | y3
+            const v4i B0 = {(int)q0.x, (int)q0.y, (int)y2a, (int)y2b};
+            const v4i B1 = {(int)y2a, (int)y2b, (int)(lh ? q0.z : q0.x), (int)(lh ? q0.w : q0.y)};
+#pragma unroll
+            for (int a = 0; a < TM; ++a) {
+                acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    __builtin_bit_cast(v8bf, A0[a]), __builtin_bit_cast(v8bf, B0), acc[a][b], 0, 0, 0);
+                acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    __builtin_bit_cast(v8bf, A1[a]), __builtin_bit_cast(v8bf, B1), acc[a][b], 0, 0, 0);
+            }
+        }
+    }
 #pragma unroll 1
     for (int cl = 0; cl < 2; ++cl) {
         v4i raw[TN];
@@ -217,28 +282,23 @@ __device__ __forceinline__ void compute_step(const Stage &s, v16f (&acc)[TM][TN]
 #pragma unroll
                 for (int b = 0; b < TN; ++b)
                     I[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[a], bf[b], v16i{}, 0, 0, 0);
-            float fw[TN], fm[TN];
+            float fw[TN];
 #pragma unroll
-            for (int b = 0; b < TN; ++b) {
+            for (int b = 0; b < TN; ++b)
                 fw[b] = s.fw[j][(wn * TN + b) * 32 + lr];
-                fm[b] = -s.fm[j][(wn * TN + b) * 32 + lr];
-            }
 #pragma unroll
             for (int a = 0; a < TM; ++a) {
 #pragma unroll
                 for (int g4 = 0; g4 < 4; ++g4) {
                     const int tl = (wm * TM + a) * 32 + 8 * g4 + 4 * lh;
                     const float4 d4 = *reinterpret_cast<const float4 *>(&s.dx[j][tl]);
-                    const float4 s4 = *reinterpret_cast<const float4 *>(&s.sx[j][tl]);
                     const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
-                    const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
 #pragma unroll
                     for (int b = 0; b < TN; ++b) {
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
                             const int v = 4 * g4 + r;
-                            const float t = fmaf((float)I[a][b][v], dv[r] * fw[b], acc[a][b][v]);
-                            acc[a][b][v] = fmaf(sv[r], fm[b], t);
+                            acc[a][b][v] = fmaf((float)I[a][b][v], dv[r] * fw[b], acc[a][b][v]);
                         }
                     }
                 }

@@ -253,6 +253,58 @@ def test_cross_path_rows(dev):
             check_close(big[t:t + 1], ref, f"{fmt} row {t} of M={M}")
 
 
+
+def _both_paths(fmt, W, x, N, K, what):
+    """GEMM on all rows and GEMV on the first 8, each against the oracle."""
+    rq, rd, _ = oracle.quantize_act(x)
+    q, d, s = gpu_plane(x)
+    ref = oracle_mm(fmt, W, rq, rd, N, K)
+    check_close(host(run_matmul(fmt, W, q, d, s, N, K, path=mq.MQ_PATH_GEMM)), ref, what + " GEMM")
+    q8, d8, s8 = gpu_plane(x[:8])
+    check_close(host(run_matmul(fmt, W, q8, d8, s8, N, K, path=mq.MQ_PATH_GEMV)), ref[:8], what + " GEMV")
+
+
+def test_min_term_dominated(dev):
+    """Q4_K outputs made mostly of the min term: large dmin, small d, and
+    activations with a common offset so that the block sums are large."""
+    rng = np.random.default_rng(12)
+    N, K, M = 200, 2048, 150
+    W = synth.q4k_weights(rng, N, K, d_range=(1e-5, 2e-5), dmin_range=(5e-3, 1e-2))
+    x = (rng.standard_normal((M, K)) + 3.0).astype(np.float32)
+    _both_paths("q4k", W, x, N, K, "min-dominated")
+
+
+def _log_uniform_f16(rng, shape, lo, hi):
+    return np.exp(rng.uniform(np.log(lo), np.log(hi), size=shape)).astype(np.float16)
+
+
+@pytest.mark.parametrize("fmt", ["q4k", "q6k"])
+def test_wide_scale_range(dev, fmt):
+    """Block scales spread over the whole f16 range (subnormal to 6e4) and
+    activation rows whose magnitudes differ by 2^+-40."""
+    rng = np.random.default_rng(13)
+    N, K, M = 96, 1536, 130
+    W = synth.weights(fmt, rng, N, K).reshape(N, K // 256, -1)
+    if fmt == "q4k":
+        W[:, :, 0:2] = _log_uniform_f16(rng, (N, K // 256), 1e-7, 6e4).view(np.uint8).reshape(N, K // 256, 2)
+        W[:, :, 2:4] = _log_uniform_f16(rng, (N, K // 256), 1e-7, 6e4).view(np.uint8).reshape(N, K // 256, 2)
+    else:
+        W[:, :, 208:210] = _log_uniform_f16(rng, (N, K // 256), 1e-7, 6e4).view(np.uint8).reshape(N, K // 256, 2)
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    x *= np.exp2(rng.integers(-40, 41, size=(M, 1))).astype(np.float32)
+    W = W.reshape(N, -1)
+    rq, rd, _ = oracle.quantize_act(x)
+    q, d, s = gpu_plane(x)
+    ref = oracle_mm(fmt, W, rq, rd, N, K)
+    for path in (mq.MQ_PATH_GEMM, mq.MQ_PATH_GEMV):
+        rows = slice(None) if path == mq.MQ_PATH_GEMM else slice(0, 8)
+        if path == mq.MQ_PATH_GEMV:
+            q, d, s = gpu_plane(x[:8])
+        got = host(run_matmul(fmt, W, q, d, s, N, K, path=path))
+        # one bar per token row: rows differ in scale by up to 2^80
+        for t in range(got.shape[0]):
+            check_close(got[t], ref[rows][t], f"{fmt} path {path} row {t}")
+
 # ---------------------------------------------------------------- full-size workloads
 
 _SAMPLE_TOKENS = [0, 1, 2, 63, 64, 127, 128, 129, 511, 1000, 2047, 2048, 3199, 3200, 3201, 3250, 3312, 3313]
