@@ -113,21 +113,6 @@ __device__ __forceinline__ void limbs4(const float (&x)[4], uint4 &r0, uint4 &r1
 __device__ __forceinline__ int a_slot(int r, int c) { return r * 8 + (c ^ (r & 7)); }
 __device__ __forceinline__ int q_slot(int r, int c) { return r * 4 + (c ^ ((r >> 2) & 3)); }
 
-// One 16-byte global->LDS DMA per lane: lane L's chunk lands at LDS byte
-// address lds_base + 16 * L (lds_base wave-uniform). Issued as inline asm so
-// that the compiler does not serialize the LDS reads of the other buffer
-// behind it; completion is awaited explicitly (wait_dma) before the barrier
-// that publishes the buffer.
-__device__ __forceinline__ void dma16(const void *src, const void *lds_dst)
-{
-    const uint32_t base = __builtin_amdgcn_readfirstlane(
-        (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)lds_dst);
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-                 :
-                 : "v"(src), "s"(base)
-                 : "memory", "m0");
-}
-
 // Start the DMA of step st's activation and quant tiles into s. Rows past M
 // or N read the last valid row instead: their results are never stored.
 __device__ __forceinline__ void issue_tiles(Stage &s, const uint8_t *__restrict__ W,
@@ -307,11 +292,6 @@ __device__ __forceinline__ void compute_step(const Stage &s, v16f (&acc)[TM][TN]
     }
 }
 
-__device__ __forceinline__ void wait_dma()
-{
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-}
-
 __global__ __launch_bounds__(NTHR, MQ_Q4K_OCC) void gemm_q4k_kernel(
     const uint8_t *__restrict__ W, const int8_t *__restrict__ q,
     const float *__restrict__ dx, const float *__restrict__ sx, int M, int N,
@@ -341,14 +321,14 @@ __global__ __launch_bounds__(NTHR, MQ_Q4K_OCC) void gemm_q4k_kernel(
     Side p;
     issue_tiles(S0, W, q, M, N, K, t0, n0, 0, wave, lane);
     load_side(p, W, dx, sx, M, N, K, t0, n0, 0);
-    wait_dma();
+    wait_vm<0>();
     store_side(S0, p, 0, M, N, t0, n0);
     __syncthreads();
     for (int st = 0; st < nsteps; st += 2) {
         issue_tiles(S1, W, q, M, N, K, t0, n0, st + 1, wave, lane);
         load_side(p, W, dx, sx, M, N, K, t0, n0, st + 1);
         compute_step(S0, acc, wm, wn, lr, lh);
-        wait_dma();
+        wait_vm<0>();
         store_side(S1, p, st + 1, M, N, t0, n0);
         __syncthreads();
         const bool more = st + 2 < nsteps;
@@ -358,7 +338,7 @@ __global__ __launch_bounds__(NTHR, MQ_Q4K_OCC) void gemm_q4k_kernel(
         }
         compute_step(S1, acc, wm, wn, lr, lh);
         if (more) {
-            wait_dma();
+            wait_vm<0>();
             store_side(S0, p, st + 2, M, N, t0, n0);
         }
         __syncthreads();

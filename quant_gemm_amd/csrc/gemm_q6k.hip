@@ -57,21 +57,6 @@ struct alignas(16) WgtStage {
 
 __device__ __forceinline__ int slot8(int r, int c) { return r * 8 + (c ^ (r & 7)); }
 
-__device__ __forceinline__ void dma16(const void *src, const void *lds_dst)
-{
-    const uint32_t base = __builtin_amdgcn_readfirstlane(
-        (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)lds_dst);
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-                 :
-                 : "v"(src), "s"(base)
-                 : "memory", "m0");
-}
-
-__device__ __forceinline__ void wait_dma()
-{
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-}
-
 // Activation tile of step st by DMA; rows past M read the last valid row.
 __device__ __forceinline__ void issue_act(ActStage &s, const int8_t *__restrict__ q, int M,
                                           int K, int t0, int st, int wave, int lane)
@@ -275,7 +260,7 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_q6k_kernel(
     Raw p;
     issue_act(A0, q, M, K, t0, 0, wave, lane);
     load_raw(p, W, dx, M, N, K, t0, n0, 0);
-    wait_dma();
+    wait_vm<0>();
     store_raw(B, A0, p, M, N, t0, n0);
     __syncthreads();
     for (int st = 0; st < nsteps; st += 2) {
@@ -285,7 +270,7 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_q6k_kernel(
         issue_act(A1, q, M, K, t0, st + 1, wave, lane);
         compute_step(A0, B, acc, wm, lr, lh);
         __syncthreads();                      // limb planes of step st consumed
-        wait_dma();
+        wait_vm<0>();
         store_raw(B, A1, p, M, N, t0, n0);
         __syncthreads();
         const bool more = st + 2 < nsteps;
@@ -296,7 +281,7 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_q6k_kernel(
         compute_step(A1, B, acc, wm, lr, lh);
         __syncthreads();
         if (more) {
-            wait_dma();
+            wait_vm<0>();
             store_raw(B, A0, p, M, N, t0, n0);
             __syncthreads();
         }

@@ -452,6 +452,199 @@ __global__ __launch_bounds__(64 * GEMV_WAVES) void gemv_q6k_kernel(
     }
 }
 
+// ---------------------------------------------------------------- Q6_K stream
+// The 210-byte Q6_K blocks are only 2-byte aligned, so instead of loading
+// each lane's fields straight from memory, a wavefront copies its weight
+// bytes into LDS with 16-byte global->LDS DMA (aligned chunks covering the
+// byte range, 64 lanes x 16 bytes per instruction: fully coalesced) and the
+// lanes decode from there, realigning dwords in registers. A wavefront owns
+// the rows n = w, w + NW, w + 2 NW, ... (NW wavefronts in all) and walks
+// them in segments of 16 blocks, one 64-weight unit per lane per segment;
+// segments stream through a ring of Q6S_D LDS slots, Q6S_D - 1 ahead of the
+// one being decoded. The activation plane (int8 values, per-32 scales and
+// the sums of each 16-value group) is staged in LDS once per workgroup, so
+// the only vector-memory loads in the loop are the DMAs and the waits on
+// them are exact.
+constexpr int Q6S_WAVES = 4;                  // wavefronts per workgroup
+constexpr int Q6S_D = 2;                      // ring slots per wavefront
+constexpr int Q6S_SEG = 16;                   // blocks per segment
+constexpr int Q6S_SLOT = 4096;                // bytes per slot (16*210 + alignment, whole DMA rows)
+constexpr int Q6S_DMA = Q6S_SLOT / 1024;      // DMA instructions per segment
+constexpr int Q6S_ACT_MAX = 40 * 1024;        // LDS budget of the activation plane
+constexpr size_t Q6S_LDS_PER_CU = 160 * 1024;  // gfx950 LDS per compute unit
+static_assert(Q6S_SEG * 210 + 16 <= Q6S_SLOT, "segment fits a slot");
+
+// LDS bytes of the staged activation plane of M tokens: int8 values, f32
+// per-32 scales, int16 per-16 sums.
+__host__ __device__ constexpr int q6s_act_bytes(int M, int K)
+{
+    return M * K + M * (K / 32) * 4 + M * (K / 16) * 2;
+}
+
+// n dwords at byte offset p (even) of an LDS buffer, realigned in registers.
+template <int n>
+__device__ __forceinline__ void lds_dwords_a2(const uint8_t *buf, int p, uint32_t (&out)[n])
+{
+    const uint32_t *b = reinterpret_cast<const uint32_t *>(buf + (p & ~3));
+    const uint32_t sh = (uint32_t)(p & 3);
+    uint32_t wv[n + 1];
+#pragma unroll
+    for (int i = 0; i <= n; ++i)
+        wv[i] = b[i];
+#pragma unroll
+    for (int i = 0; i < n; ++i)
+        out[i] = __builtin_amdgcn_alignbyte(wv[i + 1], wv[i], sh);
+}
+
+template <int MT>
+__global__ __launch_bounds__(64 * Q6S_WAVES) void gemv_q6k_stream_kernel(
+    const uint8_t *__restrict__ W, const int8_t *__restrict__ q,
+    const float *__restrict__ dx, int M, int N, int K, float *__restrict__ out)
+{
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int nb = K >> 8, nb32 = K >> 5, ng = K >> 4;
+    int8_t *xq = reinterpret_cast<int8_t *>(smem);
+    float *xd = reinterpret_cast<float *>(smem + M * K);
+    int16_t *xs = reinterpret_cast<int16_t *>(smem + M * K + M * nb32 * 4);
+    uint8_t *ring = smem + q6s_act_bytes(M, K) + wave * (Q6S_D * Q6S_SLOT);
+
+    const int nw = gridDim.x * Q6S_WAVES;
+    const int w = blockIdx.x * Q6S_WAVES + wave;
+    const int nrows = w < N ? (N - 1 - w) / nw + 1 : 0;
+    const int nseg = (nb + Q6S_SEG - 1) / Q6S_SEG;
+    const int nitems = nrows * nseg;
+    const int64_t rowb = (int64_t)nb * 210;
+
+    // DMA of item it (row w + (it / nseg) * NW, segment it % nseg) into slot
+    // it % Q6S_D. Items past the end reload the last one (same number of
+    // DMAs per item keeps the waits exact); lanes past the segment's last
+    // chunk reload that chunk into the slot's unused tail.
+    auto issue = [&](int it) {
+        const int ic = min(it, nitems - 1);
+        const int ri = ic / nseg, seg = ic - ri * nseg;
+        const int64_t rs = (int64_t)(w + ri * nw) * rowb + (int64_t)seg * (Q6S_SEG * 210);
+        const int nbytes = min(Q6S_SEG, nb - seg * Q6S_SEG) * 210;
+        const int64_t c0 = rs >> 4, c1 = (rs + nbytes - 1) >> 4;
+        uint8_t *slot = ring + (it % Q6S_D) * Q6S_SLOT;
+#pragma unroll
+        for (int i = 0; i < Q6S_DMA; ++i)
+            dma16(W + 16 * min(c0 + 64 * i + lane, c1), slot + 1024 * i);
+    };
+
+    // Activation plane -> LDS: all loads first (one memory latency), with the
+    // ring's first segments already in flight, then the stores. Then the sums
+    // of the 16-value groups, stored in the order the lanes read them: group
+    // (blk, g, hh, r) at ((4 blk + 2 g + hh) * 4 + r).
+    constexpr int ACT_C = (Q6S_ACT_MAX / 16 + 64 * Q6S_WAVES - 1) / (64 * Q6S_WAVES);
+    const int qch = M * K / 16, dch = M * nb32 / 4;
+    v4i av[ACT_C];
+#pragma unroll
+    for (int i = 0; i < ACT_C; ++i) {
+        const int c = threadIdx.x + i * 64 * Q6S_WAVES;
+        av[i] = c < qch ? reinterpret_cast<const v4i *>(q)[c]
+                        : reinterpret_cast<const v4i *>(dx)[min(c - qch, dch - 1)];
+    }
+    if (nitems > 0) {
+#pragma unroll
+        for (int d = 0; d < Q6S_D - 1; ++d)
+            issue(d);
+    }
+#pragma unroll
+    for (int i = 0; i < ACT_C; ++i) {
+        const int c = threadIdx.x + i * 64 * Q6S_WAVES;
+        if (c < qch + dch)
+            reinterpret_cast<v4i *>(smem)[c] = av[i];      // q, then d right after it
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < M * ng; i += 64 * Q6S_WAVES) {
+        const int m = i / ng, gi = i - m * ng;
+        const int r = gi & 3, hh = (gi >> 2) & 1, g = (gi >> 3) & 1, blk = gi >> 4;
+        const v4i x = *reinterpret_cast<const v4i *>(xq + m * K + blk * 256 + 128 * g + 32 * r + 16 * hh);
+        int t = dot4(x.x, 0x01010101, 0);
+        t = dot4(x.y, 0x01010101, t);
+        t = dot4(x.z, 0x01010101, t);
+        xs[i] = (int16_t)dot4(x.w, 0x01010101, t);
+    }
+    __syncthreads();
+    if (nitems == 0)
+        return;
+
+    const int bl = lane >> 2, g = (lane >> 1) & 1, hh = lane & 1;
+    float acc[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+        acc[m] = 0.0f;
+    for (int it = 0; it < nitems; ++it) {
+        issue(it + Q6S_D - 1);
+        wait_vm<Q6S_DMA * (Q6S_D - 1)>();
+        const int ri = it / nseg, seg = it - ri * nseg;
+        const int n = w + ri * nw;
+        const int blk = seg * Q6S_SEG + bl;
+        if (blk < nb) {
+            const uint8_t *sl = ring + (it % Q6S_D) * Q6S_SLOT;
+            const int64_t rs = (int64_t)n * rowb + (int64_t)seg * (Q6S_SEG * 210);
+            const int p = (int)(rs & 15) + 210 * bl;    // this block in the slot
+            uint32_t l0[4], l1[4], h[4], sc[2], dw[1];
+            lds_dwords_a2<4>(sl, p + 64 * g + 16 * hh, l0);
+            lds_dwords_a2<4>(sl, p + 64 * g + 32 + 16 * hh, l1);
+            lds_dwords_a2<4>(sl, p + 128 + 32 * g + 16 * hh, h);
+            lds_dwords_a2<2>(sl, p + 192 + 8 * g, sc);
+            lds_dwords_a2<1>(sl, p + 208, dw);
+            const float dd = f16_bits_to_f32(dw[0]);
+            // int8 scales 8g + 2r + hh: bytes hh, 2 + hh, 4 + hh, 6 + hh of sc
+            const float ds0 = dd * (float)(int)(int8_t)(sc[0] >> (8 * hh));
+            const float ds1 = dd * (float)(int)(int8_t)(sc[0] >> (16 + 8 * hh));
+            const float ds2 = dd * (float)(int)(int8_t)(sc[1] >> (8 * hh));
+            const float ds3 = dd * (float)(int)(int8_t)(sc[1] >> (16 + 8 * hh));
+            int qr[4][4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                qr[0][i] = (int)((l0[i] & 0x0f0f0f0fu) | ((h[i] << 4) & 0x30303030u));
+                qr[1][i] = (int)((l1[i] & 0x0f0f0f0fu) | ((h[i] << 2) & 0x30303030u));
+                qr[2][i] = (int)(((l0[i] >> 4) & 0x0f0f0f0fu) | (h[i] & 0x30303030u));
+                qr[3][i] = (int)(((l1[i] >> 4) & 0x0f0f0f0fu) | ((h[i] >> 2) & 0x30303030u));
+            }
+            const int kb = (blk << 8) + (g << 7) + (hh << 4);   // + 32 r
+            const int b0 = (blk << 3) + (g << 2);               // + r
+            const int gs = ((blk << 2) + (g << 1) + hh) << 2;   // + r
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                if (m < M) {
+                    const v4f dr = *reinterpret_cast<const v4f *>(xd + m * nb32 + b0);
+                    const v2i s2 = *reinterpret_cast<const v2i *>(xs + m * ng + gs);
+                    const int xsum[4] = {(int)(int16_t)s2.x, s2.x >> 16, (int)(int16_t)s2.y, s2.y >> 16};
+                    const float dsr[4] = {ds0, ds1, ds2, ds3};
+                    float a = acc[m];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const v4i x = *reinterpret_cast<const v4i *>(xq + m * K + kb + 32 * r);
+                        int t = dot4(qr[r][0], x.x, 0);
+                        t = dot4(qr[r][1], x.y, t);
+                        t = dot4(qr[r][2], x.z, t);
+                        t = dot4(qr[r][3], x.w, t);
+                        const int J = t - 32 * xsum[r];           // sum (q - 32) * x
+                        a = fmaf((float)J, dr[r] * dsr[r], a);
+                    }
+                    acc[m] = a;
+                }
+            }
+        }
+        if (seg == nseg - 1) {
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                const float v = wave_sum(acc[m]);
+                if (lane == 0 && m < M)
+                    out[(int64_t)m * N + n] = v;
+                acc[m] = 0.0f;
+            }
+        }
+    }
+    // the ring's last DMAs target this workgroup's LDS: let them land first
+    wait_vm<0>();
+}
+
 template <int MT>
 hipError_t gemv_q4k_mt(const uint8_t *W, const int8_t *q, const float *d,
                        const float *s, int M, int N, int K, float *out,
@@ -513,6 +706,27 @@ hipError_t launch_gemv_q4k(const uint8_t *W, const int8_t *q, const float *d,
 hipError_t launch_gemv_q6k(const uint8_t *W, const int8_t *q, const float *d,
                            int M, int N, int K, float *out, hipStream_t st)
 {
+    if (q6s_act_bytes(M, K) <= Q6S_ACT_MAX) {
+        // as many workgroups as fit on the chip at once (LDS-limited)
+        static int n_cu = 0;
+        if (n_cu == 0) {
+            int dev = 0, v = 0;
+            if (hipGetDevice(&dev) == hipSuccess &&
+                hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+                n_cu = v;
+            else
+                n_cu = 256;
+        }
+        const size_t lds = (size_t)q6s_act_bytes(M, K) + (size_t)Q6S_WAVES * Q6S_D * Q6S_SLOT;
+        const int per_cu = max(1, (int)(Q6S_LDS_PER_CU / lds));
+        const int nwg = max(1, min((N + Q6S_WAVES - 1) / Q6S_WAVES, per_cu * n_cu));
+        dim3 grid(nwg), block(64 * Q6S_WAVES);
+        if (M <= 1) gemv_q6k_stream_kernel<1><<<grid, block, lds, st>>>(W, q, d, M, N, K, out);
+        else if (M <= 2) gemv_q6k_stream_kernel<2><<<grid, block, lds, st>>>(W, q, d, M, N, K, out);
+        else if (M <= 4) gemv_q6k_stream_kernel<4><<<grid, block, lds, st>>>(W, q, d, M, N, K, out);
+        else gemv_q6k_stream_kernel<8><<<grid, block, lds, st>>>(W, q, d, M, N, K, out);
+        return hipGetLastError();
+    }
     if (M <= 1) return gemv_q6k_mt<1>(W, q, d, M, N, K, out, st);
     if (M <= 2) return gemv_q6k_mt<2>(W, q, d, M, N, K, out, st);
     if (M <= 4) return gemv_q6k_mt<4>(W, q, d, M, N, K, out, st);

@@ -70,4 +70,36 @@ __device__ __forceinline__ void load_dwords_a2(const uint8_t *p, uint32_t (&out)
         out[i] = __builtin_amdgcn_alignbyte(w[i + 1], w[i], sh);
 }
 
+// One 16-byte global->LDS DMA per lane (global_load_lds_dwordx4): lane L's
+// 16 bytes land at LDS byte address lds_dst + 16 * L, where lds_dst must be
+// wave-uniform and 16-byte aligned, src 16-byte aligned. Issued as inline asm
+// so that the compiler neither waits for it at the next LDS access nor
+// reorders LDS accesses around it; completion is awaited with wait_vm(). The
+// instruction takes its LDS address from M0, which the compiler may hold a
+// value in: the asm saves it and puts it back.
+__device__ __forceinline__ void dma16(const void *src, const void *lds_dst)
+{
+    const uint32_t base = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)lds_dst);
+    uint32_t saved;
+    asm volatile("s_mov_b32 %0, m0\n\t"
+                 "s_mov_b32 m0, %2\n\t"
+                 "global_load_lds_dwordx4 %1, off\n\t"
+                 "s_mov_b32 m0, %0"
+                 : "=&s"(saved)
+                 : "v"(src), "s"(base)
+                 : "memory");
+}
+
+// Wait until at most N vector memory operations of this wavefront are
+// outstanding. Loads complete in issue order, so with N = the number of
+// loads issued after some load L, L has completed (any stores in between
+// only make the wait longer).
+template <int N>
+__device__ __forceinline__ void wait_vm()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit field");
+    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
 } // namespace mq
