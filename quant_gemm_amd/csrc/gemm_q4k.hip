@@ -61,6 +61,9 @@ constexpr int BN = 32 * TN * WN;          // weight rows per tile
 constexpr int BK = 128;                   // K values per step
 constexpr int NWAVES = WM * WN;
 constexpr int NTHR = 64 * NWAVES;
+// int8 ops per second of one resident workgroup (about 500 TOPS over 512
+// resident workgroups), for the split-K choice
+constexpr double Q4K_SLOT_OPS = 1.0e12;
 constexpr int A_CHUNKS = BM * BK / 16;      // 16-byte activation chunks per step
 constexpr int Q_CHUNKS = BN * BK / 2 / 16;  // 16-byte raw quant chunks per step
 static_assert(A_CHUNKS % (64 * NWAVES) == 0 && Q_CHUNKS % (64 * NWAVES) == 0, "DMA split");
@@ -295,11 +298,21 @@ __device__ __forceinline__ void compute_step(const Stage &s, v16f (&acc)[TM][TN]
 __global__ __launch_bounds__(NTHR, MQ_Q4K_OCC) void gemm_q4k_kernel(
     const uint8_t *__restrict__ W, const int8_t *__restrict__ q,
     const float *__restrict__ dx, const float *__restrict__ sx, int M, int N,
-    int K, int tiles_m, float *__restrict__ out)
+    int K, int tiles_m, int nsplit, float *__restrict__ out)
 {
     __shared__ Stage S0, S1;
-    const int tile_m = blockIdx.x % tiles_m;
-    const int tile_n = blockIdx.x / tiles_m;
+    // blockIdx = split * tiles + tile_n * tiles_m + tile_m; split s of nsplit
+    // covers the super-blocks [s*P/nsplit, (s+1)*P/nsplit) of P = K/256 and,
+    // when nsplit > 1, writes its partial sums to out + s*M*N.
+    const int tiles = gridDim.x / nsplit;
+    const int split = blockIdx.x / tiles;
+    const int tile = blockIdx.x - split * tiles;
+    const int tile_m = tile % tiles_m;
+    const int tile_n = tile / tiles_m;
+    const int pairs = K >> 8;
+    const int st_begin = 2 * (int)((int64_t)split * pairs / nsplit);
+    const int st_end = 2 * (int)((int64_t)(split + 1) * pairs / nsplit);
+    float *dst = out + (int64_t)split * M * N;
     const int t0 = tile_m * BM;
     const int n0 = tile_n * BN;
     const int lane = threadIdx.x & 63;
@@ -316,22 +329,21 @@ __global__ __launch_bounds__(NTHR, MQ_Q4K_OCC) void gemm_q4k_kernel(
             for (int v = 0; v < 16; ++v)
                 acc[a][b][v] = 0.0f;
 
-    // K / BK is even (K is a multiple of 256): steps alternate S0, S1.
-    const int nsteps = K / BK;
+    // The step range is even (whole super-blocks): steps alternate S0, S1.
     Side p;
-    issue_tiles(S0, W, q, M, N, K, t0, n0, 0, wave, lane);
-    load_side(p, W, dx, sx, M, N, K, t0, n0, 0);
+    issue_tiles(S0, W, q, M, N, K, t0, n0, st_begin, wave, lane);
+    load_side(p, W, dx, sx, M, N, K, t0, n0, st_begin);
     wait_vm<0>();
-    store_side(S0, p, 0, M, N, t0, n0);
+    store_side(S0, p, st_begin, M, N, t0, n0);
     __syncthreads();
-    for (int st = 0; st < nsteps; st += 2) {
+    for (int st = st_begin; st < st_end; st += 2) {
         issue_tiles(S1, W, q, M, N, K, t0, n0, st + 1, wave, lane);
         load_side(p, W, dx, sx, M, N, K, t0, n0, st + 1);
         compute_step(S0, acc, wm, wn, lr, lh);
         wait_vm<0>();
         store_side(S1, p, st + 1, M, N, t0, n0);
         __syncthreads();
-        const bool more = st + 2 < nsteps;
+        const bool more = st + 2 < st_end;
         if (more) {
             issue_tiles(S0, W, q, M, N, K, t0, n0, st + 2, wave, lane);
             load_side(p, W, dx, sx, M, N, K, t0, n0, st + 2);
@@ -354,7 +366,7 @@ __global__ __launch_bounds__(NTHR, MQ_Q4K_OCC) void gemm_q4k_kernel(
                 for (int v = 0; v < 16; ++v) {
                     const int t = t0 + (wm * TM + a) * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
                     if (t < M)
-                        out[(int64_t)t * N + n] = acc[a][b][v];
+                        dst[(int64_t)t * N + n] = acc[a][b][v];
                 }
             }
         }
@@ -369,9 +381,13 @@ hipError_t launch_gemm_q4k(const uint8_t *W, const int8_t *q, const float *d,
 {
     const int tiles_m = (M + BM - 1) / BM;
     const int tiles_n = (N + BN - 1) / BN;
-    const int64_t grid = (int64_t)tiles_m * tiles_n;
-    gemm_q4k_kernel<<<dim3((unsigned)grid), dim3(NTHR), 0, st>>>(W, q, d, s, M, N, K, tiles_m, out);
-    return hipGetLastError();
+    const int tiles = tiles_m * tiles_n;
+    const int nsplit = gemm_splits(tiles, K >> 8, M, N, K, Q4K_SLOT_OPS);
+    return run_split_k(nsplit, (int64_t)M * N, out, st, [&](float *dst) {
+        gemm_q4k_kernel<<<dim3((unsigned)(tiles * nsplit)), dim3(NTHR), 0, st>>>(W, q, d, s, M, N, K,
+                                                                                 tiles_m, nsplit, dst);
+        return hipGetLastError();
+    });
 }
 
 } // namespace mq

@@ -39,6 +39,8 @@ constexpr int BN = 32 * TN * WN;            // 128 rows
 constexpr int BK = 128;
 constexpr int NWAVES = WM * WN;
 constexpr int NTHR = 64 * NWAVES;
+// int8 ops per second of one resident workgroup, for the split-K choice
+constexpr double Q6K_SLOT_OPS = 0.6e12;
 constexpr int A_CHUNKS = BM * BK / 16;      // 16-byte activation chunks per step
 static_assert(A_CHUNKS % (64 * NWAVES) == 0, "DMA split");
 static_assert(NTHR == 2 * BN && NTHR >= BM, "one thread per (row, half) and per token");
@@ -234,13 +236,23 @@ __device__ __forceinline__ void compute_step(const ActStage &a, const WgtStage &
 
 __global__ __launch_bounds__(NTHR, 2) void gemm_q6k_kernel(
     const uint8_t *__restrict__ W, const int8_t *__restrict__ q,
-    const float *__restrict__ dx, int M, int N, int K, int tiles_m,
+    const float *__restrict__ dx, int M, int N, int K, int tiles_m, int nsplit,
     float *__restrict__ out)
 {
     __shared__ ActStage A0, A1;
     __shared__ WgtStage B;
-    const int tile_m = blockIdx.x % tiles_m;
-    const int tile_n = blockIdx.x / tiles_m;
+    // blockIdx = split * tiles + tile_n * tiles_m + tile_m; split s of nsplit
+    // covers the super-blocks [s*P/nsplit, (s+1)*P/nsplit) of P = K/256 and,
+    // when nsplit > 1, writes its partial sums to out + s*M*N.
+    const int tiles = gridDim.x / nsplit;
+    const int split = blockIdx.x / tiles;
+    const int tile = blockIdx.x - split * tiles;
+    const int tile_m = tile % tiles_m;
+    const int tile_n = tile / tiles_m;
+    const int pairs = K >> 8;
+    const int st_begin = 2 * (int)((int64_t)split * pairs / nsplit);
+    const int st_end = 2 * (int)((int64_t)(split + 1) * pairs / nsplit);
+    float *dst = out + (int64_t)split * M * N;
     const int t0 = tile_m * BM;
     const int n0 = tile_n * BN;
     const int lane = threadIdx.x & 63;
@@ -255,15 +267,15 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_q6k_kernel(
         for (int v = 0; v < 16; ++v)
             acc[b][v] = 0.0f;
 
-    // K / BK is even: steps alternate activation buffers A0, A1.
-    const int nsteps = K / BK;
+    // The step range is even (whole super-blocks): steps alternate the
+    // activation buffers A0, A1.
     Raw p;
-    issue_act(A0, q, M, K, t0, 0, wave, lane);
-    load_raw(p, W, dx, M, N, K, t0, n0, 0);
+    issue_act(A0, q, M, K, t0, st_begin, wave, lane);
+    load_raw(p, W, dx, M, N, K, t0, n0, st_begin);
     wait_vm<0>();
     store_raw(B, A0, p, M, N, t0, n0);
     __syncthreads();
-    for (int st = 0; st < nsteps; st += 2) {
+    for (int st = st_begin; st < st_end; st += 2) {
         // register loads before the DMA: any wait the compiler puts in front
         // of them then has no DMA in flight to wait for
         load_raw(p, W, dx, M, N, K, t0, n0, st + 1);
@@ -273,7 +285,7 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_q6k_kernel(
         wait_vm<0>();
         store_raw(B, A1, p, M, N, t0, n0);
         __syncthreads();
-        const bool more = st + 2 < nsteps;
+        const bool more = st + 2 < st_end;
         if (more) {
             load_raw(p, W, dx, M, N, K, t0, n0, st + 2);
             issue_act(A0, q, M, K, t0, st + 2, wave, lane);
@@ -295,7 +307,7 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_q6k_kernel(
             for (int v = 0; v < 16; ++v) {
                 const int t = t0 + wm * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
                 if (t < M)
-                    out[(int64_t)t * N + n] = acc[b][v];
+                    dst[(int64_t)t * N + n] = acc[b][v];
             }
         }
     }
@@ -308,9 +320,13 @@ hipError_t launch_gemm_q6k(const uint8_t *W, const int8_t *q, const float *d,
 {
     const int tiles_m = (M + BM - 1) / BM;
     const int tiles_n = (N + BN - 1) / BN;
-    const int64_t grid = (int64_t)tiles_m * tiles_n;
-    gemm_q6k_kernel<<<dim3((unsigned)grid), dim3(NTHR), 0, st>>>(W, q, d, M, N, K, tiles_m, out);
-    return hipGetLastError();
+    const int tiles = tiles_m * tiles_n;
+    const int nsplit = gemm_splits(tiles, K >> 8, M, N, K, Q6K_SLOT_OPS);
+    return run_split_k(nsplit, (int64_t)M * N, out, st, [&](float *dst) {
+        gemm_q6k_kernel<<<dim3((unsigned)(tiles * nsplit)), dim3(NTHR), 0, st>>>(W, q, d, M, N, K, tiles_m,
+                                                                                 nsplit, dst);
+        return hipGetLastError();
+    });
 }
 
 } // namespace mq

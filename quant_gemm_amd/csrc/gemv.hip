@@ -708,15 +708,7 @@ hipError_t launch_gemv_q6k(const uint8_t *W, const int8_t *q, const float *d,
 {
     if (q6s_act_bytes(M, K) <= Q6S_ACT_MAX) {
         // as many workgroups as fit on the chip at once (LDS-limited)
-        static int n_cu = 0;
-        if (n_cu == 0) {
-            int dev = 0, v = 0;
-            if (hipGetDevice(&dev) == hipSuccess &&
-                hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-                n_cu = v;
-            else
-                n_cu = 256;
-        }
+        const int n_cu = device_cu_count();
         const size_t lds = (size_t)q6s_act_bytes(M, K) + (size_t)Q6S_WAVES * Q6S_D * Q6S_SLOT;
         const int per_cu = max(1, (int)(Q6S_LDS_PER_CU / lds));
         const int nwg = max(1, min((N + Q6S_WAVES - 1) / Q6S_WAVES, per_cu * n_cu));

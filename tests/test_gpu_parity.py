@@ -137,6 +137,23 @@ def test_small_shapes_all_paths(dev, fmt, M, N, K):
         check_close(out, ref, f"{fmt} M={M} N={N} K={K} path={p}")
 
 
+
+# Shapes whose tile count is small against the chip, so the GEMM cuts K into
+# several ranges (uneven ones included) and sums the partial planes.
+@pytest.mark.parametrize("fmt,M,N,K", [("q4k", 64, 2000, 3584), ("q4k", 40, 130, 6912),
+                                       ("q6k", 300, 700, 4608), ("q6k", 17, 257, 2560)])
+def test_split_k_shapes(dev, fmt, M, N, K):
+    rng = np.random.default_rng(M * 7919 + N + K)
+    W = synth.weights(fmt, rng, N, K)
+    x = synth.activations(rng, M, K, outliers=True)
+    rq, rd, _ = oracle.quantize_act(x)
+    q, d, s = gpu_plane(x)
+    ref = oracle_mm(fmt, W, rq, rd, N, K)
+    got = host(run_matmul(fmt, W, q, d, s, N, K, path=mq.MQ_PATH_GEMM))
+    check_close(got, ref, f"{fmt} M={M} N={N} K={K}")
+    again = host(run_matmul(fmt, W, q, d, s, N, K, path=mq.MQ_PATH_GEMM))
+    assert np.array_equal(got, again), "split-K result must not depend on scheduling"
+
 def test_config0_exact_workload(dev):
     case = synth.case_by_name("tiny_q4k")
     W = case.make_weights()
