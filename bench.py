@@ -268,6 +268,74 @@ def run_all(args):
         print(json.dumps(row), flush=True)
         del Ws, W0, out, q, d, s, x
         torch.cuda.empty_cache()
+    run_producers(dev)
+
+
+def _time_rotating(fn, copies, reps):
+    import torch
+    for i in range(3):
+        fn(i % copies)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(reps):
+        fn(i % copies)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / reps
+
+
+def run_producers(dev):
+    """Producer-fused quantizers (RMSNorm / SwiGLU -> int8 plane) against the
+    unfused pair (producer writing f32, then the quantizer reading it). Inputs
+    rotate through >= 1 GiB of copies so that they come from HBM."""
+    import numpy as np
+    import torch
+
+    import quant_gemm_amd as mq
+    from quant_gemm_amd import synth
+
+    rng = np.random.default_rng(2024)
+    for M, K in ((3314, 3584), (1, 3584)):
+        x0 = torch.from_numpy(synth.activations(rng, M, K, outliers=True)).to(dev)
+        w = torch.from_numpy((1.0 + 0.3 * rng.standard_normal(K)).astype(np.float32)).to(dev)
+        copies = max(1, -(-ROTATE_BYTES // (x0.numel() * 4)))
+        xs = [x0] + [x0.clone() for _ in range(copies - 1)]
+        q, d, s = mq.quantize_act(x0)
+        y = torch.empty_like(x0)
+        reps = max(2 * copies, 20)
+        fused = _time_rotating(lambda i: mq.rmsnorm_quantize(xs[i], w, 1e-6, q=q, d=d, s=s), copies, reps)
+        unfused = _time_rotating(lambda i: (mq.rmsnorm_quantize(xs[i], w, 1e-6, q=q, d=d, s=s, y=y),
+                                            mq.quantize_act(y, q=q, d=d, s=s)), copies, reps)
+        b = M * K * 4 + K * 4 + M * K + 8 * M * (K // 32)
+        row = {"group": "producers", "case": f"rmsnorm_quantize M={M} K={K}", "us": round(fused, 2),
+               "GBs": round(b / (fused * 1e-6) / 1e9, 1), "frac_hbm": round(b / (fused * 1e-6) / 1e9 / HBM_PEAK_GBS, 3),
+               "unfused_us": round(unfused, 2)}
+        print(json.dumps(row), flush=True)
+        del xs, x0
+        torch.cuda.empty_cache()
+    for M, K in ((3314, 18944), (1, 18944)):
+        gu0 = torch.from_numpy(np.concatenate([(rng.standard_normal((M, K)) * 2.5).astype(np.float32),
+                                               synth.activations(rng, M, K, outliers=True)], axis=1)).to(dev)
+        copies = max(1, -(-ROTATE_BYTES // (gu0.numel() * 4)))
+        gus = [gu0] + [gu0.clone() for _ in range(copies - 1)]
+        q = torch.empty((M, K), dtype=torch.int8, device=dev)
+        d = torch.empty((M, K // 32), dtype=torch.float32, device=dev)
+        s = torch.empty_like(d)
+        y = torch.empty((M, K), dtype=torch.float32, device=dev)
+        reps = max(4 * copies, 20)
+        fused = _time_rotating(lambda i: mq.swiglu_quantize(gus[i][:, :K], gus[i][:, K:], q=q, d=d, s=s),
+                               copies, reps)
+        unfused = _time_rotating(lambda i: (mq.swiglu_quantize(gus[i][:, :K], gus[i][:, K:], q=q, d=d, s=s, y=y),
+                                            mq.quantize_act(y, q=q, d=d, s=s)), copies, reps)
+        b = 2 * M * K * 4 + M * K + 8 * M * (K // 32)
+        row = {"group": "producers", "case": f"swiglu_quantize M={M} K={K}", "us": round(fused, 2),
+               "GBs": round(b / (fused * 1e-6) / 1e9, 1), "frac_hbm": round(b / (fused * 1e-6) / 1e9 / HBM_PEAK_GBS, 3),
+               "unfused_us": round(unfused, 2)}
+        print(json.dumps(row), flush=True)
+        del gus, gu0
+        torch.cuda.empty_cache()
 
 
 def run_copy_calibration(args):

@@ -10,10 +10,14 @@
  * quantized once and that plane serves every matmul that reads it.)
  *
  * Conventions for every entry point
- *   - Pointers are device pointers owned by the caller. The library never
- *     allocates, frees or synchronizes inside these calls; it enqueues kernels
- *     on `stream` (a hipStream_t passed as void*, NULL = the null stream) and
- *     returns. Inputs are read-only; outputs are overwritten.
+ *   - Pointers are device pointers owned by the caller. The calls enqueue
+ *     kernels on `stream` (a hipStream_t passed as void*, NULL = the null
+ *     stream) and return; nothing synchronizes. Inputs are read-only; outputs
+ *     are overwritten. The only allocation is the matmuls' split-K
+ *     workspace: when a GEMM has too few output tiles to fill the device it
+ *     splits K, takes nsplit*M*N f32 of stream-ordered memory
+ *     (hipMallocAsync on `stream`) and returns it (hipFreeAsync) after the
+ *     reduction; a failed allocation is MQ_ERR_LAUNCH.
  *   - Arguments are validated on the host before any HIP call. A failed
  *     check returns a nonzero mq_status and nothing is launched; the
  *     calling thread's mq_last_error() then names the argument and its value.
@@ -54,7 +58,7 @@
 extern "C" {
 #endif
 
-#define MQ_ABI_VERSION 1
+#define MQ_ABI_VERSION 2
 
 typedef enum {
     MQ_OK = 0,
@@ -85,6 +89,42 @@ enum { MQ_PATH_AUTO = 0, MQ_PATH_GEMV = 1, MQ_PATH_GEMM = 2 };
  */
 int mq_quantize_act(const float *x, int64_t M, int64_t K, int64_t ldx,
                     int8_t *q, float *d, float *s, void *stream);
+
+/*
+ * Producer-fused quantization, RMSNorm: the int8 plane of
+ *   y[t][k] = (x[t][k] * r_t) * w[k],  r_t = f32(1 / sqrt(ss_t / K + eps)),
+ * where ss_t = sum_k x[t][k]^2 is the exact sum rounded once to f64 and
+ * 1 / sqrt(ss / K + eps) is evaluated with correctly rounded f64 operations;
+ * the two products are f32 (no fused multiply-add). q, d and s are what
+ * mq_quantize_act would write for y, so the matmuls take them unchanged.
+ * The pages have the norm emit the int8 plane directly instead of an f32
+ * tensor (minfer Features, "GPU — CUDA"); the op is RmsNorm{eps} with its
+ * weight (minfer Compute Graph Design, "The Op vocabulary"). The arithmetic
+ * is the reading taken: the pages give none.
+ *   x  f32 [M][ldx] (16-byte aligned, ldx >= K and a multiple of 4)
+ *   w  f32 [K] (16-byte aligned); eps finite and >= 0
+ *   y  optional f32 [M][K] (16-byte aligned): when not NULL, y itself is
+ *      written too.
+ */
+int mq_rmsnorm_quantize(const float *x, const float *w, int64_t M, int64_t K,
+                        int64_t ldx, float eps, int8_t *q, float *d, float *s,
+                        float *y, void *stream);
+
+/*
+ * Producer-fused quantization, SwiGLU: the int8 plane of
+ *   y[t][k] = f32(g / (1 + exp(-g)))  * u[t][k],  g = g[t][k],
+ * the SiLU evaluated in f64 (exp within an f64 ulp) and rounded once, the
+ * product in f32. The op is SwiGLU = Silu(gate) * up (minfer Compute Graph
+ * Design, "The Op vocabulary"), emitting the plane directly as the norm
+ * above. g and u have row strides ldg and ldu, so the two halves of a
+ * concatenated gate|up output ([M][2K], u = g + K, ldg = ldu = 2K) are read
+ * in place.
+ *   g, u  f32, 16-byte aligned, ldg and ldu >= K and multiples of 4
+ *   y     optional f32 [M][K] (16-byte aligned), written when not NULL.
+ */
+int mq_swiglu_quantize(const float *g, const float *u, int64_t M, int64_t K,
+                       int64_t ldg, int64_t ldu, int8_t *q, float *d, float *s,
+                       float *y, void *stream);
 
 /*
  * Q4_K matmul: out[t][n] = sum_k w[n][k] * d[t][k/32] * q[t][k], where

@@ -7,6 +7,8 @@ libmq. torch provides device memory and streams. There is no CPU fallback:
 if libmq.so is missing, ``load()`` raises.
 
     q, d, s = quantize_act(x)                  # x: f32 [M, K] on cuda
+    q, d, s = rmsnorm_quantize(x, w, eps)      # plane of RMSNorm(x) * w
+    q, d, s = swiglu_quantize(g, u)            # plane of SiLU(g) * u
     out = matmul_q4k(W, q, d, s, N, K)         # W: uint8 [N, K/256*144]
     out = matmul_q6k(W, q, d, None, N, K)      # W: uint8 [N, K/256*210]
 """
@@ -22,7 +24,7 @@ MQ_PATH_AUTO, MQ_PATH_GEMV, MQ_PATH_GEMM = 0, 1, 2
 STATUS_NAMES = {0: "MQ_OK", 1: "MQ_ERR_INVALID_ARG", 2: "MQ_ERR_SHAPE",
                 3: "MQ_ERR_ALIGN", 4: "MQ_ERR_UNSUPPORTED", 5: "MQ_ERR_DEVICE",
                 6: "MQ_ERR_LAUNCH"}
-ABI_VERSION = 1
+ABI_VERSION = 2
 Q4K_BLOCK_BYTES = 144
 Q6K_BLOCK_BYTES = 210
 
@@ -32,6 +34,8 @@ _I64 = ctypes.c_int64
 _MATMUL_ARGS = [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P]
 SIGNATURES = {
     "mq_quantize_act": ([_P, _I64, _I64, _I64, _P, _P, _P, _P], ctypes.c_int),
+    "mq_rmsnorm_quantize": ([_P, _P, _I64, _I64, _I64, ctypes.c_float, _P, _P, _P, _P, _P], ctypes.c_int),
+    "mq_swiglu_quantize": ([_P, _P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P], ctypes.c_int),
     "mq_matmul_q4k": (_MATMUL_ARGS, ctypes.c_int),
     "mq_matmul_q6k": (_MATMUL_ARGS, ctypes.c_int),
     "mq_matmul_q4k_ex": (_MATMUL_ARGS + [ctypes.c_int], ctypes.c_int),
@@ -115,6 +119,55 @@ def quantize_act(x, q=None, d=None, s=None, stream=None):
     _check(L.mq_quantize_act(x.data_ptr(), M, K, x.stride(0), q.data_ptr(),
                              d.data_ptr(), s.data_ptr(), _stream(stream)))
     return q, d, s
+
+
+def _plane_outputs(M, K, device, q, d, s):
+    import torch
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.int8, device=device)
+    if d is None:
+        d = torch.empty((M, K // 32), dtype=torch.float32, device=device)
+    if s is None:
+        s = torch.empty((M, K // 32), dtype=torch.float32, device=device)
+    assert q.is_contiguous() and d.is_contiguous() and s.is_contiguous()
+    return q, d, s
+
+
+def rmsnorm_quantize(x, w, eps, q=None, d=None, s=None, y=None, stream=None):
+    """The int8 plane of RMSNorm(x) * w (x f32 [M, K], row stride x.stride(0);
+    w f32 [K]). Returns (q, d, s), plus y f32 [M, K] (the normalised values)
+    when a y tensor is passed."""
+    import torch
+    L = load()
+    assert x.is_cuda and x.dtype == torch.float32 and x.dim() == 2 and x.stride(1) == 1
+    M, K = x.shape
+    assert w.is_cuda and w.dtype == torch.float32 and w.is_contiguous() and w.numel() == K
+    q, d, s = _plane_outputs(M, K, x.device, q, d, s)
+    if y is not None:
+        assert y.dtype == torch.float32 and y.is_contiguous() and tuple(y.shape) == (M, K)
+    _check(L.mq_rmsnorm_quantize(x.data_ptr(), w.data_ptr(), M, K, x.stride(0), float(eps),
+                                 q.data_ptr(), d.data_ptr(), s.data_ptr(),
+                                 None if y is None else y.data_ptr(), _stream(stream)))
+    return (q, d, s) if y is None else (q, d, s, y)
+
+
+def swiglu_quantize(g, u, q=None, d=None, s=None, y=None, stream=None):
+    """The int8 plane of SiLU(g) * u (g, u f32 [M, K] with their own row
+    strides, e.g. the two halves of a gate|up output). Returns (q, d, s),
+    plus y when a y tensor is passed."""
+    import torch
+    L = load()
+    for a in (g, u):
+        assert a.is_cuda and a.dtype == torch.float32 and a.dim() == 2 and a.stride(1) == 1
+    assert g.shape == u.shape
+    M, K = g.shape
+    q, d, s = _plane_outputs(M, K, g.device, q, d, s)
+    if y is not None:
+        assert y.dtype == torch.float32 and y.is_contiguous() and tuple(y.shape) == (M, K)
+    _check(L.mq_swiglu_quantize(g.data_ptr(), u.data_ptr(), M, K, g.stride(0), u.stride(0),
+                                q.data_ptr(), d.data_ptr(), s.data_ptr(),
+                                None if y is None else y.data_ptr(), _stream(stream)))
+    return (q, d, s) if y is None else (q, d, s, y)
 
 
 def _matmul(fn, block_bytes, W, q, d, s, N, K, out, stream, path):

@@ -150,6 +150,65 @@ int mq_quantize_act(const float *x, int64_t M, int64_t K, int64_t ldx, int8_t *q
     return launched(mq::launch_quantize(x, M, K, ldx, q, d, s, static_cast<hipStream_t>(stream)), fn);
 }
 
+int mq_rmsnorm_quantize(const float *x, const float *w, int64_t M, int64_t K, int64_t ldx, float eps,
+                        int8_t *q, float *d, float *s, float *y, void *stream)
+{
+    g_err[0] = '\0';
+    const char *fn = "mq_rmsnorm_quantize";
+    if (!x) return fail(MQ_ERR_INVALID_ARG, "%s: x is NULL", fn);
+    if (!w) return fail(MQ_ERR_INVALID_ARG, "%s: w is NULL", fn);
+    if (!q) return fail(MQ_ERR_INVALID_ARG, "%s: q is NULL", fn);
+    if (!d) return fail(MQ_ERR_INVALID_ARG, "%s: d is NULL", fn);
+    if (!s) return fail(MQ_ERR_INVALID_ARG, "%s: s is NULL", fn);
+    if (M <= 0) return fail(MQ_ERR_INVALID_ARG, "%s: M=%lld must be positive", fn, (long long)M);
+    if (!(eps >= 0.0f) || eps > 3.4e38f)
+        return fail(MQ_ERR_INVALID_ARG, "%s: eps=%g must be finite and >= 0", fn, (double)eps);
+    if (int rc = check_K(K, fn)) return rc;
+    if (ldx < K) return fail(MQ_ERR_SHAPE, "%s: ldx=%lld is smaller than K=%lld", fn, (long long)ldx, (long long)K);
+    if (ldx % 4 != 0) return fail(MQ_ERR_ALIGN, "%s: ldx=%lld is not a multiple of 4", fn, (long long)ldx);
+    if (M > kMaxDim) return fail(MQ_ERR_SHAPE, "%s: M=%lld exceeds %lld", fn, (long long)M, (long long)kMaxDim);
+    if (!aligned(x, 16)) return fail(MQ_ERR_ALIGN, "%s: x=%p is not 16-byte aligned", fn, (const void *)x);
+    if (!aligned(w, 16)) return fail(MQ_ERR_ALIGN, "%s: w=%p is not 16-byte aligned", fn, (const void *)w);
+    if (!aligned(q, 16)) return fail(MQ_ERR_ALIGN, "%s: q=%p is not 16-byte aligned", fn, (const void *)q);
+    if (!aligned(d, 16)) return fail(MQ_ERR_ALIGN, "%s: d=%p is not 16-byte aligned", fn, (const void *)d);
+    if (!aligned(s, 16)) return fail(MQ_ERR_ALIGN, "%s: s=%p is not 16-byte aligned", fn, (const void *)s);
+    if (y && !aligned(y, 16)) return fail(MQ_ERR_ALIGN, "%s: y=%p is not 16-byte aligned", fn, (const void *)y);
+    if (int rc = check_device()) return rc;
+    return launched(mq::launch_rmsnorm_quantize(x, w, M, K, ldx, eps, q, d, s, y,
+                                                static_cast<hipStream_t>(stream)), fn);
+}
+
+int mq_swiglu_quantize(const float *g, const float *u, int64_t M, int64_t K, int64_t ldg, int64_t ldu,
+                       int8_t *q, float *d, float *s, float *y, void *stream)
+{
+    g_err[0] = '\0';
+    const char *fn = "mq_swiglu_quantize";
+    if (!g) return fail(MQ_ERR_INVALID_ARG, "%s: g is NULL", fn);
+    if (!u) return fail(MQ_ERR_INVALID_ARG, "%s: u is NULL", fn);
+    if (!q) return fail(MQ_ERR_INVALID_ARG, "%s: q is NULL", fn);
+    if (!d) return fail(MQ_ERR_INVALID_ARG, "%s: d is NULL", fn);
+    if (!s) return fail(MQ_ERR_INVALID_ARG, "%s: s is NULL", fn);
+    if (M <= 0) return fail(MQ_ERR_INVALID_ARG, "%s: M=%lld must be positive", fn, (long long)M);
+    if (int rc = check_K(K, fn)) return rc;
+    if (ldg < K) return fail(MQ_ERR_SHAPE, "%s: ldg=%lld is smaller than K=%lld", fn, (long long)ldg, (long long)K);
+    if (ldu < K) return fail(MQ_ERR_SHAPE, "%s: ldu=%lld is smaller than K=%lld", fn, (long long)ldu, (long long)K);
+    if (ldg % 4 != 0) return fail(MQ_ERR_ALIGN, "%s: ldg=%lld is not a multiple of 4", fn, (long long)ldg);
+    if (ldu % 4 != 0) return fail(MQ_ERR_ALIGN, "%s: ldu=%lld is not a multiple of 4", fn, (long long)ldu);
+    if (M > kMaxDim) return fail(MQ_ERR_SHAPE, "%s: M=%lld exceeds %lld", fn, (long long)M, (long long)kMaxDim);
+    // 8 threads per 32-value block: the grid must fit in 2^31-1 workgroups
+    if (M > (kMaxDim * 256 / 8) / (K / 32))
+        return fail(MQ_ERR_SHAPE, "%s: M=%lld x K=%lld is too large for one launch", fn, (long long)M, (long long)K);
+    if (!aligned(g, 16)) return fail(MQ_ERR_ALIGN, "%s: g=%p is not 16-byte aligned", fn, (const void *)g);
+    if (!aligned(u, 16)) return fail(MQ_ERR_ALIGN, "%s: u=%p is not 16-byte aligned", fn, (const void *)u);
+    if (!aligned(q, 16)) return fail(MQ_ERR_ALIGN, "%s: q=%p is not 16-byte aligned", fn, (const void *)q);
+    if (!aligned(d, 16)) return fail(MQ_ERR_ALIGN, "%s: d=%p is not 16-byte aligned", fn, (const void *)d);
+    if (!aligned(s, 16)) return fail(MQ_ERR_ALIGN, "%s: s=%p is not 16-byte aligned", fn, (const void *)s);
+    if (y && !aligned(y, 16)) return fail(MQ_ERR_ALIGN, "%s: y=%p is not 16-byte aligned", fn, (const void *)y);
+    if (int rc = check_device()) return rc;
+    return launched(mq::launch_swiglu_quantize(g, u, M, K, ldg, ldu, q, d, s, y,
+                                               static_cast<hipStream_t>(stream)), fn);
+}
+
 int mq_matmul_q4k(const void *W, const int8_t *q, const float *d, const float *s, int64_t M,
                   int64_t N, int64_t K, float *out, void *stream)
 {

@@ -19,6 +19,11 @@ hipError_t launch_gemv_q4k(const uint8_t *W, const int8_t *q, const float *d,
 hipError_t launch_gemv_q6k(const uint8_t *W, const int8_t *q, const float *d,
                            int M, int N, int K, float *out, hipStream_t st);
 
+hipError_t launch_rmsnorm_quantize(const float *x, const float *w, int64_t M, int64_t K, int64_t ldx,
+                                   float eps, int8_t *q, float *d, float *s, float *y, hipStream_t st);
+hipError_t launch_swiglu_quantize(const float *g, const float *u, int64_t M, int64_t K, int64_t ldg,
+                                  int64_t ldu, int8_t *q, float *d, float *s, float *y, hipStream_t st);
+
 hipError_t launch_gemm_q4k(const uint8_t *W, const int8_t *q, const float *d,
                            const float *s, int M, int N, int K, float *out,
                            hipStream_t st);

@@ -11,62 +11,63 @@
 // operation (correctly rounded division, no contraction, no denormal flush),
 // so the plane is bit-exact against a host evaluation of the same rule.
 //
-// HBM-bound: 4 B read and 1 + 8/32 B written per element. One lane owns 4
-// consecutive values (one 16-byte load, one 4-byte store); 8 lanes own a
-// 32-value block and combine amax and sum(q) with cross-lane swizzles.
+// HBM-bound: 4 B read and 1 + 8/32 B written per element. A lane owns 4
+// consecutive values of each of QA_ITEMS blocks (16-byte loads, 4-byte
+// stores); 8 lanes own a 32-value block and combine amax and sum(q) with
+// cross-lane swizzles (quant_core.h).
 #include "mq_device.h"
 #include "mq_launch.h"
+#include "quant_core.h"
 
 #pragma clang fp contract(off)
 
 namespace mq {
 namespace {
 
-__device__ __forceinline__ int quant1(float v, float db, bool zero)
+// Scalar form of the rule for the unaligned path (the quotient as in
+// quant_chunks).
+__device__ __forceinline__ int quant1(float v, float db, float rdb, bool zero)
 {
     if (zero)
         return 0;
-    float r = __builtin_roundf(v / db);
-    r = r > 127.0f ? 127.0f : r;
-    r = r < -127.0f ? -127.0f : r;
-    return (int)r;
+    const float t = v * rdb;
+    return (int)q_clamp_round(db < 0x1p-100f || q_near_half(t) ? v / db : t);
 }
 
-// Vector path: x 16-byte aligned and ldx % 4 == 0.
+// Vector path: x 16-byte aligned and ldx % 4 == 0. A workgroup covers
+// QA_ITEMS * 1024 consecutive values of one token row: QA_ITEMS float4 per
+// thread, 8 threads per 32-value block, all loads issued first.
+constexpr int QA_ITEMS = 4;
+
 __global__ __launch_bounds__(256) void quantize_act_v4(
-    const float *__restrict__ x, int64_t nblk, int64_t nbk, int64_t K,
-    int64_t ldx, int8_t *__restrict__ q, float *__restrict__ d,
-    float *__restrict__ s)
+    const float *__restrict__ x, int K, int chunks, int64_t ldx, int8_t *__restrict__ q,
+    float *__restrict__ d, float *__restrict__ s)
 {
-    const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t blk = g >> 3;            // flat (token, block) index
-    if (blk >= nblk)
-        return;                            // whole 8-lane groups exit together
-    const int li = (int)(g & 7);
-    const int64_t t = blk / nbk;
-    const int64_t b = blk - t * nbk;
-    const float4 v = *reinterpret_cast<const float4 *>(x + t * ldx + 32 * b + 4 * li);
-
-    float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-    amax = fmaxf(amax, __shfl_xor(amax, 1, 8));
-    amax = fmaxf(amax, __shfl_xor(amax, 2, 8));
-    amax = fmaxf(amax, __shfl_xor(amax, 4, 8));
-
-    const float db = amax / 127.0f;
-    const bool zero = db == 0.0f;
-    const int q0 = quant1(v.x, db, zero), q1 = quant1(v.y, db, zero);
-    const int q2 = quant1(v.z, db, zero), q3 = quant1(v.w, db, zero);
-    const uint32_t packed = (uint32_t)(q0 & 0xff) | ((uint32_t)(q1 & 0xff) << 8) |
-                            ((uint32_t)(q2 & 0xff) << 16) | ((uint32_t)(q3 & 0xff) << 24);
-    *reinterpret_cast<uint32_t *>(q + t * K + 32 * b + 4 * li) = packed;
-
-    int sum = q0 + q1 + q2 + q3;
-    sum += __shfl_xor(sum, 1, 8);
-    sum += __shfl_xor(sum, 2, 8);
-    sum += __shfl_xor(sum, 4, 8);
-    if (li == 0) {
-        d[blk] = db;
-        s[blk] = db * (float)sum;
+    const int t = blockIdx.x / chunks;
+    const int c = blockIdx.x - t * chunks;
+    const int li = threadIdx.x & 7;
+    const float *xr = x + (int64_t)t * ldx;
+    const int nbk = K >> 5;
+    float4 v[QA_ITEMS];
+#pragma unroll
+    for (int i = 0; i < QA_ITEMS; ++i) {
+        const int k = (c * QA_ITEMS + i) * 1024 + 4 * threadIdx.x;
+        v[i] = *reinterpret_cast<const float4 *>(xr + (k < K ? k : K - 4));   // in range; not stored past K
+    }
+    uint32_t qp[QA_ITEMS];
+    float db[QA_ITEMS], sb[QA_ITEMS];
+    quant_chunks<QA_ITEMS>(v, qp, db, sb);
+#pragma unroll
+    for (int i = 0; i < QA_ITEMS; ++i) {
+        const int k = (c * QA_ITEMS + i) * 1024 + 4 * threadIdx.x;
+        if (k < K) {                          // whole 8-lane groups (K is a multiple of 32)
+            *reinterpret_cast<uint32_t *>(q + (int64_t)t * K + k) = qp[i];
+            if (li == 0) {
+                const int64_t b = (int64_t)t * nbk + (k >> 5);
+                d[b] = db[i];
+                s[b] = sb[i];
+            }
+        }
     }
 }
 
@@ -90,7 +91,7 @@ __global__ __launch_bounds__(256) void quantize_act_v1(
     for (int o = 1; o < 32; o <<= 1)
         amax = fmaxf(amax, __shfl_xor(amax, o, 32));
     const float db = amax / 127.0f;
-    const int qi = quant1(v, db, db == 0.0f);
+    const int qi = quant1(v, db, db == 0.0f ? 0.0f : 1.0f / db, db == 0.0f);
     q[t * K + 32 * b + li] = (int8_t)qi;
     int sum = qi;
 #pragma unroll
@@ -107,15 +108,16 @@ __global__ __launch_bounds__(256) void quantize_act_v1(
 hipError_t launch_quantize(const float *x, int64_t M, int64_t K, int64_t ldx,
                            int8_t *q, float *d, float *s, hipStream_t st)
 {
-    const int64_t nbk = K / 32;
-    const int64_t nblk = M * nbk;
     const bool vec = (reinterpret_cast<uintptr_t>(x) % 16 == 0) && (ldx % 4 == 0);
-    const int64_t threads = nblk * (vec ? 8 : 32);
-    const int64_t grid = (threads + 255) / 256;
-    if (vec)
-        quantize_act_v4<<<dim3((unsigned)grid), dim3(256), 0, st>>>(x, nblk, nbk, K, ldx, q, d, s);
-    else
+    if (vec) {
+        const int chunks = (int)((K + QA_ITEMS * 1024 - 1) / (QA_ITEMS * 1024));
+        quantize_act_v4<<<dim3((unsigned)(M * chunks)), dim3(256), 0, st>>>(x, (int)K, chunks, ldx, q, d, s);
+    } else {
+        const int64_t nbk = K / 32;
+        const int64_t nblk = M * nbk;
+        const int64_t grid = (nblk * 32 + 255) / 256;
         quantize_act_v1<<<dim3((unsigned)grid), dim3(256), 0, st>>>(x, nblk, nbk, K, ldx, q, d, s);
+    }
     return hipGetLastError();
 }
 

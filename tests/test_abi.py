@@ -122,6 +122,59 @@ def test_quantize_validation(L, kw, status, needle):
     assert "mq_quantize_act" in msg and needle in msg
 
 
+
+def _rms(L, x=P, w=P, M=4, K=256, ldx=256, eps=1e-6, q=P, d=P, s=P, y=None):
+    return L.mq_rmsnorm_quantize(x, w, M, K, ldx, eps, q, d, s, y, None)
+
+
+def _swi(L, g=P, u=P, M=4, K=256, ldg=512, ldu=512, q=P, d=P, s=P, y=None):
+    return L.mq_swiglu_quantize(g, u, M, K, ldg, ldu, q, d, s, y, None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(x=None), INVALID, "x is NULL"),
+    (dict(w=None), INVALID, "w is NULL"),
+    (dict(q=None), INVALID, "q is NULL"),
+    (dict(M=0), INVALID, "M=0"),
+    (dict(eps=-1.0), INVALID, "eps="),
+    (dict(eps=float("nan")), INVALID, "eps="),
+    (dict(eps=float("inf")), INVALID, "eps="),
+    (dict(K=160), SHAPE, "K=160"),
+    (dict(ldx=200), SHAPE, "ldx=200"),
+    (dict(ldx=258), ALIGN, "ldx=258"),
+    (dict(x=P + 4), ALIGN, "x="),
+    (dict(w=P + 8), ALIGN, "w="),
+    (dict(s=P + 4), ALIGN, "s="),
+    (dict(y=P + 4), ALIGN, "y="),
+])
+def test_rmsnorm_quantize_validation(L, kw, status, needle):
+    rc = _rms(L, **kw)
+    assert rc == status
+    msg = L.mq_last_error().decode()
+    assert "mq_rmsnorm_quantize" in msg and needle in msg
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(g=None), INVALID, "g is NULL"),
+    (dict(u=None), INVALID, "u is NULL"),
+    (dict(d=None), INVALID, "d is NULL"),
+    (dict(M=-1), INVALID, "M=-1"),
+    (dict(K=300), SHAPE, "K=300"),
+    (dict(ldg=128), SHAPE, "ldg=128"),
+    (dict(ldu=255), SHAPE, "ldu=255"),
+    (dict(ldu=258), ALIGN, "ldu=258"),
+    (dict(g=P + 4), ALIGN, "g="),
+    (dict(u=P + 12), ALIGN, "u="),
+    (dict(q=P + 1), ALIGN, "q="),
+    (dict(y=P + 8), ALIGN, "y="),
+    (dict(M=2 ** 40), SHAPE, "M="),
+])
+def test_swiglu_quantize_validation(L, kw, status, needle):
+    rc = _swi(L, **kw)
+    assert rc == status
+    msg = L.mq_last_error().decode()
+    assert "mq_swiglu_quantize" in msg and needle in msg
+
 def test_error_is_cleared_by_next_call(L):
     assert _q4k(L, W=None) == INVALID
     assert L.mq_last_error().decode() != ""
