@@ -300,7 +300,7 @@ def run_producers(dev):
     for M, K in ((3314, 3584), (1, 3584)):
         x0 = torch.from_numpy(synth.activations(rng, M, K, outliers=True)).to(dev)
         w = torch.from_numpy((1.0 + 0.3 * rng.standard_normal(K)).astype(np.float32)).to(dev)
-        copies = max(1, -(-ROTATE_BYTES // (x0.numel() * 4)))
+        copies = min(64, max(1, -(-ROTATE_BYTES // (x0.numel() * 4))))   # tiny inputs stay cached anyway
         xs = [x0] + [x0.clone() for _ in range(copies - 1)]
         q, d, s = mq.quantize_act(x0)
         y = torch.empty_like(x0)
@@ -318,7 +318,7 @@ def run_producers(dev):
     for M, K in ((3314, 18944), (1, 18944)):
         gu0 = torch.from_numpy(np.concatenate([(rng.standard_normal((M, K)) * 2.5).astype(np.float32),
                                                synth.activations(rng, M, K, outliers=True)], axis=1)).to(dev)
-        copies = max(1, -(-ROTATE_BYTES // (gu0.numel() * 4)))
+        copies = min(64, max(1, -(-ROTATE_BYTES // (gu0.numel() * 4))))
         gus = [gu0] + [gu0.clone() for _ in range(copies - 1)]
         q = torch.empty((M, K), dtype=torch.int8, device=dev)
         d = torch.empty((M, K // 32), dtype=torch.float32, device=dev)
