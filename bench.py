@@ -269,6 +269,7 @@ def run_all(args):
         del Ws, W0, out, q, d, s, x
         torch.cuda.empty_cache()
     run_producers(dev)
+    run_ffn(dev)
 
 
 def _time_rotating(fn, copies, reps):
@@ -284,6 +285,56 @@ def _time_rotating(fn, copies, reps):
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) * 1e3 / reps
+
+
+def run_ffn(dev):
+    """Fused FFN up half (gate and up matmuls + SwiGLU + plane in one launch)
+    against the separate launches (two matmuls, then mq_swiglu_quantize).
+    Weights rotate through >= 1 GiB of copies at M = 1."""
+    import numpy as np
+    import torch
+
+    import quant_gemm_amd as mq
+    from quant_gemm_amd import synth
+
+    for grp, M, N, K in (("ffn", 1, 18944, 3584), ("ffn", 3314, 18944, 3584)):
+        rng = np.random.default_rng(3000 + M)
+        Wg0 = torch.from_numpy(synth.q4k_weights(rng, N, K).reshape(-1)).to(dev)
+        Wu0 = torch.from_numpy(synth.q4k_weights(rng, N, K).reshape(-1)).to(dev)
+        x = torch.from_numpy(synth.activations(rng, M, K, outliers=True)).to(dev)
+        q, d, s = mq.quantize_act(x)
+        copies = max(1, -(-ROTATE_BYTES // (2 * Wg0.numel()))) if M <= mq.gemv_max_m() else 1
+        Wgs = [Wg0] + [Wg0.clone() for _ in range(copies - 1)]
+        Wus = [Wu0] + [Wu0.clone() for _ in range(copies - 1)]
+        qo = torch.empty((M, N), dtype=torch.int8, device=dev)
+        do = torch.empty((M, N // 32), dtype=torch.float32, device=dev)
+        so = torch.empty_like(do)
+        reps = max(2 * copies, 10)
+        fused_fn = lambda i: mq.ffn_q4k(Wgs[i], Wus[i], q, d, s, N, K, qo=qo, do=do, so=so)
+
+        g_out = torch.empty((M, N), dtype=torch.float32, device=dev)
+        u_out = torch.empty((M, N), dtype=torch.float32, device=dev)
+        sep_fn = lambda i: (mq.matmul_q4k(Wgs[i], q, d, s, N, K, out=g_out),
+                            mq.matmul_q4k(Wus[i], q, d, s, N, K, out=u_out),
+                            mq.swiglu_quantize(g_out, u_out, q=qo, d=do, s=so))
+        # alternate the two, 3 rounds each, and keep the medians (clocks drift)
+        ft, st_ = [], []
+        for _ in range(3):
+            ft.append(_time_rotating(fused_fn, copies, reps))
+            st_.append(_time_rotating(sep_fn, copies, reps))
+        fused, sep = float(np.median(ft)), float(np.median(st_))
+        ops = 2 * 2 * M * N * K
+        row = {"group": grp, "case": f"ffn_q4k gate|up+SwiGLU+plane M={M} N={N} K={K}", "us": round(fused, 2),
+               "TOPS": round(ops / (fused * 1e-6) / 1e12, 2), "separate_us": round(sep, 2)}
+        if M <= mq.gemv_max_m():
+            b = 2 * N * (K // 256) * 144 + M * (K + 8 * (K // 32)) + M * (N + 8 * (N // 32))
+            row["GBs"] = round(b / (fused * 1e-6) / 1e9, 1)
+            row["frac_hbm"] = round(row["GBs"] / HBM_PEAK_GBS, 3)
+        else:
+            row["frac_int8_peak"] = round(row["TOPS"] / INT8_PEAK_TOPS, 4)
+        print(json.dumps(row), flush=True)
+        del Wgs, Wus, Wg0, Wu0, g_out, u_out
+        torch.cuda.empty_cache()
 
 
 def run_producers(dev):

@@ -162,6 +162,30 @@ int mq_matmul_q6k_ex(const void *W, const int8_t *q, const float *d,
                      const float *s, int64_t M, int64_t N, int64_t K,
                      float *out, void *stream, int path);
 
+/*
+ * Fused FFN up half: the gate and up projections and SwiGLU in one launch,
+ * producing the int8 plane of the down projection's input. The pages fuse
+ * the decode FFN as one gate|up matmul with an in-place SwiGLU (FusedFFN,
+ * minfer Compute Graph Design, "The Op vocabulary") and have the SwiGLU
+ * epilogue emit the int8 plane (minfer Features, "GPU — CUDA").
+ *   g = the Q4_K matmul of Wg with the plane (q, d, s), u the same with Wu,
+ *       each as mq_matmul_q4k computes it (f32, within its tolerance);
+ *   y[t][n] = f32(SiLU(g[t][n]) in f64) * u[t][n], as mq_swiglu_quantize;
+ *   qo [M][N], do_ and so [M][N/32]: the quantizer's plane of y (exactly
+ *       what mq_quantize_act would write for y);
+ *   y  optional f32 [M][N], written when not NULL.
+ * Wg and Wu are N rows of K each (Q4_K layout); N is a positive multiple of
+ * 256 (it is the down projection's K). M <= mq_gemv_max_m() runs a fused
+ * GEMV, larger M a GEMM whose tiles pair 64 gate rows with the same 64 up
+ * rows. Alignment as for the matmuls; qo, do_, so and y 16-byte aligned.
+ */
+int mq_ffn_q4k(const void *Wg, const void *Wu, const int8_t *q, const float *d,
+               const float *s, int64_t M, int64_t N, int64_t K, int8_t *qo,
+               float *do_, float *so, float *y, void *stream);
+int mq_ffn_q4k_ex(const void *Wg, const void *Wu, const int8_t *q, const float *d,
+                  const float *s, int64_t M, int64_t N, int64_t K, int8_t *qo,
+                  float *do_, float *so, float *y, void *stream, int path);
+
 /* Largest M served by the GEMV path under MQ_PATH_AUTO. */
 int64_t mq_gemv_max_m(void);
 

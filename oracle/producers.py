@@ -78,3 +78,16 @@ def swiglu_quantize(g, u):
     y = swiglu(g, u)
     q, d, s = quantize_act(y)
     return q, d, s, y
+
+
+def ffn_q4k(Wg, Wu, q, d, N, K, tokens=None):
+    """Fused FFN up half: (q, d, s, y) with y = SwiGLU(g, u), g and u the
+    oracle's f32 Q4_K matmuls of the plane (q, d) with Wg and Wu (minfer
+    Compute Graph Design, "The Op vocabulary": FusedFFN, a gate|up matmul with
+    an in-place SwiGLU). Only composes the pinned pieces. With `tokens`, only
+    those rows of the plane are computed (each row is independent)."""
+    from . import matmul_q4k
+    g = matmul_q4k(Wg, q, d, N, K, tokens=tokens)
+    u = matmul_q4k(Wu, q, d, N, K, tokens=tokens)
+    return swiglu_quantize(g, u)
+

@@ -36,6 +36,8 @@ SIGNATURES = {
     "mq_quantize_act": ([_P, _I64, _I64, _I64, _P, _P, _P, _P], ctypes.c_int),
     "mq_rmsnorm_quantize": ([_P, _P, _I64, _I64, _I64, ctypes.c_float, _P, _P, _P, _P, _P], ctypes.c_int),
     "mq_swiglu_quantize": ([_P, _P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P], ctypes.c_int),
+    "mq_ffn_q4k": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P], ctypes.c_int),
+    "mq_ffn_q4k_ex": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P, ctypes.c_int], ctypes.c_int),
     "mq_matmul_q4k": (_MATMUL_ARGS, ctypes.c_int),
     "mq_matmul_q6k": (_MATMUL_ARGS, ctypes.c_int),
     "mq_matmul_q4k_ex": (_MATMUL_ARGS + [ctypes.c_int], ctypes.c_int),
@@ -197,3 +199,26 @@ def matmul_q4k(W, q, d, s, N, K, out=None, stream=None, path=MQ_PATH_AUTO):
 def matmul_q6k(W, q, d, s, N, K, out=None, stream=None, path=MQ_PATH_AUTO):
     """out [M, N] f32 = Q6_K weights W (N rows of K) times the activation plane (q, d); s unused."""
     return _matmul("mq_matmul_q6k_ex", Q6K_BLOCK_BYTES, W, q, d, s, N, K, out, stream, path)
+
+
+def ffn_q4k(Wg, Wu, q, d, s, N, K, qo=None, do=None, so=None, y=None, stream=None, path=MQ_PATH_AUTO):
+    """The int8 plane of SiLU(x Wg^T) * (x Wu^T) for Q4_K gate and up weights
+    (each N rows of K) and the activation plane (q, d, s). Returns (qo, do, so),
+    plus y when a y tensor is passed."""
+    import torch
+    L = load()
+    for W in (Wg, Wu):
+        assert W.is_cuda and W.dtype == torch.uint8 and W.is_contiguous()
+        assert W.numel() == N * (K // 256) * Q4K_BLOCK_BYTES, "W size does not match N, K"
+    assert q.dtype == torch.int8 and q.is_contiguous() and q.dim() == 2 and q.shape[1] == K
+    M = q.shape[0]
+    for t in (d, s):
+        assert t.dtype == torch.float32 and t.is_contiguous() and tuple(t.shape) == (M, K // 32)
+    qo, do, so = _plane_outputs(M, N, q.device, qo, do, so)
+    if y is not None:
+        assert y.dtype == torch.float32 and y.is_contiguous() and tuple(y.shape) == (M, N)
+    _check(L.mq_ffn_q4k_ex(Wg.data_ptr(), Wu.data_ptr(), q.data_ptr(), d.data_ptr(), s.data_ptr(),
+                           M, N, K, qo.data_ptr(), do.data_ptr(), so.data_ptr(),
+                           None if y is None else y.data_ptr(), _stream(stream), path))
+    return (qo, do, so) if y is None else (qo, do, so, y)
+

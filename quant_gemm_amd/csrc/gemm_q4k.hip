@@ -37,6 +37,7 @@
 // tokens), B = weights (columns = output rows).
 #include "mq_device.h"
 #include "mq_launch.h"
+#include "quant_core.h"
 
 namespace mq {
 namespace {
@@ -113,18 +114,40 @@ __device__ __forceinline__ void limbs4(const float (&x)[4], uint4 &r0, uint4 &r1
     r1 = make_uint4(l[0] | (l[1] << 16), l[2] | (l[3] << 16), 0u, 0u);
 }
 
+// Weight row r (0..BN-1) of a tile. Plain GEMM: row n0 + r of W. Gate|up
+// (FFN): rows 0..63 are the gate rows n0..n0+63 (W) and rows 64..127 the up
+// rows n0..n0+63 (W2), so that a lane's tiles b and b+2 hold g and u of the
+// same output column. Rows past N read the last row (never stored).
+struct WRows {
+    const uint8_t *W, *W2;
+    int n0, N;
+    int64_t rowb;
+    template <bool FFN>
+    __device__ __forceinline__ const uint8_t *row(int r) const
+    {
+        if (FFN)
+            return (r < 64 ? W : W2) + (int64_t)min(n0 + (r & 63), N - 1) * rowb;
+        return W + (int64_t)min(n0 + r, N - 1) * rowb;
+    }
+    template <bool FFN>
+    __device__ __forceinline__ bool valid(int r) const
+    {
+        return (FFN ? n0 + (r & 63) : n0 + r) < N;
+    }
+};
+
 __device__ __forceinline__ int a_slot(int r, int c) { return r * 8 + (c ^ (r & 7)); }
 __device__ __forceinline__ int q_slot(int r, int c) { return r * 4 + (c ^ ((r >> 2) & 3)); }
 
 // Start the DMA of step st's activation and quant tiles into s. Rows past M
 // or N read the last valid row instead: their results are never stored.
-__device__ __forceinline__ void issue_tiles(Stage &s, const uint8_t *__restrict__ W,
-                                            const int8_t *__restrict__ q, int M, int N, int K,
-                                            int t0, int n0, int st, int wave, int lane)
+template <bool FFN>
+__device__ __forceinline__ void issue_tiles(Stage &s, const WRows &rows,
+                                            const int8_t *__restrict__ q, int M, int K,
+                                            int t0, int st, int wave, int lane)
 {
     const int k0 = st * BK;
     const int sb = st >> 1, hf = st & 1;
-    const int64_t rowb = (int64_t)(K >> 8) * 144;
 #pragma unroll
     for (int ii = 0; ii < A_CHUNKS / 64 / NWAVES; ++ii) {
         const int i = wave * (A_CHUNKS / 64 / NWAVES) + ii;
@@ -140,8 +163,7 @@ __device__ __forceinline__ void issue_tiles(Stage &s, const uint8_t *__restrict_
         const int p = 64 * i + lane;
         const int r = p >> 2;
         const int c = (p & 3) ^ ((r >> 2) & 3);
-        const int n = min(n0 + r, N - 1);
-        dma16(W + (int64_t)n * rowb + (int64_t)sb * 144 + 16 + 64 * hf + 16 * c, s.qs + 1024 * i);
+        dma16(rows.row<FFN>(r) + (int64_t)sb * 144 + 16 + 64 * hf + 16 * c, s.qs + 1024 * i);
     }
 }
 
@@ -154,18 +176,16 @@ struct Side {
     float4 ds;      // 4 scales (tid < BM) or 4 sums (tid >= BM) of token t0 + tid % BM
 };
 
-__device__ __forceinline__ void load_side(Side &p, const uint8_t *__restrict__ W,
+template <bool FFN>
+__device__ __forceinline__ void load_side(Side &p, const WRows &rows,
                                           const float *__restrict__ dx,
-                                          const float *__restrict__ sx, int M, int N, int K,
-                                          int t0, int n0, int st)
+                                          const float *__restrict__ sx, int M, int K,
+                                          int t0, int st)
 {
     const int tid = threadIdx.x;
     const int k0 = st * BK;
-    const int64_t rowb = (int64_t)(K >> 8) * 144;
-    if (tid < BN) {
-        const int n = min(n0 + tid, N - 1);
-        p.hdr = *reinterpret_cast<const uint4 *>(W + (int64_t)n * rowb + (int64_t)(st >> 1) * 144);
-    }
+    if (tid < BN)
+        p.hdr = *reinterpret_cast<const uint4 *>(rows.row<FFN>(tid) + (int64_t)(st >> 1) * 144);
     if (tid < 2 * BM) {
         const int t = min(t0 + (tid & (BM - 1)), M - 1);
         const float *src = tid < BM ? dx : sx;
@@ -173,8 +193,9 @@ __device__ __forceinline__ void load_side(Side &p, const uint8_t *__restrict__ W
     }
 }
 
-__device__ __forceinline__ void store_side(Stage &s, const Side &p, int st, int M, int N,
-                                           int t0, int n0)
+template <bool FFN>
+__device__ __forceinline__ void store_side(Stage &s, const Side &p, const WRows &rows, int st, int M,
+                                           int t0)
 {
     const int tid = threadIdx.x;
     const int hf = st & 1;
@@ -195,7 +216,7 @@ __device__ __forceinline__ void store_side(Stage &s, const Side &p, int st, int 
         // are bytes 0..3 (scale) and 4..7 (min) masked to 6 bits; codes
         // 4..7 take their low 4 bits from bytes 8..11 and their high 2 bits
         // from the top of bytes 0..3 (scale) or 4..7 (min).
-        const uint4 h = n0 + tid < N ? p.hdr : make_uint4(0, 0, 0, 0);
+        const uint4 h = rows.valid<FFN>(tid) ? p.hdr : make_uint4(0, 0, 0, 0);
         const float dd = f16_bits_to_f32(h.x);
         const float dm = f16_bits_to_f32(h.x >> 16);
         const uint32_t scw = hf == 0 ? (h.y & 0x3f3f3f3fu)
@@ -295,10 +316,42 @@ __device__ __forceinline__ void compute_step(const Stage &s, v16f (&acc)[TM][TN]
     }
 }
 
+// Max / sum over the 32 lanes of each wavefront half, result in all of them:
+// DPP within 16-lane rows, then one swap of the row pairs.
+__device__ __forceinline__ float half_max(float v)
+{
+    v = fmaxf(v, dpp_move<0xb1>(v));
+    v = fmaxf(v, dpp_move<0x4e>(v));
+    v = fmaxf(v, dpp_move<0x141>(v));
+    v = fmaxf(v, dpp_move<0x140>(v));
+    return fmaxf(v, __shfl_xor(v, 16));
+}
+__device__ __forceinline__ int half_sum(int v)
+{
+    v += __builtin_amdgcn_update_dpp(0, v, 0xb1, 0xf, 0xf, true);
+    v += __builtin_amdgcn_update_dpp(0, v, 0x4e, 0xf, 0xf, true);
+    v += __builtin_amdgcn_update_dpp(0, v, 0x141, 0xf, 0xf, true);
+    v += __builtin_amdgcn_update_dpp(0, v, 0x140, 0xf, 0xf, true);
+    return v + __shfl_xor(v, 16);
+}
+
+// SiLU(g) * u as the SwiGLU producer computes it (f64 SiLU rounded once,
+// f32 product).
+__device__ __forceinline__ float swiglu1(float g, float u)
+{
+    const double g64 = (double)g;
+    return (float)(g64 / (1.0 + exp(-g64))) * u;
+}
+
+// Plain: out (or a split-K partial plane) = the f32 result. FFN (W = gate,
+// W2 = up, tiles of 64 output columns): y = SiLU(g) * u per output, written
+// as its int8 plane qo / do_ / so (and y itself when y != nullptr).
+template <bool FFN>
 __global__ __launch_bounds__(NTHR, MQ_Q4K_OCC) void gemm_q4k_kernel(
-    const uint8_t *__restrict__ W, const int8_t *__restrict__ q,
+    const uint8_t *__restrict__ W, const uint8_t *__restrict__ W2, const int8_t *__restrict__ q,
     const float *__restrict__ dx, const float *__restrict__ sx, int M, int N,
-    int K, int tiles_m, int nsplit, float *__restrict__ out)
+    int K, int tiles_m, int nsplit, float *__restrict__ out, int8_t *__restrict__ qo,
+    float *__restrict__ do_, float *__restrict__ so)
 {
     __shared__ Stage S0, S1;
     // blockIdx = split * tiles + tile_n * tiles_m + tile_m; split s of nsplit
@@ -314,7 +367,8 @@ __global__ __launch_bounds__(NTHR, MQ_Q4K_OCC) void gemm_q4k_kernel(
     const int st_end = 2 * (int)((int64_t)(split + 1) * pairs / nsplit);
     float *dst = out + (int64_t)split * M * N;
     const int t0 = tile_m * BM;
-    const int n0 = tile_n * BN;
+    const int n0 = tile_n * (FFN ? BN / 2 : BN);
+    const WRows rows{W, W2, n0, N, (int64_t)(K >> 8) * 144};
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int wm = wave % WM, wn = wave / WM;
@@ -331,31 +385,95 @@ __global__ __launch_bounds__(NTHR, MQ_Q4K_OCC) void gemm_q4k_kernel(
 
     // The step range is even (whole super-blocks): steps alternate S0, S1.
     Side p;
-    issue_tiles(S0, W, q, M, N, K, t0, n0, st_begin, wave, lane);
-    load_side(p, W, dx, sx, M, N, K, t0, n0, st_begin);
+    issue_tiles<FFN>(S0, rows, q, M, K, t0, st_begin, wave, lane);
+    load_side<FFN>(p, rows, dx, sx, M, K, t0, st_begin);
     wait_vm<0>();
-    store_side(S0, p, st_begin, M, N, t0, n0);
+    store_side<FFN>(S0, p, rows, st_begin, M, t0);
     __syncthreads();
     for (int st = st_begin; st < st_end; st += 2) {
-        issue_tiles(S1, W, q, M, N, K, t0, n0, st + 1, wave, lane);
-        load_side(p, W, dx, sx, M, N, K, t0, n0, st + 1);
+        issue_tiles<FFN>(S1, rows, q, M, K, t0, st + 1, wave, lane);
+        load_side<FFN>(p, rows, dx, sx, M, K, t0, st + 1);
         compute_step(S0, acc, wm, wn, lr, lh);
         wait_vm<0>();
-        store_side(S1, p, st + 1, M, N, t0, n0);
+        store_side<FFN>(S1, p, rows, st + 1, M, t0);
         __syncthreads();
         const bool more = st + 2 < st_end;
         if (more) {
-            issue_tiles(S0, W, q, M, N, K, t0, n0, st + 2, wave, lane);
-            load_side(p, W, dx, sx, M, N, K, t0, n0, st + 2);
+            issue_tiles<FFN>(S0, rows, q, M, K, t0, st + 2, wave, lane);
+            load_side<FFN>(p, rows, dx, sx, M, K, t0, st + 2);
         }
         compute_step(S1, acc, wm, wn, lr, lh);
         if (more) {
             wait_vm<0>();
-            store_side(S0, p, st + 2, M, N, t0, n0);
+            store_side<FFN>(S0, p, rows, st + 2, M, t0);
         }
         __syncthreads();
     }
 
+    if (FFN) {
+        static_assert(TM == 1 && TN == 4 && WN == 1, "gate|up tiles: b and b + 2 share columns");
+        // y for (token t, column n): tiles b = 0, 1 hold g, tiles b + 2 the u of
+        // the same columns. A 32-value block of the plane is one tile row:
+        // lanes lr = 0..31 of one half (lh) at one v, combined across lanes.
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const int n = n0 + 32 * b + lr;
+            float y[16];
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                y[v] = swiglu1(acc[0][b][v], acc[0][b + 2][v]);
+            float amax[16];
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                amax[v] = fabsf(y[v]);
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                amax[v] = half_max(amax[v]);
+            float db[16], qf[16];
+            bool slow = false;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                db[v] = amax[v] / 127.0f;
+                const bool zero = db[v] == 0.0f;
+                const float t = y[v] * (zero ? 0.0f : 1.0f / db[v]);
+                slow |= !zero && (db[v] < 0x1p-100f || q_near_half(t));
+                qf[v] = q_clamp_round(t);
+            }
+            if (__any(slow)) {
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const bool zero = db[v] == 0.0f;
+                    const float t = y[v] * (zero ? 0.0f : 1.0f / db[v]);
+                    if (!zero && (db[v] < 0x1p-100f || q_near_half(t)))
+                        qf[v] = q_clamp_round(y[v] / db[v]);
+                }
+            }
+            int sum[16];
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                sum[v] = (int)qf[v];
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                sum[v] = half_sum(sum[v]);
+            if (n < N) {
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int t = t0 + wm * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
+                    if (t < M) {
+                        qo[(int64_t)t * N + n] = (int8_t)(int)qf[v];
+                        if (out)
+                            out[(int64_t)t * N + n] = y[v];
+                        if (lr == 0) {
+                            const int64_t blk = (int64_t)t * (N >> 5) + (n >> 5);
+                            do_[blk] = db[v];
+                            so[blk] = db[v] * (float)sum[v];
+                        }
+                    }
+                }
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int a = 0; a < TM; ++a) {
 #pragma unroll
@@ -384,10 +502,21 @@ hipError_t launch_gemm_q4k(const uint8_t *W, const int8_t *q, const float *d,
     const int tiles = tiles_m * tiles_n;
     const int nsplit = gemm_splits(tiles, K >> 8, M, N, K, Q4K_SLOT_OPS);
     return run_split_k(nsplit, (int64_t)M * N, out, st, [&](float *dst) {
-        gemm_q4k_kernel<<<dim3((unsigned)(tiles * nsplit)), dim3(NTHR), 0, st>>>(W, q, d, s, M, N, K,
-                                                                                 tiles_m, nsplit, dst);
+        gemm_q4k_kernel<false><<<dim3((unsigned)(tiles * nsplit)), dim3(NTHR), 0, st>>>(
+            W, nullptr, q, d, s, M, N, K, tiles_m, nsplit, dst, nullptr, nullptr, nullptr);
         return hipGetLastError();
     });
+}
+
+hipError_t launch_gemm_q4k_ffn(const uint8_t *Wg, const uint8_t *Wu, const int8_t *q, const float *d,
+                               const float *s, int M, int N, int K, int8_t *qo, float *do_, float *so,
+                               float *y, hipStream_t st)
+{
+    const int tiles_m = (M + BM - 1) / BM;
+    const int tiles_n = (N + BN / 2 - 1) / (BN / 2);
+    gemm_q4k_kernel<true><<<dim3((unsigned)(tiles_m * tiles_n)), dim3(NTHR), 0, st>>>(
+        Wg, Wu, q, d, s, M, N, K, tiles_m, 1, y, qo, do_, so);
+    return hipGetLastError();
 }
 
 } // namespace mq

@@ -18,6 +18,9 @@
 // Q6_K); activations (K bytes + K/8 floats per token) stay in cache.
 #include "mq_device.h"
 #include "mq_launch.h"
+#include "quant_core.h"
+
+#include <type_traits>
 
 namespace mq {
 namespace {
@@ -82,46 +85,25 @@ __device__ __forceinline__ void act_store(const ActCopy &c, v4i *lds, int M, int
     }
 }
 
-template <int MT, int R, int IT, bool ACT_LDS>
-__global__ __launch_bounds__(64 * GEMV_WAVES) void gemv_q4k_kernel(
-    const uint8_t *__restrict__ W, const int8_t *__restrict__ q,
-    const float *__restrict__ dx, const float *__restrict__ sx, int M, int N,
-    int K, float *__restrict__ out)
+// This lane's partial dot products for the R consecutive rows that start at
+// `base` (each nb blocks; `rows` of them are real), accumulated into
+// acc[r][m]. qa / da / sa are the activation plane (global memory or its
+// LDS copy). after_first_loads() runs once, right after the first batch of
+// weight loads is issued: the activation copy into LDS goes there, so that
+// it overlaps the weight stream.
+template <int MT, int R, int IT, class F>
+__device__ __forceinline__ void q4k_rows(const uint8_t *__restrict__ base, int rows, int nb, int K, int M,
+                                         const int8_t *qa, const float *da, const float *sa, int lane,
+                                         float (&acc)[R][MT], F &&after_first_loads)
 {
-    __shared__ v4i act[ACT_LDS ? GEMV_ACT_LDS / 16 : 1];
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int row0 = (blockIdx.x * GEMV_WAVES + wave) * R;
-    ActCopy ac;
-    if constexpr (ACT_LDS)
-        act_load(ac, q, dx, sx, M, K);
-    const int nb = K >> 8;                       // blocks per row
     const int nb32 = K >> 5;
-    const int rows = max(0, min(R, N - row0));  // 0 for a wavefront past the last row
     const int total = rows * nb;                 // blocks of this wavefront
     const int slot = lane / 9;                   // block within a pass (7 = idle lane)
     const int part = lane - 9 * slot;            // chunk within the block
     const int hdr_lane = 9 * slot;
-    const uint8_t *base = W + (int64_t)row0 * nb * 144;
-
-    float acc[R][MT];
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-        for (int m = 0; m < MT; ++m)
-            acc[r][m] = 0.0f;
-
     // this lane's (row, block) position, advanced by 7 blocks per pass
     int rl = 0, blk = slot;
     while (blk >= nb) { blk -= nb; ++rl; }
-
-    const int8_t *qa = q;                        // activation sources: global or LDS
-    const float *da = dx, *sa = sx;
-    if constexpr (ACT_LDS) {
-        qa = reinterpret_cast<const int8_t *>(act);
-        da = reinterpret_cast<const float *>(qa + M * K);
-        sa = da + M * nb32;
-    }
     for (int it0 = 0; it0 < max(total, 1); it0 += 7 * IT) {
         v4i v[IT];
 #pragma unroll
@@ -131,10 +113,8 @@ __global__ __launch_bounds__(64 * GEMV_WAVES) void gemv_q4k_kernel(
                        ? __builtin_nontemporal_load(reinterpret_cast<const v4i *>(base + (int64_t)fb * 144 + 16 * part))
                        : v4i{0, 0, 0, 0};
         }
-        if (ACT_LDS && it0 == 0) {
-            act_store(ac, act, M, K);
-            __syncthreads();
-        }
+        if (it0 == 0)
+            after_first_loads();
 #pragma unroll
         for (int i = 0; i < IT; ++i) {
             const int fb = it0 + 7 * i + slot;
@@ -193,6 +173,44 @@ __global__ __launch_bounds__(64 * GEMV_WAVES) void gemv_q4k_kernel(
             while (blk >= nb) { blk -= nb; ++rl; }
         }
     }
+}
+
+template <int MT, int R, int IT, bool ACT_LDS>
+__global__ __launch_bounds__(64 * GEMV_WAVES) void gemv_q4k_kernel(
+    const uint8_t *__restrict__ W, const int8_t *__restrict__ q,
+    const float *__restrict__ dx, const float *__restrict__ sx, int M, int N,
+    int K, float *__restrict__ out)
+{
+    __shared__ v4i act[ACT_LDS ? GEMV_ACT_LDS / 16 : 1];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int row0 = (blockIdx.x * GEMV_WAVES + wave) * R;
+    ActCopy ac;
+    if constexpr (ACT_LDS)
+        act_load(ac, q, dx, sx, M, K);
+    const int nb = K >> 8;
+    const int rows = max(0, min(R, N - row0));  // 0 for a wavefront past the last row
+    const uint8_t *base = W + (int64_t)row0 * nb * 144;
+
+    float acc[R][MT];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+            acc[r][m] = 0.0f;
+    const int8_t *qa = q;                        // activation sources: global or LDS
+    const float *da = dx, *sa = sx;
+    if constexpr (ACT_LDS) {
+        qa = reinterpret_cast<const int8_t *>(act);
+        da = reinterpret_cast<const float *>(qa + M * K);
+        sa = da + M * (K >> 5);
+    }
+    q4k_rows<MT, R, IT>(base, rows, nb, K, M, qa, da, sa, lane, acc, [&] {
+        if constexpr (ACT_LDS) {
+            act_store(ac, act, M, K);
+            __syncthreads();
+        }
+    });
 #pragma unroll
     for (int r = 0; r < R; ++r) {
 #pragma unroll
@@ -200,6 +218,97 @@ __global__ __launch_bounds__(64 * GEMV_WAVES) void gemv_q4k_kernel(
             const float v = wave_sum(acc[r][m]);
             if (lane == 0 && m < M && r < rows)
                 out[(int64_t)m * N + row0 + r] = v;
+        }
+    }
+}
+
+// Fused FFN up half at small M: a workgroup owns 32 consecutive output
+// columns n0..n0+31; wavefront w computes the gate and the up rows
+// n0 + 8w .. n0 + 8w + 7 (the same stream as the plain kernel, gate rows then
+// up rows), the 32 x M results meet in LDS, and each 32-lane half of the
+// first wavefront turns one token's 32 values into y = SiLU(g) * u and one
+// quantized block of the down projection's plane.
+constexpr int FFN_ROWS = 8;                       // rows of each matrix per wavefront
+
+template <int MT, bool ACT_LDS>
+__global__ __launch_bounds__(64 * GEMV_WAVES) void gemv_q4k_ffn_kernel(
+    const uint8_t *__restrict__ Wg, const uint8_t *__restrict__ Wu, const int8_t *__restrict__ q,
+    const float *__restrict__ dx, const float *__restrict__ sx, int M, int N, int K,
+    int8_t *__restrict__ qo, float *__restrict__ do_, float *__restrict__ so, float *__restrict__ y)
+{
+    static_assert(GEMV_WAVES * FFN_ROWS == 32, "one workgroup per 32-value block");
+    __shared__ v4i act[ACT_LDS ? GEMV_ACT_LDS / 16 : 1];
+    __shared__ float res[2][MT][32];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int n0 = blockIdx.x * 32;
+    const int nb = K >> 8;
+    ActCopy ac;
+    if constexpr (ACT_LDS)
+        act_load(ac, q, dx, sx, M, K);
+    const int8_t *qa = q;
+    const float *da = dx, *sa = sx;
+    if constexpr (ACT_LDS) {
+        qa = reinterpret_cast<const int8_t *>(act);
+        da = reinterpret_cast<const float *>(qa + M * K);
+        sa = da + M * (K >> 5);
+    }
+    const int64_t off = (int64_t)(n0 + FFN_ROWS * wave) * nb * 144;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        float acc[FFN_ROWS][MT];
+#pragma unroll
+        for (int r = 0; r < FFN_ROWS; ++r)
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+                acc[r][m] = 0.0f;
+        q4k_rows<MT, FFN_ROWS, 8>((h == 0 ? Wg : Wu) + off, FFN_ROWS, nb, K, M, qa, da, sa, lane, acc, [&] {
+            if constexpr (ACT_LDS) {
+                if (h == 0) {
+                    act_store(ac, act, M, K);
+                    __syncthreads();
+                }
+            }
+        });
+#pragma unroll
+        for (int r = 0; r < FFN_ROWS; ++r)
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                const float v = wave_sum(acc[r][m]);
+                if (lane == 0)
+                    res[h][m][FFN_ROWS * wave + r] = v;
+            }
+    }
+    __syncthreads();
+    if (wave != 0)
+        return;
+    const int c = lane & 31;
+    for (int m0 = 0; m0 < MT; m0 += 2) {
+        const int m = m0 + (lane >> 5);
+        const bool tok = m < M;
+        const double g64 = (double)res[0][m < MT ? m : 0][c];
+        const float yv = tok ? (float)(g64 / (1.0 + exp(-g64))) * res[1][m < MT ? m : 0][c] : 0.0f;
+        float amax = fabsf(yv);
+#pragma unroll
+        for (int k = 1; k < 32; k <<= 1)
+            amax = fmaxf(amax, __shfl_xor(amax, k, 32));
+        const float db = amax / 127.0f;
+        const bool zero = db == 0.0f;
+        const float t = yv * (zero ? 0.0f : 1.0f / db);
+        const int qi = zero ? 0 : (int)q_clamp_round(db < 0x1p-100f || q_near_half(t) ? yv / db : t);
+        int sum = qi;
+#pragma unroll
+        for (int k = 1; k < 32; k <<= 1)
+            sum += __shfl_xor(sum, k, 32);
+        if (tok) {
+            qo[(int64_t)m * N + n0 + c] = (int8_t)qi;
+            if (y)
+                y[(int64_t)m * N + n0 + c] = yv;
+            if (c == 0) {
+                const int64_t b = (int64_t)m * (N >> 5) + (n0 >> 5);
+                do_[b] = db;
+                so[b] = db * (float)sum;
+            }
         }
     }
 }
@@ -701,6 +810,26 @@ hipError_t launch_gemv_q4k(const uint8_t *W, const int8_t *q, const float *d,
     if (M <= 2) return gemv_q4k_mt<2>(W, q, d, s, M, N, K, out, st);
     if (M <= 4) return gemv_q4k_mt<4>(W, q, d, s, M, N, K, out, st);
     return gemv_q4k_mt<8>(W, q, d, s, M, N, K, out, st);
+}
+
+hipError_t launch_gemv_q4k_ffn(const uint8_t *Wg, const uint8_t *Wu, const int8_t *q, const float *d,
+                               const float *s, int M, int N, int K, int8_t *qo, float *do_, float *so,
+                               float *y, hipStream_t st)
+{
+    const dim3 grid((unsigned)(N / 32)), block(64 * GEMV_WAVES);
+    const bool lds = (int64_t)M * K * 5 / 4 <= GEMV_ACT_LDS;
+    auto go = [&](auto mt) {
+        constexpr int MT = decltype(mt)::value;
+        if (lds)
+            gemv_q4k_ffn_kernel<MT, true><<<grid, block, 0, st>>>(Wg, Wu, q, d, s, M, N, K, qo, do_, so, y);
+        else
+            gemv_q4k_ffn_kernel<MT, false><<<grid, block, 0, st>>>(Wg, Wu, q, d, s, M, N, K, qo, do_, so, y);
+    };
+    if (M <= 1) go(std::integral_constant<int, 1>{});
+    else if (M <= 2) go(std::integral_constant<int, 2>{});
+    else if (M <= 4) go(std::integral_constant<int, 4>{});
+    else go(std::integral_constant<int, 8>{});
+    return hipGetLastError();
 }
 
 hipError_t launch_gemv_q6k(const uint8_t *W, const int8_t *q, const float *d,

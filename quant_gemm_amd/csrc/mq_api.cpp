@@ -122,6 +122,52 @@ int matmul(bool q6, const void *W, const int8_t *q, const float *d, const float 
     return launched(e, fn);
 }
 
+int ffn(const void *Wg, const void *Wu, const int8_t *q, const float *d, const float *s, int64_t M,
+        int64_t N, int64_t K, int8_t *qo, float *do_, float *so, float *y, void *stream, int path)
+{
+    const char *fn = "mq_ffn_q4k";
+    if (!Wg) return fail(MQ_ERR_INVALID_ARG, "%s: Wg is NULL", fn);
+    if (!Wu) return fail(MQ_ERR_INVALID_ARG, "%s: Wu is NULL", fn);
+    if (!q) return fail(MQ_ERR_INVALID_ARG, "%s: q is NULL", fn);
+    if (!d) return fail(MQ_ERR_INVALID_ARG, "%s: d is NULL", fn);
+    if (!s) return fail(MQ_ERR_INVALID_ARG, "%s: s is NULL (the Q4_K min term needs it)", fn);
+    if (!qo) return fail(MQ_ERR_INVALID_ARG, "%s: qo is NULL", fn);
+    if (!do_) return fail(MQ_ERR_INVALID_ARG, "%s: do_ is NULL", fn);
+    if (!so) return fail(MQ_ERR_INVALID_ARG, "%s: so is NULL", fn);
+    if (M <= 0) return fail(MQ_ERR_INVALID_ARG, "%s: M=%lld must be positive", fn, (long long)M);
+    if (N <= 0 || N % 256 != 0)
+        return fail(MQ_ERR_SHAPE, "%s: N=%lld must be a positive multiple of 256", fn, (long long)N);
+    if (int rc = check_K(K, fn)) return rc;
+    if (M > kMaxDim || N > kMaxDim)
+        return fail(MQ_ERR_SHAPE, "%s: M=%lld, N=%lld: each must be at most %lld", fn, (long long)M,
+                    (long long)N, (long long)kMaxDim);
+    if (path != MQ_PATH_AUTO && path != MQ_PATH_GEMV && path != MQ_PATH_GEMM)
+        return fail(MQ_ERR_INVALID_ARG, "%s: path=%d is not MQ_PATH_AUTO/GEMV/GEMM", fn, path);
+    if (path == MQ_PATH_GEMV && M > mq::GEMV_MAX_M)
+        return fail(MQ_ERR_INVALID_ARG, "%s: path=MQ_PATH_GEMV needs M <= %d, got M=%lld", fn,
+                    mq::GEMV_MAX_M, (long long)M);
+    if (!aligned(Wg, 16)) return fail(MQ_ERR_ALIGN, "%s: Wg=%p is not 16-byte aligned", fn, Wg);
+    if (!aligned(Wu, 16)) return fail(MQ_ERR_ALIGN, "%s: Wu=%p is not 16-byte aligned", fn, Wu);
+    if (!aligned(q, 16)) return fail(MQ_ERR_ALIGN, "%s: q=%p is not 16-byte aligned", fn, (const void *)q);
+    if (!aligned(d, 16)) return fail(MQ_ERR_ALIGN, "%s: d=%p is not 16-byte aligned", fn, (const void *)d);
+    if (!aligned(s, 16)) return fail(MQ_ERR_ALIGN, "%s: s=%p is not 16-byte aligned", fn, (const void *)s);
+    if (!aligned(qo, 16)) return fail(MQ_ERR_ALIGN, "%s: qo=%p is not 16-byte aligned", fn, (const void *)qo);
+    if (!aligned(do_, 16)) return fail(MQ_ERR_ALIGN, "%s: do_=%p is not 16-byte aligned", fn, (const void *)do_);
+    if (!aligned(so, 16)) return fail(MQ_ERR_ALIGN, "%s: so=%p is not 16-byte aligned", fn, (const void *)so);
+    if (y && !aligned(y, 16)) return fail(MQ_ERR_ALIGN, "%s: y=%p is not 16-byte aligned", fn, (const void *)y);
+    const int64_t tiles = ((M + 127) / 128) * (N / 64);
+    if (tiles > kMaxDim)
+        return fail(MQ_ERR_SHAPE, "%s: M=%lld x N=%lld needs too many tiles", fn, (long long)M, (long long)N);
+    if (int rc = check_device()) return rc;
+    const bool gemv = path == MQ_PATH_GEMV || (path == MQ_PATH_AUTO && M <= mq::GEMV_MAX_M);
+    const auto *Wgb = static_cast<const uint8_t *>(Wg);
+    const auto *Wub = static_cast<const uint8_t *>(Wu);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const hipError_t e = gemv ? mq::launch_gemv_q4k_ffn(Wgb, Wub, q, d, s, (int)M, (int)N, (int)K, qo, do_, so, y, st)
+                              : mq::launch_gemm_q4k_ffn(Wgb, Wub, q, d, s, (int)M, (int)N, (int)K, qo, do_, so, y, st);
+    return launched(e, fn);
+}
+
 } // namespace
 
 extern "C" {
@@ -235,6 +281,20 @@ int mq_matmul_q6k_ex(const void *W, const int8_t *q, const float *d, const float
 {
     g_err[0] = '\0';
     return matmul(true, W, q, d, s, M, N, K, out, stream, path);
+}
+
+int mq_ffn_q4k(const void *Wg, const void *Wu, const int8_t *q, const float *d, const float *s, int64_t M,
+               int64_t N, int64_t K, int8_t *qo, float *do_, float *so, float *y, void *stream)
+{
+    g_err[0] = '\0';
+    return ffn(Wg, Wu, q, d, s, M, N, K, qo, do_, so, y, stream, MQ_PATH_AUTO);
+}
+
+int mq_ffn_q4k_ex(const void *Wg, const void *Wu, const int8_t *q, const float *d, const float *s, int64_t M,
+                  int64_t N, int64_t K, int8_t *qo, float *do_, float *so, float *y, void *stream, int path)
+{
+    g_err[0] = '\0';
+    return ffn(Wg, Wu, q, d, s, M, N, K, qo, do_, so, y, stream, path);
 }
 
 int64_t mq_gemv_max_m(void) { return mq::GEMV_MAX_M; }

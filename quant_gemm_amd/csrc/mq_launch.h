@@ -27,6 +27,12 @@ hipError_t launch_swiglu_quantize(const float *g, const float *u, int64_t M, int
 hipError_t launch_gemm_q4k(const uint8_t *W, const int8_t *q, const float *d,
                            const float *s, int M, int N, int K, float *out,
                            hipStream_t st);
+hipError_t launch_gemm_q4k_ffn(const uint8_t *Wg, const uint8_t *Wu, const int8_t *q, const float *d,
+                               const float *s, int M, int N, int K, int8_t *qo, float *do_, float *so,
+                               float *y, hipStream_t st);
+hipError_t launch_gemv_q4k_ffn(const uint8_t *Wg, const uint8_t *Wu, const int8_t *q, const float *d,
+                               const float *s, int M, int N, int K, int8_t *qo, float *do_, float *so,
+                               float *y, hipStream_t st);
 hipError_t launch_gemm_q6k(const uint8_t *W, const int8_t *q, const float *d,
                            int M, int N, int K, float *out, hipStream_t st);
 

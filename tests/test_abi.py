@@ -175,6 +175,33 @@ def test_swiglu_quantize_validation(L, kw, status, needle):
     msg = L.mq_last_error().decode()
     assert "mq_swiglu_quantize" in msg and needle in msg
 
+
+def _ffn(L, Wg=P, Wu=P, q=P, d=P, s=P, M=4, N=256, K=256, qo=P, do=P, so=P, y=None, path=0):
+    return L.mq_ffn_q4k_ex(Wg, Wu, q, d, s, M, N, K, qo, do, so, y, None, path)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(Wg=None), INVALID, "Wg is NULL"),
+    (dict(Wu=None), INVALID, "Wu is NULL"),
+    (dict(s=None), INVALID, "s is NULL"),
+    (dict(qo=None), INVALID, "qo is NULL"),
+    (dict(so=None), INVALID, "so is NULL"),
+    (dict(M=0), INVALID, "M=0"),
+    (dict(N=128), SHAPE, "N=128"),
+    (dict(N=0), SHAPE, "N=0"),
+    (dict(K=320), SHAPE, "K=320"),
+    (dict(path=5), INVALID, "path=5"),
+    (dict(path=1, M=9), INVALID, "M=9"),
+    (dict(Wu=P + 2), ALIGN, "Wu="),
+    (dict(qo=P + 4), ALIGN, "qo="),
+    (dict(y=P + 4), ALIGN, "y="),
+])
+def test_ffn_validation(L, kw, status, needle):
+    rc = _ffn(L, **kw)
+    assert rc == status
+    msg = L.mq_last_error().decode()
+    assert "mq_ffn_q4k" in msg and needle in msg
+
 def test_error_is_cleared_by_next_call(L):
     assert _q4k(L, W=None) == INVALID
     assert L.mq_last_error().decode() != ""

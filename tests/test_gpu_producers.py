@@ -139,3 +139,38 @@ def test_swiglu_quantize_edge_values(dev):
     # rows whose SiLU is zero everywhere give an all-zero plane
     q, d, s, y, *_ = gpu_swiglu(np.zeros((2, K), np.float32), u[:2], False)
     assert not q.any() and not d.any() and not s.any()
+
+
+# ---------------------------------------------------------------- fused FFN up half
+
+FFN_CASES = [(1, 256, 1024, (1, 2)), (3, 512, 3584, (1, 2)), (8, 768, 2048, (1, 2)),
+             (9, 256, 1024, (2,)), (130, 512, 3584, (2,)), (1, 18944, 3584, (1,)),
+             (3314, 18944, 3584, (2,))]
+
+
+@pytest.mark.parametrize("M,N,K,paths", FFN_CASES)
+def test_ffn_q4k(dev, M, N, K, paths):
+    import torch
+    rng = np.random.default_rng(M * 131 + N + K)
+    Wg = synth.q4k_weights(rng, N, K)
+    Wu = synth.q4k_weights(rng, N, K)
+    x = synth.activations(rng, M, K, outliers=True)
+    q, d, s = mq.quantize_act(to_dev(x))
+    toks = None if M <= 130 else np.array([0, 1, 127, 128, 1000, 2047, 3200, M - 1])
+    rq, rd, _ = oracle.quantize_act(x)
+    _, _, _, ry = producers.ffn_q4k(Wg, Wu, rq, rd, N, K, tokens=toks)
+    Wgd, Wud = to_dev(Wg.reshape(-1)), to_dev(Wu.reshape(-1))
+    for path in paths:
+        print(f"[producers] ffn M={M} N={N} K={K} path={path}", flush=True)
+        y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        qo, do, so, y = mq.ffn_q4k(Wgd, Wud, q, d, s, N, K, y=y, path=path)
+        qo2, do2, so2 = mq.ffn_q4k(Wgd, Wud, q, d, s, N, K, path=path)
+        qo, do, so, y = host(qo), host(do), host(so), host(y)
+        assert_plane_of(qo, do, so, y, f"ffn path {path}")
+        assert np.array_equal(host(qo2), qo) and np.array_equal(host(do2), do) and np.array_equal(host(so2), so)
+        got = y if toks is None else y[toks]
+        err = np.abs(got.astype(np.float64) - ry).max()
+        bar = 1e-4 * np.abs(ry).max()
+        assert err <= bar, f"ffn path {path}: max|d| {err:.3e} > {bar:.3e}"
+        print(f"[producers] ffn M={M} N={N} K={K} path={path}: max|d|/max|y| = {err / np.abs(ry).max():.2e}", flush=True)
+
