@@ -132,9 +132,13 @@ int mq_swiglu_quantize(const float *g, const float *u, int64_t M, int64_t K,
  * and 32-value sub-block j. The int8 dot of each 32-value sub-block is exact
  * (int32); scales, mins and the min term (which uses s) are applied in f32.
  * Result within 1e-4 * max|out| of the exact value for the workloads tested.
- * M <= mq_gemv_max_m() runs the weight-streaming GEMV, larger M the int8
- * MFMA GEMM (the CUDA dispatch splits decode from prefill by token count:
- * minfer Support Matrix, "CUDA notes").
+ * Small M runs the weight-streaming GEMV, larger M the int8 MFMA GEMM (the
+ * CUDA dispatch splits decode from prefill by token count: minfer Support
+ * Matrix, "CUDA notes"). MQ_PATH_AUTO switches at crossovers measured on
+ * MI355X: Q4_K runs the GEMV for M <= 2, and up to 16 tokens while
+ * M*N*K <= 2.6e8; Q6_K for M <= 4. The GEMM uses 32-token tiles up to
+ * M = 96 (Q4_K) / 32 (Q6_K) and 128-token tiles above. The GEMV serves up to
+ * mq_gemv_max_m() tokens when forced.
  * W as described above; q, d, s from mq_quantize_act (s is required).
  */
 int mq_matmul_q4k(const void *W, const int8_t *q, const float *d,
@@ -152,7 +156,7 @@ int mq_matmul_q6k(const void *W, const int8_t *q, const float *d,
 /*
  * As mq_matmul_q4k / mq_matmul_q6k with the kernel chosen by `path`
  * (MQ_PATH_AUTO, MQ_PATH_GEMV, MQ_PATH_GEMM). MQ_PATH_GEMV requires
- * M <= mq_gemv_max_m(). Both paths meet the same contract; tests use this
+ * M <= mq_gemv_max_m() (M <= 8 for mq_ffn_q4k_ex). Both paths meet the same contract; tests use this
  * to check each path on the same inputs.
  */
 int mq_matmul_q4k_ex(const void *W, const int8_t *q, const float *d,
@@ -186,7 +190,7 @@ int mq_ffn_q4k_ex(const void *Wg, const void *Wu, const int8_t *q, const float *
                   const float *s, int64_t M, int64_t N, int64_t K, int8_t *qo,
                   float *do_, float *so, float *y, void *stream, int path);
 
-/* Largest M served by the GEMV path under MQ_PATH_AUTO. */
+/* Largest M the GEMV path serves (MQ_PATH_GEMV); 16. */
 int64_t mq_gemv_max_m(void);
 
 /* Message for the calling thread's last failed call ("" if none). The

@@ -410,7 +410,7 @@ __global__ __launch_bounds__(NTHR, MQ_Q4K_OCC) void gemm_q4k_kernel(
         __syncthreads();
     }
 
-    if (FFN) {
+    if constexpr (FFN) {
         static_assert(TM == 1 && TN == 4 && WN == 1, "gate|up tiles: b and b + 2 share columns");
         // y for (token t, column n): tiles b = 0, 1 hold g, tiles b + 2 the u of
         // the same columns. A 32-value block of the plane is one tile row:
@@ -493,14 +493,20 @@ __global__ __launch_bounds__(NTHR, MQ_Q4K_OCC) void gemm_q4k_kernel(
 
 } // namespace
 
+#ifdef MQ_Q4K_SMALL
+hipError_t launch_gemm_q4k_small(const uint8_t *W, const int8_t *q, const float *d,
+                                 const float *s, int M, int N, int K, float *out,
+                                 hipStream_t st)
+#else
 hipError_t launch_gemm_q4k(const uint8_t *W, const int8_t *q, const float *d,
                            const float *s, int M, int N, int K, float *out,
                            hipStream_t st)
+#endif
 {
     const int tiles_m = (M + BM - 1) / BM;
     const int tiles_n = (N + BN - 1) / BN;
     const int tiles = tiles_m * tiles_n;
-    const int nsplit = gemm_splits(tiles, K >> 8, M, N, K, Q4K_SLOT_OPS);
+    const int nsplit = gemm_splits(tiles, BM * BN, K >> 8, M, N, K, Q4K_SLOT_OPS);
     return run_split_k(nsplit, (int64_t)M * N, out, st, [&](float *dst) {
         gemm_q4k_kernel<false><<<dim3((unsigned)(tiles * nsplit)), dim3(NTHR), 0, st>>>(
             W, nullptr, q, d, s, M, N, K, tiles_m, nsplit, dst, nullptr, nullptr, nullptr);
@@ -508,6 +514,7 @@ hipError_t launch_gemm_q4k(const uint8_t *W, const int8_t *q, const float *d,
     });
 }
 
+#ifndef MQ_Q4K_SMALL
 hipError_t launch_gemm_q4k_ffn(const uint8_t *Wg, const uint8_t *Wu, const int8_t *q, const float *d,
                                const float *s, int M, int N, int K, int8_t *qo, float *do_, float *so,
                                float *y, hipStream_t st)
@@ -518,5 +525,6 @@ hipError_t launch_gemm_q4k_ffn(const uint8_t *Wg, const uint8_t *Wu, const int8_
         Wg, Wu, q, d, s, M, N, K, tiles_m, 1, y, qo, do_, so);
     return hipGetLastError();
 }
+#endif
 
 } // namespace mq

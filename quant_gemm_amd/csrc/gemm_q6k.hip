@@ -33,9 +33,15 @@
 namespace mq {
 namespace {
 
-constexpr int TM = 1, TN = 4, WM = 4, WN = 1;
-constexpr int BM = 32 * TM * WM;            // 128 tokens
-constexpr int BN = 32 * TN * WN;            // 128 rows
+// Workgroup tile: WM x WN wavefronts, each 1 x TN MFMA tiles of 32 x 32.
+#ifndef MQ_Q6K_TN
+#define MQ_Q6K_TN 4
+#define MQ_Q6K_WM 4
+#define MQ_Q6K_WN 1
+#endif
+constexpr int TM = 1, TN = MQ_Q6K_TN, WM = MQ_Q6K_WM, WN = MQ_Q6K_WN;
+constexpr int BM = 32 * TM * WM;            // tokens per tile
+constexpr int BN = 32 * TN * WN;            // rows per tile
 constexpr int BK = 128;
 constexpr int NWAVES = WM * WN;
 constexpr int NTHR = 64 * NWAVES;
@@ -199,12 +205,12 @@ __device__ __forceinline__ void store_raw(WgtStage &w, ActStage &a, const Raw &p
 }
 
 __device__ __forceinline__ void compute_step(const ActStage &a, const WgtStage &w,
-                                             v16f (&acc)[TN], int wm, int lr, int lh)
+                                             v16f (&acc)[TN], int wm, int wn, int lr, int lh)
 {
     float dwv[TN];
 #pragma unroll
     for (int b = 0; b < TN; ++b)
-        dwv[b] = w.dw[b * 32 + lr];
+        dwv[b] = w.dw[(wn * TN + b) * 32 + lr];
 #pragma unroll 1
     for (int j = 0; j < BK / 32; ++j) {
         const int tr = wm * 32 + lr;
@@ -220,7 +226,7 @@ __device__ __forceinline__ void compute_step(const ActStage &a, const WgtStage &
         }
 #pragma unroll
         for (int b = 0; b < TN; ++b) {
-            const int r = b * 32 + lr;
+            const int r = (wn * TN + b) * 32 + lr;
             const v4i blo = *reinterpret_cast<const v4i *>(w.lo + 16 * slot8(r, 2 * j + lh));
             const v4i bhi = *reinterpret_cast<const v4i *>(w.hi + 16 * slot8(r, 2 * j + lh));
             const v16i il = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, blo, v16i{}, 0, 0, 0);
@@ -257,7 +263,7 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_q6k_kernel(
     const int n0 = tile_n * BN;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int wm = wave;                      // WN == 1
+    const int wm = wave % WM, wn = wave / WM;
     const int lr = lane & 31, lh = lane >> 5;
 
     v16f acc[TN];
@@ -280,7 +286,7 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_q6k_kernel(
         // of them then has no DMA in flight to wait for
         load_raw(p, W, dx, M, N, K, t0, n0, st + 1);
         issue_act(A1, q, M, K, t0, st + 1, wave, lane);
-        compute_step(A0, B, acc, wm, lr, lh);
+        compute_step(A0, B, acc, wm, wn, lr, lh);
         __syncthreads();                      // limb planes of step st consumed
         wait_vm<0>();
         store_raw(B, A1, p, M, N, t0, n0);
@@ -290,7 +296,7 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_q6k_kernel(
             load_raw(p, W, dx, M, N, K, t0, n0, st + 2);
             issue_act(A0, q, M, K, t0, st + 2, wave, lane);
         }
-        compute_step(A1, B, acc, wm, lr, lh);
+        compute_step(A1, B, acc, wm, wn, lr, lh);
         __syncthreads();
         if (more) {
             wait_vm<0>();
@@ -301,7 +307,7 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_q6k_kernel(
 
 #pragma unroll
     for (int b = 0; b < TN; ++b) {
-        const int n = n0 + b * 32 + lr;
+        const int n = n0 + (wn * TN + b) * 32 + lr;
         if (n < N) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
@@ -315,13 +321,18 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_q6k_kernel(
 
 } // namespace
 
+#ifdef MQ_Q6K_SMALL
+hipError_t launch_gemm_q6k_small(const uint8_t *W, const int8_t *q, const float *d,
+                                 int M, int N, int K, float *out, hipStream_t st)
+#else
 hipError_t launch_gemm_q6k(const uint8_t *W, const int8_t *q, const float *d,
                            int M, int N, int K, float *out, hipStream_t st)
+#endif
 {
     const int tiles_m = (M + BM - 1) / BM;
     const int tiles_n = (N + BN - 1) / BN;
     const int tiles = tiles_m * tiles_n;
-    const int nsplit = gemm_splits(tiles, K >> 8, M, N, K, Q6K_SLOT_OPS);
+    const int nsplit = gemm_splits(tiles, BM * BN, K >> 8, M, N, K, Q6K_SLOT_OPS);
     return run_split_k(nsplit, (int64_t)M * N, out, st, [&](float *dst) {
         gemm_q6k_kernel<<<dim3((unsigned)(tiles * nsplit)), dim3(NTHR), 0, st>>>(W, q, d, M, N, K, tiles_m,
                                                                                  nsplit, dst);

@@ -809,7 +809,8 @@ hipError_t launch_gemv_q4k(const uint8_t *W, const int8_t *q, const float *d,
     if (M <= 1) return gemv_q4k_mt<1>(W, q, d, s, M, N, K, out, st);
     if (M <= 2) return gemv_q4k_mt<2>(W, q, d, s, M, N, K, out, st);
     if (M <= 4) return gemv_q4k_mt<4>(W, q, d, s, M, N, K, out, st);
-    return gemv_q4k_mt<8>(W, q, d, s, M, N, K, out, st);
+    if (M <= 8) return gemv_q4k_mt<8>(W, q, d, s, M, N, K, out, st);
+    return gemv_q4k_mt<16>(W, q, d, s, M, N, K, out, st);
 }
 
 hipError_t launch_gemv_q4k_ffn(const uint8_t *Wg, const uint8_t *Wu, const int8_t *q, const float *d,
@@ -845,13 +846,15 @@ hipError_t launch_gemv_q6k(const uint8_t *W, const int8_t *q, const float *d,
         if (M <= 1) gemv_q6k_stream_kernel<1><<<grid, block, lds, st>>>(W, q, d, M, N, K, out);
         else if (M <= 2) gemv_q6k_stream_kernel<2><<<grid, block, lds, st>>>(W, q, d, M, N, K, out);
         else if (M <= 4) gemv_q6k_stream_kernel<4><<<grid, block, lds, st>>>(W, q, d, M, N, K, out);
-        else gemv_q6k_stream_kernel<8><<<grid, block, lds, st>>>(W, q, d, M, N, K, out);
+        else if (M <= 8) gemv_q6k_stream_kernel<8><<<grid, block, lds, st>>>(W, q, d, M, N, K, out);
+        else gemv_q6k_stream_kernel<16><<<grid, block, lds, st>>>(W, q, d, M, N, K, out);
         return hipGetLastError();
     }
     if (M <= 1) return gemv_q6k_mt<1>(W, q, d, M, N, K, out, st);
     if (M <= 2) return gemv_q6k_mt<2>(W, q, d, M, N, K, out, st);
     if (M <= 4) return gemv_q6k_mt<4>(W, q, d, M, N, K, out, st);
-    return gemv_q6k_mt<8>(W, q, d, M, N, K, out, st);
+    if (M <= 8) return gemv_q6k_mt<8>(W, q, d, M, N, K, out, st);
+    return gemv_q6k_mt<16>(W, q, d, M, N, K, out, st);
 }
 
 } // namespace mq

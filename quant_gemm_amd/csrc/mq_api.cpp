@@ -108,17 +108,23 @@ int matmul(bool q6, const void *W, const int8_t *q, const float *d, const float 
         return fail(MQ_ERR_SHAPE, "%s: M=%lld x N=%lld needs too many tiles", fn, (long long)M, (long long)N);
     if (int rc = check_device()) return rc;
 
-    const bool gemv = path == MQ_PATH_GEMV || (path == MQ_PATH_AUTO && M <= mq::GEMV_MAX_M);
+    const bool gemv = path == MQ_PATH_GEMV || (path == MQ_PATH_AUTO && mq::gemv_auto(q6, M, N, K));
     const auto *Wb = static_cast<const uint8_t *>(W);
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int m = (int)M, n = (int)N, k = (int)K;
     hipError_t e;
-    if (q6)
-        e = gemv ? mq::launch_gemv_q6k(Wb, q, d, m, n, k, out, st)
-                 : mq::launch_gemm_q6k(Wb, q, d, m, n, k, out, st);
+    if (q6 && gemv)
+        e = mq::launch_gemv_q6k(Wb, q, d, m, n, k, out, st);
+    else if (q6 && m <= mq::GEMM_SMALL_M_Q6K)
+        e = mq::launch_gemm_q6k_small(Wb, q, d, m, n, k, out, st);
+    else if (q6)
+        e = mq::launch_gemm_q6k(Wb, q, d, m, n, k, out, st);
+    else if (gemv)
+        e = mq::launch_gemv_q4k(Wb, q, d, s, m, n, k, out, st);
+    else if (m <= mq::GEMM_SMALL_M_Q4K)
+        e = mq::launch_gemm_q4k_small(Wb, q, d, s, m, n, k, out, st);
     else
-        e = gemv ? mq::launch_gemv_q4k(Wb, q, d, s, m, n, k, out, st)
-                 : mq::launch_gemm_q4k(Wb, q, d, s, m, n, k, out, st);
+        e = mq::launch_gemm_q4k(Wb, q, d, s, m, n, k, out, st);
     return launched(e, fn);
 }
 
@@ -143,9 +149,9 @@ int ffn(const void *Wg, const void *Wu, const int8_t *q, const float *d, const f
                     (long long)N, (long long)kMaxDim);
     if (path != MQ_PATH_AUTO && path != MQ_PATH_GEMV && path != MQ_PATH_GEMM)
         return fail(MQ_ERR_INVALID_ARG, "%s: path=%d is not MQ_PATH_AUTO/GEMV/GEMM", fn, path);
-    if (path == MQ_PATH_GEMV && M > mq::GEMV_MAX_M)
+    if (path == MQ_PATH_GEMV && M > mq::FFN_GEMV_MAX_M)
         return fail(MQ_ERR_INVALID_ARG, "%s: path=MQ_PATH_GEMV needs M <= %d, got M=%lld", fn,
-                    mq::GEMV_MAX_M, (long long)M);
+                    mq::FFN_GEMV_MAX_M, (long long)M);
     if (!aligned(Wg, 16)) return fail(MQ_ERR_ALIGN, "%s: Wg=%p is not 16-byte aligned", fn, Wg);
     if (!aligned(Wu, 16)) return fail(MQ_ERR_ALIGN, "%s: Wu=%p is not 16-byte aligned", fn, Wu);
     if (!aligned(q, 16)) return fail(MQ_ERR_ALIGN, "%s: q=%p is not 16-byte aligned", fn, (const void *)q);
@@ -159,7 +165,7 @@ int ffn(const void *Wg, const void *Wu, const int8_t *q, const float *d, const f
     if (tiles > kMaxDim)
         return fail(MQ_ERR_SHAPE, "%s: M=%lld x N=%lld needs too many tiles", fn, (long long)M, (long long)N);
     if (int rc = check_device()) return rc;
-    const bool gemv = path == MQ_PATH_GEMV || (path == MQ_PATH_AUTO && M <= mq::GEMV_MAX_M);
+    const bool gemv = path == MQ_PATH_GEMV || (path == MQ_PATH_AUTO && M <= mq::FFN_AUTO_M);
     const auto *Wgb = static_cast<const uint8_t *>(Wg);
     const auto *Wub = static_cast<const uint8_t *>(Wu);
     hipStream_t st = static_cast<hipStream_t>(stream);

@@ -7,8 +7,26 @@
 
 namespace mq {
 
-// Largest token count the GEMV kernels serve.
-constexpr int GEMV_MAX_M = 8;
+// Largest token count the GEMV kernels serve (MQ_PATH_GEMV), and the fused
+// FFN GEMV's.
+constexpr int GEMV_MAX_M = 16;
+constexpr int FFN_GEMV_MAX_M = 8;
+// MQ_PATH_AUTO: GEMV or GEMM, at the crossovers measured on MI355X (weights
+// streamed from HBM). The GEMV's cost grows with M (its dot products are
+// VALU work per token) while the small-M GEMM's stays near its launch floor
+// (~28 us for Q4_K, ~48 us for Q6_K at K = 18944): Q4_K gains from the GEMV
+// while the matmul is small (M*N*K up to about 2.6e8), Q6_K up to 4 tokens.
+inline bool gemv_auto(bool q6, int64_t M, int64_t N, int64_t K)
+{
+    if (q6)
+        return M <= 4;
+    return M <= 2 || (M <= GEMV_MAX_M && (double)M * (double)N * (double)K <= 2.6e8);
+}
+constexpr int FFN_AUTO_M = 8;
+// The GEMMs run their small-M configuration (32-token tiles) up to these
+// token counts, measured crossovers against the 128-token tiles.
+constexpr int GEMM_SMALL_M_Q4K = 96;
+constexpr int GEMM_SMALL_M_Q6K = 32;
 
 hipError_t launch_quantize(const float *x, int64_t M, int64_t K, int64_t ldx,
                            int8_t *q, float *d, float *s, hipStream_t st);
@@ -27,6 +45,13 @@ hipError_t launch_swiglu_quantize(const float *g, const float *u, int64_t M, int
 hipError_t launch_gemm_q4k(const uint8_t *W, const int8_t *q, const float *d,
                            const float *s, int M, int N, int K, float *out,
                            hipStream_t st);
+// Small-M configuration of the Q4_K GEMM (32 tokens x 256 rows per workgroup).
+hipError_t launch_gemm_q4k_small(const uint8_t *W, const int8_t *q, const float *d,
+                                 const float *s, int M, int N, int K, float *out,
+                                 hipStream_t st);
+// Small-M configuration of the Q6_K GEMM (32 tokens x 128 rows per workgroup).
+hipError_t launch_gemm_q6k_small(const uint8_t *W, const int8_t *q, const float *d,
+                                 int M, int N, int K, float *out, hipStream_t st);
 hipError_t launch_gemm_q4k_ffn(const uint8_t *Wg, const uint8_t *Wu, const int8_t *q, const float *d,
                                const float *s, int M, int N, int K, int8_t *qo, float *do_, float *so,
                                float *y, hipStream_t st);
@@ -39,10 +64,10 @@ hipError_t launch_gemm_q6k(const uint8_t *W, const int8_t *q, const float *d,
 // Compute units of the current device (cached per device).
 int device_cu_count();
 
-// Number of K ranges (1 = no split) for a GEMM of `tiles` 128x128 output
-// tiles over `pairs` = K/256 super-blocks; slot_ops is the int8 rate of one
-// resident workgroup.
-int gemm_splits(int tiles, int pairs, int64_t M, int64_t N, int K, double slot_ops);
+// Number of K ranges (1 = no split) for a GEMM of `tiles` output tiles of
+// tile_elems outputs each over `pairs` = K/256 super-blocks; slot_ops is the
+// int8 rate of one resident workgroup.
+int gemm_splits(int tiles, int tile_elems, int pairs, int64_t M, int64_t N, int K, double slot_ops);
 
 // out[i] = sum over s = 0..nsplit-1, in that order, of part[s * n + i].
 hipError_t splitk_reduce(const float *part, int nsplit, int64_t n, float *out, hipStream_t st);

@@ -58,14 +58,14 @@ int device_cu_count()
     return v;
 }
 
-int gemm_splits(int tiles, int pairs, int64_t M, int64_t N, int K, double slot_ops)
+int gemm_splits(int tiles, int tile_elems, int pairs, int64_t M, int64_t N, int K, double slot_ops)
 {
-    // Time in units of one tile over all of K at two workgroups per CU. A
+    // Time of the tiles over all of K at two workgroups per CU. A
     // last, partial wave of at most one workgroup per CU runs about 1.6x as
     // fast (its workgroups do not share a CU), so it counts 0.6.
     const int ncu = device_cu_count();
     const int slots = 2 * ncu;
-    const double t_tile = 2.0 * 128 * 128 * K / slot_ops;   // seconds
+    const double t_tile = 2.0 * tile_elems * K / slot_ops;  // seconds, one tile over all of K
     const double bw = 4.0e12;                                // bytes/s of the reduction pass
     auto waves = [&](int64_t n) {
         const int64_t full = n / slots, rem = n % slots;

@@ -75,7 +75,7 @@ def _quant(L, x=P, M=4, K=256, ldx=256, q=P, d=P, s=P):
     (dict(K=384), SHAPE, "K=384"),
     (dict(M=2 ** 31), SHAPE, "M=2147483648"),
     (dict(path=3), INVALID, "path=3"),
-    (dict(path=1, M=9), INVALID, "M=9"),
+    (dict(path=1, M=17), INVALID, "M=17"),
     (dict(W=P + 4), ALIGN, "W="),
     (dict(q=P + 8), ALIGN, "q="),
     (dict(d=P + 4), ALIGN, "d="),

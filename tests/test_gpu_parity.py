@@ -154,6 +154,23 @@ def test_split_k_shapes(dev, fmt, M, N, K):
     again = host(run_matmul(fmt, W, q, d, s, N, K, path=mq.MQ_PATH_GEMM))
     assert np.array_equal(got, again), "split-K result must not depend on scheduling"
 
+
+# The small-M band: token counts around the switches between the GEMV, the
+# GEMM's 32-token tiles and its 128-token tiles, for every path.
+@pytest.mark.parametrize("fmt", ["q4k", "q6k"])
+@pytest.mark.parametrize("M", [3, 5, 9, 16, 24, 32, 33, 64, 96, 97])
+def test_small_m_band(dev, fmt, M):
+    N, K = 700, 2560
+    rng = np.random.default_rng(M * 17 + (fmt == "q6k"))
+    W = synth.weights(fmt, rng, N, K)
+    x = synth.activations(rng, M, K, outliers=True)
+    rq, rd, _ = oracle.quantize_act(x)
+    q, d, s = gpu_plane(x)
+    ref = oracle_mm(fmt, W, rq, rd, N, K)
+    paths = [mq.MQ_PATH_AUTO, mq.MQ_PATH_GEMM] + ([mq.MQ_PATH_GEMV] if M <= mq.gemv_max_m() else [])
+    for path in paths:
+        check_close(host(run_matmul(fmt, W, q, d, s, N, K, path=path)), ref, f"{fmt} M={M} path {path}")
+
 def test_config0_exact_workload(dev):
     case = synth.case_by_name("tiny_q4k")
     W = case.make_weights()
