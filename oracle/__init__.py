@@ -48,12 +48,14 @@ def lib() -> ctypes.CDLL:
         I64 = ctypes.c_int64
         L.oracle_quantize_act.argtypes = [P, I64, I64, I64, P, P, P]
         L.oracle_quantize_act.restype = None
-        for name in ("oracle_matmul_q4k", "oracle_matmul_q6k"):
+        for name in ("oracle_matmul_q4k", "oracle_matmul_q5k", "oracle_matmul_q6k"):
             f = getattr(L, name)
             f.argtypes = [P, P, P, I64, I64, I64, P, I64, P, P]
             f.restype = None
-        L.oracle_q4k_block_decode.argtypes = [P, P, P, P, P, P]
-        L.oracle_q4k_block_decode.restype = None
+        for name in ("oracle_q4k_block_decode", "oracle_q5k_block_decode"):
+            f = getattr(L, name)
+            f.argtypes = [P, P, P, P, P, P]
+            f.restype = None
         L.oracle_q6k_block_decode.argtypes = [P, P, P, P]
         L.oracle_q6k_block_decode.restype = None
         L.oracle_max_threads.argtypes = []
@@ -104,6 +106,12 @@ def matmul_q4k(W, q, d, N, K, tokens=None, f64=False):
     return _matmul("oracle_matmul_q4k", W, q, d, N, K, tokens, f64)
 
 
+def matmul_q5k(W, q, d, N, K, tokens=None, f64=False):
+    """Q5_K weights [N rows, K/256 blocks] x activation plane -> out [M or len(tokens), N]."""
+    assert W.size == N * (K // 256) * 176
+    return _matmul("oracle_matmul_q5k", W, q, d, N, K, tokens, f64)
+
+
 def matmul_q6k(W, q, d, N, K, tokens=None, f64=False):
     """Q6_K weights [N rows, K/256 blocks] x activation plane -> out [M or len(tokens), N]."""
     assert W.size == N * (K // 256) * 210
@@ -122,6 +130,20 @@ def q4k_block_decode(blk: np.ndarray):
     lib().oracle_q4k_block_decode(_ptr(blk), _ptr(d), _ptr(dmin), _ptr(sc),
                                   _ptr(m), _ptr(q4))
     return dict(d=float(d[0]), dmin=float(dmin[0]), sc=sc, m=m, q=q4)
+
+
+def q5k_block_decode(blk: np.ndarray):
+    """One 176-byte Q5_K block -> dict(d, dmin, sc[8], m[8], q[256] in 0..31)."""
+    blk = np.ascontiguousarray(blk, dtype=np.uint8)
+    assert blk.size == 176
+    d = np.zeros(1, np.float64)
+    dmin = np.zeros(1, np.float64)
+    sc = np.zeros(8, np.int32)
+    m = np.zeros(8, np.int32)
+    q5 = np.zeros(256, np.uint8)
+    lib().oracle_q5k_block_decode(_ptr(blk), _ptr(d), _ptr(dmin), _ptr(sc),
+                                  _ptr(m), _ptr(q5))
+    return dict(d=float(d[0]), dmin=float(dmin[0]), sc=sc, m=m, q=q5)
 
 
 def q6k_block_decode(blk: np.ndarray):

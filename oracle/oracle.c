@@ -23,14 +23,15 @@
  *     quotient underflows to zero.
  *
  *  2. The matmul. out[t][n] = sum_k w[n][k] * d[t][k/32] * q[t][k], with w
- *     the dequantized weight of GGML's Q4_K or Q6_K 256-value super-block
+ *     the dequantized weight of GGML's Q4_K, Q5_K or Q6_K 256-value super-block
  *     (minfer Architecture, §6 Quantization & Tensor Layout: blocks match
  *     ggml-common.h) and weights stored [out][in] row-major (minfer
  *     Architecture, §4.5 Core invariants, item 3). It is evaluated as exact
- *     integer dots over each scale group (32 values for Q4_K, 16 for Q6_K),
+ *     integer dots over each scale group (32 values for Q4_K and Q5_K, 16 for
+ *     Q6_K),
  *     combined in double from exact decodes of the f16 fields, and rounded
- *     once to f32. The stored activation sum s is not used: the Q4_K min
- *     term recomputes the exact integer sum of q.
+ *     once to f32. The stored activation sum s is not used: the Q4_K / Q5_K
+ *     min term recomputes the exact integer sum of q.
  *
  * Block layouts (all fields little-endian):
  *   Q4_K, 144 B: f16 d | f16 dmin | 12 B of eight 6-bit scale codes and eight
@@ -41,6 +42,13 @@
  *     f16 d. Weight w = 128g + 32r + i has low 4 bits
  *     (ql[64g + 32(r%2) + i] >> 4(r/2)) & 15 and high 2 bits
  *     (qh[32g + i] >> 2r) & 3; its value is d*scales[w/16]*(q - 32).
+ *   Q5_K, 176 B: f16 d | f16 dmin | the same 12 B of scale and min codes as
+ *     Q4_K | 32 B of high bits | 128 B of low nibbles. Weight w = 64c + 32h + i
+ *     lies in sub-block j = 2c + h; its 5-bit quant has low 4 bits
+ *     (qs[32c + i] >> 4h) & 15 and high bit (qh[i] >> (2c + h)) & 1, and its
+ *     value is d*sc_j*q - dmin*m_j (the pages list q5_K among the MMVQ
+ *     formats, minfer Support Matrix, "Supported Quantization Formats"; the
+ *     layout is GGML's).
  */
 #include <math.h>
 #include <stdint.h>
@@ -109,12 +117,13 @@ void oracle_quantize_act(const float *x, int64_t M, int64_t K, int64_t ldx,
 /* Block decoders.                                                         */
 /* ---------------------------------------------------------------------- */
 
-void oracle_q4k_block_decode(const uint8_t *blk, double *d, double *dmin,
-                             int32_t sc[8], int32_t m[8], uint8_t q4[256])
+/* The 12-byte field of eight 6-bit scale codes and eight 6-bit min codes
+ * shared by Q4_K and Q5_K: codes 0..3 are the low 6 bits of bytes 0..3
+ * (scales) and 4..7 (mins); codes 4..7 take their low 4 bits from the low
+ * (scale) or high (min) nibble of bytes 8..11 and their top 2 bits from the
+ * top bits of bytes 0..3 (scale) or 4..7 (min). */
+static void decode_scale_min(const uint8_t *B, int32_t sc[8], int32_t m[8])
 {
-    *d = f16_to_double((uint16_t)(blk[0] | (blk[1] << 8)));
-    *dmin = f16_to_double((uint16_t)(blk[2] | (blk[3] << 8)));
-    const uint8_t *B = blk + 4;
     for (int j = 0; j < 4; ++j) {
         sc[j] = B[j] & 63;
         m[j] = B[j + 4] & 63;
@@ -123,10 +132,34 @@ void oracle_q4k_block_decode(const uint8_t *blk, double *d, double *dmin,
         sc[j] = (B[j + 4] & 15) | ((B[j - 4] >> 6) << 4);
         m[j] = (B[j + 4] >> 4) | ((B[j] >> 6) << 4);
     }
+}
+
+void oracle_q4k_block_decode(const uint8_t *blk, double *d, double *dmin,
+                             int32_t sc[8], int32_t m[8], uint8_t q4[256])
+{
+    *d = f16_to_double((uint16_t)(blk[0] | (blk[1] << 8)));
+    *dmin = f16_to_double((uint16_t)(blk[2] | (blk[3] << 8)));
+    decode_scale_min(blk + 4, sc, m);
     const uint8_t *qs = blk + 16;
     for (int w = 0; w < 256; ++w) {
         int c = w / 64, h = (w / 32) % 2, i = w % 32;
         q4[w] = (uint8_t)((qs[32 * c + i] >> (4 * h)) & 15);
+    }
+}
+
+void oracle_q5k_block_decode(const uint8_t *blk, double *d, double *dmin,
+                             int32_t sc[8], int32_t m[8], uint8_t q5[256])
+{
+    *d = f16_to_double((uint16_t)(blk[0] | (blk[1] << 8)));
+    *dmin = f16_to_double((uint16_t)(blk[2] | (blk[3] << 8)));
+    decode_scale_min(blk + 4, sc, m);
+    const uint8_t *qh = blk + 16;
+    const uint8_t *qs = blk + 48;
+    for (int w = 0; w < 256; ++w) {
+        int c = w / 64, h = (w / 32) % 2, i = w % 32;
+        int low4 = (qs[32 * c + i] >> (4 * h)) & 15;
+        int high1 = (qh[i] >> (2 * c + h)) & 1;
+        q5[w] = (uint8_t)(low4 | (high1 << 4));
     }
 }
 
@@ -152,18 +185,24 @@ void oracle_q6k_block_decode(const uint8_t *blk, double *d, int32_t sc[16],
 /* NULL). Exactly one of out64 / out32 is non-NULL.                        */
 /* ---------------------------------------------------------------------- */
 
-void oracle_matmul_q4k(const uint8_t *W, const int8_t *q, const float *dx,
-                       int64_t M, int64_t N, int64_t K,
-                       const int64_t *toks, int64_t ntok,
-                       double *out64, float *out32)
+/* Q4_K and Q5_K: per 32-value sub-block, d*sc*(exact int dot of the quants
+ * with q) - dmin*m*(exact int sum of q), scaled by the activation block's d. */
+typedef void (*scale_min_decoder)(const uint8_t *, double *, double *, int32_t *,
+                                  int32_t *, uint8_t *);
+
+static void matmul_scale_min(const uint8_t *W, int64_t block_bytes,
+                             scale_min_decoder decode, const int8_t *q,
+                             const float *dx, int64_t M, int64_t N, int64_t K,
+                             const int64_t *toks, int64_t ntok, double *out64,
+                             float *out32)
 {
     const int64_t nsb = K / 256, nb = K / 32;
-    const int64_t rowb = nsb * 144;
+    const int64_t rowb = nsb * block_bytes;
     if (!toks)
         ntok = M;
 #pragma omp parallel
     {
-        uint8_t *q4 = (uint8_t *)malloc((size_t)K);
+        uint8_t *qw = (uint8_t *)malloc((size_t)K);
         double *dsc = (double *)malloc(sizeof(double) * (size_t)nb);
         double *dmm = (double *)malloc(sizeof(double) * (size_t)nb);
 #pragma omp for schedule(static)
@@ -171,8 +210,8 @@ void oracle_matmul_q4k(const uint8_t *W, const int8_t *q, const float *dx,
             for (int64_t sb = 0; sb < nsb; ++sb) {
                 double d, dmin;
                 int32_t sc[8], m[8];
-                oracle_q4k_block_decode(W + n * rowb + sb * 144, &d, &dmin, sc,
-                                        m, q4 + 256 * sb);
+                decode(W + n * rowb + sb * block_bytes, &d, &dmin, sc, m,
+                       qw + 256 * sb);
                 for (int j = 0; j < 8; ++j) {
                     dsc[8 * sb + j] = d * sc[j];
                     dmm[8 * sb + j] = dmin * m[j];
@@ -186,7 +225,7 @@ void oracle_matmul_q4k(const uint8_t *W, const int8_t *q, const float *dx,
                     int32_t I = 0, Qs = 0;
                     for (int i = 0; i < 32; ++i) {
                         int32_t xq = qt[32 * b + i];
-                        I += (int32_t)q4[32 * b + i] * xq;
+                        I += (int32_t)qw[32 * b + i] * xq;
                         Qs += xq;
                     }
                     double dxb = (double)dx[t * nb + b];
@@ -198,10 +237,28 @@ void oracle_matmul_q4k(const uint8_t *W, const int8_t *q, const float *dx,
                     out32[tt * N + n] = (float)acc;
             }
         }
-        free(q4);
+        free(qw);
         free(dsc);
         free(dmm);
     }
+}
+
+void oracle_matmul_q4k(const uint8_t *W, const int8_t *q, const float *dx,
+                       int64_t M, int64_t N, int64_t K,
+                       const int64_t *toks, int64_t ntok,
+                       double *out64, float *out32)
+{
+    matmul_scale_min(W, 144, oracle_q4k_block_decode, q, dx, M, N, K, toks,
+                     ntok, out64, out32);
+}
+
+void oracle_matmul_q5k(const uint8_t *W, const int8_t *q, const float *dx,
+                       int64_t M, int64_t N, int64_t K,
+                       const int64_t *toks, int64_t ntok,
+                       double *out64, float *out32)
+{
+    matmul_scale_min(W, 176, oracle_q5k_block_decode, q, dx, M, N, K, toks,
+                     ntok, out64, out32);
 }
 
 void oracle_matmul_q6k(const uint8_t *W, const int8_t *q, const float *dx,

@@ -7,15 +7,17 @@ arithmetic (no block decoding, no activation quantization, no dot products).
 What it does know is where the two f16 fields sit inside a super-block, so
 that it can overwrite the random bytes there with drawn scales. The blocks are
 GGML's 256-value super-blocks (minfer Architecture, §6 Quantization & Tensor
-Layout): a Q4_K block is 144 bytes with f16 ``d`` at byte 0 and f16 ``dmin``
-at byte 2; a Q6_K block is 210 bytes with f16 ``d`` at byte 208.
+Layout): a Q4_K block is 144 bytes and a Q5_K block 176 bytes, both with f16
+``d`` at byte 0 and f16 ``dmin`` at byte 2; a Q6_K block is 210 bytes with f16
+``d`` at byte 208.
 
 Because every bit of a block outside those f16 fields belongs to exactly one
 quant or one scale/min code, uniform random bytes give independent uniform
-quants (0..15 or 0..63), uniform 6-bit scale/min codes (0..63) and uniform
-int8 Q6_K scales (-128..127), whatever the packing.
+quants (0..15, 0..31 or 0..63), uniform 6-bit scale/min codes (0..63) and
+uniform int8 Q6_K scales (-128..127), whatever the packing.
 
-Draw order for one matrix: weight bytes, then ``d`` (then ``dmin`` for Q4_K),
+Draw order for one matrix: weight bytes, then ``d`` (then ``dmin`` for Q4_K
+and Q5_K),
 from the weight stream; activations, then the outlier columns, from the
 activation stream. Scales are drawn in float64 and rounded to f16 by numpy
 (round to nearest even); the stored f16 is authoritative.
@@ -28,10 +30,11 @@ import numpy as np
 
 QK_K = 256
 Q4K_BLOCK_BYTES = 144
+Q5K_BLOCK_BYTES = 176
 Q6K_BLOCK_BYTES = 210
 QK8 = 32  # activation quantization block
 
-BLOCK_BYTES = {"q4k": Q4K_BLOCK_BYTES, "q6k": Q6K_BLOCK_BYTES}
+BLOCK_BYTES = {"q4k": Q4K_BLOCK_BYTES, "q5k": Q5K_BLOCK_BYTES, "q6k": Q6K_BLOCK_BYTES}
 
 
 def row_bytes(fmt: str, K: int) -> int:
@@ -52,6 +55,19 @@ def q4k_weights(rng: np.random.Generator, N: int, K: int,
     return raw.reshape(N, nb * Q4K_BLOCK_BYTES)
 
 
+def q5k_weights(rng: np.random.Generator, N: int, K: int,
+                d_range=(5e-4, 5e-3), dmin_range=(0.0, 5e-3)) -> np.ndarray:
+    """N rows of K/256 Q5_K blocks as a uint8 array [N, (K/256)*176]."""
+    assert K % QK_K == 0
+    nb = K // QK_K
+    raw = rng.integers(0, 256, size=(N, nb, Q5K_BLOCK_BYTES), dtype=np.uint8)
+    d = rng.uniform(d_range[0], d_range[1], size=(N, nb)).astype(np.float16)
+    dmin = rng.uniform(dmin_range[0], dmin_range[1], size=(N, nb)).astype(np.float16)
+    raw[:, :, 0:2] = d.view(np.uint8).reshape(N, nb, 2)
+    raw[:, :, 2:4] = dmin.view(np.uint8).reshape(N, nb, 2)
+    return raw.reshape(N, nb * Q5K_BLOCK_BYTES)
+
+
 def q6k_weights(rng: np.random.Generator, N: int, K: int,
                 d_range=(1e-4, 1e-3)) -> np.ndarray:
     """N rows of K/256 Q6_K blocks as a uint8 array [N, (K/256)*210]."""
@@ -64,7 +80,8 @@ def q6k_weights(rng: np.random.Generator, N: int, K: int,
 
 
 def weights(fmt: str, rng: np.random.Generator, N: int, K: int) -> np.ndarray:
-    return q4k_weights(rng, N, K) if fmt == "q4k" else q6k_weights(rng, N, K)
+    gen = {"q4k": q4k_weights, "q5k": q5k_weights, "q6k": q6k_weights}[fmt]
+    return gen(rng, N, K)
 
 
 def activations(rng: np.random.Generator, M: int, K: int,

@@ -1,8 +1,8 @@
 """Test-only helpers: block encoders and a brute-force float64 reference.
 
 Nothing here is used by the product library or by the oracle. The decoders in
-this file are a second, vectorized numpy coding of the GGML Q4_K / Q6_K
-super-block layouts (minfer Architecture, §6 Quantization & Tensor Layout),
+this file are a second, vectorized numpy coding of the GGML Q4_K / Q5_K /
+Q6_K super-block layouts (minfer Architecture, §6 Quantization & Tensor Layout),
 written independently of the loop-by-loop C decoders of the oracle, so that the
 brute-force pin compares two separate readings of the same layout.
 
@@ -12,6 +12,9 @@ Layouts (little-endian):
     sub-block j = w // 32. Codes: for j < 4, sc_j = B[j] & 63 and
     m_j = B[j+4] & 63; for j >= 4, sc_j = (B[j+4] & 15) | (B[j-4] >> 6) << 4
     and m_j = (B[j+4] >> 4) | (B[j] >> 6) << 4.
+  Q5_K (176 B): f16 d @0, f16 dmin @2, the Q4_K scale/min field @4, qh[32]
+    @16, qs[128] @48. Weight w = 64c + 32h + i -> (qs[32c+i] >> 4h) & 15 |
+    ((qh[i] >> (2c + h)) & 1) << 4, in sub-block j = w // 32 = 2c + h.
   Q6_K (210 B): ql[128] @0, qh[64] @128, int8 scales[16] @192, f16 d @208.
     Weight w = 128g + 32r + i -> low4 = (ql[64g + 32(r%2) + i] >> 4(r//2)) & 15,
     high2 = (qh[32g + i] >> 2r) & 3, value d*scales[w//16]*(low4|high2<<4 - 32).
@@ -46,6 +49,22 @@ def q4k_pack(d: float, dmin: float, sc, m, q) -> np.ndarray:
         c, h, i = w // 64, (w // 32) % 2, w % 32
         qs[32 * c + i] |= int(q[w]) << (4 * h)
     blk[16:144] = qs.astype(np.uint8)
+    return blk
+
+
+def q5k_pack(d: float, dmin: float, sc, m, q) -> np.ndarray:
+    """Pack one Q5_K block. sc, m: 8 codes in 0..63; q: 256 quants in 0..31."""
+    q = np.asarray(q, dtype=np.int64)
+    assert q.shape == (256,) and q.min() >= 0 and q.max() < 32
+    low = q4k_pack(d, dmin, sc, m, q & 15)          # d, dmin, codes and low nibbles
+    blk = np.zeros(176, np.uint8)
+    blk[0:16] = low[0:16]
+    blk[48:176] = low[16:144]
+    qh = np.zeros(32, np.int64)
+    for w in range(256):
+        j, i = w // 32, w % 32
+        qh[i] |= (int(q[w]) >> 4) << j
+    blk[16:48] = qh.astype(np.uint8)
     return blk
 
 
@@ -91,6 +110,17 @@ def q4k_fields(W: np.ndarray, N: int, K: int):
     return d, dmin, sc, m, q
 
 
+def q5k_fields(W: np.ndarray, N: int, K: int):
+    """Decode all Q5_K blocks -> (d, dmin [N, nb] f64, sc, m [N, nb, 8], q [N, nb, 256] in 0..31)."""
+    nb = K // 256
+    blk = np.ascontiguousarray(W, dtype=np.uint8).reshape(N, nb, 176)
+    as_q4 = np.concatenate([blk[:, :, 0:16], blk[:, :, 48:176]], axis=2)
+    d, dmin, sc, m, low = q4k_fields(as_q4.reshape(N, nb * 144), N, K)
+    qh = blk[:, :, 16:48].astype(np.int64)                          # [N, nb, 32]
+    high = np.stack([(qh >> j) & 1 for j in range(8)], axis=2)      # [N, nb, 8 sub-blocks, 32]
+    return d, dmin, sc, m, low | (high.reshape(N, nb, 256) << 4)
+
+
 def q6k_fields(W: np.ndarray, N: int, K: int):
     """Decode all Q6_K blocks -> (d [N, nb] f64, scales [N, nb, 16], q [N, nb, 256] stored)."""
     nb = K // 256
@@ -108,8 +138,8 @@ def q6k_fields(W: np.ndarray, N: int, K: int):
 def dequant_f64(fmt: str, W: np.ndarray, N: int, K: int) -> np.ndarray:
     """Every weight value in float64, [N, K]. Exact: all products fit in 53 bits."""
     nb = K // 256
-    if fmt == "q4k":
-        d, dmin, sc, m, q = q4k_fields(W, N, K)
+    if fmt in ("q4k", "q5k"):
+        d, dmin, sc, m, q = (q4k_fields if fmt == "q4k" else q5k_fields)(W, N, K)
         j = np.arange(256) // 32
         w = d[:, :, None] * sc[:, :, j] * q - dmin[:, :, None] * m[:, :, j]
     else:

@@ -39,6 +39,19 @@ def q4k_case():
     return fx, blk, q, d
 
 
+def q5k_case():
+    fx = load("q5k_hand_block.json")
+    blk = np.zeros(176, np.uint8)
+    blk[0:2] = np.frombuffer(bytes.fromhex(fx["d_f16_hex"])[::-1], np.uint8)
+    blk[2:4] = np.frombuffer(bytes.fromhex(fx["dmin_f16_hex"])[::-1], np.uint8)
+    blk[4:16] = np.frombuffer(bytes.fromhex(fx["scales_hex"]), np.uint8)
+    blk[16:48] = (9 * np.arange(32)) % 256
+    i = np.arange(128)
+    blk[48:176] = ((i + 1) % 16) | (((i + 7) % 16) << 4)
+    q, d = _plane(fx)
+    return fx, blk, q, d
+
+
 def q6k_case():
     fx = load("q6k_hand_block.json")
     blk = np.zeros(210, np.uint8)

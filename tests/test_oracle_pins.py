@@ -51,13 +51,16 @@ def test_oracle_matches_bruteforce_config0_shape(fmt):
     assert _rel_err(got, ref) <= 1e-12
 
 
-@pytest.mark.parametrize("fmt", ["q4k", "q6k"])
+MATMUL = {"q4k": oracle.matmul_q4k, "q5k": oracle.matmul_q5k, "q6k": oracle.matmul_q6k}
+
+
+@pytest.mark.parametrize("fmt", ["q4k", "q5k", "q6k"])
 @pytest.mark.parametrize("M,N,K", [(1, 1, 256), (3, 7, 512), (8, 33, 256), (2, 5, 768)])
 def test_oracle_matches_bruteforce_tiny(fmt, M, N, K):
     rng = np.random.default_rng(M * 1000 + N * 10 + K)
     W = synth.weights(fmt, rng, N, K)
     q, d = _qplane(rng, M, K)
-    mm = oracle.matmul_q4k if fmt == "q4k" else oracle.matmul_q6k
+    mm = MATMUL[fmt]
     got = mm(W, q, d, N, K, f64=True)
     ref = bruteforce_f64(fmt, W, q, d, N, K)
     assert _rel_err(got, ref) <= 1e-12
@@ -166,14 +169,14 @@ def test_q6k_stored_32_gives_zero():
     assert np.all(out == 0.0)
 
 
-@pytest.mark.parametrize("fmt", ["q4k", "q6k"])
+@pytest.mark.parametrize("fmt", ["q4k", "q5k", "q6k"])
 def test_zero_activations_give_zero(fmt):
     rng = np.random.default_rng(43)
     N, K, M = 4, 256, 2
     W = synth.weights(fmt, rng, N, K)
     q, d, s = oracle.quantize_act(np.zeros((M, K), np.float32))
     assert not q.any() and not d.any() and not s.any()
-    mm = oracle.matmul_q4k if fmt == "q4k" else oracle.matmul_q6k
+    mm = MATMUL[fmt]
     assert np.all(mm(W, q, d, N, K) == 0.0)
 
 
