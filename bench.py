@@ -76,6 +76,10 @@ def q4k_gemv_bytes(M, N, K):
     return N * (K // 256) * 144 + M * (K + 2 * 4 * (K // 32)) + 4 * M * N
 
 
+def q5k_gemv_bytes(M, N, K):
+    return N * (K // 256) * 176 + M * (K + 2 * 4 * (K // 32)) + 4 * M * N
+
+
 def q6k_gemv_bytes(M, N, K):
     return N * (K // 256) * 210 + M * (K + 4 * (K // 32)) + 4 * M * N
 
@@ -242,7 +246,7 @@ def run_all(args):
         copies = max(1, -(-ROTATE_BYTES // W0.numel())) if hbm else 1
         Ws = [W0] + [W0.clone() for _ in range(copies - 1)]
         q, d, s = mq.quantize_act(x)
-        mm = mq.matmul_q4k if case.fmt == "q4k" else mq.matmul_q6k
+        mm = {"q4k": mq.matmul_q4k, "q5k": mq.matmul_q5k, "q6k": mq.matmul_q6k}[case.fmt]
         out = torch.empty((case.M, case.N), dtype=torch.float32, device=dev)
         for i in range(3):
             mm(Ws[i % copies], q, d, s, case.N, case.K, out=out)
@@ -259,7 +263,7 @@ def run_all(args):
         row = {"group": grp, "case": case.name, "fmt": case.fmt, "M": case.M, "N": case.N,
                "K": case.K, "us": round(us, 2), "TOPS": round(case.ops / (us * 1e-6) / 1e12, 2)}
         if hbm:
-            b = (q4k_gemv_bytes if case.fmt == "q4k" else q6k_gemv_bytes)(case.M, case.N, case.K)
+            b = {"q4k": q4k_gemv_bytes, "q5k": q5k_gemv_bytes, "q6k": q6k_gemv_bytes}[case.fmt](case.M, case.N, case.K)
             row["GBs"] = round(b / (us * 1e-6) / 1e9, 1)
             row["frac_hbm"] = round(row["GBs"] / HBM_PEAK_GBS, 3)
         else:

@@ -2,7 +2,7 @@
  * mq.h - k-quant weight matmul on AMD MI355X (gfx950): the C ABI.
  *
  * The operation is the quantized matmul of the CUDA prefill/decode path of
- * the minfer pages: GGML Q4_K / Q6_K weight super-blocks multiplied against
+ * the minfer pages: GGML Q4_K / Q5_K / Q6_K weight super-blocks multiplied against
  * f32 activations that are first quantized to a per-32 int8 plane
  * (minfer Features, "GPU — CUDA": int8 MMQ GEMMs for q4_K and q6_K fed by an
  * int8 activation plane; decode by the MMVQ weight-streaming path.
@@ -40,6 +40,9 @@
  *   W    N rows, each K/256 consecutive super-blocks, rows back to back:
  *          Q4_K: 144-byte blocks  (f16 d, f16 dmin, 12 B of 6-bit scale and
  *                min codes, 128 B of 4-bit quants); row = K/256*144 bytes
+ *          Q5_K: 176-byte blocks  (f16 d, f16 dmin, the 12 B of codes of
+ *                Q4_K, 32 B of fifth bits, 128 B of low nibbles); row =
+ *                K/256*176 bytes
  *          Q6_K: 210-byte blocks  (128 B low nibbles, 64 B high bit pairs,
  *                16 int8 scales, f16 d); row = K/256*210 bytes
  *        (GGML's layouts: minfer Architecture, §6 Quantization & Tensor
@@ -58,7 +61,7 @@
 extern "C" {
 #endif
 
-#define MQ_ABI_VERSION 2
+#define MQ_ABI_VERSION 3
 
 typedef enum {
     MQ_OK = 0,
@@ -154,12 +157,27 @@ int mq_matmul_q6k(const void *W, const int8_t *q, const float *d,
                   float *out, void *stream);
 
 /*
- * As mq_matmul_q4k / mq_matmul_q6k with the kernel chosen by `path`
+ * Q5_K matmul: as mq_matmul_q4k with 5-bit quants,
+ * w[n][k] = d_blk * sc_j * q5 - dmin_blk * m_j, where q5 of position i of
+ * sub-block j = 2c + h is the nibble (qs[32c + i] >> 4h) & 15 plus 16 times
+ * bit j of qh[i] (q5_K is among the k-quants of the pages' decode path:
+ * minfer Support Matrix, "Supported Quantization Formats"; GGML's block).
+ * s is required. MQ_PATH_AUTO uses the Q4_K crossovers.
+ */
+int mq_matmul_q5k(const void *W, const int8_t *q, const float *d,
+                  const float *s, int64_t M, int64_t N, int64_t K,
+                  float *out, void *stream);
+
+/*
+ * As mq_matmul_q4k / mq_matmul_q5k / mq_matmul_q6k with the kernel chosen by `path`
  * (MQ_PATH_AUTO, MQ_PATH_GEMV, MQ_PATH_GEMM). MQ_PATH_GEMV requires
  * M <= mq_gemv_max_m() (M <= 8 for mq_ffn_q4k_ex). Both paths meet the same contract; tests use this
  * to check each path on the same inputs.
  */
 int mq_matmul_q4k_ex(const void *W, const int8_t *q, const float *d,
+                     const float *s, int64_t M, int64_t N, int64_t K,
+                     float *out, void *stream, int path);
+int mq_matmul_q5k_ex(const void *W, const int8_t *q, const float *d,
                      const float *s, int64_t M, int64_t N, int64_t K,
                      float *out, void *stream, int path);
 int mq_matmul_q6k_ex(const void *W, const int8_t *q, const float *d,

@@ -10,6 +10,7 @@ if libmq.so is missing, ``load()`` raises.
     q, d, s = rmsnorm_quantize(x, w, eps)      # plane of RMSNorm(x) * w
     q, d, s = swiglu_quantize(g, u)            # plane of SiLU(g) * u
     out = matmul_q4k(W, q, d, s, N, K)         # W: uint8 [N, K/256*144]
+    out = matmul_q5k(W, q, d, s, N, K)         # W: uint8 [N, K/256*176]
     out = matmul_q6k(W, q, d, None, N, K)      # W: uint8 [N, K/256*210]
 """
 from __future__ import annotations
@@ -24,8 +25,9 @@ MQ_PATH_AUTO, MQ_PATH_GEMV, MQ_PATH_GEMM = 0, 1, 2
 STATUS_NAMES = {0: "MQ_OK", 1: "MQ_ERR_INVALID_ARG", 2: "MQ_ERR_SHAPE",
                 3: "MQ_ERR_ALIGN", 4: "MQ_ERR_UNSUPPORTED", 5: "MQ_ERR_DEVICE",
                 6: "MQ_ERR_LAUNCH"}
-ABI_VERSION = 2
+ABI_VERSION = 3
 Q4K_BLOCK_BYTES = 144
+Q5K_BLOCK_BYTES = 176
 Q6K_BLOCK_BYTES = 210
 
 # Exported symbols of libmq and their C signatures (see include/mq.h).
@@ -39,8 +41,10 @@ SIGNATURES = {
     "mq_ffn_q4k": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P], ctypes.c_int),
     "mq_ffn_q4k_ex": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P, ctypes.c_int], ctypes.c_int),
     "mq_matmul_q4k": (_MATMUL_ARGS, ctypes.c_int),
+    "mq_matmul_q5k": (_MATMUL_ARGS, ctypes.c_int),
     "mq_matmul_q6k": (_MATMUL_ARGS, ctypes.c_int),
     "mq_matmul_q4k_ex": (_MATMUL_ARGS + [ctypes.c_int], ctypes.c_int),
+    "mq_matmul_q5k_ex": (_MATMUL_ARGS + [ctypes.c_int], ctypes.c_int),
     "mq_matmul_q6k_ex": (_MATMUL_ARGS + [ctypes.c_int], ctypes.c_int),
     "mq_gemv_max_m": ([], ctypes.c_int64),
     "mq_last_error": ([], ctypes.c_char_p),
@@ -194,6 +198,11 @@ def _matmul(fn, block_bytes, W, q, d, s, N, K, out, stream, path):
 def matmul_q4k(W, q, d, s, N, K, out=None, stream=None, path=MQ_PATH_AUTO):
     """out [M, N] f32 = Q4_K weights W (N rows of K) times the activation plane (q, d, s)."""
     return _matmul("mq_matmul_q4k_ex", Q4K_BLOCK_BYTES, W, q, d, s, N, K, out, stream, path)
+
+
+def matmul_q5k(W, q, d, s, N, K, out=None, stream=None, path=MQ_PATH_AUTO):
+    """out [M, N] f32 = Q5_K weights W (N rows of K) times the activation plane (q, d, s)."""
+    return _matmul("mq_matmul_q5k_ex", Q5K_BLOCK_BYTES, W, q, d, s, N, K, out, stream, path)
 
 
 def matmul_q6k(W, q, d, s, N, K, out=None, stream=None, path=MQ_PATH_AUTO):

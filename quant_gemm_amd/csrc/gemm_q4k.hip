@@ -1,9 +1,15 @@
-// Prefill GEMM for Q4_K weights x per-32 int8 activations (gfx950).
+// Prefill GEMM for Q4_K (and, built with MQ_Q5K, Q5_K) weights x per-32
+// int8 activations (gfx950).
 //
 // The pages' prefill runs an int8 tensor-core GEMM on the raw 4-bit quants
 // against the int8 activation plane, with the block scales applied after
 // each integer product (minfer Features, "GPU — CUDA": raw-nibble int8 GEMMs
-// for q4_K and q6_K). This is a CDNA4 design of that step.
+// for q4_K and q6_K). This is a CDNA4 design of that step. Q5_K (listed with
+// the k-quants the pages' decode path serves, minfer Support Matrix,
+// "Supported Quantization Formats") has the same header and sub-blocks plus
+// a plane of fifth bits: its quants 0..31 are still exact int8 operands, so
+// the same kernel runs it with one more DMA'd tile (32 bytes of high bits
+// per row and step) merged into the B operand.
 //
 // Tiling. A 256-thread workgroup computes 128 tokens x 128 weight rows as
 // 4 wavefronts of 32 tokens x 128 rows, each 1 x 4 MFMA tiles of 32 x 32.
@@ -46,6 +52,12 @@ namespace {
 // One wavefront owns 32 tokens x 128 rows: each activation scale/sum read
 // from LDS then serves four row tiles (measured fastest on MI355X among
 // 64x64, 32x64 and 64x32 wave tiles).
+#ifndef MQ_Q5K
+#define MQ_Q5K 0
+#endif
+constexpr bool Q5 = MQ_Q5K;
+constexpr int BLK_BYTES = Q5 ? 176 : 144; // super-block size
+constexpr int QS_OFF = Q5 ? 48 : 16;      // offset of the 128 low-nibble bytes
 #ifndef MQ_Q4K_TM
 #define MQ_Q4K_TM 1
 #define MQ_Q4K_TN 4
@@ -64,10 +76,12 @@ constexpr int NWAVES = WM * WN;
 constexpr int NTHR = 64 * NWAVES;
 // int8 ops per second of one resident workgroup (about 500 TOPS over 512
 // resident workgroups), for the split-K choice
-constexpr double Q4K_SLOT_OPS = 1.0e12;
+constexpr double Q4K_SLOT_OPS = Q5 ? 0.85e12 : 1.0e12;
 constexpr int A_CHUNKS = BM * BK / 16;      // 16-byte activation chunks per step
 constexpr int Q_CHUNKS = BN * BK / 2 / 16;  // 16-byte raw quant chunks per step
-static_assert(A_CHUNKS % (64 * NWAVES) == 0 && Q_CHUNKS % (64 * NWAVES) == 0, "DMA split");
+constexpr int H_CHUNKS = Q5 ? BN * 2 : 0;   // 16-byte high-bit chunks per step (Q5_K)
+static_assert(A_CHUNKS % (64 * NWAVES) == 0 && Q_CHUNKS % (64 * NWAVES) == 0 &&
+              H_CHUNKS % (64 * NWAVES) == 0, "DMA split");
 static_assert(NTHR >= 2 * BM && NTHR >= BN, "side loads need one thread per row");
 
 // LDS layout of one step. The activation and quant tiles are filled by
@@ -76,10 +90,12 @@ static_assert(NTHR >= 2 * BM && NTHR >= BN, "side loads need one thread per row"
 // rows: chunk c of row r sits in slot  r*8 + (c ^ (r & 7))  (activations,
 // 8 chunks per row) or  r*4 + (c ^ ((r >> 2) & 3))  (quants, 4 per row).
 // Eight consecutive rows reading the same chunk then hit eight different
-// bank groups.
+// bank groups. Q5_K's high bits (the block's whole qh[32], of which a step
+// uses 4 bit positions) sit in slot  r*2 + (c ^ ((r >> 2) & 1)).
 struct alignas(16) Stage {
     int8_t a[A_CHUNKS * 16];
     uint8_t qs[Q_CHUNKS * 16];
+    uint8_t qh[Q5 ? H_CHUNKS * 16 : 16];
     float dx[BK / 32][BM];
     float fw[BK / 32][BN];
     uint4 sxl[BM][2];       // bf16 limbs of s_x for the step's 4 sub-blocks (see Limbs)
@@ -138,6 +154,7 @@ struct WRows {
 
 __device__ __forceinline__ int a_slot(int r, int c) { return r * 8 + (c ^ (r & 7)); }
 __device__ __forceinline__ int q_slot(int r, int c) { return r * 4 + (c ^ ((r >> 2) & 3)); }
+__device__ __forceinline__ int h_slot(int r, int c) { return r * 2 + (c ^ ((r >> 2) & 1)); }
 
 // Start the DMA of step st's activation and quant tiles into s. Rows past M
 // or N read the last valid row instead: their results are never stored.
@@ -163,7 +180,17 @@ __device__ __forceinline__ void issue_tiles(Stage &s, const WRows &rows,
         const int p = 64 * i + lane;
         const int r = p >> 2;
         const int c = (p & 3) ^ ((r >> 2) & 3);
-        dma16(rows.row<FFN>(r) + (int64_t)sb * 144 + 16 + 64 * hf + 16 * c, s.qs + 1024 * i);
+        dma16(rows.row<FFN>(r) + (int64_t)sb * BLK_BYTES + QS_OFF + 64 * hf + 16 * c, s.qs + 1024 * i);
+    }
+    if constexpr (Q5) {
+#pragma unroll
+        for (int ii = 0; ii < H_CHUNKS / 64 / NWAVES; ++ii) {
+            const int i = wave * (H_CHUNKS / 64 / NWAVES) + ii;
+            const int p = 64 * i + lane;
+            const int r = p >> 1;
+            const int c = (p & 1) ^ ((r >> 2) & 1);
+            dma16(rows.row<FFN>(r) + (int64_t)sb * BLK_BYTES + 16 + 16 * c, s.qh + 1024 * i);
+        }
     }
 }
 
@@ -185,7 +212,7 @@ __device__ __forceinline__ void load_side(Side &p, const WRows &rows,
     const int tid = threadIdx.x;
     const int k0 = st * BK;
     if (tid < BN)
-        p.hdr = *reinterpret_cast<const uint4 *>(rows.row<FFN>(tid) + (int64_t)(st >> 1) * 144);
+        p.hdr = *reinterpret_cast<const uint4 *>(rows.row<FFN>(tid) + (int64_t)(st >> 1) * BLK_BYTES);
     if (tid < 2 * BM) {
         const int t = min(t0 + (tid & (BM - 1)), M - 1);
         const float *src = tid < BM ? dx : sx;
@@ -233,6 +260,8 @@ __device__ __forceinline__ void store_side(Stage &s, const Side &p, const WRows 
     }
 }
 
+// HF: which half super-block the step covers (its sub-blocks are 4 HF + j).
+template <int HF>
 __device__ __forceinline__ void compute_step(const Stage &s, v16f (&acc)[TM][TN], int wm, int wn,
                                              int lr, int lh)
 {
@@ -280,6 +309,20 @@ __device__ __forceinline__ void compute_step(const Stage &s, v16f (&acc)[TM][TN]
 #pragma unroll
             for (int b = 0; b < TN; ++b)
                 bf[b] = h ? ((raw[b] >> 4) & 0x0f0f0f0f) : (raw[b] & 0x0f0f0f0f);
+            if constexpr (Q5) {
+                // Q5_K: this lane's 16 high-bit bytes (positions 16 lh.. of
+                // the row's sub-blocks), read per sub-block to keep registers
+                // free; bit 4 HF + j of every byte rotated to bit 4
+                const int rot = (4 * HF + j + 28) & 31;
+#pragma unroll
+                for (int b = 0; b < TN; ++b) {
+                    const v4i hq = *reinterpret_cast<const volatile v4i *>(
+                        s.qh + 16 * h_slot((wn * TN + b) * 32 + lr, lh));
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        bf[b][e] |= (int)(__builtin_rotateright32((uint32_t)hq[e], rot) & 0x10101010u);
+                }
+            }
 #pragma unroll
             for (int a = 0; a < TM; ++a) {
                 const int r = (wm * TM + a) * 32 + lr;
@@ -368,7 +411,7 @@ __global__ __launch_bounds__(NTHR, MQ_Q4K_OCC) void gemm_q4k_kernel(
     float *dst = out + (int64_t)split * M * N;
     const int t0 = tile_m * BM;
     const int n0 = tile_n * (FFN ? BN / 2 : BN);
-    const WRows rows{W, W2, n0, N, (int64_t)(K >> 8) * 144};
+    const WRows rows{W, W2, n0, N, (int64_t)(K >> 8) * BLK_BYTES};
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int wm = wave % WM, wn = wave / WM;
@@ -393,7 +436,7 @@ __global__ __launch_bounds__(NTHR, MQ_Q4K_OCC) void gemm_q4k_kernel(
     for (int st = st_begin; st < st_end; st += 2) {
         issue_tiles<FFN>(S1, rows, q, M, K, t0, st + 1, wave, lane);
         load_side<FFN>(p, rows, dx, sx, M, K, t0, st + 1);
-        compute_step(S0, acc, wm, wn, lr, lh);
+        compute_step<0>(S0, acc, wm, wn, lr, lh);
         wait_vm<0>();
         store_side<FFN>(S1, p, rows, st + 1, M, t0);
         __syncthreads();
@@ -402,7 +445,7 @@ __global__ __launch_bounds__(NTHR, MQ_Q4K_OCC) void gemm_q4k_kernel(
             issue_tiles<FFN>(S0, rows, q, M, K, t0, st + 2, wave, lane);
             load_side<FFN>(p, rows, dx, sx, M, K, t0, st + 2);
         }
-        compute_step(S1, acc, wm, wn, lr, lh);
+        compute_step<1>(S1, acc, wm, wn, lr, lh);
         if (more) {
             wait_vm<0>();
             store_side<FFN>(S0, p, rows, st + 2, M, t0);
@@ -493,7 +536,15 @@ __global__ __launch_bounds__(NTHR, MQ_Q4K_OCC) void gemm_q4k_kernel(
 
 } // namespace
 
-#ifdef MQ_Q4K_SMALL
+#if MQ_Q5K && defined(MQ_Q4K_SMALL)
+hipError_t launch_gemm_q5k_small(const uint8_t *W, const int8_t *q, const float *d,
+                                 const float *s, int M, int N, int K, float *out,
+                                 hipStream_t st)
+#elif MQ_Q5K
+hipError_t launch_gemm_q5k(const uint8_t *W, const int8_t *q, const float *d,
+                           const float *s, int M, int N, int K, float *out,
+                           hipStream_t st)
+#elif defined(MQ_Q4K_SMALL)
 hipError_t launch_gemm_q4k_small(const uint8_t *W, const int8_t *q, const float *d,
                                  const float *s, int M, int N, int K, float *out,
                                  hipStream_t st)
@@ -514,7 +565,7 @@ hipError_t launch_gemm_q4k(const uint8_t *W, const int8_t *q, const float *d,
     });
 }
 
-#ifndef MQ_Q4K_SMALL
+#if !defined(MQ_Q4K_SMALL) && !MQ_Q5K
 hipError_t launch_gemm_q4k_ffn(const uint8_t *Wg, const uint8_t *Wu, const int8_t *q, const float *d,
                                const float *s, int M, int N, int K, int8_t *qo, float *do_, float *so,
                                float *y, hipStream_t st)

@@ -1,4 +1,4 @@
-// Decode GEMV for Q4_K / Q6_K weights x per-32 int8 activations (gfx950).
+// Decode GEMV for Q4_K / Q5_K / Q6_K weights x per-32 int8 activations (gfx950).
 //
 // The decode path of the pages streams the quantized weight bytes once per
 // token with 4-way int8 dot products (minfer Features, "GPU — CUDA": decode
@@ -448,6 +448,152 @@ __global__ __launch_bounds__(64 * GEMV_WAVES) void gemv_q4k_stream_kernel(
     }
 }
 
+// ---------------------------------------------------------------- Q5_K
+// 176-byte blocks (16-byte aligned): header (d, dmin, 6-bit codes) at 0, the
+// high-bit plane qh[32] at 16, the low nibbles qs[128] at 48. Eight lanes
+// share a block, 8 blocks per pass: lane 8s + c loads the 16 quant bytes
+// 16c..16c+15 (positions po..po+15, po = 16 (c & 1), of sub-blocks
+// j0 = 2 (c >> 1) in the low nibbles and j0 + 1 in the high ones), the
+// matching half qh[po..po+15] of the high-bit plane (bit j of qh[i] is the
+// fifth bit of position i of sub-block j) and the header itself: three
+// 16-byte loads, no cross-lane exchange. The replicated header and qh loads
+// hit the lines the block's own loads bring in, so HBM sees each byte once.
+template <int MT, int R, int IT, class F>
+__device__ __forceinline__ void q5k_rows(const uint8_t *__restrict__ base, int rows, int nb, int K, int M,
+                                         const int8_t *qa, const float *da, const float *sa, int lane,
+                                         float (&acc)[R][MT], F &&after_first_loads)
+{
+    const int nb32 = K >> 5;
+    const int total = rows * nb;
+    const int slot = lane >> 3;                  // block within a pass
+    const int c = lane & 7;                      // quant chunk within the block
+    const int cc = c >> 1, po = (c & 1) << 4;
+    const int j0 = 2 * cc;
+    // rotating a qh dword right by j + 28 (mod 32) puts bit j of every byte
+    // at bit 4 of the same byte
+    const int rot0 = (j0 + 28) & 31, rot1 = (j0 + 29) & 31;
+    int rl = 0, blk = slot;
+    while (blk >= nb) { blk -= nb; ++rl; }
+    for (int it0 = 0; it0 < max(total, 1); it0 += 8 * IT) {
+        v4i hv[IT], hq[IT], v[IT];
+#pragma unroll
+        for (int i = 0; i < IT; ++i) {
+            const int fb = it0 + 8 * i + slot;
+            const uint8_t *b = base + (int64_t)min(fb, max(total, 1) - 1) * 176;
+            hv[i] = __builtin_nontemporal_load(reinterpret_cast<const v4i *>(b));
+            hq[i] = __builtin_nontemporal_load(reinterpret_cast<const v4i *>(b + 16 + po));
+            v[i] = __builtin_nontemporal_load(reinterpret_cast<const v4i *>(b + 48 + 16 * c));
+        }
+        if (it0 == 0)
+            after_first_loads();
+#pragma unroll
+        for (int i = 0; i < IT; ++i) {
+            const int fb = it0 + 8 * i + slot;
+            if (fb < total) {
+                const uint32_t h0 = hv[i].x, h1 = hv[i].y, h2 = hv[i].z, h3 = hv[i].w;
+                const int k0 = (blk << 8) + (cc << 6) + po;
+                const int b0 = (blk << 3) + (cc << 1);
+                const float dd = f16_bits_to_f32(h0);
+                const float dm = f16_bits_to_f32(h0 >> 16);
+                const uint32_t scw = cc < 2 ? (h1 & 0x3f3f3f3fu)
+                                            : ((h3 & 0x0f0f0f0fu) | ((h1 >> 2) & 0x30303030u));
+                const uint32_t mw = cc < 2 ? (h2 & 0x3f3f3f3fu)
+                                           : (((h3 >> 4) & 0x0f0f0f0fu) | ((h2 >> 2) & 0x30303030u));
+                const int sh = (cc & 1) << 4;
+                const float f0 = dd * (float)((scw >> sh) & 0xffu);
+                const float f1 = dd * (float)((scw >> (sh + 8)) & 0xffu);
+                const float g0 = po == 0 ? dm * (float)((mw >> sh) & 0xffu) : 0.0f;
+                const float g1 = po == 0 ? dm * (float)((mw >> (sh + 8)) & 0xffu) : 0.0f;
+                // 5-bit quants: bit j0 (j0 + 1) of each qh byte rotated to bit 4
+                const uint32_t hx = (uint32_t)hq[i].x, hy = (uint32_t)hq[i].y;
+                const uint32_t hz = (uint32_t)hq[i].z, hw = (uint32_t)hq[i].w;
+                const int lo0 = (v[i].x & 0x0f0f0f0f) | (int)(__builtin_rotateright32(hx, rot0) & 0x10101010u);
+                const int lo1 = (v[i].y & 0x0f0f0f0f) | (int)(__builtin_rotateright32(hy, rot0) & 0x10101010u);
+                const int lo2 = (v[i].z & 0x0f0f0f0f) | (int)(__builtin_rotateright32(hz, rot0) & 0x10101010u);
+                const int lo3 = (v[i].w & 0x0f0f0f0f) | (int)(__builtin_rotateright32(hw, rot0) & 0x10101010u);
+                const int hi0 = ((v[i].x >> 4) & 0x0f0f0f0f) | (int)(__builtin_rotateright32(hx, rot1) & 0x10101010u);
+                const int hi1 = ((v[i].y >> 4) & 0x0f0f0f0f) | (int)(__builtin_rotateright32(hy, rot1) & 0x10101010u);
+                const int hi2 = ((v[i].z >> 4) & 0x0f0f0f0f) | (int)(__builtin_rotateright32(hz, rot1) & 0x10101010u);
+                const int hi3 = ((v[i].w >> 4) & 0x0f0f0f0f) | (int)(__builtin_rotateright32(hw, rot1) & 0x10101010u);
+#pragma unroll
+                for (int m = 0; m < MT; ++m) {
+                    if (m < M) {
+                        const v4i xa = *reinterpret_cast<const v4i *>(qa + (int64_t)m * K + k0);
+                        const v4i xb = *reinterpret_cast<const v4i *>(qa + (int64_t)m * K + k0 + 32);
+                        const float2 dpair = *reinterpret_cast<const float2 *>(da + (int64_t)m * nb32 + b0);
+                        const float2 spair = *reinterpret_cast<const float2 *>(sa + (int64_t)m * nb32 + b0);
+                        int i0 = dot4(lo0, xa.x, 0);
+                        i0 = dot4(lo1, xa.y, i0);
+                        i0 = dot4(lo2, xa.z, i0);
+                        i0 = dot4(lo3, xa.w, i0);
+                        int i1 = dot4(hi0, xb.x, 0);
+                        i1 = dot4(hi1, xb.y, i1);
+                        i1 = dot4(hi2, xb.z, i1);
+                        i1 = dot4(hi3, xb.w, i1);
+                        float contrib = (float)i0 * (dpair.x * f0);
+                        contrib = fmaf((float)i1, dpair.y * f1, contrib);
+                        contrib = fmaf(-g0, spair.x, contrib);
+                        contrib = fmaf(-g1, spair.y, contrib);
+#pragma unroll
+                        for (int r = 0; r < R; ++r)
+                            acc[r][m] += rl == r ? contrib : 0.0f;
+                    }
+                }
+            }
+            blk += 8;
+            while (blk >= nb) { blk -= nb; ++rl; }
+        }
+    }
+}
+
+template <int MT, int R, int IT, bool ACT_LDS>
+__global__ __launch_bounds__(64 * GEMV_WAVES) void gemv_q5k_kernel(
+    const uint8_t *__restrict__ W, const int8_t *__restrict__ q,
+    const float *__restrict__ dx, const float *__restrict__ sx, int M, int N,
+    int K, float *__restrict__ out)
+{
+    __shared__ v4i act[ACT_LDS ? GEMV_ACT_LDS / 16 : 1];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int row0 = (blockIdx.x * GEMV_WAVES + wave) * R;
+    ActCopy ac;
+    if constexpr (ACT_LDS)
+        act_load(ac, q, dx, sx, M, K);
+    const int nb = K >> 8;
+    const int rows = max(0, min(R, N - row0));
+    // a wavefront past the last row reads (and discards) the last block
+    const uint8_t *base = W + (int64_t)(rows > 0 ? row0 : N - 1) * nb * 176;
+
+    float acc[R][MT];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+            acc[r][m] = 0.0f;
+    const int8_t *qa = q;
+    const float *da = dx, *sa = sx;
+    if constexpr (ACT_LDS) {
+        qa = reinterpret_cast<const int8_t *>(act);
+        da = reinterpret_cast<const float *>(qa + M * K);
+        sa = da + M * (K >> 5);
+    }
+    q5k_rows<MT, R, IT>(base, max(rows, 1), nb, K, M, qa, da, sa, lane, acc, [&] {
+        if constexpr (ACT_LDS) {
+            act_store(ac, act, M, K);
+            __syncthreads();
+        }
+    });
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            const float v = wave_sum(acc[r][m]);
+            if (lane == 0 && m < M && r < rows)
+                out[(int64_t)m * N + row0 + r] = v;
+        }
+    }
+}
+
 // ---------------------------------------------------------------- Q6_K
 // Row slice owned by one lane: unit u = (blk, g, hh) = 64 weights
 // w = 128g + 32r + 16hh + i (r = 0..3, i = 0..15) of block blk. It reads
@@ -771,6 +917,26 @@ hipError_t gemv_q4k_mt(const uint8_t *W, const int8_t *q, const float *d,
     return hipGetLastError();
 }
 
+#ifndef GEMV_Q5K_IT
+#define GEMV_Q5K_IT 4
+#endif
+template <int MT>
+hipError_t gemv_q5k_mt(const uint8_t *W, const int8_t *q, const float *d,
+                       const float *s, int M, int N, int K, float *out,
+                       hipStream_t st)
+{
+    constexpr int R = MT <= 2 ? 4 : 2;           // rows per wavefront
+    constexpr int IT = GEMV_Q5K_IT;              // passes (of 8 blocks) in flight
+    const int rows_per_wg = GEMV_WAVES * R;
+    const int grid = (N + rows_per_wg - 1) / rows_per_wg;
+    const bool act_lds = (int64_t)M * K * 5 / 4 <= GEMV_ACT_LDS;
+    if (act_lds)
+        gemv_q5k_kernel<MT, R, IT, true><<<dim3(grid), dim3(64 * GEMV_WAVES), 0, st>>>(W, q, d, s, M, N, K, out);
+    else
+        gemv_q5k_kernel<MT, R, IT, false><<<dim3(grid), dim3(64 * GEMV_WAVES), 0, st>>>(W, q, d, s, M, N, K, out);
+    return hipGetLastError();
+}
+
 template <int MT, int R>
 hipError_t gemv_q6k_launch(const uint8_t *W, const int8_t *q, const float *d,
                            int M, int N, int K, float *out, hipStream_t st)
@@ -811,6 +977,17 @@ hipError_t launch_gemv_q4k(const uint8_t *W, const int8_t *q, const float *d,
     if (M <= 4) return gemv_q4k_mt<4>(W, q, d, s, M, N, K, out, st);
     if (M <= 8) return gemv_q4k_mt<8>(W, q, d, s, M, N, K, out, st);
     return gemv_q4k_mt<16>(W, q, d, s, M, N, K, out, st);
+}
+
+hipError_t launch_gemv_q5k(const uint8_t *W, const int8_t *q, const float *d,
+                           const float *s, int M, int N, int K, float *out,
+                           hipStream_t st)
+{
+    if (M <= 1) return gemv_q5k_mt<1>(W, q, d, s, M, N, K, out, st);
+    if (M <= 2) return gemv_q5k_mt<2>(W, q, d, s, M, N, K, out, st);
+    if (M <= 4) return gemv_q5k_mt<4>(W, q, d, s, M, N, K, out, st);
+    if (M <= 8) return gemv_q5k_mt<8>(W, q, d, s, M, N, K, out, st);
+    return gemv_q5k_mt<16>(W, q, d, s, M, N, K, out, st);
 }
 
 hipError_t launch_gemv_q4k_ffn(const uint8_t *Wg, const uint8_t *Wu, const int8_t *q, const float *d,

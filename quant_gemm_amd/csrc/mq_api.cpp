@@ -77,14 +77,17 @@ int check_K(int64_t K, const char *fn)
     return MQ_OK;
 }
 
-int matmul(bool q6, const void *W, const int8_t *q, const float *d, const float *s,
+enum class Fmt { Q4K, Q5K, Q6K };
+
+int matmul(Fmt fmt, const void *W, const int8_t *q, const float *d, const float *s,
            int64_t M, int64_t N, int64_t K, float *out, void *stream, int path)
 {
-    const char *fn = q6 ? "mq_matmul_q6k" : "mq_matmul_q4k";
+    const bool q6 = fmt == Fmt::Q6K;
+    const char *fn = q6 ? "mq_matmul_q6k" : fmt == Fmt::Q5K ? "mq_matmul_q5k" : "mq_matmul_q4k";
     if (!W) return fail(MQ_ERR_INVALID_ARG, "%s: W is NULL", fn);
     if (!q) return fail(MQ_ERR_INVALID_ARG, "%s: q is NULL", fn);
     if (!d) return fail(MQ_ERR_INVALID_ARG, "%s: d is NULL", fn);
-    if (!q6 && !s) return fail(MQ_ERR_INVALID_ARG, "%s: s is NULL (the Q4_K min term needs it)", fn);
+    if (!q6 && !s) return fail(MQ_ERR_INVALID_ARG, "%s: s is NULL (the min term needs it)", fn);
     if (!out) return fail(MQ_ERR_INVALID_ARG, "%s: out is NULL", fn);
     if (M <= 0) return fail(MQ_ERR_INVALID_ARG, "%s: M=%lld must be positive", fn, (long long)M);
     if (N <= 0) return fail(MQ_ERR_INVALID_ARG, "%s: N=%lld must be positive", fn, (long long)N);
@@ -108,7 +111,9 @@ int matmul(bool q6, const void *W, const int8_t *q, const float *d, const float 
         return fail(MQ_ERR_SHAPE, "%s: M=%lld x N=%lld needs too many tiles", fn, (long long)M, (long long)N);
     if (int rc = check_device()) return rc;
 
-    const bool gemv = path == MQ_PATH_GEMV || (path == MQ_PATH_AUTO && mq::gemv_auto(q6, M, N, K));
+    const bool gemv = path == MQ_PATH_GEMV ||
+                      (path == MQ_PATH_AUTO && (fmt == Fmt::Q5K ? mq::gemv_auto_q5k(M, N, K)
+                                                                : mq::gemv_auto(q6, M, N, K)));
     const auto *Wb = static_cast<const uint8_t *>(W);
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int m = (int)M, n = (int)N, k = (int)K;
@@ -119,6 +124,12 @@ int matmul(bool q6, const void *W, const int8_t *q, const float *d, const float 
         e = mq::launch_gemm_q6k_small(Wb, q, d, m, n, k, out, st);
     else if (q6)
         e = mq::launch_gemm_q6k(Wb, q, d, m, n, k, out, st);
+    else if (fmt == Fmt::Q5K && gemv)
+        e = mq::launch_gemv_q5k(Wb, q, d, s, m, n, k, out, st);
+    else if (fmt == Fmt::Q5K && m <= mq::GEMM_SMALL_M_Q5K)
+        e = mq::launch_gemm_q5k_small(Wb, q, d, s, m, n, k, out, st);
+    else if (fmt == Fmt::Q5K)
+        e = mq::launch_gemm_q5k(Wb, q, d, s, m, n, k, out, st);
     else if (gemv)
         e = mq::launch_gemv_q4k(Wb, q, d, s, m, n, k, out, st);
     else if (m <= mq::GEMM_SMALL_M_Q4K)
@@ -265,28 +276,42 @@ int mq_matmul_q4k(const void *W, const int8_t *q, const float *d, const float *s
                   int64_t N, int64_t K, float *out, void *stream)
 {
     g_err[0] = '\0';
-    return matmul(false, W, q, d, s, M, N, K, out, stream, MQ_PATH_AUTO);
+    return matmul(Fmt::Q4K, W, q, d, s, M, N, K, out, stream, MQ_PATH_AUTO);
+}
+
+int mq_matmul_q5k(const void *W, const int8_t *q, const float *d, const float *s, int64_t M,
+                  int64_t N, int64_t K, float *out, void *stream)
+{
+    g_err[0] = '\0';
+    return matmul(Fmt::Q5K, W, q, d, s, M, N, K, out, stream, MQ_PATH_AUTO);
+}
+
+int mq_matmul_q5k_ex(const void *W, const int8_t *q, const float *d, const float *s, int64_t M,
+                     int64_t N, int64_t K, float *out, void *stream, int path)
+{
+    g_err[0] = '\0';
+    return matmul(Fmt::Q5K, W, q, d, s, M, N, K, out, stream, path);
 }
 
 int mq_matmul_q6k(const void *W, const int8_t *q, const float *d, const float *s, int64_t M,
                   int64_t N, int64_t K, float *out, void *stream)
 {
     g_err[0] = '\0';
-    return matmul(true, W, q, d, s, M, N, K, out, stream, MQ_PATH_AUTO);
+    return matmul(Fmt::Q6K, W, q, d, s, M, N, K, out, stream, MQ_PATH_AUTO);
 }
 
 int mq_matmul_q4k_ex(const void *W, const int8_t *q, const float *d, const float *s, int64_t M,
                      int64_t N, int64_t K, float *out, void *stream, int path)
 {
     g_err[0] = '\0';
-    return matmul(false, W, q, d, s, M, N, K, out, stream, path);
+    return matmul(Fmt::Q4K, W, q, d, s, M, N, K, out, stream, path);
 }
 
 int mq_matmul_q6k_ex(const void *W, const int8_t *q, const float *d, const float *s, int64_t M,
                      int64_t N, int64_t K, float *out, void *stream, int path)
 {
     g_err[0] = '\0';
-    return matmul(true, W, q, d, s, M, N, K, out, stream, path);
+    return matmul(Fmt::Q6K, W, q, d, s, M, N, K, out, stream, path);
 }
 
 int mq_ffn_q4k(const void *Wg, const void *Wu, const int8_t *q, const float *d, const float *s, int64_t M,

@@ -22,11 +22,14 @@ inline bool gemv_auto(bool q6, int64_t M, int64_t N, int64_t K)
         return M <= 4;
     return M <= 2 || (M <= GEMV_MAX_M && (double)M * (double)N * (double)K <= 2.6e8);
 }
+// Q5_K: the Q4_K rule until measured on its own.
+inline bool gemv_auto_q5k(int64_t M, int64_t N, int64_t K) { return gemv_auto(false, M, N, K); }
 constexpr int FFN_AUTO_M = 8;
 // The GEMMs run their small-M configuration (32-token tiles) up to these
 // token counts, measured crossovers against the 128-token tiles.
 constexpr int GEMM_SMALL_M_Q4K = 96;
 constexpr int GEMM_SMALL_M_Q6K = 32;
+constexpr int GEMM_SMALL_M_Q5K = 96;
 
 hipError_t launch_quantize(const float *x, int64_t M, int64_t K, int64_t ldx,
                            int8_t *q, float *d, float *s, hipStream_t st);
@@ -36,6 +39,9 @@ hipError_t launch_gemv_q4k(const uint8_t *W, const int8_t *q, const float *d,
                            hipStream_t st);
 hipError_t launch_gemv_q6k(const uint8_t *W, const int8_t *q, const float *d,
                            int M, int N, int K, float *out, hipStream_t st);
+hipError_t launch_gemv_q5k(const uint8_t *W, const int8_t *q, const float *d,
+                           const float *s, int M, int N, int K, float *out,
+                           hipStream_t st);
 
 hipError_t launch_rmsnorm_quantize(const float *x, const float *w, int64_t M, int64_t K, int64_t ldx,
                                    float eps, int8_t *q, float *d, float *s, float *y, hipStream_t st);
@@ -52,6 +58,13 @@ hipError_t launch_gemm_q4k_small(const uint8_t *W, const int8_t *q, const float 
 // Small-M configuration of the Q6_K GEMM (32 tokens x 128 rows per workgroup).
 hipError_t launch_gemm_q6k_small(const uint8_t *W, const int8_t *q, const float *d,
                                  int M, int N, int K, float *out, hipStream_t st);
+hipError_t launch_gemm_q5k(const uint8_t *W, const int8_t *q, const float *d,
+                           const float *s, int M, int N, int K, float *out,
+                           hipStream_t st);
+// Small-M configuration of the Q5_K GEMM (32 tokens x 128 rows per workgroup).
+hipError_t launch_gemm_q5k_small(const uint8_t *W, const int8_t *q, const float *d,
+                                 const float *s, int M, int N, int K, float *out,
+                                 hipStream_t st);
 hipError_t launch_gemm_q4k_ffn(const uint8_t *Wg, const uint8_t *Wu, const int8_t *q, const float *d,
                                const float *s, int M, int N, int K, int8_t *qo, float *do_, float *so,
                                float *y, hipStream_t st);

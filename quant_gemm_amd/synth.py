@@ -103,7 +103,7 @@ def activations(rng: np.random.Generator, M: int, K: int,
 class Case:
     """One matrix of a workload: weights [N rows of K] times activations [M, K]."""
     name: str
-    fmt: str          # "q4k" or "q6k"
+    fmt: str          # "q4k", "q5k" or "q6k"
     M: int
     N: int
     K: int
@@ -149,6 +149,9 @@ WORKLOAD_GROUPS = {
         _c("layer_up", "q4k", 3314, 18944, 3584, True, 1004, 3, 2),
         _c("layer_down", "q6k", 3314, 3584, 18944, True, 1004, 4, 3),
         _c("output_head", "q6k", 1, 152064, 3584, True, 1004, 5, 4)],
+    # Q5_K at the ffn_up shape, decode and prefill
+    "q5k": [_c("q5k_decode_ffn_up", "q5k", 1, 18944, 3584, False, 1005, 0, 0),
+            _c("q5k_prefill_ffn_up", "q5k", 3314, 18944, 3584, True, 1005, 0, 1)],
 }
 
 

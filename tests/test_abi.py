@@ -53,6 +53,10 @@ def _q4k(L, W=P, q=P, d=P, s=P, M=4, N=8, K=256, out=P, path=0):
     return L.mq_matmul_q4k_ex(W, q, d, s, M, N, K, out, None, path)
 
 
+def _q5k(L, W=P, q=P, d=P, s=P, M=4, N=8, K=256, out=P, path=0):
+    return L.mq_matmul_q5k_ex(W, q, d, s, M, N, K, out, None, path)
+
+
 def _q6k(L, W=P, q=P, d=P, s=None, M=4, N=8, K=256, out=P, path=0):
     return L.mq_matmul_q6k_ex(W, q, d, s, M, N, K, out, None, path)
 
@@ -87,6 +91,23 @@ def test_q4k_validation(L, kw, status, needle):
     assert rc == status
     msg = L.mq_last_error().decode()
     assert "mq_matmul_q4k" in msg and needle in msg
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(W=None), INVALID, "W is NULL"),
+    (dict(s=None), INVALID, "s is NULL"),
+    (dict(K=512 + 128), SHAPE, "K=640"),
+    (dict(M=0), INVALID, "M=0"),
+    (dict(path=1, M=17), INVALID, "M=17"),
+    (dict(W=P + 8), ALIGN, "W="),
+    (dict(out=P + 2), ALIGN, "out="),
+])
+def test_q5k_validation(L, kw, status, needle):
+    rc = _q5k(L, **kw)
+    assert rc == status
+    msg = L.mq_last_error().decode()
+    assert "mq_matmul_q5k" in msg and needle in msg
+    assert L.mq_matmul_q5k(P, P, P, None, 4, 8, 256, P, None) == INVALID
 
 
 @pytest.mark.parametrize("kw,status,needle", [

@@ -14,7 +14,7 @@ import pytest
 
 import oracle
 import quant_gemm_amd as mq
-from blocks import q4k_pack, q6k_pack
+from blocks import q4k_pack, q5k_pack, q6k_pack
 from quant_gemm_amd import synth
 
 pytestmark = pytest.mark.gpu
@@ -49,15 +49,20 @@ def check_close(got, ref, what):
     return err / max(scale, 1e-300)
 
 
+GPU_MM = {"q4k": mq.matmul_q4k, "q5k": mq.matmul_q5k, "q6k": mq.matmul_q6k}
+ORACLE_MM = {"q4k": oracle.matmul_q4k, "q5k": oracle.matmul_q5k, "q6k": oracle.matmul_q6k}
+
+
 def run_matmul(fmt, W_np, q, d, s, N, K, path=mq.MQ_PATH_AUTO):
     W = to_dev(W_np.reshape(-1))
-    f = mq.matmul_q4k if fmt == "q4k" else mq.matmul_q6k
-    return f(W, q, d, s if fmt == "q4k" else None, N, K, path=path)
+    return GPU_MM[fmt](W, q, d, None if fmt == "q6k" else s, N, K, path=path)
 
 
 def oracle_mm(fmt, W_np, q_np, d_np, N, K, tokens=None):
-    f = oracle.matmul_q4k if fmt == "q4k" else oracle.matmul_q6k
-    return f(W_np, q_np, d_np, N, K, tokens=tokens)
+    return ORACLE_MM[fmt](W_np, q_np, d_np, N, K, tokens=tokens)
+
+
+FMT_SEED = {"q4k": 0, "q6k": 1, "q5k": 2}
 
 
 # ---------------------------------------------------------------- quantizer
@@ -120,10 +125,10 @@ SMALL = [(1, 1, 256), (2, 7, 512), (3, 33, 256), (5, 129, 768), (8, 256, 1024),
          (9, 31, 256), (31, 100, 512), (127, 129, 256), (129, 300, 1280), (200, 64, 2048)]
 
 
-@pytest.mark.parametrize("fmt", ["q4k", "q6k"])
+@pytest.mark.parametrize("fmt", ["q4k", "q5k", "q6k"])
 @pytest.mark.parametrize("M,N,K", SMALL)
 def test_small_shapes_all_paths(dev, fmt, M, N, K):
-    rng = np.random.default_rng(M * 10007 + N * 101 + K + (fmt == "q6k"))
+    rng = np.random.default_rng(M * 10007 + N * 101 + K + FMT_SEED[fmt])
     W = synth.weights(fmt, rng, N, K)
     x = synth.activations(rng, M, K, outliers=True)
     q, d, s = gpu_plane(x)
@@ -141,7 +146,8 @@ def test_small_shapes_all_paths(dev, fmt, M, N, K):
 # Shapes whose tile count is small against the chip, so the GEMM cuts K into
 # several ranges (uneven ones included) and sums the partial planes.
 @pytest.mark.parametrize("fmt,M,N,K", [("q4k", 64, 2000, 3584), ("q4k", 40, 130, 6912),
-                                       ("q6k", 300, 700, 4608), ("q6k", 17, 257, 2560)])
+                                       ("q6k", 300, 700, 4608), ("q6k", 17, 257, 2560),
+                                       ("q5k", 200, 900, 4608), ("q5k", 24, 300, 5120)])
 def test_split_k_shapes(dev, fmt, M, N, K):
     rng = np.random.default_rng(M * 7919 + N + K)
     W = synth.weights(fmt, rng, N, K)
@@ -157,11 +163,11 @@ def test_split_k_shapes(dev, fmt, M, N, K):
 
 # The small-M band: token counts around the switches between the GEMV, the
 # GEMM's 32-token tiles and its 128-token tiles, for every path.
-@pytest.mark.parametrize("fmt", ["q4k", "q6k"])
+@pytest.mark.parametrize("fmt", ["q4k", "q5k", "q6k"])
 @pytest.mark.parametrize("M", [3, 5, 9, 16, 24, 32, 33, 64, 96, 97])
 def test_small_m_band(dev, fmt, M):
     N, K = 700, 2560
-    rng = np.random.default_rng(M * 17 + (fmt == "q6k"))
+    rng = np.random.default_rng(M * 17 + FMT_SEED[fmt])
     W = synth.weights(fmt, rng, N, K)
     x = synth.activations(rng, M, K, outliers=True)
     rq, rd, _ = oracle.quantize_act(x)
@@ -184,47 +190,47 @@ def test_config0_exact_workload(dev):
 
 # ---------------------------------------------------------------- position probes
 
-@pytest.mark.parametrize("fmt", ["q4k", "q6k"])
+def _one_hot_rows(fmt):
+    """256 weight rows; row p has a single nonzero weight, at position p,
+    of value val[p] (Q5_K alternates values with and without the fifth bit)."""
+    rows, val = [], np.zeros(256)
+    for p in range(256):
+        if fmt == "q4k":
+            qv = np.zeros(256, int)
+            qv[p] = val[p] = 1 + p % 15
+            rows.append(q4k_pack(1.0, 0.0, [1] * 8, [0] * 8, qv))
+        elif fmt == "q5k":
+            qv = np.zeros(256, int)
+            qv[p] = val[p] = (16, 31, 1 + p % 15, 17 + p % 15)[p % 4]
+            rows.append(q5k_pack(1.0, 0.0, [1] * 8, [0] * 8, qv))
+        else:
+            qv = np.full(256, 32)
+            qv[p] = 33 + p % 30
+            val[p] = 1 + p % 30
+            rows.append(q6k_pack(1.0, [1] * 16, qv))
+    return np.stack(rows), val
+
+
+@pytest.mark.parametrize("fmt", ["q4k", "q5k", "q6k"])
 def test_one_hot_positions_gemm(dev, fmt):
     """Row n holds one nonzero quant at position n; token t is 127 e_t.
     out[t, n] != 0 exactly when t == n, for all 256 positions of a block."""
     K = N = M = 256
-    rows = []
-    for p in range(256):
-        if fmt == "q4k":
-            qv = np.zeros(256, int)
-            qv[p] = 1 + p % 15
-            rows.append(q4k_pack(1.0, 0.0, [1] * 8, [0] * 8, qv))
-        else:
-            qv = np.full(256, 32)
-            qv[p] = 33 + p % 30
-            rows.append(q6k_pack(1.0, [1] * 16, qv))
-    W = np.stack(rows)
+    W, val = _one_hot_rows(fmt)
     x = np.zeros((M, K), np.float32)
     x[np.arange(256), np.arange(256)] = 127.0
     q, d, s = gpu_plane(x)
     out = host(run_matmul(fmt, W, q, d, s, N, K, path=mq.MQ_PATH_GEMM))
     diag = np.diag(out).copy()
-    expect = 127.0 * (1 + np.arange(256) % 15) if fmt == "q4k" else 127.0 * (1 + np.arange(256) % 30)
-    assert np.array_equal(diag, expect)
+    assert np.array_equal(diag, 127.0 * val)
     off = out - np.diag(diag)
     assert not off.any()
 
 
-@pytest.mark.parametrize("fmt", ["q4k", "q6k"])
+@pytest.mark.parametrize("fmt", ["q4k", "q5k", "q6k"])
 def test_one_hot_positions_gemv(dev, fmt):
     K, N = 256, 256
-    rows = []
-    for p in range(256):
-        if fmt == "q4k":
-            qv = np.zeros(256, int)
-            qv[p] = 1 + p % 15
-            rows.append(q4k_pack(1.0, 0.0, [1] * 8, [0] * 8, qv))
-        else:
-            qv = np.full(256, 32)
-            qv[p] = 33 + p % 30
-            rows.append(q6k_pack(1.0, [1] * 16, qv))
-    W = np.stack(rows)
+    W, val = _one_hot_rows(fmt)
     for t0 in range(0, 256, 8):
         x = np.zeros((8, K), np.float32)
         x[np.arange(8), t0 + np.arange(8)] = 127.0
@@ -232,22 +238,24 @@ def test_one_hot_positions_gemv(dev, fmt):
         out = host(run_matmul(fmt, W, q, d, s, N, K, path=mq.MQ_PATH_GEMV))
         nz = np.argwhere(out != 0)
         assert nz.tolist() == [[i, t0 + i] for i in range(8)]
+        assert np.array_equal(out[np.arange(8), t0 + np.arange(8)], 127.0 * val[t0:t0 + 8])
 
 
 # ---------------------------------------------------------------- invariants
 
-def test_zero_quants_zero_dmin_give_zero(dev):
+@pytest.mark.parametrize("fmt", ["q4k", "q5k"])
+def test_zero_quants_zero_dmin_give_zero(dev, fmt):
     rng = np.random.default_rng(9)
     N, K, M = 130, 512, 70
-    W = synth.q4k_weights(rng, N, K).reshape(N, K // 256, 144)
-    W[:, :, 16:] = 0
+    W = synth.weights(fmt, rng, N, K).reshape(N, K // 256, -1)
+    W[:, :, 16:] = 0                      # quants (and Q5_K's high bits)
     W[:, :, 2:4] = np.array([0.0], np.float16).view(np.uint8)
     x = rng.standard_normal((M, K)).astype(np.float32)
     q, d, s = gpu_plane(x)
     for p in (mq.MQ_PATH_GEMM, mq.MQ_PATH_AUTO):
-        assert not host(run_matmul("q4k", W.reshape(N, -1), q, d, s, N, K, path=p)).any()
+        assert not host(run_matmul(fmt, W.reshape(N, -1), q, d, s, N, K, path=p)).any()
     q8, d8, s8 = gpu_plane(x[:8])
-    assert not host(run_matmul("q4k", W.reshape(N, -1), q8, d8, s8, N, K, path=mq.MQ_PATH_GEMV)).any()
+    assert not host(run_matmul(fmt, W.reshape(N, -1), q8, d8, s8, N, K, path=mq.MQ_PATH_GEMV)).any()
 
 
 def test_determinism_and_streams(dev):
@@ -273,7 +281,7 @@ def test_cross_path_rows(dev):
     """Token rows computed alone (GEMV, M=1) agree with the same rows inside a large GEMM."""
     rng = np.random.default_rng(11)
     N, K, M = 500, 3584, 300
-    for fmt in ("q4k", "q6k"):
+    for fmt in ("q4k", "q5k", "q6k"):
         W = synth.weights(fmt, rng, N, K)
         x = synth.activations(rng, M, K, outliers=True)
         q, d, s = gpu_plane(x)
@@ -298,28 +306,30 @@ def _both_paths(fmt, W, x, N, K, what):
     check_close(host(run_matmul(fmt, W, q8, d8, s8, N, K, path=mq.MQ_PATH_GEMV)), ref[:8], what + " GEMV")
 
 
-def test_min_term_dominated(dev):
-    """Q4_K outputs made mostly of the min term: large dmin, small d, and
+@pytest.mark.parametrize("fmt", ["q4k", "q5k"])
+def test_min_term_dominated(dev, fmt):
+    """Outputs made mostly of the min term: large dmin, small d, and
     activations with a common offset so that the block sums are large."""
     rng = np.random.default_rng(12)
     N, K, M = 200, 2048, 150
-    W = synth.q4k_weights(rng, N, K, d_range=(1e-5, 2e-5), dmin_range=(5e-3, 1e-2))
+    gen = synth.q4k_weights if fmt == "q4k" else synth.q5k_weights
+    W = gen(rng, N, K, d_range=(1e-5, 2e-5), dmin_range=(5e-3, 1e-2))
     x = (rng.standard_normal((M, K)) + 3.0).astype(np.float32)
-    _both_paths("q4k", W, x, N, K, "min-dominated")
+    _both_paths(fmt, W, x, N, K, "min-dominated")
 
 
 def _log_uniform_f16(rng, shape, lo, hi):
     return np.exp(rng.uniform(np.log(lo), np.log(hi), size=shape)).astype(np.float16)
 
 
-@pytest.mark.parametrize("fmt", ["q4k", "q6k"])
+@pytest.mark.parametrize("fmt", ["q4k", "q5k", "q6k"])
 def test_wide_scale_range(dev, fmt):
     """Block scales spread over the whole f16 range (subnormal to 6e4) and
     activation rows whose magnitudes differ by 2^+-40."""
     rng = np.random.default_rng(13)
     N, K, M = 96, 1536, 130
     W = synth.weights(fmt, rng, N, K).reshape(N, K // 256, -1)
-    if fmt == "q4k":
+    if fmt in ("q4k", "q5k"):
         W[:, :, 0:2] = _log_uniform_f16(rng, (N, K // 256), 1e-7, 6e4).view(np.uint8).reshape(N, K // 256, 2)
         W[:, :, 2:4] = _log_uniform_f16(rng, (N, K // 256), 1e-7, 6e4).view(np.uint8).reshape(N, K // 256, 2)
     else:
