@@ -28,7 +28,9 @@ namespace {
 constexpr int GEMV_WAVES = 4;   // wavefronts per workgroup
 #ifndef GEMV_STREAM_WGS
 #define GEMV_STREAM_WGS 1024        // workgroups of the persistent stream kernel
-#define GEMV_STREAM_D 2             // rows in flight per wavefront
+#endif
+#ifndef GEMV_STREAM_D
+#define GEMV_STREAM_D 1             // rows in flight per wavefront (beside the one computed)
 #endif
 
 // ---------------------------------------------------------------- Q4_K
@@ -318,9 +320,10 @@ __global__ __launch_bounds__(64 * GEMV_WAVES) void gemv_q4k_ffn_kernel(
 // n = w, w + NW, w + 2 NW, ... (NW wavefronts in all, so neighbouring
 // wavefronts read neighbouring rows). Each row is NP passes of 7 blocks; the
 // loads of the next D rows stay in flight while a row is reduced across the
-// wavefront and stored. Loads always use a valid address (the last row or
-// block) and are masked afterwards, so every wavefront issues the same
-// number of loads per row and the waits stay exact.
+// wavefront and stored. Blocks past the end of a row are clamped to its last
+// block and masked afterwards; past its last row a wavefront loads nothing
+// (measured on MI355X: one row ahead, without clamped tail loads, is the
+// fastest depth, most of all for short matrices).
 template <int MT, int NP, int D>
 __global__ __launch_bounds__(64 * GEMV_WAVES) void gemv_q4k_stream_kernel(
     const uint8_t *__restrict__ W, const int8_t *__restrict__ q,
@@ -428,9 +431,11 @@ __global__ __launch_bounds__(64 * GEMV_WAVES) void gemv_q4k_stream_kernel(
                         }
                     }
                 }
-                // refill this ring slot with the row D ahead
-                {
-                    const int n = min(w + (i + D) * nw, N - 1);
+                // refill this ring slot with the row D ahead (a wave-uniform
+                // branch: past its last row the wavefront loads nothing, so
+                // the tail does not pile clamped loads onto one row)
+                if (i + D < nrows) {
+                    const int n = w + (i + D) * nw;
 #pragma unroll
                     for (int p = 0; p < NP; ++p)
                         ring[d][p] = __builtin_nontemporal_load(
@@ -590,6 +595,140 @@ __global__ __launch_bounds__(64 * GEMV_WAVES) void gemv_q5k_kernel(
             const float v = wave_sum(acc[r][m]);
             if (lane == 0 && m < M && r < rows)
                 out[(int64_t)m * N + row0 + r] = v;
+        }
+    }
+}
+
+// Persistent form of the Q5_K stream for short rows (K <= NP * 8 * 256),
+// organised as the Q4_K one: wavefront w of NW walks rows w, w + NW, ...,
+// each row NP passes of 8 blocks, the loads of the next D rows in flight
+// while a row is reduced and stored; blocks past a row's end are clamped and
+// masked, and nothing is loaded past the wavefront's last row.
+template <int MT, int NP, int D>
+__global__ __launch_bounds__(64 * GEMV_WAVES) void gemv_q5k_stream_kernel(
+    const uint8_t *__restrict__ W, const int8_t *__restrict__ q,
+    const float *__restrict__ dx, const float *__restrict__ sx, int M, int N,
+    int K, float *__restrict__ out)
+{
+    __shared__ v4i act[GEMV_ACT_LDS / 16];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int nw = gridDim.x * GEMV_WAVES;
+    const int w = blockIdx.x * GEMV_WAVES + wave;
+    ActCopy ac;
+    act_load(ac, q, dx, sx, M, K);
+
+    const int nb = K >> 8;
+    const int nb32 = K >> 5;
+    const int64_t rowb = (int64_t)nb * 176;
+    const int slot = lane >> 3;
+    const int c = lane & 7;
+    const int cc = c >> 1, po = (c & 1) << 4;
+    const int j0 = 2 * cc;
+    const int rot0 = (j0 + 28) & 31, rot1 = (j0 + 29) & 31;
+    const int nrows = w < N ? (N - 1 - w) / nw + 1 : 0;
+
+    bool valid[NP];
+    int boff[NP];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        const int blk = 8 * p + slot;
+        valid[p] = blk < nb;
+        boff[p] = min(blk, nb - 1) * 176;
+    }
+    struct Blk {
+        v4i h, qh, qs;
+    };
+    auto load = [&](Blk &b, int n, int p) {
+        const uint8_t *a = W + (int64_t)n * rowb + boff[p];
+        b.h = __builtin_nontemporal_load(reinterpret_cast<const v4i *>(a));
+        b.qh = __builtin_nontemporal_load(reinterpret_cast<const v4i *>(a + 16 + po));
+        b.qs = __builtin_nontemporal_load(reinterpret_cast<const v4i *>(a + 48 + 16 * c));
+    };
+
+    Blk ring[D][NP];
+#pragma unroll
+    for (int d = 0; d < D; ++d)
+#pragma unroll
+        for (int p = 0; p < NP; ++p)
+            load(ring[d][p], min(w + d * nw, N - 1), p);
+    act_store(ac, act, M, K);
+    __syncthreads();
+    const int8_t *qa = reinterpret_cast<const int8_t *>(act);
+    const float *da = reinterpret_cast<const float *>(qa + M * K);
+    const float *sa = da + M * nb32;
+
+    for (int i0 = 0; i0 < nrows; i0 += D) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            const int i = i0 + d;
+            if (i < nrows) {
+                float acc[MT];
+#pragma unroll
+                for (int m = 0; m < MT; ++m)
+                    acc[m] = 0.0f;
+#pragma unroll
+                for (int p = 0; p < NP; ++p) {
+                    if (valid[p]) {
+                        const Blk &b = ring[d][p];
+                        const int blk = 8 * p + slot;
+                        const uint32_t h0 = b.h.x, h1 = b.h.y, h2 = b.h.z, h3 = b.h.w;
+                        const int k0 = (blk << 8) + (cc << 6) + po;
+                        const int b0 = (blk << 3) + (cc << 1);
+                        const float dd = f16_bits_to_f32(h0);
+                        const float dm = f16_bits_to_f32(h0 >> 16);
+                        const uint32_t scw = cc < 2 ? (h1 & 0x3f3f3f3fu)
+                                                    : ((h3 & 0x0f0f0f0fu) | ((h1 >> 2) & 0x30303030u));
+                        const uint32_t mw = cc < 2 ? (h2 & 0x3f3f3f3fu)
+                                                   : (((h3 >> 4) & 0x0f0f0f0fu) | ((h2 >> 2) & 0x30303030u));
+                        const int sh = (cc & 1) << 4;
+                        const float f0 = dd * (float)((scw >> sh) & 0xffu);
+                        const float f1 = dd * (float)((scw >> (sh + 8)) & 0xffu);
+                        const float g0 = po == 0 ? dm * (float)((mw >> sh) & 0xffu) : 0.0f;
+                        const float g1 = po == 0 ? dm * (float)((mw >> (sh + 8)) & 0xffu) : 0.0f;
+                        int lo[4], hi[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const uint32_t hb = (uint32_t)b.qh[e];
+                            lo[e] = (b.qs[e] & 0x0f0f0f0f) | (int)(__builtin_rotateright32(hb, rot0) & 0x10101010u);
+                            hi[e] = ((b.qs[e] >> 4) & 0x0f0f0f0f) | (int)(__builtin_rotateright32(hb, rot1) & 0x10101010u);
+                        }
+#pragma unroll
+                        for (int m = 0; m < MT; ++m) {
+                            if (m < M) {
+                                const v4i xa = *reinterpret_cast<const v4i *>(qa + m * K + k0);
+                                const v4i xb = *reinterpret_cast<const v4i *>(qa + m * K + k0 + 32);
+                                const float2 dp = *reinterpret_cast<const float2 *>(da + m * nb32 + b0);
+                                const float2 sp = *reinterpret_cast<const float2 *>(sa + m * nb32 + b0);
+                                int i0v = dot4(lo[0], xa.x, 0);
+                                i0v = dot4(lo[1], xa.y, i0v);
+                                i0v = dot4(lo[2], xa.z, i0v);
+                                i0v = dot4(lo[3], xa.w, i0v);
+                                int i1v = dot4(hi[0], xb.x, 0);
+                                i1v = dot4(hi[1], xb.y, i1v);
+                                i1v = dot4(hi[2], xb.z, i1v);
+                                i1v = dot4(hi[3], xb.w, i1v);
+                                float a = fmaf((float)i0v, dp.x * f0, acc[m]);
+                                a = fmaf((float)i1v, dp.y * f1, a);
+                                a = fmaf(-g0, sp.x, a);
+                                acc[m] = fmaf(-g1, sp.y, a);
+                            }
+                        }
+                    }
+                }
+                if (i + D < nrows) {
+#pragma unroll
+                    for (int p = 0; p < NP; ++p)
+                        load(ring[d][p], w + (i + D) * nw, p);
+                }
+                const int n = w + i * nw;
+#pragma unroll
+                for (int m = 0; m < MT; ++m) {
+                    const float v = wave_sum(acc[m]);
+                    if (lane == 0 && m < M)
+                        out[(int64_t)m * N + n] = v;
+                }
+            }
         }
     }
 }
@@ -983,6 +1122,14 @@ hipError_t launch_gemv_q5k(const uint8_t *W, const int8_t *q, const float *d,
                            const float *s, int M, int N, int K, float *out,
                            hipStream_t st)
 {
+    if (M <= 2 && K <= 2 * 8 * 256 && (int64_t)M * K * 5 / 4 <= GEMV_ACT_LDS) {
+        const int nwg = max(1, min((N + GEMV_WAVES - 1) / GEMV_WAVES, GEMV_STREAM_WGS));
+        if (M == 1)
+            gemv_q5k_stream_kernel<1, 2, GEMV_STREAM_D><<<dim3(nwg), dim3(64 * GEMV_WAVES), 0, st>>>(W, q, d, s, M, N, K, out);
+        else
+            gemv_q5k_stream_kernel<2, 2, GEMV_STREAM_D><<<dim3(nwg), dim3(64 * GEMV_WAVES), 0, st>>>(W, q, d, s, M, N, K, out);
+        return hipGetLastError();
+    }
     if (M <= 1) return gemv_q5k_mt<1>(W, q, d, s, M, N, K, out, st);
     if (M <= 2) return gemv_q5k_mt<2>(W, q, d, s, M, N, K, out, st);
     if (M <= 4) return gemv_q5k_mt<4>(W, q, d, s, M, N, K, out, st);
