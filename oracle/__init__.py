@@ -56,6 +56,10 @@ def lib() -> ctypes.CDLL:
             f = getattr(L, name)
             f.argtypes = [P, P, P, P, P, P]
             f.restype = None
+        L.oracle_expand_q6k.argtypes = [P, I64, I64, P, P, P]
+        L.oracle_expand_q6k.restype = None
+        L.oracle_dsc_q4k.argtypes = [P, I64, I64, P, P]
+        L.oracle_dsc_q4k.restype = None
         L.oracle_q6k_block_decode.argtypes = [P, P, P, P]
         L.oracle_q6k_block_decode.restype = None
         L.oracle_max_threads.argtypes = []
@@ -155,6 +159,29 @@ def q6k_block_decode(blk: np.ndarray):
     q6 = np.zeros(256, np.uint8)
     lib().oracle_q6k_block_decode(_ptr(blk), _ptr(d), _ptr(sc), _ptr(q6))
     return dict(d=float(d[0]), sc=sc, q=q6)
+
+
+def expand_q6k(W, N, K):
+    """Q6_K expansion planes of W [N rows of K]: (lo int8 [N, K] in 0..63,
+    hi int8 [N, K] in -64..64, dw f32 [N, K/256]) with 64*hi + lo = sc*(q - 32)."""
+    W = np.ascontiguousarray(W, dtype=np.uint8)
+    assert W.size == N * (K // 256) * 210
+    lo = np.empty((N, K), np.int8)
+    hi = np.empty((N, K), np.int8)
+    dw = np.empty((N, K // 256), np.float32)
+    lib().oracle_expand_q6k(_ptr(W), N, K, _ptr(lo), _ptr(hi), _ptr(dw))
+    return lo, hi, dw
+
+
+def dsc_q4k(W, N, K):
+    """Q4_K decoded-scale planes of W [N rows of K]: (fw, fm) f32 [N, K/32],
+    fw = d*sc_j and fm = dmin*m_j per 32-value sub-block."""
+    W = np.ascontiguousarray(W, dtype=np.uint8)
+    assert W.size == N * (K // 256) * 144
+    fw = np.empty((N, K // 32), np.float32)
+    fm = np.empty((N, K // 32), np.float32)
+    lib().oracle_dsc_q4k(_ptr(W), N, K, _ptr(fw), _ptr(fm))
+    return fw, fm
 
 
 def max_threads() -> int:

@@ -181,6 +181,63 @@ void oracle_q6k_block_decode(const uint8_t *blk, double *d, int32_t sc[16],
 }
 
 /* ---------------------------------------------------------------------- */
+/* Registration-time planes (the pages add weight-expansion planes for    */
+/* the q6_K MMQ GEMM and a decoded-scale plane for q4_K at weight         */
+/* registration: minfer Features, "GPU — CUDA", the W_exp / W_dsc planes  */
+/* and their memory knob). Their contents are not given; readings taken:  */
+/*  - Q6_K expansion: every weight's integer p = sc_g * (q - 32) (g its    */
+/*    16-value group) as two int8 planes, lo = p mod 64 (0..63) and        */
+/*    hi = floor(p / 64) (-64..64), so p = 64 hi + lo; plus d per super-   */
+/*    block as f32. Planes are [N][K] and [N][K/256].                      */
+/*  - Q4_K decoded scales: d*sc_j and dmin*m_j per 32-value sub-block j as */
+/*    f32 (both exact: an f16 times a 6-bit integer), planes [N][K/32].    */
+/* ---------------------------------------------------------------------- */
+
+void oracle_expand_q6k(const uint8_t *W, int64_t N, int64_t K, int8_t *lo,
+                       int8_t *hi, float *dw)
+{
+    const int64_t nsb = K / 256;
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t sb = 0; sb < nsb; ++sb) {
+            double d;
+            int32_t sc[16];
+            uint8_t q6[256];
+            oracle_q6k_block_decode(W + (n * nsb + sb) * 210, &d, sc, q6);
+            dw[n * nsb + sb] = (float)d;
+            for (int w = 0; w < 256; ++w) {
+                const int32_t p = sc[w / 16] * ((int32_t)q6[w] - 32);
+                /* floor division and the matching non-negative remainder */
+                int32_t h = p / 64;
+                if (p % 64 != 0 && p < 0)
+                    h -= 1;
+                const int64_t k = n * K + sb * 256 + w;
+                hi[k] = (int8_t)h;
+                lo[k] = (int8_t)(p - 64 * h);
+            }
+        }
+    }
+}
+
+void oracle_dsc_q4k(const uint8_t *W, int64_t N, int64_t K, float *fw, float *fm)
+{
+    const int64_t nsb = K / 256;
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t sb = 0; sb < nsb; ++sb) {
+            double d, dmin;
+            int32_t sc[8], m[8];
+            uint8_t q4[256];
+            oracle_q4k_block_decode(W + (n * nsb + sb) * 144, &d, &dmin, sc, m, q4);
+            for (int j = 0; j < 8; ++j) {
+                fw[n * nsb * 8 + sb * 8 + j] = (float)(d * sc[j]);
+                fm[n * nsb * 8 + sb * 8 + j] = (float)(dmin * m[j]);
+            }
+        }
+    }
+}
+
+/* ---------------------------------------------------------------------- */
 /* Matmuls. out is [ntok][N]; token tt is toks[tt] (or tt when toks is    */
 /* NULL). Exactly one of out64 / out32 is non-NULL.                        */
 /* ---------------------------------------------------------------------- */
