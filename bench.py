@@ -274,6 +274,7 @@ def run_all(args):
         torch.cuda.empty_cache()
     run_producers(dev)
     run_ffn(dev)
+    run_planes(dev)
 
 
 def _time_rotating(fn, copies, reps):
@@ -338,6 +339,48 @@ def run_ffn(dev):
             row["frac_int8_peak"] = round(row["TOPS"] / INT8_PEAK_TOPS, 4)
         print(json.dumps(row), flush=True)
         del Wgs, Wus, Wg0, Wu0, g_out, u_out
+        torch.cuda.empty_cache()
+
+
+def run_planes(dev):
+    """The GEMMs reading registration-time planes (Q6_K expansion, Q4_K
+    decoded scales) against the same GEMMs on the raw blocks, on the
+    prefill workloads; the planes' build time and size beside them."""
+    import numpy as np
+    import torch
+
+    import quant_gemm_amd as mq
+    from quant_gemm_amd import synth
+
+    for name in ("layer_down", "q6k_ffn_down_m512", "q4k_prefill_ffn_up", "q4k_prefill_attn_o"):
+        c = synth.case_by_name(name)
+        W = torch.from_numpy(c.make_weights().reshape(-1)).to(dev)
+        x = torch.from_numpy(c.make_activations()).to(dev)
+        q, d, s = mq.quantize_act(x)
+        out = torch.empty((c.M, c.N), dtype=torch.float32, device=dev)
+        if c.fmt == "q6k":
+            lo, hi, dw = mq.expand_q6k(W, c.N, c.K)
+            build = lambda i: mq.expand_q6k(W, c.N, c.K, lo, hi, dw)
+            raw = lambda i: mq.matmul_q6k(W, q, d, None, c.N, c.K, out=out, path=mq.MQ_PATH_GEMM)
+            planes = lambda i: mq.matmul_q6k_x(lo, hi, dw, q, d, c.N, c.K, out=out)
+            kind, plane_bytes = "q6k expansion (lo, hi, d)", 2 * lo.numel() + 4 * dw.numel()
+        else:
+            fw, fm = mq.dsc_q4k(W, c.N, c.K)
+            build = lambda i: mq.dsc_q4k(W, c.N, c.K, fw, fm)
+            raw = lambda i: mq.matmul_q4k(W, q, d, s, c.N, c.K, out=out, path=mq.MQ_PATH_GEMM)
+            planes = lambda i: mq.matmul_q4k_dsc(W, fw, fm, q, d, s, c.N, c.K, out=out)
+            kind, plane_bytes = "q4k decoded scales (fw, fm)", 8 * fw.numel()
+        rt, pt = [], []
+        for _ in range(3):                        # alternate; medians (clocks drift)
+            rt.append(_time_rotating(raw, 1, 20))
+            pt.append(_time_rotating(planes, 1, 20))
+        r, p_ = float(np.median(rt)), float(np.median(pt))
+        row = {"group": "planes", "case": f"{name} {kind}", "M": c.M, "N": c.N, "K": c.K,
+               "us": round(p_, 2), "TOPS": round(c.ops / (p_ * 1e-6) / 1e12, 2), "raw_us": round(r, 2),
+               "speedup": round(r / p_, 3), "build_us": round(_time_rotating(build, 1, 3), 1),
+               "plane_MB": round(plane_bytes / 1e6, 1), "raw_MB": round(W.numel() / 1e6, 1)}
+        print(json.dumps(row), flush=True)
+        del W, x, out
         torch.cuda.empty_cache()
 
 

@@ -197,8 +197,8 @@ int mq_matmul_q6k_ex(const void *W, const int8_t *q, const float *d,
  *       what mq_quantize_act would write for y);
  *   y  optional f32 [M][N], written when not NULL.
  * Wg and Wu are N rows of K each (Q4_K layout); N is a positive multiple of
- * 256 (it is the down projection's K). M <= mq_gemv_max_m() runs a fused
- * GEMV, larger M a GEMM whose tiles pair 64 gate rows with the same 64 up
+ * 256 (it is the down projection's K). M <= 8 runs a fused GEMV, larger
+ * M a GEMM whose tiles pair 64 gate rows with the same 64 up
  * rows. Alignment as for the matmuls; qo, do_, so and y 16-byte aligned.
  */
 int mq_ffn_q4k(const void *Wg, const void *Wu, const int8_t *q, const float *d,
@@ -207,6 +207,52 @@ int mq_ffn_q4k(const void *Wg, const void *Wu, const int8_t *q, const float *d,
 int mq_ffn_q4k_ex(const void *Wg, const void *Wu, const int8_t *q, const float *d,
                   const float *s, int64_t M, int64_t N, int64_t K, int8_t *qo,
                   float *do_, float *so, float *y, void *stream, int path);
+
+/*
+ * Registration-time weight planes for the prefill GEMM. The pages build
+ * weight-expansion planes for q6_K and a decoded-scale plane for q4_K when
+ * weights are registered, and their MMQ GEMM reads those instead of
+ * decoding the raw blocks per tile (minfer Features, "GPU — CUDA": W_exp /
+ * W_dsc, about 3.3 GB for about +6% prefill). Build once per weight matrix;
+ * the planes are plain device arrays owned by the caller. They serve the
+ * GEMM (prefill) only: a decode step reads the raw blocks (mq_matmul_*),
+ * which are 2.4x (Q6_K) fewer bytes.
+ *
+ * mq_expand_q6k: W (Q6_K, N rows of K) -> lo, hi int8 [N][K] and dw f32
+ * [N][K/256]: for every weight p = sc_g * (q - 32) (g its 16-value group,
+ * p in -4064..4096) is lo + 64 * hi with lo in 0..63, hi in -64..64; dw is
+ * each super-block's d. Exact. W, lo, hi, dw 16-byte aligned.
+ */
+int mq_expand_q6k(const void *W, int64_t N, int64_t K, int8_t *lo, int8_t *hi,
+                  float *dw, void *stream);
+
+/*
+ * Q6_K matmul from the expansion planes: the same result and contract as
+ * mq_matmul_q6k on the blocks they were built from (f32, within its
+ * tolerance), always on the int8 MFMA GEMM (32-token tiles up to M = 32).
+ * lo, hi 16-byte aligned, dw 4-byte aligned; q, d, out as for the matmuls.
+ */
+int mq_matmul_q6k_x(const int8_t *lo, const int8_t *hi, const float *dw,
+                    const int8_t *q, const float *d, int64_t M, int64_t N,
+                    int64_t K, float *out, void *stream);
+
+/*
+ * mq_dsc_q4k: W (Q4_K, N rows of K) -> fw, fm f32 [N][K/32] with
+ * fw = d * sc_j and fm = dmin * m_j for each 32-value sub-block j (exact:
+ * an f16 times a 6-bit code). W, fw, fm 16-byte aligned.
+ */
+int mq_dsc_q4k(const void *W, int64_t N, int64_t K, float *fw, float *fm,
+               void *stream);
+
+/*
+ * Q4_K matmul reading the quants from W and the factors from the
+ * decoded-scale planes (no block header decoded per tile): the same result
+ * and contract as mq_matmul_q4k, always on the GEMM (32-token tiles up to
+ * M = 96). fw, fm as built by mq_dsc_q4k from this W; s is required.
+ */
+int mq_matmul_q4k_dsc(const void *W, const float *fw, const float *fm,
+                      const int8_t *q, const float *d, const float *s,
+                      int64_t M, int64_t N, int64_t K, float *out, void *stream);
 
 /* Largest M the GEMV path serves (MQ_PATH_GEMV); 16. */
 int64_t mq_gemv_max_m(void);

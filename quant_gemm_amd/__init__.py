@@ -46,6 +46,10 @@ SIGNATURES = {
     "mq_matmul_q4k_ex": (_MATMUL_ARGS + [ctypes.c_int], ctypes.c_int),
     "mq_matmul_q5k_ex": (_MATMUL_ARGS + [ctypes.c_int], ctypes.c_int),
     "mq_matmul_q6k_ex": (_MATMUL_ARGS + [ctypes.c_int], ctypes.c_int),
+    "mq_expand_q6k": ([_P, _I64, _I64, _P, _P, _P, _P], ctypes.c_int),
+    "mq_matmul_q6k_x": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P], ctypes.c_int),
+    "mq_dsc_q4k": ([_P, _I64, _I64, _P, _P, _P], ctypes.c_int),
+    "mq_matmul_q4k_dsc": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P], ctypes.c_int),
     "mq_gemv_max_m": ([], ctypes.c_int64),
     "mq_last_error": ([], ctypes.c_char_p),
     "mq_abi_version": ([], ctypes.c_int),
@@ -208,6 +212,74 @@ def matmul_q5k(W, q, d, s, N, K, out=None, stream=None, path=MQ_PATH_AUTO):
 def matmul_q6k(W, q, d, s, N, K, out=None, stream=None, path=MQ_PATH_AUTO):
     """out [M, N] f32 = Q6_K weights W (N rows of K) times the activation plane (q, d); s unused."""
     return _matmul("mq_matmul_q6k_ex", Q6K_BLOCK_BYTES, W, q, d, s, N, K, out, stream, path)
+
+
+def expand_q6k(W, N, K, lo=None, hi=None, dw=None, stream=None):
+    """Q6_K expansion planes of W (uint8, N rows of K): (lo, hi) int8 [N, K]
+    and dw f32 [N, K/256], for matmul_q6k_x."""
+    import torch
+    L = load()
+    assert W.is_cuda and W.dtype == torch.uint8 and W.is_contiguous()
+    assert W.numel() == N * (K // 256) * Q6K_BLOCK_BYTES, "W size does not match N, K"
+    lo = torch.empty((N, K), dtype=torch.int8, device=W.device) if lo is None else lo
+    hi = torch.empty((N, K), dtype=torch.int8, device=W.device) if hi is None else hi
+    dw = torch.empty((N, K // 256), dtype=torch.float32, device=W.device) if dw is None else dw
+    for t, dt, shp in ((lo, torch.int8, (N, K)), (hi, torch.int8, (N, K)), (dw, torch.float32, (N, K // 256))):
+        assert t.dtype == dt and t.is_contiguous() and tuple(t.shape) == shp
+    _check(L.mq_expand_q6k(W.data_ptr(), N, K, lo.data_ptr(), hi.data_ptr(), dw.data_ptr(), _stream(stream)))
+    return lo, hi, dw
+
+
+def matmul_q6k_x(lo, hi, dw, q, d, N, K, out=None, stream=None):
+    """out [M, N] f32 from the Q6_K expansion planes and the activation plane (q, d)."""
+    import torch
+    L = load()
+    assert lo.dtype == torch.int8 and hi.dtype == torch.int8 and dw.dtype == torch.float32
+    assert tuple(lo.shape) == (N, K) and tuple(hi.shape) == (N, K) and tuple(dw.shape) == (N, K // 256)
+    assert lo.is_contiguous() and hi.is_contiguous() and dw.is_contiguous()
+    M = q.shape[0]
+    assert q.dtype == torch.int8 and q.is_contiguous() and tuple(q.shape) == (M, K)
+    assert d.dtype == torch.float32 and d.is_contiguous() and tuple(d.shape) == (M, K // 32)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=q.device)
+    assert out.dtype == torch.float32 and out.is_contiguous() and tuple(out.shape) == (M, N)
+    _check(L.mq_matmul_q6k_x(lo.data_ptr(), hi.data_ptr(), dw.data_ptr(), q.data_ptr(), d.data_ptr(),
+                             M, N, K, out.data_ptr(), _stream(stream)))
+    return out
+
+
+def dsc_q4k(W, N, K, fw=None, fm=None, stream=None):
+    """Q4_K decoded-scale planes of W: (fw, fm) f32 [N, K/32], for matmul_q4k_dsc."""
+    import torch
+    L = load()
+    assert W.is_cuda and W.dtype == torch.uint8 and W.is_contiguous()
+    assert W.numel() == N * (K // 256) * Q4K_BLOCK_BYTES, "W size does not match N, K"
+    fw = torch.empty((N, K // 32), dtype=torch.float32, device=W.device) if fw is None else fw
+    fm = torch.empty((N, K // 32), dtype=torch.float32, device=W.device) if fm is None else fm
+    for t in (fw, fm):
+        assert t.dtype == torch.float32 and t.is_contiguous() and tuple(t.shape) == (N, K // 32)
+    _check(L.mq_dsc_q4k(W.data_ptr(), N, K, fw.data_ptr(), fm.data_ptr(), _stream(stream)))
+    return fw, fm
+
+
+def matmul_q4k_dsc(W, fw, fm, q, d, s, N, K, out=None, stream=None):
+    """out [M, N] f32 = Q4_K W times the plane (q, d, s), factors from (fw, fm)."""
+    import torch
+    L = load()
+    assert W.is_cuda and W.dtype == torch.uint8 and W.is_contiguous()
+    assert W.numel() == N * (K // 256) * Q4K_BLOCK_BYTES, "W size does not match N, K"
+    for t in (fw, fm):
+        assert t.dtype == torch.float32 and t.is_contiguous() and tuple(t.shape) == (N, K // 32)
+    M = q.shape[0]
+    assert q.dtype == torch.int8 and q.is_contiguous() and tuple(q.shape) == (M, K)
+    for t in (d, s):
+        assert t.dtype == torch.float32 and t.is_contiguous() and tuple(t.shape) == (M, K // 32)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=q.device)
+    assert out.dtype == torch.float32 and out.is_contiguous() and tuple(out.shape) == (M, N)
+    _check(L.mq_matmul_q4k_dsc(W.data_ptr(), fw.data_ptr(), fm.data_ptr(), q.data_ptr(), d.data_ptr(),
+                               s.data_ptr(), M, N, K, out.data_ptr(), _stream(stream)))
+    return out
 
 
 def ffn_q4k(Wg, Wu, q, d, s, N, K, qo=None, do=None, so=None, y=None, stream=None, path=MQ_PATH_AUTO):

@@ -11,6 +11,11 @@
 // the same kernel runs it with one more DMA'd tile (32 bytes of high bits
 // per row and step) merged into the B operand.
 //
+// Decoded-scale planes (DSC): the Q4_K kernel can instead take the per
+// sub-block factors d*sc and dmin*m from f32 planes built once at
+// registration (mq_dsc_q4k; the pages' q4_K decoded-scale plane, minfer
+// Features, "GPU — CUDA"), so no block header is decoded per tile.
+//
 // Tiling. A 256-thread workgroup computes 128 tokens x 128 weight rows as
 // 4 wavefronts of 32 tokens x 128 rows, each 1 x 4 MFMA tiles of 32 x 32.
 // The K loop moves in half super-blocks (128 values = 4 sub-blocks of 32).
@@ -200,19 +205,32 @@ __device__ __forceinline__ void issue_tiles(Stage &s, const WRows &rows,
 // stored, so their contributions vanish.
 struct Side {
     uint4 hdr;      // block header of row n0 + tid (tid < BN)
+    float4 fw, fm;  // DSC: d*sc_j and dmin*m_j of the step's 4 sub-blocks, row n0 + tid
     float4 ds;      // 4 scales (tid < BM) or 4 sums (tid >= BM) of token t0 + tid % BM
 };
 
-template <bool FFN>
-__device__ __forceinline__ void load_side(Side &p, const WRows &rows,
+// Decoded-scale planes fw / fm [N][K/32] (DSC) or none.
+struct Dsc {
+    const float *fw, *fm;
+};
+
+template <bool FFN, bool DSC>
+__device__ __forceinline__ void load_side(Side &p, const WRows &rows, const Dsc &dsc,
                                           const float *__restrict__ dx,
                                           const float *__restrict__ sx, int M, int K,
                                           int t0, int st)
 {
     const int tid = threadIdx.x;
     const int k0 = st * BK;
-    if (tid < BN)
-        p.hdr = *reinterpret_cast<const uint4 *>(rows.row<FFN>(tid) + (int64_t)(st >> 1) * BLK_BYTES);
+    if (tid < BN) {
+        if constexpr (DSC) {
+            const int64_t i = (int64_t)min(rows.n0 + tid, rows.N - 1) * (K >> 5) + (k0 >> 5);
+            p.fw = *reinterpret_cast<const float4 *>(dsc.fw + i);
+            p.fm = *reinterpret_cast<const float4 *>(dsc.fm + i);
+        } else {
+            p.hdr = *reinterpret_cast<const uint4 *>(rows.row<FFN>(tid) + (int64_t)(st >> 1) * BLK_BYTES);
+        }
+    }
     if (tid < 2 * BM) {
         const int t = min(t0 + (tid & (BM - 1)), M - 1);
         const float *src = tid < BM ? dx : sx;
@@ -220,7 +238,7 @@ __device__ __forceinline__ void load_side(Side &p, const WRows &rows,
     }
 }
 
-template <bool FFN>
+template <bool FFN, bool DSC>
 __device__ __forceinline__ void store_side(Stage &s, const Side &p, const WRows &rows, int st, int M,
                                            int t0)
 {
@@ -238,7 +256,16 @@ __device__ __forceinline__ void store_side(Stage &s, const Side &p, const WRows 
                             tok ? p.ds.w : 0.0f};
         limbs4(x, s.sxl[row][0], s.sxl[row][1]);
     }
-    if (tid < BN) {
+    if (DSC && tid < BN) {
+        const bool ok = rows.valid<FFN>(tid);
+        const float fw[4] = {p.fw.x, p.fw.y, p.fw.z, p.fw.w};
+        const float fm[4] = {ok ? -p.fm.x : 0.0f, ok ? -p.fm.y : 0.0f, ok ? -p.fm.z : 0.0f,
+                             ok ? -p.fm.w : 0.0f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            s.fw[j][tid] = ok ? fw[j] : 0.0f;
+        limbs4(fm, s.fml[tid][0], s.fml[tid][1]);
+    } else if (tid < BN) {
         // header: f16 d | f16 dmin | 12 bytes of 6-bit codes. Codes j = 0..3
         // are bytes 0..3 (scale) and 4..7 (min) masked to 6 bits; codes
         // 4..7 take their low 4 bits from bytes 8..11 and their high 2 bits
@@ -389,9 +416,9 @@ __device__ __forceinline__ float swiglu1(float g, float u)
 // Plain: out (or a split-K partial plane) = the f32 result. FFN (W = gate,
 // W2 = up, tiles of 64 output columns): y = SiLU(g) * u per output, written
 // as its int8 plane qo / do_ / so (and y itself when y != nullptr).
-template <bool FFN>
+template <bool FFN, bool DSC>
 __global__ __launch_bounds__(NTHR, MQ_Q4K_OCC) void gemm_q4k_kernel(
-    const uint8_t *__restrict__ W, const uint8_t *__restrict__ W2, const int8_t *__restrict__ q,
+    const uint8_t *__restrict__ W, const uint8_t *__restrict__ W2, const Dsc dsc, const int8_t *__restrict__ q,
     const float *__restrict__ dx, const float *__restrict__ sx, int M, int N,
     int K, int tiles_m, int nsplit, float *__restrict__ out, int8_t *__restrict__ qo,
     float *__restrict__ do_, float *__restrict__ so)
@@ -429,26 +456,26 @@ __global__ __launch_bounds__(NTHR, MQ_Q4K_OCC) void gemm_q4k_kernel(
     // The step range is even (whole super-blocks): steps alternate S0, S1.
     Side p;
     issue_tiles<FFN>(S0, rows, q, M, K, t0, st_begin, wave, lane);
-    load_side<FFN>(p, rows, dx, sx, M, K, t0, st_begin);
+    load_side<FFN, DSC>(p, rows, dsc, dx, sx, M, K, t0, st_begin);
     wait_vm<0>();
-    store_side<FFN>(S0, p, rows, st_begin, M, t0);
+    store_side<FFN, DSC>(S0, p, rows, st_begin, M, t0);
     __syncthreads();
     for (int st = st_begin; st < st_end; st += 2) {
         issue_tiles<FFN>(S1, rows, q, M, K, t0, st + 1, wave, lane);
-        load_side<FFN>(p, rows, dx, sx, M, K, t0, st + 1);
+        load_side<FFN, DSC>(p, rows, dsc, dx, sx, M, K, t0, st + 1);
         compute_step<0>(S0, acc, wm, wn, lr, lh);
         wait_vm<0>();
-        store_side<FFN>(S1, p, rows, st + 1, M, t0);
+        store_side<FFN, DSC>(S1, p, rows, st + 1, M, t0);
         __syncthreads();
         const bool more = st + 2 < st_end;
         if (more) {
             issue_tiles<FFN>(S0, rows, q, M, K, t0, st + 2, wave, lane);
-            load_side<FFN>(p, rows, dx, sx, M, K, t0, st + 2);
+            load_side<FFN, DSC>(p, rows, dsc, dx, sx, M, K, t0, st + 2);
         }
         compute_step<1>(S1, acc, wm, wn, lr, lh);
         if (more) {
             wait_vm<0>();
-            store_side<FFN>(S0, p, rows, st + 2, M, t0);
+            store_side<FFN, DSC>(S0, p, rows, st + 2, M, t0);
         }
         __syncthreads();
     }
@@ -559,11 +586,34 @@ hipError_t launch_gemm_q4k(const uint8_t *W, const int8_t *q, const float *d,
     const int tiles = tiles_m * tiles_n;
     const int nsplit = gemm_splits(tiles, BM * BN, K >> 8, M, N, K, Q4K_SLOT_OPS);
     return run_split_k(nsplit, (int64_t)M * N, out, st, [&](float *dst) {
-        gemm_q4k_kernel<false><<<dim3((unsigned)(tiles * nsplit)), dim3(NTHR), 0, st>>>(
-            W, nullptr, q, d, s, M, N, K, tiles_m, nsplit, dst, nullptr, nullptr, nullptr);
+        gemm_q4k_kernel<false, false><<<dim3((unsigned)(tiles * nsplit)), dim3(NTHR), 0, st>>>(
+            W, nullptr, Dsc{nullptr, nullptr}, q, d, s, M, N, K, tiles_m, nsplit, dst, nullptr, nullptr, nullptr);
         return hipGetLastError();
     });
 }
+
+#if !MQ_Q5K
+#ifdef MQ_Q4K_SMALL
+hipError_t launch_gemm_q4k_dsc_small(const uint8_t *W, const float *fw, const float *fm, const int8_t *q,
+                                     const float *d, const float *s, int M, int N, int K, float *out,
+                                     hipStream_t st)
+#else
+hipError_t launch_gemm_q4k_dsc(const uint8_t *W, const float *fw, const float *fm, const int8_t *q,
+                               const float *d, const float *s, int M, int N, int K, float *out,
+                               hipStream_t st)
+#endif
+{
+    const int tiles_m = (M + BM - 1) / BM;
+    const int tiles_n = (N + BN - 1) / BN;
+    const int tiles = tiles_m * tiles_n;
+    const int nsplit = gemm_splits(tiles, BM * BN, K >> 8, M, N, K, Q4K_SLOT_OPS);
+    return run_split_k(nsplit, (int64_t)M * N, out, st, [&](float *dst) {
+        gemm_q4k_kernel<false, true><<<dim3((unsigned)(tiles * nsplit)), dim3(NTHR), 0, st>>>(
+            W, nullptr, Dsc{fw, fm}, q, d, s, M, N, K, tiles_m, nsplit, dst, nullptr, nullptr, nullptr);
+        return hipGetLastError();
+    });
+}
+#endif
 
 #if !defined(MQ_Q4K_SMALL) && !MQ_Q5K
 hipError_t launch_gemm_q4k_ffn(const uint8_t *Wg, const uint8_t *Wu, const int8_t *q, const float *d,
@@ -572,8 +622,8 @@ hipError_t launch_gemm_q4k_ffn(const uint8_t *Wg, const uint8_t *Wu, const int8_
 {
     const int tiles_m = (M + BM - 1) / BM;
     const int tiles_n = (N + BN / 2 - 1) / (BN / 2);
-    gemm_q4k_kernel<true><<<dim3((unsigned)(tiles_m * tiles_n)), dim3(NTHR), 0, st>>>(
-        Wg, Wu, q, d, s, M, N, K, tiles_m, 1, y, qo, do_, so);
+    gemm_q4k_kernel<true, false><<<dim3((unsigned)(tiles_m * tiles_n)), dim3(NTHR), 0, st>>>(
+        Wg, Wu, Dsc{nullptr, nullptr}, q, d, s, M, N, K, tiles_m, 1, y, qo, do_, so);
     return hipGetLastError();
 }
 #endif

@@ -5,8 +5,8 @@
 // for q4_K and q6_K). Q6_K has an int8 scale per 16 values, so one int8
 // product per 32-value activation block would mix two scales. Here the scale
 // is folded into the weights exactly: each weight becomes
-//     p = sc * (q - 32)  in [-4096, 4064],  split as  p = 64 * hi + lo,
-// lo = p & 63 in [0, 63] and hi = p >> 6 in [-64, 63], both int8. Two
+//     p = sc * (q - 32)  in [-4064, 4096],  split as  p = 64 * hi + lo,
+// lo = p & 63 in [0, 63] and hi = p >> 6 in [-64, 64], both int8. Two
 // v_mfma_i32_32x32x32_i8 per 32-value block (one per limb) give
 //     J = 64 * I_hi + I_lo = sum_k sc_k * (q_k - 32) * x_k
 // exactly in int32 (|J| <= 32 * 4096 * 127 < 2^31), and the f32 epilogue
@@ -23,12 +23,21 @@
 // with aligned dword loads realigned in registers): the limb planes use one
 // buffer, written between two barriers.
 //
+// Expansion planes (X): the same kernel reads the two limbs and d from
+// planes built once at registration (mq_expand_q6k) instead of decoding
+// the raw blocks on every tile, as the pages' q6_K expansion planes do
+// (minfer Features, "GPU — CUDA"). The per-step decode then reduces to two
+// 16-byte loads per limb chunk, passed through registers into the same LDS
+// layout.
+//
 // MFMA operand layout (32x32x32): lane l supplies row (l % 32) of A and
 // column (l % 32) of B, 16 consecutive K values from 16 * (l / 32) each;
 // both operands split K alike. The result gives lane l column (l % 32) and
 // rows 8*(v/4) + 4*(l/32) + (v%4). A = activations, B = weight limbs.
 #include "mq_device.h"
 #include "mq_launch.h"
+
+#include <type_traits>
 
 namespace mq {
 namespace {
@@ -47,6 +56,8 @@ constexpr int NWAVES = WM * WN;
 constexpr int NTHR = 64 * NWAVES;
 // int8 ops per second of one resident workgroup, for the split-K choice
 constexpr double Q6K_SLOT_OPS = 0.6e12;
+// the same split choice for the expansion planes, so both give one result
+constexpr double Q6K_X_SLOT_OPS = Q6K_SLOT_OPS;
 constexpr int A_CHUNKS = BM * BK / 16;      // 16-byte activation chunks per step
 static_assert(A_CHUNKS % (64 * NWAVES) == 0, "DMA split");
 static_assert(NTHR == 2 * BN && NTHR >= BM, "one thread per (row, half) and per token");
@@ -81,16 +92,30 @@ __device__ __forceinline__ void issue_act(ActStage &s, const int8_t *__restrict_
     }
 }
 
+// Expansion planes of the weights (X): limbs lo / hi [N][K], d [N][K/256].
+struct Planes {
+    const int8_t *lo, *hi;
+    const float *dw;
+};
+
 // One thread's raw share of a step: row n0 + tid/2, half hh = tid & 1 of
 // the 128 weights (positions 32r + 16hh + i, r = 0..3, i = 0..15). The
 // fields start 2 bytes into a dword when the block does; the aligned dwords
 // covering them are kept as loaded and realigned only after the step's
 // compute, so the loads stay in flight during it.
+template <bool X>
 struct Raw {
     uint32_t w0[5], w1[5], wh[5], ws[3];
     uint32_t sh;                             // 0 or 2: byte offset of the fields in their dwords
     uint32_t dbits;
     float4 ds;                               // 4 activation scales of token tid (tid < BM)
+};
+// X: the thread's four 16-byte chunks c = 2r + hh of each limb plane
+template <>
+struct Raw<true> {
+    v4i lo[4], hi[4];
+    float dw;
+    float4 ds;
 };
 
 template <int n>
@@ -113,7 +138,24 @@ __device__ __forceinline__ void realign(const uint32_t (&w)[n + 1], uint32_t sh,
         o[i] = __builtin_amdgcn_alignbyte(w[i + 1], w[i], sh);
 }
 
-__device__ __forceinline__ void load_raw(Raw &p, const uint8_t *__restrict__ W,
+__device__ __forceinline__ void load_raw(Raw<true> &p, const Planes &E, const float *__restrict__ dx,
+                                         int M, int N, int K, int t0, int n0, int st)
+{
+    const int tid = threadIdx.x;
+    const int row = tid >> 1, hh = tid & 1;
+    const int64_t n = min(n0 + row, N - 1);
+    const int64_t base = n * K + (int64_t)st * BK + 16 * hh;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        p.lo[r] = *reinterpret_cast<const v4i *>(E.lo + base + 32 * r);
+        p.hi[r] = *reinterpret_cast<const v4i *>(E.hi + base + 32 * r);
+    }
+    p.dw = E.dw[n * (K >> 8) + (st >> 1)];
+    const int t = min(t0 + (tid & (BM - 1)), M - 1);
+    p.ds = *reinterpret_cast<const float4 *>(dx + (int64_t)t * (K >> 5) + (st * BK >> 5));
+}
+
+__device__ __forceinline__ void load_raw(Raw<false> &p, const uint8_t *__restrict__ W,
                                          const float *__restrict__ dx, int M, int N, int K,
                                          int t0, int n0, int st)
 {
@@ -158,7 +200,36 @@ __device__ __forceinline__ void limbs4(uint32_t qv, int s, uint32_t &lo, uint32_
     hi = __builtin_amdgcn_perm(hb, ha, 0x06020400u);
 }
 
-__device__ __forceinline__ void store_raw(WgtStage &w, ActStage &a, const Raw &p, int M, int N,
+__device__ __forceinline__ void store_act_scales(ActStage &a, const float4 &ds, int M, int t0)
+{
+    const int tid = threadIdx.x;
+    const bool tok = t0 + (tid & (BM - 1)) < M;
+    const float4 v = tok ? ds : make_float4(0.f, 0.f, 0.f, 0.f);
+    if (tid < BM) {
+        a.dx[0][tid] = v.x;
+        a.dx[1][tid] = v.y;
+        a.dx[2][tid] = v.z;
+        a.dx[3][tid] = v.w;
+    }
+}
+
+__device__ __forceinline__ void store_raw(WgtStage &w, ActStage &a, const Raw<true> &p, int M, int N,
+                                          int t0, int n0)
+{
+    const int tid = threadIdx.x;
+    const int row = tid >> 1, hh = tid & 1;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        *reinterpret_cast<v4i *>(w.lo + 16 * slot8(row, 2 * r + hh)) = p.lo[r];
+        *reinterpret_cast<v4i *>(w.hi + 16 * slot8(row, 2 * r + hh)) = p.hi[r];
+    }
+    // a row past N reads the last row's limbs; its d of 0 cancels them
+    if (hh == 0)
+        w.dw[row] = n0 + row < N ? p.dw : 0.0f;
+    store_act_scales(a, p.ds, M, t0);
+}
+
+__device__ __forceinline__ void store_raw(WgtStage &w, ActStage &a, const Raw<false> &p, int M, int N,
                                           int t0, int n0)
 {
     const int tid = threadIdx.x;
@@ -192,16 +263,9 @@ __device__ __forceinline__ void store_raw(WgtStage &w, ActStage &a, const Raw &p
     // every thread consumes its loaded values (only some store them), so no
     // load into these registers is left pending into the next step
     const float dwv = rok ? f16_bits_to_f32(p.dbits) : 0.0f;
-    const bool tok = t0 + (tid & (BM - 1)) < M;
-    const float4 ds = tok ? p.ds : make_float4(0.f, 0.f, 0.f, 0.f);
     if (hh == 0)
         w.dw[row] = dwv;
-    if (tid < BM) {
-        a.dx[0][tid] = ds.x;
-        a.dx[1][tid] = ds.y;
-        a.dx[2][tid] = ds.z;
-        a.dx[3][tid] = ds.w;
-    }
+    store_act_scales(a, p.ds, M, t0);
 }
 
 __device__ __forceinline__ void compute_step(const ActStage &a, const WgtStage &w,
@@ -240,11 +304,14 @@ __device__ __forceinline__ void compute_step(const ActStage &a, const WgtStage &
     }
 }
 
+// Src: the raw blocks (const uint8_t *) or the expansion planes (Planes).
+template <class Src>
 __global__ __launch_bounds__(NTHR, 2) void gemm_q6k_kernel(
-    const uint8_t *__restrict__ W, const int8_t *__restrict__ q,
+    const Src W, const int8_t *__restrict__ q,
     const float *__restrict__ dx, int M, int N, int K, int tiles_m, int nsplit,
     float *__restrict__ out)
 {
+    constexpr bool X = std::is_same<Src, Planes>::value;
     __shared__ ActStage A0, A1;
     __shared__ WgtStage B;
     // blockIdx = split * tiles + tile_n * tiles_m + tile_m; split s of nsplit
@@ -275,7 +342,7 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_q6k_kernel(
 
     // The step range is even (whole super-blocks): steps alternate the
     // activation buffers A0, A1.
-    Raw p;
+    Raw<X> p;
     issue_act(A0, q, M, K, t0, st_begin, wave, lane);
     load_raw(p, W, dx, M, N, K, t0, n0, st_begin);
     wait_vm<0>();
@@ -335,6 +402,26 @@ hipError_t launch_gemm_q6k(const uint8_t *W, const int8_t *q, const float *d,
     const int nsplit = gemm_splits(tiles, BM * BN, K >> 8, M, N, K, Q6K_SLOT_OPS);
     return run_split_k(nsplit, (int64_t)M * N, out, st, [&](float *dst) {
         gemm_q6k_kernel<<<dim3((unsigned)(tiles * nsplit)), dim3(NTHR), 0, st>>>(W, q, d, M, N, K, tiles_m,
+                                                                                 nsplit, dst);
+        return hipGetLastError();
+    });
+}
+
+#ifdef MQ_Q6K_SMALL
+hipError_t launch_gemm_q6k_x_small(const int8_t *lo, const int8_t *hi, const float *dw, const int8_t *q,
+                                   const float *d, int M, int N, int K, float *out, hipStream_t st)
+#else
+hipError_t launch_gemm_q6k_x(const int8_t *lo, const int8_t *hi, const float *dw, const int8_t *q,
+                             const float *d, int M, int N, int K, float *out, hipStream_t st)
+#endif
+{
+    const int tiles_m = (M + BM - 1) / BM;
+    const int tiles_n = (N + BN - 1) / BN;
+    const int tiles = tiles_m * tiles_n;
+    const int nsplit = gemm_splits(tiles, BM * BN, K >> 8, M, N, K, Q6K_X_SLOT_OPS);
+    const Planes E{lo, hi, dw};
+    return run_split_k(nsplit, (int64_t)M * N, out, st, [&](float *dst) {
+        gemm_q6k_kernel<<<dim3((unsigned)(tiles * nsplit)), dim3(NTHR), 0, st>>>(E, q, d, M, N, K, tiles_m,
                                                                                  nsplit, dst);
         return hipGetLastError();
     });

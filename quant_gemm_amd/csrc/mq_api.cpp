@@ -139,6 +139,40 @@ int matmul(Fmt fmt, const void *W, const int8_t *q, const float *d, const float 
     return launched(e, fn);
 }
 
+// Shared checks of a GEMM-only matmul over registration-time planes.
+int check_gemm_shape(const char *fn, const int8_t *q, const float *d, float *out, int64_t M, int64_t N,
+                     int64_t K)
+{
+    if (!q) return fail(MQ_ERR_INVALID_ARG, "%s: q is NULL", fn);
+    if (!d) return fail(MQ_ERR_INVALID_ARG, "%s: d is NULL", fn);
+    if (!out) return fail(MQ_ERR_INVALID_ARG, "%s: out is NULL", fn);
+    if (M <= 0) return fail(MQ_ERR_INVALID_ARG, "%s: M=%lld must be positive", fn, (long long)M);
+    if (N <= 0) return fail(MQ_ERR_INVALID_ARG, "%s: N=%lld must be positive", fn, (long long)N);
+    if (int rc = check_K(K, fn)) return rc;
+    if (M > kMaxDim || N > kMaxDim)
+        return fail(MQ_ERR_SHAPE, "%s: M=%lld, N=%lld: each must be at most %lld", fn,
+                    (long long)M, (long long)N, (long long)kMaxDim);
+    if (((M + 127) / 128) * ((N + 127) / 128) > kMaxDim)
+        return fail(MQ_ERR_SHAPE, "%s: M=%lld x N=%lld needs too many tiles", fn, (long long)M, (long long)N);
+    if (!aligned(q, 16)) return fail(MQ_ERR_ALIGN, "%s: q=%p is not 16-byte aligned", fn, (const void *)q);
+    if (!aligned(d, 16)) return fail(MQ_ERR_ALIGN, "%s: d=%p is not 16-byte aligned", fn, (const void *)d);
+    if (!aligned(out, 4)) return fail(MQ_ERR_ALIGN, "%s: out=%p is not 4-byte aligned", fn, (const void *)out);
+    return MQ_OK;
+}
+
+// Shared checks of a plane builder reading N rows of K.
+int check_planes(const char *fn, const void *W, int64_t N, int64_t K)
+{
+    if (!W) return fail(MQ_ERR_INVALID_ARG, "%s: W is NULL", fn);
+    if (N <= 0) return fail(MQ_ERR_INVALID_ARG, "%s: N=%lld must be positive", fn, (long long)N);
+    if (int rc = check_K(K, fn)) return rc;
+    if (N > kMaxDim) return fail(MQ_ERR_SHAPE, "%s: N=%lld exceeds %lld", fn, (long long)N, (long long)kMaxDim);
+    if (N * (K / 256) > kMaxDim * 4)
+        return fail(MQ_ERR_SHAPE, "%s: N=%lld x K=%lld has too many blocks", fn, (long long)N, (long long)K);
+    if (!aligned(W, 16)) return fail(MQ_ERR_ALIGN, "%s: W=%p is not 16-byte aligned", fn, W);
+    return MQ_OK;
+}
+
 int ffn(const void *Wg, const void *Wu, const int8_t *q, const float *d, const float *s, int64_t M,
         int64_t N, int64_t K, int8_t *qo, float *do_, float *so, float *y, void *stream, int path)
 {
@@ -326,6 +360,80 @@ int mq_ffn_q4k_ex(const void *Wg, const void *Wu, const int8_t *q, const float *
 {
     g_err[0] = '\0';
     return ffn(Wg, Wu, q, d, s, M, N, K, qo, do_, so, y, stream, path);
+}
+
+int mq_expand_q6k(const void *W, int64_t N, int64_t K, int8_t *lo, int8_t *hi, float *dw, void *stream)
+{
+    g_err[0] = '\0';
+    const char *fn = "mq_expand_q6k";
+    if (int rc = check_planes(fn, W, N, K)) return rc;
+    if (!lo) return fail(MQ_ERR_INVALID_ARG, "%s: lo is NULL", fn);
+    if (!hi) return fail(MQ_ERR_INVALID_ARG, "%s: hi is NULL", fn);
+    if (!dw) return fail(MQ_ERR_INVALID_ARG, "%s: dw is NULL", fn);
+    if (!aligned(lo, 16)) return fail(MQ_ERR_ALIGN, "%s: lo=%p is not 16-byte aligned", fn, (void *)lo);
+    if (!aligned(hi, 16)) return fail(MQ_ERR_ALIGN, "%s: hi=%p is not 16-byte aligned", fn, (void *)hi);
+    if (!aligned(dw, 16)) return fail(MQ_ERR_ALIGN, "%s: dw=%p is not 16-byte aligned", fn, (void *)dw);
+    if (int rc = check_device()) return rc;
+    return launched(mq::launch_expand_q6k(static_cast<const uint8_t *>(W), N, K, lo, hi, dw,
+                                          static_cast<hipStream_t>(stream)), fn);
+}
+
+int mq_matmul_q6k_x(const int8_t *lo, const int8_t *hi, const float *dw, const int8_t *q, const float *d,
+                    int64_t M, int64_t N, int64_t K, float *out, void *stream)
+{
+    g_err[0] = '\0';
+    const char *fn = "mq_matmul_q6k_x";
+    if (!lo) return fail(MQ_ERR_INVALID_ARG, "%s: lo is NULL", fn);
+    if (!hi) return fail(MQ_ERR_INVALID_ARG, "%s: hi is NULL", fn);
+    if (!dw) return fail(MQ_ERR_INVALID_ARG, "%s: dw is NULL", fn);
+    if (int rc = check_gemm_shape(fn, q, d, out, M, N, K)) return rc;
+    if (!aligned(lo, 16)) return fail(MQ_ERR_ALIGN, "%s: lo=%p is not 16-byte aligned", fn, (const void *)lo);
+    if (!aligned(hi, 16)) return fail(MQ_ERR_ALIGN, "%s: hi=%p is not 16-byte aligned", fn, (const void *)hi);
+    if (!aligned(dw, 4)) return fail(MQ_ERR_ALIGN, "%s: dw=%p is not 4-byte aligned", fn, (const void *)dw);
+    if (int rc = check_device()) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int m = (int)M, n = (int)N, k = (int)K;
+    const hipError_t e = m <= mq::GEMM_SMALL_M_Q6K ? mq::launch_gemm_q6k_x_small(lo, hi, dw, q, d, m, n, k, out, st)
+                                                   : mq::launch_gemm_q6k_x(lo, hi, dw, q, d, m, n, k, out, st);
+    return launched(e, fn);
+}
+
+int mq_dsc_q4k(const void *W, int64_t N, int64_t K, float *fw, float *fm, void *stream)
+{
+    g_err[0] = '\0';
+    const char *fn = "mq_dsc_q4k";
+    if (int rc = check_planes(fn, W, N, K)) return rc;
+    if (!fw) return fail(MQ_ERR_INVALID_ARG, "%s: fw is NULL", fn);
+    if (!fm) return fail(MQ_ERR_INVALID_ARG, "%s: fm is NULL", fn);
+    if (!aligned(fw, 16)) return fail(MQ_ERR_ALIGN, "%s: fw=%p is not 16-byte aligned", fn, (void *)fw);
+    if (!aligned(fm, 16)) return fail(MQ_ERR_ALIGN, "%s: fm=%p is not 16-byte aligned", fn, (void *)fm);
+    if (int rc = check_device()) return rc;
+    return launched(mq::launch_dsc_q4k(static_cast<const uint8_t *>(W), N, K, fw, fm,
+                                       static_cast<hipStream_t>(stream)), fn);
+}
+
+int mq_matmul_q4k_dsc(const void *W, const float *fw, const float *fm, const int8_t *q, const float *d,
+                      const float *s, int64_t M, int64_t N, int64_t K, float *out, void *stream)
+{
+    g_err[0] = '\0';
+    const char *fn = "mq_matmul_q4k_dsc";
+    if (!W) return fail(MQ_ERR_INVALID_ARG, "%s: W is NULL", fn);
+    if (!fw) return fail(MQ_ERR_INVALID_ARG, "%s: fw is NULL", fn);
+    if (!fm) return fail(MQ_ERR_INVALID_ARG, "%s: fm is NULL", fn);
+    if (!s) return fail(MQ_ERR_INVALID_ARG, "%s: s is NULL (the min term needs it)", fn);
+    if (int rc = check_gemm_shape(fn, q, d, out, M, N, K)) return rc;
+    if (!aligned(W, 16)) return fail(MQ_ERR_ALIGN, "%s: W=%p is not 16-byte aligned", fn, W);
+    if (!aligned(fw, 16)) return fail(MQ_ERR_ALIGN, "%s: fw=%p is not 16-byte aligned", fn, (const void *)fw);
+    if (!aligned(fm, 16)) return fail(MQ_ERR_ALIGN, "%s: fm=%p is not 16-byte aligned", fn, (const void *)fm);
+    if (!aligned(s, 16)) return fail(MQ_ERR_ALIGN, "%s: s=%p is not 16-byte aligned", fn, (const void *)s);
+    if (int rc = check_device()) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const auto *Wb = static_cast<const uint8_t *>(W);
+    const int m = (int)M, n = (int)N, k = (int)K;
+    const hipError_t e = m <= mq::GEMM_SMALL_M_Q4K
+                             ? mq::launch_gemm_q4k_dsc_small(Wb, fw, fm, q, d, s, m, n, k, out, st)
+                             : mq::launch_gemm_q4k_dsc(Wb, fw, fm, q, d, s, m, n, k, out, st);
+    return launched(e, fn);
 }
 
 int64_t mq_gemv_max_m(void) { return mq::GEMV_MAX_M; }

@@ -74,6 +74,22 @@ hipError_t launch_gemv_q4k_ffn(const uint8_t *Wg, const uint8_t *Wu, const int8_
 hipError_t launch_gemm_q6k(const uint8_t *W, const int8_t *q, const float *d,
                            int M, int N, int K, float *out, hipStream_t st);
 
+// Registration-time planes (Q6_K expansion, Q4_K decoded scales) and the
+// GEMMs that read them.
+hipError_t launch_expand_q6k(const uint8_t *W, int64_t N, int64_t K, int8_t *lo, int8_t *hi, float *dw,
+                             hipStream_t st);
+hipError_t launch_dsc_q4k(const uint8_t *W, int64_t N, int64_t K, float *fw, float *fm, hipStream_t st);
+hipError_t launch_gemm_q6k_x(const int8_t *lo, const int8_t *hi, const float *dw, const int8_t *q,
+                             const float *d, int M, int N, int K, float *out, hipStream_t st);
+hipError_t launch_gemm_q6k_x_small(const int8_t *lo, const int8_t *hi, const float *dw, const int8_t *q,
+                                   const float *d, int M, int N, int K, float *out, hipStream_t st);
+hipError_t launch_gemm_q4k_dsc(const uint8_t *W, const float *fw, const float *fm, const int8_t *q,
+                               const float *d, const float *s, int M, int N, int K, float *out,
+                               hipStream_t st);
+hipError_t launch_gemm_q4k_dsc_small(const uint8_t *W, const float *fw, const float *fm, const int8_t *q,
+                                     const float *d, const float *s, int M, int N, int K, float *out,
+                                     hipStream_t st);
+
 // Compute units of the current device (cached per device).
 int device_cu_count();
 

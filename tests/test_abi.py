@@ -228,3 +228,31 @@ def test_error_is_cleared_by_next_call(L):
     assert L.mq_last_error().decode() != ""
     assert _q6k(L, N=0) == INVALID
     assert "N=0" in L.mq_last_error().decode()
+
+
+# ---------------------------------------------------------------- registration-time planes
+
+@pytest.mark.parametrize("call,status,needle", [
+    (lambda L: L.mq_expand_q6k(None, 8, 256, P, P, P, None), INVALID, "W is NULL"),
+    (lambda L: L.mq_expand_q6k(P, 0, 256, P, P, P, None), INVALID, "N=0"),
+    (lambda L: L.mq_expand_q6k(P, 8, 300, P, P, P, None), SHAPE, "K=300"),
+    (lambda L: L.mq_expand_q6k(P, 8, 256, None, P, P, None), INVALID, "lo is NULL"),
+    (lambda L: L.mq_expand_q6k(P, 8, 256, P, P + 4, P, None), ALIGN, "hi="),
+    (lambda L: L.mq_expand_q6k(P, 8, 256, P, P, P + 8, None), ALIGN, "dw="),
+    (lambda L: L.mq_matmul_q6k_x(P, P, None, P, P, 4, 8, 256, P, None), INVALID, "dw is NULL"),
+    (lambda L: L.mq_matmul_q6k_x(P, P, P, P, P, 0, 8, 256, P, None), INVALID, "M=0"),
+    (lambda L: L.mq_matmul_q6k_x(P, P, P, P, P, 4, 8, 512 + 64, P, None), SHAPE, "K=576"),
+    (lambda L: L.mq_matmul_q6k_x(P + 8, P, P, P, P, 4, 8, 256, P, None), ALIGN, "lo="),
+    (lambda L: L.mq_matmul_q6k_x(P, P, P, P + 4, P, 4, 8, 256, P, None), ALIGN, "q="),
+    (lambda L: L.mq_dsc_q4k(P, 8, 256, None, P, None), INVALID, "fw is NULL"),
+    (lambda L: L.mq_dsc_q4k(P + 4, 8, 256, P, P, None), ALIGN, "W="),
+    (lambda L: L.mq_dsc_q4k(P, 8, 256, P, P + 4, None), ALIGN, "fm="),
+    (lambda L: L.mq_matmul_q4k_dsc(P, P, P, P, P, None, 4, 8, 256, P, None), INVALID, "s is NULL"),
+    (lambda L: L.mq_matmul_q4k_dsc(P, None, P, P, P, P, 4, 8, 256, P, None), INVALID, "fw is NULL"),
+    (lambda L: L.mq_matmul_q4k_dsc(P, P, P, P, P, P, 4, -2, 256, P, None), INVALID, "N=-2"),
+    (lambda L: L.mq_matmul_q4k_dsc(P, P, P + 8, P, P, P, 4, 8, 256, P, None), ALIGN, "fm="),
+    (lambda L: L.mq_matmul_q4k_dsc(P, P, P, P, P, P, 4, 8, 256, P + 2, None), ALIGN, "out="),
+])
+def test_plane_entry_validation(L, call, status, needle):
+    assert call(L) == status
+    assert needle in L.mq_last_error().decode()

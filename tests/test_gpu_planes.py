@@ -1,0 +1,123 @@
+"""GPU parity of the registration-time planes and the GEMMs that read them,
+through the C ABI.
+
+  * mq_expand_q6k and mq_dsc_q4k write exactly the oracle's planes (integer
+    limbs and exact f32 products: compared bit for bit);
+  * mq_matmul_q6k_x and mq_matmul_q4k_dsc meet the matmul bar against the
+    raw-block oracle (max|d| <= 1e-4 max|oracle|), for small shapes, split-K
+    shapes and the full-size workloads (sampled token rows), and agree
+    bitwise with the raw-block GEMM where the arithmetic is the same.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import quant_gemm_amd as mq
+from quant_gemm_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-4
+
+
+def to_dev(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+
+def host(t):
+    import torch
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def check_close(got, ref, what):
+    ref = np.asarray(ref, dtype=np.float64)
+    got = np.asarray(got, dtype=np.float64)
+    assert got.shape == ref.shape and np.all(np.isfinite(got)), what
+    err = np.abs(got - ref).max()
+    assert err <= TOL * np.abs(ref).max(), f"{what}: max|d|={err:.3e}"
+    return err / np.abs(ref).max()
+
+
+@pytest.mark.parametrize("N,K", [(1, 256), (37, 768), (3584, 18944)])
+def test_expand_q6k_bit_exact(dev, N, K):
+    rng = np.random.default_rng(N + K)
+    W = synth.q6k_weights(rng, N, K)
+    print(f"[planes] expand_q6k N={N} K={K}", flush=True)
+    lo, hi, dw = mq.expand_q6k(to_dev(W.reshape(-1)), N, K)
+    rlo, rhi, rdw = oracle.expand_q6k(W, N, K)
+    assert np.array_equal(host(lo), rlo) and np.array_equal(host(hi), rhi) and np.array_equal(host(dw), rdw)
+
+
+@pytest.mark.parametrize("N,K", [(1, 256), (45, 1280), (18944, 3584)])
+def test_dsc_q4k_bit_exact(dev, N, K):
+    rng = np.random.default_rng(N * 7 + K)
+    W = synth.q4k_weights(rng, N, K)
+    print(f"[planes] dsc_q4k N={N} K={K}", flush=True)
+    fw, fm = mq.dsc_q4k(to_dev(W.reshape(-1)), N, K)
+    rfw, rfm = oracle.dsc_q4k(W, N, K)
+    assert np.array_equal(host(fw), rfw) and np.array_equal(host(fm), rfm)
+
+
+SHAPES = [(1, 1, 256), (5, 129, 768), (31, 100, 512), (33, 64, 1024), (129, 300, 1280), (200, 64, 2048),
+          (300, 700, 4608), (17, 257, 2560)]
+
+
+def _plane(x):
+    return mq.quantize_act(to_dev(x))
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_matmul_q6k_x(dev, M, N, K):
+    rng = np.random.default_rng(M * 31 + N * 7 + K)
+    W = synth.q6k_weights(rng, N, K)
+    x = synth.activations(rng, M, K, outliers=True)
+    q, d, s = _plane(x)
+    Wd = to_dev(W.reshape(-1))
+    lo, hi, dw = mq.expand_q6k(Wd, N, K)
+    got = host(mq.matmul_q6k_x(lo, hi, dw, q, d, N, K))
+    rq, rd, _ = oracle.quantize_act(x)
+    check_close(got, oracle.matmul_q6k(W, rq, rd, N, K), f"q6k_x M={M} N={N} K={K}")
+    raw = host(mq.matmul_q6k(Wd, q, d, None, N, K, path=mq.MQ_PATH_GEMM))
+    assert np.array_equal(got, raw), "same limbs, same order: the raw-block GEMM's result bit for bit"
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_matmul_q4k_dsc(dev, M, N, K):
+    rng = np.random.default_rng(M * 37 + N * 5 + K)
+    W = synth.q4k_weights(rng, N, K)
+    x = synth.activations(rng, M, K, outliers=True)
+    q, d, s = _plane(x)
+    Wd = to_dev(W.reshape(-1))
+    fw, fm = mq.dsc_q4k(Wd, N, K)
+    got = host(mq.matmul_q4k_dsc(Wd, fw, fm, q, d, s, N, K))
+    rq, rd, _ = oracle.quantize_act(x)
+    check_close(got, oracle.matmul_q4k(W, rq, rd, N, K), f"q4k_dsc M={M} N={N} K={K}")
+    raw = host(mq.matmul_q4k(Wd, q, d, s, N, K, path=mq.MQ_PATH_GEMM))
+    assert np.array_equal(got, raw), "same factors, same order: the raw-block GEMM's result bit for bit"
+
+
+_SAMPLE = [0, 1, 63, 64, 127, 128, 129, 511, 1000, 2047, 2048, 3199, 3200, 3250, 3312, 3313]
+
+
+@pytest.mark.parametrize("name", ["layer_down", "q6k_ffn_down_m512", "q4k_prefill_ffn_up", "layer_qkv"])
+def test_full_size_planes(dev, name):
+    case = synth.case_by_name(name)
+    print(f"[planes] {name} {case.fmt} M={case.M} N={case.N} K={case.K}", flush=True)
+    W = case.make_weights()
+    x = case.make_activations()
+    q, d, s = _plane(x)
+    Wd = to_dev(W.reshape(-1))
+    if case.fmt == "q6k":
+        lo, hi, dw = mq.expand_q6k(Wd, case.N, case.K)
+        out = host(mq.matmul_q6k_x(lo, hi, dw, q, d, case.N, case.K))
+        mm = oracle.matmul_q6k
+    else:
+        fw, fm = mq.dsc_q4k(Wd, case.N, case.K)
+        out = host(mq.matmul_q4k_dsc(Wd, fw, fm, q, d, s, case.N, case.K))
+        mm = oracle.matmul_q4k
+    toks = np.array(sorted({t for t in _SAMPLE if t < case.M} | {case.M - 1}))
+    rq, rd, _ = oracle.quantize_act(x)
+    rel = check_close(out[toks], mm(W, rq, rd, case.N, case.K, tokens=toks), name)
+    print(f"[planes] {name}: max|d|/max|ref| = {rel:.2e}", flush=True)
