@@ -248,18 +248,11 @@ def run_all(args):
         q, d, s = mq.quantize_act(x)
         mm = {"q4k": mq.matmul_q4k, "q5k": mq.matmul_q5k, "q6k": mq.matmul_q6k}[case.fmt]
         out = torch.empty((case.M, case.N), dtype=torch.float32, device=dev)
-        for i in range(3):
-            mm(Ws[i % copies], q, d, s, case.N, case.K, out=out)
-        torch.cuda.synchronize()
         reps = max(copies, 20 if not hbm else 2 * copies)
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for i in range(reps):
-            mm(Ws[i % copies], q, d, s, case.N, case.K, out=out)
-        e1.record()
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / reps
+        # warm-up of about the timed work, then the median of 3 rounds
+        _time_rotating(lambda i: mm(Ws[i], q, d, s, case.N, case.K, out=out), copies, reps)
+        us = float(np.median([_time_rotating(lambda i: mm(Ws[i], q, d, s, case.N, case.K, out=out), copies, reps)
+                              for _ in range(3)]))
         row = {"group": grp, "case": case.name, "fmt": case.fmt, "M": case.M, "N": case.N,
                "K": case.K, "us": round(us, 2), "TOPS": round(case.ops / (us * 1e-6) / 1e12, 2)}
         if hbm:
