@@ -26,7 +26,8 @@
  *   - After the checks the current device must be gfx950 (queried at run
  *     time, minfer Architecture, §5.3 GPU safety), else MQ_ERR_UNSUPPORTED.
  *   - Sizes are element counts. K must be a positive multiple of 256 (one
- *     super-block); M and N may be any positive value up to 2^31-1.
+ *     super-block) up to 2^31-1; M and N may be any positive value up to
+ *     0x7fff0000 (2^31 - 65536).
  *   - There is no device-side validation of data. Non-finite activations are
  *     a precondition violation with unspecified output.
  *   - Calls are thread-safe. Calls that overlap in time on the same output

@@ -103,8 +103,11 @@ struct alignas(16) Stage {
     uint8_t qh[Q5 ? H_CHUNKS * 16 : 16];
     float dx[BK / 32][BM];
     float fw[BK / 32][BN];
-    uint4 sxl[BM][2];       // bf16 limbs of s_x for the step's 4 sub-blocks (see Limbs)
-    uint4 fml[BN][2];       // bf16 limbs of -(dmin*m_j)
+    // bf16 limbs of s_x for the step's 4 sub-blocks (see limbs4), part p of
+    // token t at sxl[p][t]: 16-byte strides, so a wavefront's reads of one
+    // part hit consecutive banks
+    uint4 sxl[2][BM];
+    uint4 fml[2][BN];       // bf16 limbs of -(dmin*m_j), the same way
 };
 
 // The min term  -sum_j s_x[t,j] * (dmin*m_j)[n]  is a contraction over the
@@ -114,7 +117,7 @@ struct alignas(16) Stage {
 // the eight limb products other than x3*y3 are summed with f32 accumulation:
 // the same accuracy as one f32 multiply-add per sub-block. A record holds,
 // for one token or row, the limbs of the step's 4 sub-blocks as bf16 pairs:
-// uint4 [0] = {x1 j0j1, x1 j2j3, x2 j0j1, x2 j2j3}, [1] = {x3 j0j1, x3 j2j3, 0, 0}.
+// part 0 = {x1 j0j1, x1 j2j3, x2 j0j1, x2 j2j3}, part 1 = {x3 j0j1, x3 j2j3, 0, 0}.
 __device__ __forceinline__ uint32_t bf16_bits(float x)
 {
     return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x);
@@ -254,7 +257,7 @@ __device__ __forceinline__ void store_side(Stage &s, const Side &p, const WRows 
     } else if (tid < 2 * BM) {
         const float x[4] = {tok ? p.ds.x : 0.0f, tok ? p.ds.y : 0.0f, tok ? p.ds.z : 0.0f,
                             tok ? p.ds.w : 0.0f};
-        limbs4(x, s.sxl[row][0], s.sxl[row][1]);
+        limbs4(x, s.sxl[0][row], s.sxl[1][row]);
     }
     if (DSC && tid < BN) {
         const bool ok = rows.valid<FFN>(tid);
@@ -264,7 +267,7 @@ __device__ __forceinline__ void store_side(Stage &s, const Side &p, const WRows 
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             s.fw[j][tid] = ok ? fw[j] : 0.0f;
-        limbs4(fm, s.fml[tid][0], s.fml[tid][1]);
+        limbs4(fm, s.fml[0][tid], s.fml[1][tid]);
     } else if (tid < BN) {
         // header: f16 d | f16 dmin | 12 bytes of 6-bit codes. Codes j = 0..3
         // are bytes 0..3 (scale) and 4..7 (min) masked to 6 bits; codes
@@ -283,7 +286,7 @@ __device__ __forceinline__ void store_side(Stage &s, const Side &p, const WRows 
             s.fw[j][tid] = dd * (float)((scw >> (8 * j)) & 0xffu);
             fm[j] = -(dm * (float)((mw >> (8 * j)) & 0xffu));
         }
-        limbs4(fm, s.fml[tid][0], s.fml[tid][1]);
+        limbs4(fm, s.fml[0][tid], s.fml[1][tid]);
     }
 }
 
@@ -301,14 +304,14 @@ __device__ __forceinline__ void compute_step(const Stage &s, v16f (&acc)[TM][TN]
 #pragma unroll
         for (int a = 0; a < TM; ++a) {
             const int t = (wm * TM + a) * 32 + lr;
-            const uint4 r0 = s.sxl[t][0], r1 = s.sxl[t][1];
+            const uint4 r0 = s.sxl[0][t], r1 = s.sxl[1][t];
             A0[a] = v4i{(int)(lh ? r0.z : r0.x), (int)(lh ? r0.w : r0.y), (int)r0.x, (int)r0.y};
             A1[a] = v4i{(int)r0.z, (int)r0.w, (int)r1.x, (int)r1.y};
         }
 #pragma unroll
         for (int b = 0; b < TN; ++b) {
             const int n = (wn * TN + b) * 32 + lr;
-            const uint4 q0 = s.fml[n][0], q1 = s.fml[n][1];
+            const uint4 q0 = s.fml[0][n], q1 = s.fml[1][n];
             const uint32_t y2a = lh ? q1.x : q0.z, y2b = lh ? q1.y : q0.w;   // y2 | y3
             const v4i B0 = {(int)q0.x, (int)q0.y, (int)y2a, (int)y2b};
             const v4i B1 = {(int)y2a, (int)y2b, (int)(lh ? q0.z : q0.x), (int)(lh ? q0.w : q0.y)};

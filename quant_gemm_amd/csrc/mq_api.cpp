@@ -30,6 +30,8 @@ int fail(int status, const char *fmt, ...)
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 constexpr int64_t kMaxDim = 0x7fffffff;
+// M and N: the launchers round them up to whole tiles in 32-bit arithmetic
+constexpr int64_t kMaxRows = 0x7fff0000;
 
 // Per-device result of the architecture query: 0 unknown, 1 gfx950, 2 other.
 constexpr int kMaxDevices = 64;
@@ -92,9 +94,9 @@ int matmul(Fmt fmt, const void *W, const int8_t *q, const float *d, const float 
     if (M <= 0) return fail(MQ_ERR_INVALID_ARG, "%s: M=%lld must be positive", fn, (long long)M);
     if (N <= 0) return fail(MQ_ERR_INVALID_ARG, "%s: N=%lld must be positive", fn, (long long)N);
     if (int rc = check_K(K, fn)) return rc;
-    if (M > kMaxDim || N > kMaxDim)
+    if (M > kMaxRows || N > kMaxRows)
         return fail(MQ_ERR_SHAPE, "%s: M=%lld, N=%lld: each must be at most %lld", fn,
-                    (long long)M, (long long)N, (long long)kMaxDim);
+                    (long long)M, (long long)N, (long long)kMaxRows);
     if (path != MQ_PATH_AUTO && path != MQ_PATH_GEMV && path != MQ_PATH_GEMM)
         return fail(MQ_ERR_INVALID_ARG, "%s: path=%d is not MQ_PATH_AUTO/GEMV/GEMM", fn, path);
     if (path == MQ_PATH_GEMV && M > mq::GEMV_MAX_M)
@@ -149,9 +151,9 @@ int check_gemm_shape(const char *fn, const int8_t *q, const float *d, float *out
     if (M <= 0) return fail(MQ_ERR_INVALID_ARG, "%s: M=%lld must be positive", fn, (long long)M);
     if (N <= 0) return fail(MQ_ERR_INVALID_ARG, "%s: N=%lld must be positive", fn, (long long)N);
     if (int rc = check_K(K, fn)) return rc;
-    if (M > kMaxDim || N > kMaxDim)
+    if (M > kMaxRows || N > kMaxRows)
         return fail(MQ_ERR_SHAPE, "%s: M=%lld, N=%lld: each must be at most %lld", fn,
-                    (long long)M, (long long)N, (long long)kMaxDim);
+                    (long long)M, (long long)N, (long long)kMaxRows);
     if (((M + 127) / 128) * ((N + 127) / 128) > kMaxDim)
         return fail(MQ_ERR_SHAPE, "%s: M=%lld x N=%lld needs too many tiles", fn, (long long)M, (long long)N);
     if (!aligned(q, 16)) return fail(MQ_ERR_ALIGN, "%s: q=%p is not 16-byte aligned", fn, (const void *)q);
@@ -166,7 +168,7 @@ int check_planes(const char *fn, const void *W, int64_t N, int64_t K)
     if (!W) return fail(MQ_ERR_INVALID_ARG, "%s: W is NULL", fn);
     if (N <= 0) return fail(MQ_ERR_INVALID_ARG, "%s: N=%lld must be positive", fn, (long long)N);
     if (int rc = check_K(K, fn)) return rc;
-    if (N > kMaxDim) return fail(MQ_ERR_SHAPE, "%s: N=%lld exceeds %lld", fn, (long long)N, (long long)kMaxDim);
+    if (N > kMaxRows) return fail(MQ_ERR_SHAPE, "%s: N=%lld exceeds %lld", fn, (long long)N, (long long)kMaxRows);
     if (N * (K / 256) > kMaxDim * 4)
         return fail(MQ_ERR_SHAPE, "%s: N=%lld x K=%lld has too many blocks", fn, (long long)N, (long long)K);
     if (!aligned(W, 16)) return fail(MQ_ERR_ALIGN, "%s: W=%p is not 16-byte aligned", fn, W);
@@ -189,9 +191,9 @@ int ffn(const void *Wg, const void *Wu, const int8_t *q, const float *d, const f
     if (N <= 0 || N % 256 != 0)
         return fail(MQ_ERR_SHAPE, "%s: N=%lld must be a positive multiple of 256", fn, (long long)N);
     if (int rc = check_K(K, fn)) return rc;
-    if (M > kMaxDim || N > kMaxDim)
+    if (M > kMaxRows || N > kMaxRows)
         return fail(MQ_ERR_SHAPE, "%s: M=%lld, N=%lld: each must be at most %lld", fn, (long long)M,
-                    (long long)N, (long long)kMaxDim);
+                    (long long)N, (long long)kMaxRows);
     if (path != MQ_PATH_AUTO && path != MQ_PATH_GEMV && path != MQ_PATH_GEMM)
         return fail(MQ_ERR_INVALID_ARG, "%s: path=%d is not MQ_PATH_AUTO/GEMV/GEMM", fn, path);
     if (path == MQ_PATH_GEMV && M > mq::FFN_GEMV_MAX_M)
@@ -235,7 +237,7 @@ int mq_quantize_act(const float *x, int64_t M, int64_t K, int64_t ldx, int8_t *q
     if (M <= 0) return fail(MQ_ERR_INVALID_ARG, "%s: M=%lld must be positive", fn, (long long)M);
     if (int rc = check_K(K, fn)) return rc;
     if (ldx < K) return fail(MQ_ERR_SHAPE, "%s: ldx=%lld is smaller than K=%lld", fn, (long long)ldx, (long long)K);
-    if (M > kMaxDim) return fail(MQ_ERR_SHAPE, "%s: M=%lld exceeds %lld", fn, (long long)M, (long long)kMaxDim);
+    if (M > kMaxRows) return fail(MQ_ERR_SHAPE, "%s: M=%lld exceeds %lld", fn, (long long)M, (long long)kMaxRows);
     // the scalar path uses 32 threads per block: the grid must fit in 2^31-1 workgroups
     if (M > (kMaxDim * 256 / 32) / (K / 32))
         return fail(MQ_ERR_SHAPE, "%s: M=%lld x K=%lld is too large for one launch", fn, (long long)M, (long long)K);
@@ -263,7 +265,7 @@ int mq_rmsnorm_quantize(const float *x, const float *w, int64_t M, int64_t K, in
     if (int rc = check_K(K, fn)) return rc;
     if (ldx < K) return fail(MQ_ERR_SHAPE, "%s: ldx=%lld is smaller than K=%lld", fn, (long long)ldx, (long long)K);
     if (ldx % 4 != 0) return fail(MQ_ERR_ALIGN, "%s: ldx=%lld is not a multiple of 4", fn, (long long)ldx);
-    if (M > kMaxDim) return fail(MQ_ERR_SHAPE, "%s: M=%lld exceeds %lld", fn, (long long)M, (long long)kMaxDim);
+    if (M > kMaxRows) return fail(MQ_ERR_SHAPE, "%s: M=%lld exceeds %lld", fn, (long long)M, (long long)kMaxRows);
     if (!aligned(x, 16)) return fail(MQ_ERR_ALIGN, "%s: x=%p is not 16-byte aligned", fn, (const void *)x);
     if (!aligned(w, 16)) return fail(MQ_ERR_ALIGN, "%s: w=%p is not 16-byte aligned", fn, (const void *)w);
     if (!aligned(q, 16)) return fail(MQ_ERR_ALIGN, "%s: q=%p is not 16-byte aligned", fn, (const void *)q);
@@ -291,7 +293,7 @@ int mq_swiglu_quantize(const float *g, const float *u, int64_t M, int64_t K, int
     if (ldu < K) return fail(MQ_ERR_SHAPE, "%s: ldu=%lld is smaller than K=%lld", fn, (long long)ldu, (long long)K);
     if (ldg % 4 != 0) return fail(MQ_ERR_ALIGN, "%s: ldg=%lld is not a multiple of 4", fn, (long long)ldg);
     if (ldu % 4 != 0) return fail(MQ_ERR_ALIGN, "%s: ldu=%lld is not a multiple of 4", fn, (long long)ldu);
-    if (M > kMaxDim) return fail(MQ_ERR_SHAPE, "%s: M=%lld exceeds %lld", fn, (long long)M, (long long)kMaxDim);
+    if (M > kMaxRows) return fail(MQ_ERR_SHAPE, "%s: M=%lld exceeds %lld", fn, (long long)M, (long long)kMaxRows);
     // 8 threads per 32-value block: the grid must fit in 2^31-1 workgroups
     if (M > (kMaxDim * 256 / 8) / (K / 32))
         return fail(MQ_ERR_SHAPE, "%s: M=%lld x K=%lld is too large for one launch", fn, (long long)M, (long long)K);

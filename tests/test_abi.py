@@ -78,6 +78,7 @@ def _quant(L, x=P, M=4, K=256, ldx=256, q=P, d=P, s=P):
     (dict(K=100), SHAPE, "K=100"),
     (dict(K=384), SHAPE, "K=384"),
     (dict(M=2 ** 31), SHAPE, "M=2147483648"),
+    (dict(N=0x7fff0001), SHAPE, "N=2147418113"),
     (dict(path=3), INVALID, "path=3"),
     (dict(path=1, M=17), INVALID, "M=17"),
     (dict(W=P + 4), ALIGN, "W="),
