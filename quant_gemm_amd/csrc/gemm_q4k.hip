@@ -359,11 +359,15 @@ __device__ __forceinline__ void compute_step(const Stage &s, v16f (&acc)[TM][TN]
                 af[a] = *reinterpret_cast<const v4i *>(s.a + 16 * a_slot(r, 2 * j + lh));
             }
             v16i I[TM][TN];
+            // raised wave priority while the MFMAs issue, so that they are
+            // not queued behind the other wavefront's epilogue (measured +1.5%)
+            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int a = 0; a < TM; ++a)
 #pragma unroll
                 for (int b = 0; b < TN; ++b)
                     I[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[a], bf[b], v16i{}, 0, 0, 0);
+            __builtin_amdgcn_s_setprio(0);
             float fw[TN];
 #pragma unroll
             for (int b = 0; b < TN; ++b)

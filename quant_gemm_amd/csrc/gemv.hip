@@ -25,7 +25,11 @@
 namespace mq {
 namespace {
 
-constexpr int GEMV_WAVES = 4;   // wavefronts per workgroup
+constexpr int GEMV_WAVES = 4;          // wavefronts per workgroup
+// The persistent Q4_K stream runs 8 wavefronts per workgroup (32 per CU in
+// its 1024-workgroup grid): measured 5% faster than 4 at N = 18944, equal
+// on the smaller matrices.
+constexpr int STREAM_WAVES = 8;
 #ifndef GEMV_STREAM_WGS
 #define GEMV_STREAM_WGS 1024        // workgroups of the persistent stream kernel
 #endif
@@ -53,18 +57,22 @@ constexpr int GEMV_ACT_LDS = 16 * 1024;
 
 // Copy the activation plane (q, then d, then s: M*K + 2*M*K/8 bytes, a
 // multiple of 16) into LDS. Loads are issued here; the stores wait for them.
+// WAVES: wavefronts of the workgroup that copies.
+template <int WAVES = GEMV_WAVES>
 struct ActCopy {
-    static constexpr int MAXC = GEMV_ACT_LDS / 16 / (64 * GEMV_WAVES);  // chunks per thread
+    static constexpr int NT = 64 * WAVES;
+    static constexpr int MAXC = GEMV_ACT_LDS / 16 / NT;  // chunks per thread
     v4i v[MAXC];
 };
 
-__device__ __forceinline__ void act_load(ActCopy &c, const int8_t *q, const float *d,
+template <int WAVES>
+__device__ __forceinline__ void act_load(ActCopy<WAVES> &c, const int8_t *q, const float *d,
                                          const float *s, int M, int K)
 {
     const int qchunks = M * K / 16, dchunks = M * K / 128;
 #pragma unroll
-    for (int i = 0; i < ActCopy::MAXC; ++i) {
-        const int ch = threadIdx.x + i * 64 * GEMV_WAVES;
+    for (int i = 0; i < ActCopy<WAVES>::MAXC; ++i) {
+        const int ch = threadIdx.x + i * ActCopy<WAVES>::NT;
         const v4i *src;
         if (ch < qchunks)
             src = reinterpret_cast<const v4i *>(q) + ch;
@@ -76,12 +84,13 @@ __device__ __forceinline__ void act_load(ActCopy &c, const int8_t *q, const floa
     }
 }
 
-__device__ __forceinline__ void act_store(const ActCopy &c, v4i *lds, int M, int K)
+template <int WAVES>
+__device__ __forceinline__ void act_store(const ActCopy<WAVES> &c, v4i *lds, int M, int K)
 {
     const int nchunks = M * K / 16 + 2 * (M * K / 128);
 #pragma unroll
-    for (int i = 0; i < ActCopy::MAXC; ++i) {
-        const int ch = threadIdx.x + i * 64 * GEMV_WAVES;
+    for (int i = 0; i < ActCopy<WAVES>::MAXC; ++i) {
+        const int ch = threadIdx.x + i * ActCopy<WAVES>::NT;
         if (ch < nchunks)
             lds[ch] = c.v[i];
     }
@@ -187,7 +196,7 @@ __global__ __launch_bounds__(64 * GEMV_WAVES) void gemv_q4k_kernel(
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int row0 = (blockIdx.x * GEMV_WAVES + wave) * R;
-    ActCopy ac;
+    ActCopy<> ac;
     if constexpr (ACT_LDS)
         act_load(ac, q, dx, sx, M, K);
     const int nb = K >> 8;
@@ -230,7 +239,7 @@ __global__ __launch_bounds__(64 * GEMV_WAVES) void gemv_q4k_kernel(
 // up rows), the 32 x M results meet in LDS, and each 32-lane half of the
 // first wavefront turns one token's 32 values into y = SiLU(g) * u and one
 // quantized block of the down projection's plane.
-constexpr int FFN_ROWS = 8;                       // rows of each matrix per wavefront
+constexpr int FFN_ROWS = 32 / GEMV_WAVES;         // rows of each matrix per wavefront
 
 template <int MT, bool ACT_LDS>
 __global__ __launch_bounds__(64 * GEMV_WAVES) void gemv_q4k_ffn_kernel(
@@ -245,7 +254,7 @@ __global__ __launch_bounds__(64 * GEMV_WAVES) void gemv_q4k_ffn_kernel(
     const int wave = threadIdx.x >> 6;
     const int n0 = blockIdx.x * 32;
     const int nb = K >> 8;
-    ActCopy ac;
+    ActCopy<> ac;
     if constexpr (ACT_LDS)
         act_load(ac, q, dx, sx, M, K);
     const int8_t *qa = q;
@@ -325,7 +334,7 @@ __global__ __launch_bounds__(64 * GEMV_WAVES) void gemv_q4k_ffn_kernel(
 // (measured on MI355X: one row ahead, without clamped tail loads, is the
 // fastest depth, most of all for short matrices).
 template <int MT, int NP, int D>
-__global__ __launch_bounds__(64 * GEMV_WAVES) void gemv_q4k_stream_kernel(
+__global__ __launch_bounds__(64 * STREAM_WAVES) void gemv_q4k_stream_kernel(
     const uint8_t *__restrict__ W, const int8_t *__restrict__ q,
     const float *__restrict__ dx, const float *__restrict__ sx, int M, int N,
     int K, float *__restrict__ out)
@@ -333,9 +342,9 @@ __global__ __launch_bounds__(64 * GEMV_WAVES) void gemv_q4k_stream_kernel(
     __shared__ v4i act[GEMV_ACT_LDS / 16];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int nw = gridDim.x * GEMV_WAVES;
-    const int w = blockIdx.x * GEMV_WAVES + wave;
-    ActCopy ac;
+    const int nw = gridDim.x * STREAM_WAVES;
+    const int w = blockIdx.x * STREAM_WAVES + wave;
+    ActCopy<STREAM_WAVES> ac;
     act_load(ac, q, dx, sx, M, K);
 
     const int nb = K >> 8;
@@ -561,7 +570,7 @@ __global__ __launch_bounds__(64 * GEMV_WAVES) void gemv_q5k_kernel(
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int row0 = (blockIdx.x * GEMV_WAVES + wave) * R;
-    ActCopy ac;
+    ActCopy<> ac;
     if constexpr (ACT_LDS)
         act_load(ac, q, dx, sx, M, K);
     const int nb = K >> 8;
@@ -615,7 +624,7 @@ __global__ __launch_bounds__(64 * GEMV_WAVES) void gemv_q5k_stream_kernel(
     const int wave = threadIdx.x >> 6;
     const int nw = gridDim.x * GEMV_WAVES;
     const int w = blockIdx.x * GEMV_WAVES + wave;
-    ActCopy ac;
+    ActCopy<> ac;
     act_load(ac, q, dx, sx, M, K);
 
     const int nb = K >> 8;
@@ -1039,12 +1048,11 @@ __global__ __launch_bounds__(64 * Q6S_WAVES) void gemv_q6k_stream_kernel(
     wait_vm<0>();
 }
 
-template <int MT>
-hipError_t gemv_q4k_mt(const uint8_t *W, const int8_t *q, const float *d,
-                       const float *s, int M, int N, int K, float *out,
-                       hipStream_t st)
+template <int MT, int R>
+hipError_t gemv_q4k_launch(const uint8_t *W, const int8_t *q, const float *d,
+                           const float *s, int M, int N, int K, float *out,
+                           hipStream_t st)
 {
-    constexpr int R = MT <= 2 ? 4 : 2;           // rows per wavefront
     constexpr int IT = 8;                        // passes (of 7 blocks) in flight
     const int rows_per_wg = GEMV_WAVES * R;
     const int grid = (N + rows_per_wg - 1) / rows_per_wg;
@@ -1056,15 +1064,27 @@ hipError_t gemv_q4k_mt(const uint8_t *W, const int8_t *q, const float *d,
     return hipGetLastError();
 }
 
-#ifndef GEMV_Q5K_IT
-#define GEMV_Q5K_IT 4
-#endif
+// Rows per wavefront: several for short rows; one for long rows (K >= 8192),
+// where a few rows per wavefront would leave too few wavefronts for the
+// chip (N = 3584, K = 18944: 896 instead of 3584).
 template <int MT>
-hipError_t gemv_q5k_mt(const uint8_t *W, const int8_t *q, const float *d,
+hipError_t gemv_q4k_mt(const uint8_t *W, const int8_t *q, const float *d,
                        const float *s, int M, int N, int K, float *out,
                        hipStream_t st)
 {
-    constexpr int R = MT <= 2 ? 4 : 2;           // rows per wavefront
+    if (K >= 8192)
+        return gemv_q4k_launch<MT, 1>(W, q, d, s, M, N, K, out, st);
+    return gemv_q4k_launch<MT, MT <= 2 ? 4 : 2>(W, q, d, s, M, N, K, out, st);
+}
+
+#ifndef GEMV_Q5K_IT
+#define GEMV_Q5K_IT 4
+#endif
+template <int MT, int R>
+hipError_t gemv_q5k_launch(const uint8_t *W, const int8_t *q, const float *d,
+                           const float *s, int M, int N, int K, float *out,
+                           hipStream_t st)
+{
     constexpr int IT = GEMV_Q5K_IT;              // passes (of 8 blocks) in flight
     const int rows_per_wg = GEMV_WAVES * R;
     const int grid = (N + rows_per_wg - 1) / rows_per_wg;
@@ -1074,6 +1094,16 @@ hipError_t gemv_q5k_mt(const uint8_t *W, const int8_t *q, const float *d,
     else
         gemv_q5k_kernel<MT, R, IT, false><<<dim3(grid), dim3(64 * GEMV_WAVES), 0, st>>>(W, q, d, s, M, N, K, out);
     return hipGetLastError();
+}
+
+template <int MT>
+hipError_t gemv_q5k_mt(const uint8_t *W, const int8_t *q, const float *d,
+                       const float *s, int M, int N, int K, float *out,
+                       hipStream_t st)
+{
+    if (K >= 8192)                               // as for Q4_K
+        return gemv_q5k_launch<MT, 1>(W, q, d, s, M, N, K, out, st);
+    return gemv_q5k_launch<MT, MT <= 2 ? 4 : 2>(W, q, d, s, M, N, K, out, st);
 }
 
 template <int MT, int R>
@@ -1103,12 +1133,13 @@ hipError_t launch_gemv_q4k(const uint8_t *W, const int8_t *q, const float *d,
                            hipStream_t st)
 {
     if (M <= 2 && K <= 2 * 7 * 256 && (int64_t)M * K * 5 / 4 <= GEMV_ACT_LDS) {
-        // persistent stream: up to 8 wavefronts per CU, never more than one per row
-        const int nwg = max(1, min((N + GEMV_WAVES - 1) / GEMV_WAVES, GEMV_STREAM_WGS));
+        // persistent stream: up to 1024 workgroups of 8 wavefronts (32 per CU), never
+        // more than one wavefront per row
+        const int nwg = max(1, min((N + STREAM_WAVES - 1) / STREAM_WAVES, GEMV_STREAM_WGS));
         if (M == 1)
-            gemv_q4k_stream_kernel<1, 2, GEMV_STREAM_D><<<dim3(nwg), dim3(64 * GEMV_WAVES), 0, st>>>(W, q, d, s, M, N, K, out);
+            gemv_q4k_stream_kernel<1, 2, GEMV_STREAM_D><<<dim3(nwg), dim3(64 * STREAM_WAVES), 0, st>>>(W, q, d, s, M, N, K, out);
         else
-            gemv_q4k_stream_kernel<2, 2, GEMV_STREAM_D><<<dim3(nwg), dim3(64 * GEMV_WAVES), 0, st>>>(W, q, d, s, M, N, K, out);
+            gemv_q4k_stream_kernel<2, 2, GEMV_STREAM_D><<<dim3(nwg), dim3(64 * STREAM_WAVES), 0, st>>>(W, q, d, s, M, N, K, out);
         return hipGetLastError();
     }
     if (M <= 1) return gemv_q4k_mt<1>(W, q, d, s, M, N, K, out, st);
