@@ -102,7 +102,7 @@ __device__ __forceinline__ void act_store(const ActCopy<WAVES> &c, v4i *lds, int
 // LDS copy). after_first_loads() runs once, right after the first batch of
 // weight loads is issued: the activation copy into LDS goes there, so that
 // it overlaps the weight stream.
-template <int MT, int R, int IT, class F>
+template <int MT, int R, int IT, bool PIPE = false, class F>
 __device__ __forceinline__ void q4k_rows(const uint8_t *__restrict__ base, int rows, int nb, int K, int M,
                                          const int8_t *qa, const float *da, const float *sa, int lane,
                                          float (&acc)[R][MT], F &&after_first_loads)
@@ -115,8 +115,7 @@ __device__ __forceinline__ void q4k_rows(const uint8_t *__restrict__ base, int r
     // this lane's (row, block) position, advanced by 7 blocks per pass
     int rl = 0, blk = slot;
     while (blk >= nb) { blk -= nb; ++rl; }
-    for (int it0 = 0; it0 < max(total, 1); it0 += 7 * IT) {
-        v4i v[IT];
+    auto load = [&](v4i (&v)[IT], int it0) {
 #pragma unroll
         for (int i = 0; i < IT; ++i) {
             const int fb = it0 + 7 * i + slot;
@@ -124,8 +123,8 @@ __device__ __forceinline__ void q4k_rows(const uint8_t *__restrict__ base, int r
                        ? __builtin_nontemporal_load(reinterpret_cast<const v4i *>(base + (int64_t)fb * 144 + 16 * part))
                        : v4i{0, 0, 0, 0};
         }
-        if (it0 == 0)
-            after_first_loads();
+    };
+    auto compute = [&](const v4i (&v)[IT], int it0) {
 #pragma unroll
         for (int i = 0; i < IT; ++i) {
             const int fb = it0 + 7 * i + slot;
@@ -183,10 +182,36 @@ __device__ __forceinline__ void q4k_rows(const uint8_t *__restrict__ base, int r
             blk += 7;
             while (blk >= nb) { blk -= nb; ++rl; }
         }
+    };
+    if constexpr (!PIPE) {
+        for (int it0 = 0; it0 < max(total, 1); it0 += 7 * IT) {
+            v4i v[IT];
+            load(v, it0);
+            if (it0 == 0)
+                after_first_loads();
+            compute(v, it0);
+        }
+    } else {
+        // two batches: the loads of the next batch are in flight while this
+        // one is reduced (long rows, several batches per wavefront)
+        v4i va[IT], vb[IT];
+        load(va, 0);
+        after_first_loads();
+        for (int it0 = 0; it0 < max(total, 1); it0 += 14 * IT) {
+            const bool b_live = it0 + 7 * IT < total;
+            if (b_live)
+                load(vb, it0 + 7 * IT);
+            compute(va, it0);
+            if (!b_live)
+                break;
+            if (it0 + 14 * IT < total)
+                load(va, it0 + 14 * IT);
+            compute(vb, it0 + 7 * IT);
+        }
     }
 }
 
-template <int MT, int R, int IT, bool ACT_LDS>
+template <int MT, int R, int IT, bool ACT_LDS, bool PIPE = false>
 __global__ __launch_bounds__(64 * GEMV_WAVES) void gemv_q4k_kernel(
     const uint8_t *__restrict__ W, const int8_t *__restrict__ q,
     const float *__restrict__ dx, const float *__restrict__ sx, int M, int N,
@@ -216,7 +241,7 @@ __global__ __launch_bounds__(64 * GEMV_WAVES) void gemv_q4k_kernel(
         da = reinterpret_cast<const float *>(qa + M * K);
         sa = da + M * (K >> 5);
     }
-    q4k_rows<MT, R, IT>(base, rows, nb, K, M, qa, da, sa, lane, acc, [&] {
+    q4k_rows<MT, R, IT, PIPE>(base, rows, nb, K, M, qa, da, sa, lane, acc, [&] {
         if constexpr (ACT_LDS) {
             act_store(ac, act, M, K);
             __syncthreads();
@@ -1048,19 +1073,26 @@ __global__ __launch_bounds__(64 * Q6S_WAVES) void gemv_q6k_stream_kernel(
     wait_vm<0>();
 }
 
+#ifndef GEMV_LONG_IT
+#define GEMV_LONG_IT 4
+#define GEMV_LONG_PIPE true
+#endif
 template <int MT, int R>
 hipError_t gemv_q4k_launch(const uint8_t *W, const int8_t *q, const float *d,
                            const float *s, int M, int N, int K, float *out,
                            hipStream_t st)
 {
-    constexpr int IT = 8;                        // passes (of 7 blocks) in flight
+    // passes (of 7 blocks) in flight: 8 in one batch for short rows; long
+    // rows (one per wavefront) stream in double-buffered batches
+    constexpr bool PIPE = R == 1 && GEMV_LONG_PIPE;
+    constexpr int IT = R == 1 ? GEMV_LONG_IT : 8;
     const int rows_per_wg = GEMV_WAVES * R;
     const int grid = (N + rows_per_wg - 1) / rows_per_wg;
     const bool act_lds = (int64_t)M * K * 5 / 4 <= GEMV_ACT_LDS;
     if (act_lds)
-        gemv_q4k_kernel<MT, R, IT, true><<<dim3(grid), dim3(64 * GEMV_WAVES), 0, st>>>(W, q, d, s, M, N, K, out);
+        gemv_q4k_kernel<MT, R, IT, true, PIPE><<<dim3(grid), dim3(64 * GEMV_WAVES), 0, st>>>(W, q, d, s, M, N, K, out);
     else
-        gemv_q4k_kernel<MT, R, IT, false><<<dim3(grid), dim3(64 * GEMV_WAVES), 0, st>>>(W, q, d, s, M, N, K, out);
+        gemv_q4k_kernel<MT, R, IT, false, PIPE><<<dim3(grid), dim3(64 * GEMV_WAVES), 0, st>>>(W, q, d, s, M, N, K, out);
     return hipGetLastError();
 }
 

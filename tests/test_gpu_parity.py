@@ -375,3 +375,18 @@ def test_full_size_workloads(dev, name):
     got = out if toks is None else out[toks]
     rel = check_close(got, ref, case.name)
     print(f"[parity] {case.name}: max|d|/max|ref| = {rel:.2e}", flush=True)
+
+
+# Long rows (K >= 8192): the GEMVs give each wavefront one row and stream it
+# in double-buffered batches; ragged N and several token counts.
+@pytest.mark.parametrize("fmt", ["q4k", "q5k", "q6k"])
+@pytest.mark.parametrize("M,N,K", [(1, 300, 18944), (3, 77, 8192), (8, 129, 18944), (16, 40, 10240)])
+def test_long_rows_gemv(dev, fmt, M, N, K):
+    rng = np.random.default_rng(M * 131 + N + K + FMT_SEED[fmt])
+    W = synth.weights(fmt, rng, N, K)
+    x = synth.activations(rng, M, K, outliers=True)
+    rq, rd, _ = oracle.quantize_act(x)
+    q, d, s = gpu_plane(x)
+    ref = oracle_mm(fmt, W, rq, rd, N, K)
+    for path in (mq.MQ_PATH_GEMV, mq.MQ_PATH_AUTO):
+        check_close(host(run_matmul(fmt, W, q, d, s, N, K, path=path)), ref, f"{fmt} M={M} N={N} K={K} path {path}")
