@@ -497,7 +497,7 @@ __global__ __launch_bounds__(64 * STREAM_WAVES) void gemv_q4k_stream_kernel(
 // fifth bit of position i of sub-block j) and the header itself: three
 // 16-byte loads, no cross-lane exchange. The replicated header and qh loads
 // hit the lines the block's own loads bring in, so HBM sees each byte once.
-template <int MT, int R, int IT, class F>
+template <int MT, int R, int IT, bool PIPE = false, class F>
 __device__ __forceinline__ void q5k_rows(const uint8_t *__restrict__ base, int rows, int nb, int K, int M,
                                          const int8_t *qa, const float *da, const float *sa, int lane,
                                          float (&acc)[R][MT], F &&after_first_loads)
@@ -513,18 +513,23 @@ __device__ __forceinline__ void q5k_rows(const uint8_t *__restrict__ base, int r
     const int rot0 = (j0 + 28) & 31, rot1 = (j0 + 29) & 31;
     int rl = 0, blk = slot;
     while (blk >= nb) { blk -= nb; ++rl; }
-    for (int it0 = 0; it0 < max(total, 1); it0 += 8 * IT) {
+    struct Batch {
         v4i hv[IT], hq[IT], v[IT];
+    };
+    auto load = [&](Batch &bt, int it0) {
 #pragma unroll
         for (int i = 0; i < IT; ++i) {
             const int fb = it0 + 8 * i + slot;
             const uint8_t *b = base + (int64_t)min(fb, max(total, 1) - 1) * 176;
-            hv[i] = __builtin_nontemporal_load(reinterpret_cast<const v4i *>(b));
-            hq[i] = __builtin_nontemporal_load(reinterpret_cast<const v4i *>(b + 16 + po));
-            v[i] = __builtin_nontemporal_load(reinterpret_cast<const v4i *>(b + 48 + 16 * c));
+            bt.hv[i] = __builtin_nontemporal_load(reinterpret_cast<const v4i *>(b));
+            bt.hq[i] = __builtin_nontemporal_load(reinterpret_cast<const v4i *>(b + 16 + po));
+            bt.v[i] = __builtin_nontemporal_load(reinterpret_cast<const v4i *>(b + 48 + 16 * c));
         }
-        if (it0 == 0)
-            after_first_loads();
+    };
+    auto compute = [&](const Batch &bt, int it0) {
+        const auto &hv = bt.hv;
+        const auto &hq = bt.hq;
+        const auto &v = bt.v;
 #pragma unroll
         for (int i = 0; i < IT; ++i) {
             const int fb = it0 + 8 * i + slot;
@@ -582,10 +587,35 @@ __device__ __forceinline__ void q5k_rows(const uint8_t *__restrict__ base, int r
             blk += 8;
             while (blk >= nb) { blk -= nb; ++rl; }
         }
+    };
+    if constexpr (!PIPE) {
+        for (int it0 = 0; it0 < max(total, 1); it0 += 8 * IT) {
+            Batch bt;
+            load(bt, it0);
+            if (it0 == 0)
+                after_first_loads();
+            compute(bt, it0);
+        }
+    } else {
+        // double-buffered batches for long rows, as q4k_rows
+        Batch ba, bb;
+        load(ba, 0);
+        after_first_loads();
+        for (int it0 = 0; it0 < max(total, 1); it0 += 16 * IT) {
+            const bool b_live = it0 + 8 * IT < total;
+            if (b_live)
+                load(bb, it0 + 8 * IT);
+            compute(ba, it0);
+            if (!b_live)
+                break;
+            if (it0 + 16 * IT < total)
+                load(ba, it0 + 16 * IT);
+            compute(bb, it0 + 8 * IT);
+        }
     }
 }
 
-template <int MT, int R, int IT, bool ACT_LDS>
+template <int MT, int R, int IT, bool ACT_LDS, bool PIPE = false>
 __global__ __launch_bounds__(64 * GEMV_WAVES) void gemv_q5k_kernel(
     const uint8_t *__restrict__ W, const int8_t *__restrict__ q,
     const float *__restrict__ dx, const float *__restrict__ sx, int M, int N,
@@ -616,7 +646,7 @@ __global__ __launch_bounds__(64 * GEMV_WAVES) void gemv_q5k_kernel(
         da = reinterpret_cast<const float *>(qa + M * K);
         sa = da + M * (K >> 5);
     }
-    q5k_rows<MT, R, IT>(base, max(rows, 1), nb, K, M, qa, da, sa, lane, acc, [&] {
+    q5k_rows<MT, R, IT, PIPE>(base, max(rows, 1), nb, K, M, qa, da, sa, lane, acc, [&] {
         if constexpr (ACT_LDS) {
             act_store(ac, act, M, K);
             __syncthreads();
@@ -1112,19 +1142,24 @@ hipError_t gemv_q4k_mt(const uint8_t *W, const int8_t *q, const float *d,
 #ifndef GEMV_Q5K_IT
 #define GEMV_Q5K_IT 4
 #endif
+#ifndef GEMV_Q5K_LONG_IT
+#define GEMV_Q5K_LONG_IT 2
+#endif
 template <int MT, int R>
 hipError_t gemv_q5k_launch(const uint8_t *W, const int8_t *q, const float *d,
                            const float *s, int M, int N, int K, float *out,
                            hipStream_t st)
 {
-    constexpr int IT = GEMV_Q5K_IT;              // passes (of 8 blocks) in flight
+    // passes (of 8 blocks) in flight; long rows stream in double-buffered batches
+    constexpr bool PIPE = R == 1 && GEMV_LONG_PIPE;
+    constexpr int IT = R == 1 ? GEMV_Q5K_LONG_IT : GEMV_Q5K_IT;
     const int rows_per_wg = GEMV_WAVES * R;
     const int grid = (N + rows_per_wg - 1) / rows_per_wg;
     const bool act_lds = (int64_t)M * K * 5 / 4 <= GEMV_ACT_LDS;
     if (act_lds)
-        gemv_q5k_kernel<MT, R, IT, true><<<dim3(grid), dim3(64 * GEMV_WAVES), 0, st>>>(W, q, d, s, M, N, K, out);
+        gemv_q5k_kernel<MT, R, IT, true, PIPE><<<dim3(grid), dim3(64 * GEMV_WAVES), 0, st>>>(W, q, d, s, M, N, K, out);
     else
-        gemv_q5k_kernel<MT, R, IT, false><<<dim3(grid), dim3(64 * GEMV_WAVES), 0, st>>>(W, q, d, s, M, N, K, out);
+        gemv_q5k_kernel<MT, R, IT, false, PIPE><<<dim3(grid), dim3(64 * GEMV_WAVES), 0, st>>>(W, q, d, s, M, N, K, out);
     return hipGetLastError();
 }
 
