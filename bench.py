@@ -12,9 +12,12 @@ last-level cache cannot hold them, so its weight bytes come from HBM.
 
 Prints one JSON line: value = int8 ops of the whole step (2*M*N*K of both
 matmuls) per second, in TOPS; "roofline" for the dominant kernel (the GEMM,
-MFMA-bound) and "decode_roofline" for the GEMV (HBM-bound), both from
-per-kernel HIP events over the timed region; "cpu_baseline" = the CPU oracle
-timed on a bounded sample of the same GEMM.
+MFMA-bound) and "decode_roofline" for the GEMV (HBM-bound), both from HIP
+events over the timed region that the library records at each kernel's own
+dispatch start and end (mq_time_next_kernel, the quantity a kernel trace
+reports), with the events recorded around each call beside them
+("avg_us_call_bracket", which adds the launch gap); "cpu_baseline" = the
+CPU oracle timed on a bounded sample of the same GEMM.
 
   python bench.py [--steps K] [--warmup W] [--no-cpu]
   python bench.py --all                  # per-matrix table of every workload
@@ -108,6 +111,45 @@ def cpu_baseline(W, x, case, target_s):
     }
 
 
+class KernelClock:
+    """Raw hipEvent_t pairs that the library records at a kernel's own
+    dispatch start and end (mq.time_next_kernel): the kernel's duration by
+    HIP events, without the launch gap that events recorded around the call
+    include. Created from the HIP runtime torch has loaded."""
+
+    def __init__(self, n):
+        import ctypes
+        import torch
+        self.ct = ctypes
+        lib = ctypes.CDLL(os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so"))
+        lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.lib = lib
+        self.ev = []
+        for _ in range(n):
+            pair = [ctypes.c_void_p(), ctypes.c_void_p()]
+            for e in pair:
+                if lib.hipEventCreateWithFlags(ctypes.byref(e), 0) != 0:
+                    raise RuntimeError("hipEventCreateWithFlags failed")
+            self.ev.append(pair)
+
+    def arm(self, i):
+        import quant_gemm_amd as mq
+        mq.time_next_kernel(self.ev[i][0].value, self.ev[i][1].value)
+
+    def us(self, i):
+        ms = self.ct.c_float()
+        if self.lib.hipEventElapsedTime(self.ct.byref(ms), self.ev[i][0], self.ev[i][1]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value * 1e3
+
+    def close(self):
+        for pair in self.ev:
+            for e in pair:
+                self.lib.hipEventDestroy(e)
+
+
 def run_contract(args):
     import numpy as np
     import torch
@@ -143,14 +185,16 @@ def run_contract(args):
 
     names = ["quantize_prefill", "gemm_q4k", "quantize_decode", "gemv_q4k"]
 
-    def step(i, ev=None):
+    def step(i, ev=None, kc=None):
         if ev: ev[0].record()
         mq.quantize_act(xp, qp, dp, sp)
         if ev: ev[1].record()
+        if kc: kc[0].arm(i)
         mq.matmul_q4k(Wp, qp, dp, sp, pre.N, pre.K, out=outp)
         if ev: ev[2].record()
         mq.quantize_act(xd, qd, dd, sd)
         if ev: ev[3].record()
+        if kc: kc[1].arm(i)
         mq.matmul_q4k(Wd[i % copies], qd, dd, sd, dec.N, dec.K, out=outd)
         if ev: ev[4].record()
 
@@ -159,29 +203,37 @@ def run_contract(args):
         step(i)
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    kclocks = (KernelClock(args.steps), KernelClock(args.steps))     # GEMM, GEMV
     log(f"[bench] timing {args.steps} steps")
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record()
     for i in range(args.steps):
-        step(i, evs[i])
+        step(i, evs[i], kclocks)
     t_end.record()
     torch.cuda.synchronize()
+    kernel_us = {n: np.array([kc.us(i) for i in range(args.steps)])
+                 for n, kc in (("gemm_q4k", kclocks[0]), ("gemv_q4k", kclocks[1]))}
+    for kc in kclocks:
+        kc.close()
     total_ms = t_start.elapsed_time(t_end)
     per = {n: np.array([evs[i][k].elapsed_time(evs[i][k + 1]) for i in range(args.steps)])
            for k, n in enumerate(names)}
     avg_us = {n: float(v.mean() * 1e3) for n, v in per.items()}
-    med_us = {n: float(np.median(v) * 1e3) for n, v in per.items()}
 
     ops_pre = pre.ops
     ops_dec = dec.ops
     ms_step = total_ms / args.steps
     value = (ops_pre + ops_dec) / (ms_step * 1e-3) / 1e12
 
-    gemm_tops = ops_pre / (avg_us["gemm_q4k"] * 1e-6) / 1e12
+    # roofline figures from the kernels' own durations (dispatch-boundary
+    # events); the per-call event brackets are reported beside them
+    gemm_us = float(kernel_us["gemm_q4k"].mean())
+    gemv_us = float(kernel_us["gemv_q4k"].mean())
+    gemm_tops = ops_pre / (gemm_us * 1e-6) / 1e12
     gemv_bytes = q4k_gemv_bytes(dec.M, dec.N, dec.K)
-    gemv_gbs = gemv_bytes / (avg_us["gemv_q4k"] * 1e-6) / 1e9
+    gemv_gbs = gemv_bytes / (gemv_us * 1e-6) / 1e9
     qbytes = pre.M * pre.K * 4 + pre.M * pre.K + 2 * 4 * pre.M * (pre.K // 32)
 
     res = {
@@ -208,14 +260,17 @@ def run_contract(args):
             "peak": INT8_PEAK_TOPS, "unit": "TOPS", "frac": round(gemm_tops / INT8_PEAK_TOPS, 4),
             "traffic": measured_traffic("gemm_q4k", "prefill_ffn_up"),
             "work_per_launch": f"{ops_pre:.4g} int8 ops (2*M*N*K)",
-            "avg_us": round(avg_us["gemm_q4k"], 2),
+            "avg_us": round(gemm_us, 2), "timing": "kernel start/end events (hipExtLaunchKernel)",
+            "avg_us_call_bracket": round(avg_us["gemm_q4k"], 2),
         },
         "decode_roofline": {
             "kernel": "gemv_q4k", "bound": "hbm", "achieved": round(gemv_gbs, 1),
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gemv_gbs / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic("gemv_q4k", "decode_ffn_up"),
             "work_per_launch": f"{gemv_bytes} bytes (weights + int8 plane + output)",
-            "avg_us": round(avg_us["gemv_q4k"], 3), "median_us": round(med_us["gemv_q4k"], 3),
+            "avg_us": round(gemv_us, 3), "median_us": round(float(np.median(kernel_us["gemv_q4k"])), 3),
+            "timing": "kernel start/end events (hipExtLaunchKernel)",
+            "avg_us_call_bracket": round(avg_us["gemv_q4k"], 3),
         },
         "kernels_avg_us": {n: round(v, 3) for n, v in avg_us.items()},
         "quantize_prefill_GBs": round(qbytes / (avg_us["quantize_prefill"] * 1e-6) / 1e9, 1),

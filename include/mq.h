@@ -255,6 +255,18 @@ int mq_matmul_q4k_dsc(const void *W, const float *fw, const float *fm,
                       const int8_t *q, const float *d, const float *s,
                       int64_t M, int64_t N, int64_t K, float *out, void *stream);
 
+/*
+ * Measurement hook. The next matmul call of the calling thread (mq_matmul_*,
+ * mq_ffn_q4k*) launches its main kernel with hipExtLaunchKernel, which
+ * records start_event and stop_event (hipEvent_t, created by the caller;
+ * either may be NULL) at that kernel's own dispatch start and end, so
+ * hipEventElapsedTime gives the kernel's duration without the launch gap an
+ * event recorded before the call would include. A split-K GEMM's reduction
+ * kernel is not covered. The request is consumed by that call, and dropped
+ * by any other mq_* call in between. Always returns MQ_OK.
+ */
+int mq_time_next_kernel(void *start_event, void *stop_event);
+
 /* Largest M the GEMV path serves (MQ_PATH_GEMV); 16. */
 int64_t mq_gemv_max_m(void);
 

@@ -50,6 +50,7 @@ SIGNATURES = {
     "mq_matmul_q6k_x": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P], ctypes.c_int),
     "mq_dsc_q4k": ([_P, _I64, _I64, _P, _P, _P], ctypes.c_int),
     "mq_matmul_q4k_dsc": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P], ctypes.c_int),
+    "mq_time_next_kernel": ([_P, _P], ctypes.c_int),
     "mq_gemv_max_m": ([], ctypes.c_int64),
     "mq_last_error": ([], ctypes.c_char_p),
     "mq_abi_version": ([], ctypes.c_int),
@@ -280,6 +281,13 @@ def matmul_q4k_dsc(W, fw, fm, q, d, s, N, K, out=None, stream=None):
     _check(L.mq_matmul_q4k_dsc(W.data_ptr(), fw.data_ptr(), fm.data_ptr(), q.data_ptr(), d.data_ptr(),
                                s.data_ptr(), M, N, K, out.data_ptr(), _stream(stream)))
     return out
+
+
+def time_next_kernel(start_event, stop_event):
+    """Have the next matmul call of this thread record the raw hipEvent_t
+    handles start_event / stop_event (ints, or None) at its main kernel's own
+    start and end (see mq_time_next_kernel)."""
+    _check(load().mq_time_next_kernel(start_event, stop_event))
 
 
 def ffn_q4k(Wg, Wu, q, d, s, N, K, qo=None, do=None, so=None, y=None, stream=None, path=MQ_PATH_AUTO):

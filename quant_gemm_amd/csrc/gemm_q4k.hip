@@ -593,7 +593,7 @@ hipError_t launch_gemm_q4k(const uint8_t *W, const int8_t *q, const float *d,
     const int tiles = tiles_m * tiles_n;
     const int nsplit = gemm_splits(tiles, BM * BN, K >> 8, M, N, K, Q4K_SLOT_OPS);
     return run_split_k(nsplit, (int64_t)M * N, out, st, [&](float *dst) {
-        gemm_q4k_kernel<false, false><<<dim3((unsigned)(tiles * nsplit)), dim3(NTHR), 0, st>>>(
+        launch(gemm_q4k_kernel<false, false>, dim3((unsigned)(tiles * nsplit)), dim3(NTHR), 0, st, 
             W, nullptr, Dsc{nullptr, nullptr}, q, d, s, M, N, K, tiles_m, nsplit, dst, nullptr, nullptr, nullptr);
         return hipGetLastError();
     });
@@ -615,7 +615,7 @@ hipError_t launch_gemm_q4k_dsc(const uint8_t *W, const float *fw, const float *f
     const int tiles = tiles_m * tiles_n;
     const int nsplit = gemm_splits(tiles, BM * BN, K >> 8, M, N, K, Q4K_SLOT_OPS);
     return run_split_k(nsplit, (int64_t)M * N, out, st, [&](float *dst) {
-        gemm_q4k_kernel<false, true><<<dim3((unsigned)(tiles * nsplit)), dim3(NTHR), 0, st>>>(
+        launch(gemm_q4k_kernel<false, true>, dim3((unsigned)(tiles * nsplit)), dim3(NTHR), 0, st, 
             W, nullptr, Dsc{fw, fm}, q, d, s, M, N, K, tiles_m, nsplit, dst, nullptr, nullptr, nullptr);
         return hipGetLastError();
     });
@@ -629,7 +629,7 @@ hipError_t launch_gemm_q4k_ffn(const uint8_t *Wg, const uint8_t *Wu, const int8_
 {
     const int tiles_m = (M + BM - 1) / BM;
     const int tiles_n = (N + BN / 2 - 1) / (BN / 2);
-    gemm_q4k_kernel<true, false><<<dim3((unsigned)(tiles_m * tiles_n)), dim3(NTHR), 0, st>>>(
+    launch(gemm_q4k_kernel<true, false>, dim3((unsigned)(tiles_m * tiles_n)), dim3(NTHR), 0, st, 
         Wg, Wu, Dsc{nullptr, nullptr}, q, d, s, M, N, K, tiles_m, 1, y, qo, do_, so);
     return hipGetLastError();
 }

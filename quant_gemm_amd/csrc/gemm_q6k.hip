@@ -401,7 +401,7 @@ hipError_t launch_gemm_q6k(const uint8_t *W, const int8_t *q, const float *d,
     const int tiles = tiles_m * tiles_n;
     const int nsplit = gemm_splits(tiles, BM * BN, K >> 8, M, N, K, Q6K_SLOT_OPS);
     return run_split_k(nsplit, (int64_t)M * N, out, st, [&](float *dst) {
-        gemm_q6k_kernel<<<dim3((unsigned)(tiles * nsplit)), dim3(NTHR), 0, st>>>(W, q, d, M, N, K, tiles_m,
+        launch(gemm_q6k_kernel<const uint8_t *>, dim3((unsigned)(tiles * nsplit)), dim3(NTHR), 0, st, W, q, d, M, N, K, tiles_m,
                                                                                  nsplit, dst);
         return hipGetLastError();
     });
@@ -421,7 +421,7 @@ hipError_t launch_gemm_q6k_x(const int8_t *lo, const int8_t *hi, const float *dw
     const int nsplit = gemm_splits(tiles, BM * BN, K >> 8, M, N, K, Q6K_X_SLOT_OPS);
     const Planes E{lo, hi, dw};
     return run_split_k(nsplit, (int64_t)M * N, out, st, [&](float *dst) {
-        gemm_q6k_kernel<<<dim3((unsigned)(tiles * nsplit)), dim3(NTHR), 0, st>>>(E, q, d, M, N, K, tiles_m,
+        launch(gemm_q6k_kernel<Planes>, dim3((unsigned)(tiles * nsplit)), dim3(NTHR), 0, st, E, q, d, M, N, K, tiles_m,
                                                                                  nsplit, dst);
         return hipGetLastError();
     });

@@ -1120,9 +1120,9 @@ hipError_t gemv_q4k_launch(const uint8_t *W, const int8_t *q, const float *d,
     const int grid = (N + rows_per_wg - 1) / rows_per_wg;
     const bool act_lds = (int64_t)M * K * 5 / 4 <= GEMV_ACT_LDS;
     if (act_lds)
-        gemv_q4k_kernel<MT, R, IT, true, PIPE><<<dim3(grid), dim3(64 * GEMV_WAVES), 0, st>>>(W, q, d, s, M, N, K, out);
+        launch(gemv_q4k_kernel<MT, R, IT, true, PIPE>, dim3(grid), dim3(64 * GEMV_WAVES), 0, st, W, q, d, s, M, N, K, out);
     else
-        gemv_q4k_kernel<MT, R, IT, false, PIPE><<<dim3(grid), dim3(64 * GEMV_WAVES), 0, st>>>(W, q, d, s, M, N, K, out);
+        launch(gemv_q4k_kernel<MT, R, IT, false, PIPE>, dim3(grid), dim3(64 * GEMV_WAVES), 0, st, W, q, d, s, M, N, K, out);
     return hipGetLastError();
 }
 
@@ -1157,9 +1157,9 @@ hipError_t gemv_q5k_launch(const uint8_t *W, const int8_t *q, const float *d,
     const int grid = (N + rows_per_wg - 1) / rows_per_wg;
     const bool act_lds = (int64_t)M * K * 5 / 4 <= GEMV_ACT_LDS;
     if (act_lds)
-        gemv_q5k_kernel<MT, R, IT, true, PIPE><<<dim3(grid), dim3(64 * GEMV_WAVES), 0, st>>>(W, q, d, s, M, N, K, out);
+        launch(gemv_q5k_kernel<MT, R, IT, true, PIPE>, dim3(grid), dim3(64 * GEMV_WAVES), 0, st, W, q, d, s, M, N, K, out);
     else
-        gemv_q5k_kernel<MT, R, IT, false, PIPE><<<dim3(grid), dim3(64 * GEMV_WAVES), 0, st>>>(W, q, d, s, M, N, K, out);
+        launch(gemv_q5k_kernel<MT, R, IT, false, PIPE>, dim3(grid), dim3(64 * GEMV_WAVES), 0, st, W, q, d, s, M, N, K, out);
     return hipGetLastError();
 }
 
@@ -1179,7 +1179,7 @@ hipError_t gemv_q6k_launch(const uint8_t *W, const int8_t *q, const float *d,
 {
     const int rows_per_wg = GEMV_WAVES * R;
     const int grid = (N + rows_per_wg - 1) / rows_per_wg;
-    gemv_q6k_kernel<MT, R><<<dim3(grid), dim3(64 * GEMV_WAVES), 0, st>>>(W, q, d, M, N, K, out);
+    launch(gemv_q6k_kernel<MT, R>, dim3(grid), dim3(64 * GEMV_WAVES), 0, st, W, q, d, M, N, K, out);
     return hipGetLastError();
 }
 
@@ -1204,9 +1204,9 @@ hipError_t launch_gemv_q4k(const uint8_t *W, const int8_t *q, const float *d,
         // more than one wavefront per row
         const int nwg = max(1, min((N + STREAM_WAVES - 1) / STREAM_WAVES, GEMV_STREAM_WGS));
         if (M == 1)
-            gemv_q4k_stream_kernel<1, 2, GEMV_STREAM_D><<<dim3(nwg), dim3(64 * STREAM_WAVES), 0, st>>>(W, q, d, s, M, N, K, out);
+            launch(gemv_q4k_stream_kernel<1, 2, GEMV_STREAM_D>, dim3(nwg), dim3(64 * STREAM_WAVES), 0, st, W, q, d, s, M, N, K, out);
         else
-            gemv_q4k_stream_kernel<2, 2, GEMV_STREAM_D><<<dim3(nwg), dim3(64 * STREAM_WAVES), 0, st>>>(W, q, d, s, M, N, K, out);
+            launch(gemv_q4k_stream_kernel<2, 2, GEMV_STREAM_D>, dim3(nwg), dim3(64 * STREAM_WAVES), 0, st, W, q, d, s, M, N, K, out);
         return hipGetLastError();
     }
     if (M <= 1) return gemv_q4k_mt<1>(W, q, d, s, M, N, K, out, st);
@@ -1223,9 +1223,9 @@ hipError_t launch_gemv_q5k(const uint8_t *W, const int8_t *q, const float *d,
     if (M <= 2 && K <= 2 * 8 * 256 && (int64_t)M * K * 5 / 4 <= GEMV_ACT_LDS) {
         const int nwg = max(1, min((N + GEMV_WAVES - 1) / GEMV_WAVES, GEMV_STREAM_WGS));
         if (M == 1)
-            gemv_q5k_stream_kernel<1, 2, GEMV_STREAM_D><<<dim3(nwg), dim3(64 * GEMV_WAVES), 0, st>>>(W, q, d, s, M, N, K, out);
+            launch(gemv_q5k_stream_kernel<1, 2, GEMV_STREAM_D>, dim3(nwg), dim3(64 * GEMV_WAVES), 0, st, W, q, d, s, M, N, K, out);
         else
-            gemv_q5k_stream_kernel<2, 2, GEMV_STREAM_D><<<dim3(nwg), dim3(64 * GEMV_WAVES), 0, st>>>(W, q, d, s, M, N, K, out);
+            launch(gemv_q5k_stream_kernel<2, 2, GEMV_STREAM_D>, dim3(nwg), dim3(64 * GEMV_WAVES), 0, st, W, q, d, s, M, N, K, out);
         return hipGetLastError();
     }
     if (M <= 1) return gemv_q5k_mt<1>(W, q, d, s, M, N, K, out, st);
@@ -1244,9 +1244,9 @@ hipError_t launch_gemv_q4k_ffn(const uint8_t *Wg, const uint8_t *Wu, const int8_
     auto go = [&](auto mt) {
         constexpr int MT = decltype(mt)::value;
         if (lds)
-            gemv_q4k_ffn_kernel<MT, true><<<grid, block, 0, st>>>(Wg, Wu, q, d, s, M, N, K, qo, do_, so, y);
+            launch(gemv_q4k_ffn_kernel<MT, true>, grid, block, 0, st, Wg, Wu, q, d, s, M, N, K, qo, do_, so, y);
         else
-            gemv_q4k_ffn_kernel<MT, false><<<grid, block, 0, st>>>(Wg, Wu, q, d, s, M, N, K, qo, do_, so, y);
+            launch(gemv_q4k_ffn_kernel<MT, false>, grid, block, 0, st, Wg, Wu, q, d, s, M, N, K, qo, do_, so, y);
     };
     if (M <= 1) go(std::integral_constant<int, 1>{});
     else if (M <= 2) go(std::integral_constant<int, 2>{});
@@ -1265,11 +1265,11 @@ hipError_t launch_gemv_q6k(const uint8_t *W, const int8_t *q, const float *d,
         const int per_cu = max(1, (int)(Q6S_LDS_PER_CU / lds));
         const int nwg = max(1, min((N + Q6S_WAVES - 1) / Q6S_WAVES, per_cu * n_cu));
         dim3 grid(nwg), block(64 * Q6S_WAVES);
-        if (M <= 1) gemv_q6k_stream_kernel<1><<<grid, block, lds, st>>>(W, q, d, M, N, K, out);
-        else if (M <= 2) gemv_q6k_stream_kernel<2><<<grid, block, lds, st>>>(W, q, d, M, N, K, out);
-        else if (M <= 4) gemv_q6k_stream_kernel<4><<<grid, block, lds, st>>>(W, q, d, M, N, K, out);
-        else if (M <= 8) gemv_q6k_stream_kernel<8><<<grid, block, lds, st>>>(W, q, d, M, N, K, out);
-        else gemv_q6k_stream_kernel<16><<<grid, block, lds, st>>>(W, q, d, M, N, K, out);
+        if (M <= 1) launch(gemv_q6k_stream_kernel<1>, grid, block, lds, st, W, q, d, M, N, K, out);
+        else if (M <= 2) launch(gemv_q6k_stream_kernel<2>, grid, block, lds, st, W, q, d, M, N, K, out);
+        else if (M <= 4) launch(gemv_q6k_stream_kernel<4>, grid, block, lds, st, W, q, d, M, N, K, out);
+        else if (M <= 8) launch(gemv_q6k_stream_kernel<8>, grid, block, lds, st, W, q, d, M, N, K, out);
+        else launch(gemv_q6k_stream_kernel<16>, grid, block, lds, st, W, q, d, M, N, K, out);
         return hipGetLastError();
     }
     if (M <= 1) return gemv_q6k_mt<1>(W, q, d, M, N, K, out, st);

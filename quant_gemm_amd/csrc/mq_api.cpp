@@ -14,9 +14,21 @@
 #include "../../include/mq.h"
 #include "mq_launch.h"
 
+namespace mq {
+KernelEvents &kernel_events()
+{
+    thread_local KernelEvents ev;
+    return ev;
+}
+} // namespace mq
+
 namespace {
 
 thread_local char g_err[512];
+
+// Entry points that launch no matmul kernel drop a pending timing request,
+// so it can only ever attach to the matmul call that follows it.
+void drop_timing() { mq::kernel_events() = mq::KernelEvents{}; }
 
 int fail(int status, const char *fmt, ...)
 {
@@ -229,6 +241,7 @@ int mq_quantize_act(const float *x, int64_t M, int64_t K, int64_t ldx, int8_t *q
                     float *d, float *s, void *stream)
 {
     g_err[0] = '\0';
+    drop_timing();
     const char *fn = "mq_quantize_act";
     if (!x) return fail(MQ_ERR_INVALID_ARG, "%s: x is NULL", fn);
     if (!q) return fail(MQ_ERR_INVALID_ARG, "%s: q is NULL", fn);
@@ -253,6 +266,7 @@ int mq_rmsnorm_quantize(const float *x, const float *w, int64_t M, int64_t K, in
                         int8_t *q, float *d, float *s, float *y, void *stream)
 {
     g_err[0] = '\0';
+    drop_timing();
     const char *fn = "mq_rmsnorm_quantize";
     if (!x) return fail(MQ_ERR_INVALID_ARG, "%s: x is NULL", fn);
     if (!w) return fail(MQ_ERR_INVALID_ARG, "%s: w is NULL", fn);
@@ -281,6 +295,7 @@ int mq_swiglu_quantize(const float *g, const float *u, int64_t M, int64_t K, int
                        int8_t *q, float *d, float *s, float *y, void *stream)
 {
     g_err[0] = '\0';
+    drop_timing();
     const char *fn = "mq_swiglu_quantize";
     if (!g) return fail(MQ_ERR_INVALID_ARG, "%s: g is NULL", fn);
     if (!u) return fail(MQ_ERR_INVALID_ARG, "%s: u is NULL", fn);
@@ -367,6 +382,7 @@ int mq_ffn_q4k_ex(const void *Wg, const void *Wu, const int8_t *q, const float *
 int mq_expand_q6k(const void *W, int64_t N, int64_t K, int8_t *lo, int8_t *hi, float *dw, void *stream)
 {
     g_err[0] = '\0';
+    drop_timing();
     const char *fn = "mq_expand_q6k";
     if (int rc = check_planes(fn, W, N, K)) return rc;
     if (!lo) return fail(MQ_ERR_INVALID_ARG, "%s: lo is NULL", fn);
@@ -403,6 +419,7 @@ int mq_matmul_q6k_x(const int8_t *lo, const int8_t *hi, const float *dw, const i
 int mq_dsc_q4k(const void *W, int64_t N, int64_t K, float *fw, float *fm, void *stream)
 {
     g_err[0] = '\0';
+    drop_timing();
     const char *fn = "mq_dsc_q4k";
     if (int rc = check_planes(fn, W, N, K)) return rc;
     if (!fw) return fail(MQ_ERR_INVALID_ARG, "%s: fw is NULL", fn);
@@ -436,6 +453,13 @@ int mq_matmul_q4k_dsc(const void *W, const float *fw, const float *fm, const int
                              ? mq::launch_gemm_q4k_dsc_small(Wb, fw, fm, q, d, s, m, n, k, out, st)
                              : mq::launch_gemm_q4k_dsc(Wb, fw, fm, q, d, s, m, n, k, out, st);
     return launched(e, fn);
+}
+
+int mq_time_next_kernel(void *start_event, void *stop_event)
+{
+    g_err[0] = '\0';
+    mq::kernel_events() = mq::KernelEvents{static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event)};
+    return MQ_OK;
 }
 
 int64_t mq_gemv_max_m(void) { return mq::GEMV_MAX_M; }

@@ -3,9 +3,35 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stdint.h>
 
 namespace mq {
+
+// Kernel-boundary timing (mq_time_next_kernel): when a pair of events is set
+// for the calling thread, the next matmul kernel launched through launch()
+// records them at its own dispatch start and end (hipExtLaunchKernel) and
+// the pair is cleared. Defined in mq_api.cpp.
+struct KernelEvents {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+KernelEvents &kernel_events();
+
+// kernel<<<grid, block, lds, st>>>(args...), or with the thread's timing
+// events when set. Like <<<>>>, it leaves a launch error for the caller's
+// hipGetLastError().
+template <class F, class... Args>
+inline void launch(F kernel, dim3 grid, dim3 block, uint32_t lds, hipStream_t st, Args... args)
+{
+    KernelEvents &e = kernel_events();
+    if (e.start || e.stop) {
+        const KernelEvents ev = e;
+        e = KernelEvents{};
+        hipExtLaunchKernelGGL(kernel, grid, block, lds, st, ev.start, ev.stop, 0u, args...);
+    } else {
+        kernel<<<grid, block, lds, st>>>(args...);
+    }
+}
 
 // Largest token count the GEMV kernels serve (MQ_PATH_GEMV), and the fused
 // FFN GEMV's.

@@ -390,3 +390,39 @@ def test_long_rows_gemv(dev, fmt, M, N, K):
     ref = oracle_mm(fmt, W, rq, rd, N, K)
     for path in (mq.MQ_PATH_GEMV, mq.MQ_PATH_AUTO):
         check_close(host(run_matmul(fmt, W, q, d, s, N, K, path=path)), ref, f"{fmt} M={M} N={N} K={K} path {path}")
+
+
+def test_time_next_kernel(dev):
+    """The timing hook records the kernel's own start and end: a positive
+    duration, the same result as an untimed call, and the request is used
+    once (a later call leaves the events untouched)."""
+    import ctypes
+    import os
+    import torch
+    lib = ctypes.CDLL(os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so"))
+    lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+    lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    ev = [ctypes.c_void_p(), ctypes.c_void_p()]
+    for e in ev:
+        assert lib.hipEventCreateWithFlags(ctypes.byref(e), 0) == 0
+    rng = np.random.default_rng(21)
+    N, K, M = 4096, 3584, 1
+    W = synth.q4k_weights(rng, N, K)
+    q, d, s = gpu_plane(synth.activations(rng, M, K))
+    ref = host(run_matmul("q4k", W, q, d, s, N, K))
+    Wd = to_dev(W.reshape(-1))
+    for path in (mq.MQ_PATH_GEMV, mq.MQ_PATH_GEMM):
+        mq.time_next_kernel(ev[0].value, ev[1].value)
+        got = host(mq.matmul_q4k(Wd, q, d, s, N, K, path=path))
+        ms = ctypes.c_float()
+        assert lib.hipEventElapsedTime(ctypes.byref(ms), ev[0], ev[1]) == 0
+        assert 0.0 < ms.value < 100.0, ms.value
+        check_close(got, ref.astype(np.float64), f"timed path {path}")
+        # the request was consumed: a second call does not touch the events
+        host(mq.matmul_q4k(Wd, q, d, s, N, K, path=path))
+        ms2 = ctypes.c_float()
+        assert lib.hipEventElapsedTime(ctypes.byref(ms2), ev[0], ev[1]) == 0
+        assert ms2.value == ms.value
+    for e in ev:
+        lib.hipEventDestroy(e)
