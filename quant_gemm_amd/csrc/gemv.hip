@@ -33,6 +33,9 @@ constexpr int STREAM_WAVES = 8;
 #ifndef GEMV_STREAM_WGS
 #define GEMV_STREAM_WGS 1024        // workgroups of the persistent stream kernel
 #endif
+#ifndef GEMV_STREAM_NP_MAX
+#define GEMV_STREAM_NP_MAX 6        // passes per row the persistent Q4_K stream handles
+#endif
 #ifndef GEMV_STREAM_D
 #define GEMV_STREAM_D 1             // rows in flight per wavefront (beside the one computed)
 #endif
@@ -1199,14 +1202,30 @@ hipError_t launch_gemv_q4k(const uint8_t *W, const int8_t *q, const float *d,
                            const float *s, int M, int N, int K, float *out,
                            hipStream_t st)
 {
-    if (M <= 2 && K <= 2 * 7 * 256 && (int64_t)M * K * 5 / 4 <= GEMV_ACT_LDS) {
+    if (M <= 2 && K <= GEMV_STREAM_NP_MAX * 7 * 256 && (int64_t)M * K * 5 / 4 <= GEMV_ACT_LDS) {
         // persistent stream: up to 1024 workgroups of 8 wavefronts (32 per CU), never
-        // more than one wavefront per row
+        // more than one wavefront per row; a row is 2, 3 or 6 passes of 7 blocks
+        // (measured against the row-grid kernel: 13.2 -> 8.3 us at 14336 x 4096,
+        // 12.7 -> 11.3 us at 8192 x 8192; longer rows keep the row-grid kernel)
         const int nwg = max(1, min((N + STREAM_WAVES - 1) / STREAM_WAVES, GEMV_STREAM_WGS));
-        if (M == 1)
-            launch(gemv_q4k_stream_kernel<1, 2, GEMV_STREAM_D>, dim3(nwg), dim3(64 * STREAM_WAVES), 0, st, W, q, d, s, M, N, K, out);
-        else
-            launch(gemv_q4k_stream_kernel<2, 2, GEMV_STREAM_D>, dim3(nwg), dim3(64 * STREAM_WAVES), 0, st, W, q, d, s, M, N, K, out);
+        const dim3 grid(nwg), block(64 * STREAM_WAVES);
+        if (K <= 2 * 7 * 256) {
+            if (M == 1)
+                launch(gemv_q4k_stream_kernel<1, 2, GEMV_STREAM_D>, grid, block, 0, st, W, q, d, s, M, N, K, out);
+            else
+                launch(gemv_q4k_stream_kernel<2, 2, GEMV_STREAM_D>, grid, block, 0, st, W, q, d, s, M, N, K, out);
+        } else if (K <= 3 * 7 * 256) {
+            if (M == 1)
+                launch(gemv_q4k_stream_kernel<1, 3, GEMV_STREAM_D>, grid, block, 0, st, W, q, d, s, M, N, K, out);
+            else
+                launch(gemv_q4k_stream_kernel<2, 3, GEMV_STREAM_D>, grid, block, 0, st, W, q, d, s, M, N, K, out);
+        }
+        else {
+            if (M == 1)
+                launch(gemv_q4k_stream_kernel<1, 6, GEMV_STREAM_D>, grid, block, 0, st, W, q, d, s, M, N, K, out);
+            else
+                launch(gemv_q4k_stream_kernel<2, 6, GEMV_STREAM_D>, grid, block, 0, st, W, q, d, s, M, N, K, out);
+        }
         return hipGetLastError();
     }
     if (M <= 1) return gemv_q4k_mt<1>(W, q, d, s, M, N, K, out, st);
@@ -1220,12 +1239,22 @@ hipError_t launch_gemv_q5k(const uint8_t *W, const int8_t *q, const float *d,
                            const float *s, int M, int N, int K, float *out,
                            hipStream_t st)
 {
-    if (M <= 2 && K <= 2 * 8 * 256 && (int64_t)M * K * 5 / 4 <= GEMV_ACT_LDS) {
+    // persistent stream up to 3 passes of 8 blocks (at 4 passes and more the
+    // row-grid kernel measured faster for Q5_K)
+    if (M <= 2 && K <= 3 * 8 * 256 && (int64_t)M * K * 5 / 4 <= GEMV_ACT_LDS) {
         const int nwg = max(1, min((N + GEMV_WAVES - 1) / GEMV_WAVES, GEMV_STREAM_WGS));
-        if (M == 1)
-            launch(gemv_q5k_stream_kernel<1, 2, GEMV_STREAM_D>, dim3(nwg), dim3(64 * GEMV_WAVES), 0, st, W, q, d, s, M, N, K, out);
-        else
-            launch(gemv_q5k_stream_kernel<2, 2, GEMV_STREAM_D>, dim3(nwg), dim3(64 * GEMV_WAVES), 0, st, W, q, d, s, M, N, K, out);
+        const dim3 grid(nwg), block(64 * GEMV_WAVES);
+        if (K <= 2 * 8 * 256) {
+            if (M == 1)
+                launch(gemv_q5k_stream_kernel<1, 2, GEMV_STREAM_D>, grid, block, 0, st, W, q, d, s, M, N, K, out);
+            else
+                launch(gemv_q5k_stream_kernel<2, 2, GEMV_STREAM_D>, grid, block, 0, st, W, q, d, s, M, N, K, out);
+        } else {
+            if (M == 1)
+                launch(gemv_q5k_stream_kernel<1, 3, GEMV_STREAM_D>, grid, block, 0, st, W, q, d, s, M, N, K, out);
+            else
+                launch(gemv_q5k_stream_kernel<2, 3, GEMV_STREAM_D>, grid, block, 0, st, W, q, d, s, M, N, K, out);
+        }
         return hipGetLastError();
     }
     if (M <= 1) return gemv_q5k_mt<1>(W, q, d, s, M, N, K, out, st);

@@ -426,3 +426,19 @@ def test_time_next_kernel(dev):
         assert ms2.value == ms.value
     for e in ev:
         lib.hipEventDestroy(e)
+
+
+# Row lengths served by the persistent stream kernels with 2, 3 and 6 passes
+# per row (Q4_K up to K = 10752, Q5_K up to 6144), one and two tokens, ragged N.
+@pytest.mark.parametrize("fmt,K", [("q4k", 4096), ("q4k", 5120), ("q4k", 8192), ("q4k", 10752),
+                                   ("q5k", 4096), ("q5k", 5120), ("q5k", 6144)])
+@pytest.mark.parametrize("M", [1, 2])
+def test_stream_pass_counts(dev, fmt, K, M):
+    N = 1000 + 7 * (K // 256)
+    rng = np.random.default_rng(K + M + FMT_SEED[fmt])
+    W = synth.weights(fmt, rng, N, K)
+    x = synth.activations(rng, M, K, outliers=True)
+    rq, rd, _ = oracle.quantize_act(x)
+    q, d, s = gpu_plane(x)
+    ref = oracle_mm(fmt, W, rq, rd, N, K)
+    check_close(host(run_matmul(fmt, W, q, d, s, N, K, path=mq.MQ_PATH_GEMV)), ref, f"{fmt} M={M} K={K}")
