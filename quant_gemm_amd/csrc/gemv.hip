@@ -56,7 +56,7 @@ constexpr int STREAM_WAVES = 8;
 // into LDS; the loads for it are issued before the weight loads, so the copy
 // overlaps the weight stream, and the dot products then read activations
 // from LDS instead of making one cache round trip per pass.
-constexpr int GEMV_ACT_LDS = 16 * 1024;
+constexpr int GEMV_ACT_LDS = 32 * 1024;
 
 // Copy the activation plane (q, then d, then s: M*K + 2*M*K/8 bytes, a
 // multiple of 16) into LDS. Loads are issued here; the stores wait for them.
