@@ -13,11 +13,17 @@
  *   - Pointers are device pointers owned by the caller. The calls enqueue
  *     kernels on `stream` (a hipStream_t passed as void*, NULL = the null
  *     stream) and return; nothing synchronizes. Inputs are read-only; outputs
- *     are overwritten. The only allocation is the matmuls' split-K
- *     workspace: when a GEMM has too few output tiles to fill the device it
- *     splits K, takes nsplit*M*N f32 of stream-ordered memory
- *     (hipMallocAsync on `stream`) and returns it (hipFreeAsync) after the
- *     reduction; a failed allocation is MQ_ERR_LAUNCH.
+ *     are overwritten. Two paths use a workspace: a GEMM with too few
+ *     output tiles to fill the device splits K into nsplit*M*N f32 partial
+ *     sums, and the decode FFN (mq_ffn_q4k at M <= 8) keeps g and u in
+ *     2*M*N f32. The workspace is a device buffer the library keeps per
+ *     (device, stream) and reuses; a call that needs more than it holds
+ *     waits for that stream to drain (hipStreamSynchronize), frees it and
+ *     allocates a larger one (hipMalloc, 2 MiB granules). Buffers stay
+ *     allocated until the process ends. A failed allocation is
+ *     MQ_ERR_LAUNCH. Calls from several host threads are safe; calls on one
+ *     stream run in stream order, calls on different streams use different
+ *     buffers.
  *   - Arguments are validated on the host before any HIP call. A failed
  *     check returns a nonzero mq_status and nothing is launched; the
  *     calling thread's mq_last_error() then names the argument and its value.
@@ -186,7 +192,7 @@ int mq_matmul_q6k_ex(const void *W, const int8_t *q, const float *d,
                      float *out, void *stream, int path);
 
 /*
- * Fused FFN up half: the gate and up projections and SwiGLU in one launch,
+ * Fused FFN up half: the gate and up projections and SwiGLU in one call,
  * producing the int8 plane of the down projection's input. The pages fuse
  * the decode FFN as one gate|up matmul with an in-place SwiGLU (FusedFFN,
  * minfer Compute Graph Design, "The Op vocabulary") and have the SwiGLU
@@ -198,9 +204,13 @@ int mq_matmul_q6k_ex(const void *W, const int8_t *q, const float *d,
  *       what mq_quantize_act would write for y);
  *   y  optional f32 [M][N], written when not NULL.
  * Wg and Wu are N rows of K each (Q4_K layout); N is a positive multiple of
- * 256 (it is the down projection's K). M <= 8 runs a fused GEMV, larger
- * M a GEMM whose tiles pair 64 gate rows with the same 64 up
- * rows. Alignment as for the matmuls; qo, do_, so and y 16-byte aligned.
+ * 256 (it is the down projection's K). M > 8 (MQ_PATH_AUTO) runs one GEMM
+ * whose tiles pair 64 gate rows with the same 64 up rows and apply SwiGLU
+ * and the quantizer in their epilogue. M <= 8 runs the decode GEMV: g and u
+ * into a workspace (both matrices as one persistent stream where the plane
+ * fits it), then the SwiGLU quantizer (the workspace is the stream's, see
+ * the conventions above).
+ * Alignment as for the matmuls; qo, do_, so and y 16-byte aligned.
  */
 int mq_ffn_q4k(const void *Wg, const void *Wu, const int8_t *q, const float *d,
                const float *s, int64_t M, int64_t N, int64_t K, int8_t *qo,

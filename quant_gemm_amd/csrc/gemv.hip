@@ -61,21 +61,23 @@ constexpr int GEMV_ACT_LDS = 32 * 1024;
 // Copy the activation plane (q, then d, then s: M*K + 2*M*K/8 bytes, a
 // multiple of 16) into LDS. Loads are issued here; the stores wait for them.
 // WAVES: wavefronts of the workgroup that copies.
-template <int WAVES = GEMV_WAVES>
+// BYTES: the largest plane the copy handles.
+template <int WAVES = GEMV_WAVES, int BYTES = GEMV_ACT_LDS>
 struct ActCopy {
     static constexpr int NT = 64 * WAVES;
-    static constexpr int MAXC = GEMV_ACT_LDS / 16 / NT;  // chunks per thread
+    static constexpr int MAXC = BYTES / 16 / NT;         // chunks per thread
+    static_assert(MAXC * 16 * NT == BYTES, "whole chunks per thread");
     v4i v[MAXC];
 };
 
-template <int WAVES>
-__device__ __forceinline__ void act_load(ActCopy<WAVES> &c, const int8_t *q, const float *d,
+template <int WAVES, int BYTES>
+__device__ __forceinline__ void act_load(ActCopy<WAVES, BYTES> &c, const int8_t *q, const float *d,
                                          const float *s, int M, int K)
 {
     const int qchunks = M * K / 16, dchunks = M * K / 128;
 #pragma unroll
-    for (int i = 0; i < ActCopy<WAVES>::MAXC; ++i) {
-        const int ch = threadIdx.x + i * ActCopy<WAVES>::NT;
+    for (int i = 0; i < ActCopy<WAVES, BYTES>::MAXC; ++i) {
+        const int ch = threadIdx.x + i * ActCopy<WAVES, BYTES>::NT;
         const v4i *src;
         if (ch < qchunks)
             src = reinterpret_cast<const v4i *>(q) + ch;
@@ -87,13 +89,13 @@ __device__ __forceinline__ void act_load(ActCopy<WAVES> &c, const int8_t *q, con
     }
 }
 
-template <int WAVES>
-__device__ __forceinline__ void act_store(const ActCopy<WAVES> &c, v4i *lds, int M, int K)
+template <int WAVES, int BYTES>
+__device__ __forceinline__ void act_store(const ActCopy<WAVES, BYTES> &c, v4i *lds, int M, int K)
 {
     const int nchunks = M * K / 16 + 2 * (M * K / 128);
 #pragma unroll
-    for (int i = 0; i < ActCopy<WAVES>::MAXC; ++i) {
-        const int ch = threadIdx.x + i * ActCopy<WAVES>::NT;
+    for (int i = 0; i < ActCopy<WAVES, BYTES>::MAXC; ++i) {
+        const int ch = threadIdx.x + i * ActCopy<WAVES, BYTES>::NT;
         if (ch < nchunks)
             lds[ch] = c.v[i];
     }
@@ -261,97 +263,6 @@ __global__ __launch_bounds__(64 * GEMV_WAVES) void gemv_q4k_kernel(
     }
 }
 
-// Fused FFN up half at small M: a workgroup owns 32 consecutive output
-// columns n0..n0+31; wavefront w computes the gate and the up rows
-// n0 + 8w .. n0 + 8w + 7 (the same stream as the plain kernel, gate rows then
-// up rows), the 32 x M results meet in LDS, and each 32-lane half of the
-// first wavefront turns one token's 32 values into y = SiLU(g) * u and one
-// quantized block of the down projection's plane.
-constexpr int FFN_ROWS = 32 / GEMV_WAVES;         // rows of each matrix per wavefront
-
-template <int MT, bool ACT_LDS>
-__global__ __launch_bounds__(64 * GEMV_WAVES) void gemv_q4k_ffn_kernel(
-    const uint8_t *__restrict__ Wg, const uint8_t *__restrict__ Wu, const int8_t *__restrict__ q,
-    const float *__restrict__ dx, const float *__restrict__ sx, int M, int N, int K,
-    int8_t *__restrict__ qo, float *__restrict__ do_, float *__restrict__ so, float *__restrict__ y)
-{
-    static_assert(GEMV_WAVES * FFN_ROWS == 32, "one workgroup per 32-value block");
-    __shared__ v4i act[ACT_LDS ? GEMV_ACT_LDS / 16 : 1];
-    __shared__ float res[2][MT][32];
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int n0 = blockIdx.x * 32;
-    const int nb = K >> 8;
-    ActCopy<> ac;
-    if constexpr (ACT_LDS)
-        act_load(ac, q, dx, sx, M, K);
-    const int8_t *qa = q;
-    const float *da = dx, *sa = sx;
-    if constexpr (ACT_LDS) {
-        qa = reinterpret_cast<const int8_t *>(act);
-        da = reinterpret_cast<const float *>(qa + M * K);
-        sa = da + M * (K >> 5);
-    }
-    const int64_t off = (int64_t)(n0 + FFN_ROWS * wave) * nb * 144;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        float acc[FFN_ROWS][MT];
-#pragma unroll
-        for (int r = 0; r < FFN_ROWS; ++r)
-#pragma unroll
-            for (int m = 0; m < MT; ++m)
-                acc[r][m] = 0.0f;
-        q4k_rows<MT, FFN_ROWS, 8>((h == 0 ? Wg : Wu) + off, FFN_ROWS, nb, K, M, qa, da, sa, lane, acc, [&] {
-            if constexpr (ACT_LDS) {
-                if (h == 0) {
-                    act_store(ac, act, M, K);
-                    __syncthreads();
-                }
-            }
-        });
-#pragma unroll
-        for (int r = 0; r < FFN_ROWS; ++r)
-#pragma unroll
-            for (int m = 0; m < MT; ++m) {
-                const float v = wave_sum(acc[r][m]);
-                if (lane == 0)
-                    res[h][m][FFN_ROWS * wave + r] = v;
-            }
-    }
-    __syncthreads();
-    if (wave != 0)
-        return;
-    const int c = lane & 31;
-    for (int m0 = 0; m0 < MT; m0 += 2) {
-        const int m = m0 + (lane >> 5);
-        const bool tok = m < M;
-        const double g64 = (double)res[0][m < MT ? m : 0][c];
-        const float yv = tok ? (float)(g64 / (1.0 + exp(-g64))) * res[1][m < MT ? m : 0][c] : 0.0f;
-        float amax = fabsf(yv);
-#pragma unroll
-        for (int k = 1; k < 32; k <<= 1)
-            amax = fmaxf(amax, __shfl_xor(amax, k, 32));
-        const float db = amax / 127.0f;
-        const bool zero = db == 0.0f;
-        const float t = yv * (zero ? 0.0f : 1.0f / db);
-        const int qi = zero ? 0 : (int)q_clamp_round(db < 0x1p-100f || q_near_half(t) ? yv / db : t);
-        int sum = qi;
-#pragma unroll
-        for (int k = 1; k < 32; k <<= 1)
-            sum += __shfl_xor(sum, k, 32);
-        if (tok) {
-            qo[(int64_t)m * N + n0 + c] = (int8_t)qi;
-            if (y)
-                y[(int64_t)m * N + n0 + c] = yv;
-            if (c == 0) {
-                const int64_t b = (int64_t)m * (N >> 5) + (n0 >> 5);
-                do_[b] = db;
-                so[b] = db * (float)sum;
-            }
-        }
-    }
-}
-
 // Persistent, software-pipelined form of the same stream for short rows
 // (K <= NP * 7 * 256). A fixed grid of wavefronts walks the rows
 // n = w, w + NW, w + 2 NW, ... (NW wavefronts in all, so neighbouring
@@ -361,18 +272,26 @@ __global__ __launch_bounds__(64 * GEMV_WAVES) void gemv_q4k_ffn_kernel(
 // block and masked afterwards; past its last row a wavefront loads nothing
 // (measured on MI355X: one row ahead, without clamped tail loads, is the
 // fastest depth, most of all for short matrices).
+//
+// The N rows may come from two matrices of N1 rows each sharing the
+// activation plane (the gate and up matrices of an FFN): rows n < N1 are
+// row n of W into out, rows n >= N1 row n - N1 of W2 into out2 (both
+// outputs M x N1). A single matrix passes N1 = N.
+constexpr int stream_act_bytes(int MT) { return MT > 4 ? 40 * 1024 : GEMV_ACT_LDS; }
+
 template <int MT, int NP, int D>
 __global__ __launch_bounds__(64 * STREAM_WAVES) void gemv_q4k_stream_kernel(
-    const uint8_t *__restrict__ W, const int8_t *__restrict__ q,
-    const float *__restrict__ dx, const float *__restrict__ sx, int M, int N,
-    int K, float *__restrict__ out)
+    const uint8_t *__restrict__ W, const uint8_t *__restrict__ W2, int N1,
+    const int8_t *__restrict__ q, const float *__restrict__ dx, const float *__restrict__ sx,
+    int M, int N, int K, float *__restrict__ out, float *__restrict__ out2)
 {
-    __shared__ v4i act[GEMV_ACT_LDS / 16];
+    constexpr int AB = stream_act_bytes(MT);
+    __shared__ v4i act[AB / 16];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int nw = gridDim.x * STREAM_WAVES;
     const int w = blockIdx.x * STREAM_WAVES + wave;
-    ActCopy<STREAM_WAVES> ac;
+    ActCopy<STREAM_WAVES, AB> ac;
     act_load(ac, q, dx, sx, M, K);
 
     const int nb = K >> 8;
@@ -393,13 +312,14 @@ __global__ __launch_bounds__(64 * STREAM_WAVES) void gemv_q4k_stream_kernel(
         boff[p] = min(blk, nb - 1) * 144 + 16 * part;
     }
 
+    auto row = [&](int n) { return n < N1 ? W + (int64_t)n * rowb : W2 + (int64_t)(n - N1) * rowb; };
     v4i ring[D][NP];
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-        const int n = min(w + d * nw, N - 1);
+        const uint8_t *r = row(min(w + d * nw, N - 1));
 #pragma unroll
         for (int p = 0; p < NP; ++p)
-            ring[d][p] = __builtin_nontemporal_load(reinterpret_cast<const v4i *>(W + (int64_t)n * rowb + boff[p]));
+            ring[d][p] = __builtin_nontemporal_load(reinterpret_cast<const v4i *>(r + boff[p]));
     }
     act_store(ac, act, M, K);
     __syncthreads();
@@ -472,18 +392,18 @@ __global__ __launch_bounds__(64 * STREAM_WAVES) void gemv_q4k_stream_kernel(
                 // branch: past its last row the wavefront loads nothing, so
                 // the tail does not pile clamped loads onto one row)
                 if (i + D < nrows) {
-                    const int n = w + (i + D) * nw;
+                    const uint8_t *r = row(w + (i + D) * nw);
 #pragma unroll
                     for (int p = 0; p < NP; ++p)
-                        ring[d][p] = __builtin_nontemporal_load(
-                            reinterpret_cast<const v4i *>(W + (int64_t)n * rowb + boff[p]));
+                        ring[d][p] = __builtin_nontemporal_load(reinterpret_cast<const v4i *>(r + boff[p]));
                 }
                 const int n = w + i * nw;
+                float *o = n < N1 ? out + n : out2 + (n - N1);
 #pragma unroll
                 for (int m = 0; m < MT; ++m) {
                     const float v = wave_sum(acc[m]);
                     if (lane == 0 && m < M)
-                        out[(int64_t)m * N + n] = v;
+                        o[(int64_t)m * N1] = v;
                 }
             }
         }
@@ -1196,43 +1116,65 @@ hipError_t gemv_q6k_mt(const uint8_t *W, const int8_t *q, const float *d,
     return gemv_q6k_launch<MT, MT <= 2 ? 4 : 2>(W, q, d, M, N, K, out, st);
 }
 
+// Persistent Q4_K stream over N rows (N1 of them from W, the rest from W2;
+// see gemv_q4k_stream_kernel): up to 1024 workgroups of 8 wavefronts (32 per
+// CU), never more than one wavefront per row; a row is 2, 3 or 6 passes of 7
+// blocks. The caller has checked q4k_stream_fits().
+hipError_t q4k_stream(const uint8_t *W, const uint8_t *W2, int N1, const int8_t *q, const float *d,
+                      const float *s, int M, int N, int K, float *out, float *out2, hipStream_t st)
+{
+    const int nwg = max(1, min((N + STREAM_WAVES - 1) / STREAM_WAVES, GEMV_STREAM_WGS));
+    const dim3 grid(nwg), block(64 * STREAM_WAVES);
+    auto go = [&](auto mt, auto np) {
+        constexpr int MT = decltype(mt)::value, NP = decltype(np)::value;
+        launch(gemv_q4k_stream_kernel<MT, NP, GEMV_STREAM_D>, grid, block, 0, st, W, W2, N1, q, d, s, M, N, K,
+               out, out2);
+    };
+    auto np = [&](auto mt) {
+        if (K <= 2 * 7 * 256) go(mt, std::integral_constant<int, 2>{});
+        else if (K <= 3 * 7 * 256) go(mt, std::integral_constant<int, 3>{});
+        else go(mt, std::integral_constant<int, 6>{});
+    };
+    if (M <= 1) np(std::integral_constant<int, 1>{});
+    else if (M <= 2) np(std::integral_constant<int, 2>{});
+    else if (M <= 4) np(std::integral_constant<int, 4>{});
+    else np(std::integral_constant<int, 8>{});
+    return hipGetLastError();
+}
+
 } // namespace
+
+// The persistent stream takes up to 8 tokens with rows of up to 6 passes
+// whose activation plane fits its LDS copy.
+bool q4k_stream_fits(int64_t M, int64_t K)
+{
+    if (M < 1 || M > 8 || K > GEMV_STREAM_NP_MAX * 7 * 256)
+        return false;
+    return M * K * 5 / 4 <= stream_act_bytes(M <= 4 ? 4 : 8);
+}
 
 hipError_t launch_gemv_q4k(const uint8_t *W, const int8_t *q, const float *d,
                            const float *s, int M, int N, int K, float *out,
                            hipStream_t st)
 {
-    if (M <= 2 && K <= GEMV_STREAM_NP_MAX * 7 * 256 && (int64_t)M * K * 5 / 4 <= GEMV_ACT_LDS) {
-        // persistent stream: up to 1024 workgroups of 8 wavefronts (32 per CU), never
-        // more than one wavefront per row; a row is 2, 3 or 6 passes of 7 blocks
-        // (measured against the row-grid kernel: 13.2 -> 8.3 us at 14336 x 4096,
-        // 12.7 -> 11.3 us at 8192 x 8192; longer rows keep the row-grid kernel)
-        const int nwg = max(1, min((N + STREAM_WAVES - 1) / STREAM_WAVES, GEMV_STREAM_WGS));
-        const dim3 grid(nwg), block(64 * STREAM_WAVES);
-        if (K <= 2 * 7 * 256) {
-            if (M == 1)
-                launch(gemv_q4k_stream_kernel<1, 2, GEMV_STREAM_D>, grid, block, 0, st, W, q, d, s, M, N, K, out);
-            else
-                launch(gemv_q4k_stream_kernel<2, 2, GEMV_STREAM_D>, grid, block, 0, st, W, q, d, s, M, N, K, out);
-        } else if (K <= 3 * 7 * 256) {
-            if (M == 1)
-                launch(gemv_q4k_stream_kernel<1, 3, GEMV_STREAM_D>, grid, block, 0, st, W, q, d, s, M, N, K, out);
-            else
-                launch(gemv_q4k_stream_kernel<2, 3, GEMV_STREAM_D>, grid, block, 0, st, W, q, d, s, M, N, K, out);
-        }
-        else {
-            if (M == 1)
-                launch(gemv_q4k_stream_kernel<1, 6, GEMV_STREAM_D>, grid, block, 0, st, W, q, d, s, M, N, K, out);
-            else
-                launch(gemv_q4k_stream_kernel<2, 6, GEMV_STREAM_D>, grid, block, 0, st, W, q, d, s, M, N, K, out);
-        }
-        return hipGetLastError();
-    }
+    // rows of up to 6 passes with the plane in LDS: the persistent stream
+    // (measured against the row-grid kernel: 13.2 -> 8.3 us at 14336 x 4096,
+    // 12.7 -> 11.3 us at 8192 x 8192; longer rows keep the row-grid kernel)
+    if (q4k_stream_fits(M, K))
+        return q4k_stream(W, W, N, q, d, s, M, N, K, out, out, st);
     if (M <= 1) return gemv_q4k_mt<1>(W, q, d, s, M, N, K, out, st);
     if (M <= 2) return gemv_q4k_mt<2>(W, q, d, s, M, N, K, out, st);
     if (M <= 4) return gemv_q4k_mt<4>(W, q, d, s, M, N, K, out, st);
     if (M <= 8) return gemv_q4k_mt<8>(W, q, d, s, M, N, K, out, st);
     return gemv_q4k_mt<16>(W, q, d, s, M, N, K, out, st);
+}
+
+hipError_t launch_gemv_q4k_pair(const uint8_t *Wg, const uint8_t *Wu, const int8_t *q, const float *d,
+                                const float *s, int M, int N, int K, float *g, float *u, hipStream_t st)
+{
+    if (!q4k_stream_fits(M, K) || (int64_t)2 * N > 0x7fffffff)
+        return hipErrorInvalidValue;
+    return q4k_stream(Wg, Wu, N, q, d, s, M, 2 * N, K, g, u, st);
 }
 
 hipError_t launch_gemv_q5k(const uint8_t *W, const int8_t *q, const float *d,
@@ -1268,20 +1210,28 @@ hipError_t launch_gemv_q4k_ffn(const uint8_t *Wg, const uint8_t *Wu, const int8_
                                const float *s, int M, int N, int K, int8_t *qo, float *do_, float *so,
                                float *y, hipStream_t st)
 {
-    const dim3 grid((unsigned)(N / 32)), block(64 * GEMV_WAVES);
-    const bool lds = (int64_t)M * K * 5 / 4 <= GEMV_ACT_LDS;
-    auto go = [&](auto mt) {
-        constexpr int MT = decltype(mt)::value;
-        if (lds)
-            launch(gemv_q4k_ffn_kernel<MT, true>, grid, block, 0, st, Wg, Wu, q, d, s, M, N, K, qo, do_, so, y);
-        else
-            launch(gemv_q4k_ffn_kernel<MT, false>, grid, block, 0, st, Wg, Wu, q, d, s, M, N, K, qo, do_, so, y);
-    };
-    if (M <= 1) go(std::integral_constant<int, 1>{});
-    else if (M <= 2) go(std::integral_constant<int, 2>{});
-    else if (M <= 4) go(std::integral_constant<int, 4>{});
-    else go(std::integral_constant<int, 8>{});
-    return hipGetLastError();
+    // g and u in the stream's workspace, then the SwiGLU quantizer. Where
+    // the persistent stream takes the plane, both matrices run as one stream
+    // of 2N rows. (A single kernel with the SwiGLU in its epilogue, each
+    // workgroup owning one 32-value block of y, measured slower than these
+    // launches at every M <= 8 on 18944 x 3584: its N / 32 equal work units
+    // leave a tail, and each wavefront streams its rows without the
+    // persistent kernel's pipelining.)
+    WsLease ws((size_t)2 * M * N * sizeof(float), st);
+    if (ws.err != hipSuccess)
+        return ws.err;
+    float *g = static_cast<float *>(ws.ptr), *u = g + (int64_t)M * N;
+    hipError_t e;
+    if (q4k_stream_fits(M, K)) {
+        e = launch_gemv_q4k_pair(Wg, Wu, q, d, s, M, N, K, g, u, st);
+    } else {
+        e = launch_gemv_q4k(Wg, q, d, s, M, N, K, g, st);
+        if (e == hipSuccess)
+            e = launch_gemv_q4k(Wu, q, d, s, M, N, K, u, st);
+    }
+    if (e == hipSuccess)
+        e = launch_swiglu_quantize(g, u, M, N, N, N, qo, do_, so, y, st);
+    return e;
 }
 
 hipError_t launch_gemv_q6k(const uint8_t *W, const int8_t *q, const float *d,

@@ -6,6 +6,9 @@
 #include <hip/hip_ext.h>
 #include <stdint.h>
 
+#include <cstddef>
+#include <mutex>
+
 namespace mq {
 
 // Kernel-boundary timing (mq_time_next_kernel): when a pair of events is set
@@ -42,11 +45,16 @@ constexpr int FFN_GEMV_MAX_M = 8;
 // VALU work per token) while the small-M GEMM's stays near its launch floor
 // (~28 us for Q4_K, ~48 us for Q6_K at K = 18944): Q4_K gains from the GEMV
 // while the matmul is small (M*N*K up to about 2.6e8), Q6_K up to 4 tokens.
+// Where the persistent Q4_K stream takes the tokens (q4k_stream_fits) it
+// keeps the lead up to 8 tokens on the 7B matrices (M = 8 at 18944 x 3584:
+// 25.3 against 30.5 us; at 14336 x 4096: 23.9 against 31.0 us).
+bool q4k_stream_fits(int64_t M, int64_t K);
 inline bool gemv_auto(bool q6, int64_t M, int64_t N, int64_t K)
 {
     if (q6)
         return M <= 4;
-    return M <= 2 || (M <= GEMV_MAX_M && (double)M * (double)N * (double)K <= 2.6e8);
+    const double mnk = (double)M * (double)N * (double)K;
+    return M <= 2 || (q4k_stream_fits(M, K) && mnk <= 5.5e8) || (M <= GEMV_MAX_M && mnk <= 2.6e8);
 }
 // Q5_K: its GEMV keeps the lead over the 32-token GEMM a little longer
 // (M = 4 at 18944 x 3584: 32.7 against 38.0 us).
@@ -98,6 +106,13 @@ hipError_t launch_gemm_q5k_small(const uint8_t *W, const int8_t *q, const float 
 hipError_t launch_gemm_q4k_ffn(const uint8_t *Wg, const uint8_t *Wu, const int8_t *q, const float *d,
                                const float *s, int M, int N, int K, int8_t *qo, float *do_, float *so,
                                float *y, hipStream_t st);
+// The gate and up matrices (N rows each) as one persistent stream of 2N rows
+// over the shared plane: g = x Wg^T, u = x Wu^T (each M x N). Needs
+// q4k_stream_fits(M, K) (else hipErrorInvalidValue).
+// q4k_stream_fits(M, K): the persistent Q4_K stream takes M tokens at row
+// length K.
+hipError_t launch_gemv_q4k_pair(const uint8_t *Wg, const uint8_t *Wu, const int8_t *q, const float *d,
+                                const float *s, int M, int N, int K, float *g, float *u, hipStream_t st);
 hipError_t launch_gemv_q4k_ffn(const uint8_t *Wg, const uint8_t *Wu, const int8_t *q, const float *d,
                                const float *s, int M, int N, int K, int8_t *qo, float *do_, float *so,
                                float *y, hipStream_t st);
@@ -131,23 +146,42 @@ int gemm_splits(int tiles, int tile_elems, int pairs, int64_t M, int64_t N, int 
 // out[i] = sum over s = 0..nsplit-1, in that order, of part[s * n + i].
 hipError_t splitk_reduce(const float *part, int nsplit, int64_t n, float *out, hipStream_t st);
 
+// Workspace for the kernels a call enqueues on stream st: a device buffer
+// the library keeps per (device, stream), grown with hipMalloc when a call
+// needs more (the old one freed after st drains) and reused otherwise, so a
+// call costs no allocation. Calls on one stream run in order, so they share
+// it; other streams get their own. The lease holds a library-wide lock: keep
+// it until every kernel that reads or writes the buffer is enqueued, so that
+// no other thread grows (frees) it in between. (A stream-ordered
+// hipMallocAsync / hipFreeAsync pair per call was measured instead:
+// hipFreeAsync blocked the host until the stream drained, 0.34 ms per call
+// behind queued work.) Buffers stay allocated until the process ends.
+class WsLease {
+  public:
+    WsLease(size_t bytes, hipStream_t st);
+    void *ptr = nullptr;
+    hipError_t err = hipSuccess;
+
+  private:
+    std::unique_lock<std::mutex> lock_;
+};
+
 // Runs launch(dst) once: with dst = out when nsplit == 1, else with dst a
-// workspace of nsplit [M][N] f32 planes (n = M*N elements each), allocated and
-// freed in stream order on st, followed by the reduction into out.
+// workspace of nsplit [M][N] f32 planes (n = M*N elements each) leased on st,
+// followed by the reduction into out.
 template <class Launch>
 hipError_t run_split_k(int nsplit, int64_t n, float *out, hipStream_t st, Launch &&launch)
 {
     if (nsplit <= 1)
         return launch(out);
-    float *part = nullptr;
-    hipError_t e = hipMallocAsync(reinterpret_cast<void **>(&part), (size_t)nsplit * (size_t)n * sizeof(float), st);
-    if (e != hipSuccess)
-        return e;
-    e = launch(part);
+    WsLease ws((size_t)nsplit * (size_t)n * sizeof(float), st);
+    if (ws.err != hipSuccess)
+        return ws.err;
+    float *part = static_cast<float *>(ws.ptr);
+    hipError_t e = launch(part);
     if (e == hipSuccess)
         e = splitk_reduce(part, nsplit, n, out, st);
-    const hipError_t f = hipFreeAsync(part, st);
-    return e != hipSuccess ? e : f;
+    return e;
 }
 
 } // namespace mq

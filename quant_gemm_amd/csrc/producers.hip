@@ -158,10 +158,9 @@ __global__ __launch_bounds__(RMS_THREADS) void rmsnorm_quantize_kernel(
 // ---------------------------------------------------------------- SwiGLU
 // A workgroup covers SW_ITEMS * 1024 consecutive values of one token row
 // (SW_ITEMS float4 per thread, 8 threads per 32-value block), all loads
-// issued first.
-constexpr int SW_ITEMS = 4;
-
-template <bool Y>
+// issued first. A few tokens take one float4 per thread, which spreads a
+// decode row over 4x the workgroups (the f64 SiLU is the long pole there).
+template <int SW_ITEMS, bool Y>
 __global__ __launch_bounds__(256) void swiglu_quantize_kernel(
     const float *__restrict__ g, const float *__restrict__ u, int K, int chunks, int64_t ldg,
     int64_t ldu, int8_t *__restrict__ q, float *__restrict__ d, float *__restrict__ s,
@@ -240,12 +239,19 @@ hipError_t launch_rmsnorm_quantize(const float *x, const float *w, int64_t M, in
 hipError_t launch_swiglu_quantize(const float *g, const float *u, int64_t M, int64_t K, int64_t ldg,
                                   int64_t ldu, int8_t *q, float *d, float *s, float *y, hipStream_t st)
 {
-    const int chunks = (int)((K + SW_ITEMS * 1024 - 1) / (SW_ITEMS * 1024));
-    const dim3 grid((unsigned)(M * chunks)), block(256);
-    if (y)
-        swiglu_quantize_kernel<true><<<grid, block, 0, st>>>(g, u, (int)K, chunks, ldg, ldu, q, d, s, y);
+    auto go = [&](auto it) {
+        constexpr int IT = decltype(it)::value;
+        const int chunks = (int)((K + IT * 1024 - 1) / (IT * 1024));
+        const dim3 grid((unsigned)(M * chunks)), block(256);
+        if (y)
+            swiglu_quantize_kernel<IT, true><<<grid, block, 0, st>>>(g, u, (int)K, chunks, ldg, ldu, q, d, s, y);
+        else
+            swiglu_quantize_kernel<IT, false><<<grid, block, 0, st>>>(g, u, (int)K, chunks, ldg, ldu, q, d, s, y);
+    };
+    if (M * ((K + 4095) / 4096) < 256)
+        go(std::integral_constant<int, 1>{});
     else
-        swiglu_quantize_kernel<false><<<grid, block, 0, st>>>(g, u, (int)K, chunks, ldg, ldu, q, d, s, y);
+        go(std::integral_constant<int, 4>{});
     return hipGetLastError();
 }
 

@@ -9,6 +9,10 @@
 // result does not depend on scheduling.
 #include <atomic>
 #include <cmath>
+#include <cstdint>
+#include <map>
+#include <mutex>
+#include <utility>
 
 #include "mq_device.h"
 #include "mq_launch.h"
@@ -42,6 +46,38 @@ __global__ __launch_bounds__(256) void splitk_reduce4_kernel(const v4f *__restri
 }
 
 } // namespace
+
+WsLease::WsLease(size_t bytes, hipStream_t st)
+{
+    static std::mutex mu;
+    static std::map<std::pair<int, hipStream_t>, std::pair<void *, size_t>> bufs;
+    lock_ = std::unique_lock<std::mutex>(mu);
+    int dev = 0;
+    err = hipGetDevice(&dev);
+    if (err != hipSuccess)
+        return;
+    auto &slot = bufs[{dev, st}];
+    if (slot.second < bytes) {
+        if (slot.first) {
+            // the old buffer's last reader is on st
+            err = hipStreamSynchronize(st);
+            if (err != hipSuccess)
+                return;
+            err = hipFree(slot.first);
+            slot = {nullptr, 0};
+            if (err != hipSuccess)
+                return;
+        }
+        const size_t grain = size_t(2) << 20;
+        const size_t size = (bytes + grain - 1) / grain * grain;
+        void *p = nullptr;
+        err = hipMalloc(&p, size);
+        if (err != hipSuccess)
+            return;
+        slot = {p, size};
+    }
+    ptr = slot.first;
+}
 
 int device_cu_count()
 {

@@ -161,6 +161,37 @@ def test_split_k_shapes(dev, fmt, M, N, K):
     assert np.array_equal(got, again), "split-K result must not depend on scheduling"
 
 
+def test_workspace_reuse_across_streams(dev):
+    """Split-K GEMMs keep their partial sums in the stream's workspace, which
+    grows when a call needs more: calls queued back to back on two streams
+    (no host synchronization in between), small, large and small again,
+    give the bits the same calls give one at a time."""
+    import torch
+    cases = []
+    for fmt, M, N, K in [("q4k", 40, 130, 6912), ("q6k", 300, 700, 4608), ("q4k", 64, 2000, 3584),
+                         ("q6k", 17, 257, 2560)]:
+        rng = np.random.default_rng(M * 7919 + N + K)
+        W = synth.weights(fmt, rng, N, K)
+        q, d, s = gpu_plane(synth.activations(rng, M, K, outliers=True))
+        cases.append((fmt, to_dev(W.reshape(-1)), q, d, s, N, K))
+    mm = {"q4k": lambda W, q, d, s, N, K, st: mq.matmul_q4k(W, q, d, s, N, K, stream=st, path=mq.MQ_PATH_GEMM),
+          "q6k": lambda W, q, d, s, N, K, st: mq.matmul_q6k(W, q, d, s, N, K, stream=st, path=mq.MQ_PATH_GEMM)}
+    ref = [host(mm[c[0]](*c[1:], None)) for c in cases]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for rep in range(3):
+        for i, c in enumerate(cases):
+            if (rep + i) % 2:
+                with torch.cuda.stream(side):
+                    outs.append((i, mm[c[0]](*c[1:], side)))
+            else:
+                outs.append((i, mm[c[0]](*c[1:], None)))
+    torch.cuda.synchronize()
+    for i, o in outs:
+        assert np.array_equal(o.cpu().numpy(), ref[i]), f"case {i}: queued result differs"
+
+
 # The small-M band: token counts around the switches between the GEMV, the
 # GEMM's 32-token tiles and its 128-token tiles, for every path.
 @pytest.mark.parametrize("fmt", ["q4k", "q5k", "q6k"])
@@ -429,10 +460,12 @@ def test_time_next_kernel(dev):
 
 
 # Row lengths served by the persistent stream kernels with 2, 3 and 6 passes
-# per row (Q4_K up to K = 10752, Q5_K up to 6144), one and two tokens, ragged N.
+# per row (Q4_K up to K = 10752, Q5_K up to 6144), ragged N. Q4_K streams up
+# to 8 tokens while the plane fits its LDS copy (M = 4 at K <= 5120, M = 7 at
+# K = 4096); Q5_K up to 2; the other cases run the row-grid kernels.
 @pytest.mark.parametrize("fmt,K", [("q4k", 4096), ("q4k", 5120), ("q4k", 8192), ("q4k", 10752),
                                    ("q5k", 4096), ("q5k", 5120), ("q5k", 6144)])
-@pytest.mark.parametrize("M", [1, 2])
+@pytest.mark.parametrize("M", [1, 2, 4, 7])
 def test_stream_pass_counts(dev, fmt, K, M):
     N = 1000 + 7 * (K // 256)
     rng = np.random.default_rng(K + M + FMT_SEED[fmt])

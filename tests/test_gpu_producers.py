@@ -143,7 +143,12 @@ def test_swiglu_quantize_edge_values(dev):
 
 # ---------------------------------------------------------------- fused FFN up half
 
+# Decode sizes whose plane fits the persistent stream run gate and up as one
+# stream plus the SwiGLU quantizer; longer rows (K > 10752) and larger planes
+# run the single fused kernel, with (K = 11008, M = 2) and without
+# (K = 12288, M = 4) its LDS copy of the plane.
 FFN_CASES = [(1, 256, 1024, (1, 2)), (3, 512, 3584, (1, 2)), (8, 768, 2048, (1, 2)),
+             (8, 512, 3584, (1,)), (2, 512, 11008, (1,)), (4, 256, 12288, (1,)),
              (9, 256, 1024, (2,)), (130, 512, 3584, (2,)), (1, 18944, 3584, (1,)),
              (3314, 18944, 3584, (2,))]
 
