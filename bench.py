@@ -325,24 +325,46 @@ def run_all(args):
     run_planes(dev)
 
 
+_BUSY = []
+
+
 def _time_rotating(fn, copies, reps):
+    """GPU time per call (us) of reps calls over `copies` rotating inputs.
+
+    The calls are queued behind ~15 ms of f32 matmul, so the events bracket
+    GPU work only: back to back from Python, each call's host cost (~8.5 us
+    of ctypes marshalling and checks) would bound the small decode kernels.
+    """
+    import time
     import torch
+    if not _BUSY:
+        _BUSY.append(torch.randn(8192, 8192, device="cuda"))
+    a = _BUSY[0]
     for i in range(3):
         fn(i % copies)
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
+    b0 = torch.cuda.Event(enable_timing=True)
+    b0.record()
+    torch.mm(a, a)
+    torch.mm(a, a)
     e0.record()
+    t0 = time.perf_counter()
     for i in range(reps):
         fn(i % copies)
+    host_ms = (time.perf_counter() - t0) * 1e3
     e1.record()
     torch.cuda.synchronize()
+    if host_ms > 0.8 * b0.elapsed_time(e0):
+        log(f"[bench] warning: enqueueing {reps} calls took {host_ms:.1f} ms, about the busy "
+            f"period ({b0.elapsed_time(e0):.1f} ms): the time may include host cost")
     return e0.elapsed_time(e1) * 1e3 / reps
 
 
 def run_ffn(dev):
-    """Fused FFN up half (gate and up matmuls + SwiGLU + plane in one launch)
-    against the separate launches (two matmuls, then mq_swiglu_quantize).
+    """Fused FFN up half (gate and up matmuls + SwiGLU + plane in one call)
+    against the separate calls (two matmuls, then mq_swiglu_quantize).
     Weights rotate through >= 1 GiB of copies at M = 1."""
     import numpy as np
     import torch
@@ -350,7 +372,8 @@ def run_ffn(dev):
     import quant_gemm_amd as mq
     from quant_gemm_amd import synth
 
-    for grp, M, N, K in (("ffn", 1, 18944, 3584), ("ffn", 3314, 18944, 3584)):
+    for grp, M, N, K in (("ffn", 1, 18944, 3584), ("ffn", 4, 18944, 3584), ("ffn", 8, 18944, 3584),
+                         ("ffn", 3314, 18944, 3584)):
         rng = np.random.default_rng(3000 + M)
         Wg0 = torch.from_numpy(synth.q4k_weights(rng, N, K).reshape(-1)).to(dev)
         Wu0 = torch.from_numpy(synth.q4k_weights(rng, N, K).reshape(-1)).to(dev)

@@ -204,12 +204,14 @@ int mq_matmul_q6k_ex(const void *W, const int8_t *q, const float *d,
  *       what mq_quantize_act would write for y);
  *   y  optional f32 [M][N], written when not NULL.
  * Wg and Wu are N rows of K each (Q4_K layout); N is a positive multiple of
- * 256 (it is the down projection's K). M > 8 (MQ_PATH_AUTO) runs one GEMM
- * whose tiles pair 64 gate rows with the same 64 up rows and apply SwiGLU
- * and the quantizer in their epilogue. M <= 8 runs the decode GEMV: g and u
- * into a workspace (both matrices as one persistent stream where the plane
- * fits it), then the SwiGLU quantizer (the workspace is the stream's, see
- * the conventions above).
+ * 256 (it is the down projection's K). Above 128 tokens one GEMM launch
+ * does it all: its tiles pair 64 gate rows with the same 64 up rows and
+ * apply SwiGLU and the quantizer in their epilogue. Up to 128 tokens it
+ * runs in two passes: g and u into the stream's workspace (see the
+ * conventions above), then the SwiGLU quantizer. The first pass is the
+ * GEMV up to 8 tokens under MQ_PATH_AUTO (both matrices as one persistent
+ * stream where the plane fits it) and the GEMMs above; MQ_PATH_GEMV forces
+ * the GEMV (M <= 8), MQ_PATH_GEMM the GEMMs.
  * Alignment as for the matmuls; qo, do_, so and y 16-byte aligned.
  */
 int mq_ffn_q4k(const void *Wg, const void *Wu, const int8_t *q, const float *d,

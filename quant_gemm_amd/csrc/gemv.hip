@@ -597,12 +597,13 @@ __global__ __launch_bounds__(64 * GEMV_WAVES) void gemv_q5k_stream_kernel(
     const float *__restrict__ dx, const float *__restrict__ sx, int M, int N,
     int K, float *__restrict__ out)
 {
-    __shared__ v4i act[GEMV_ACT_LDS / 16];
+    constexpr int AB = stream_act_bytes(MT);
+    __shared__ v4i act[AB / 16];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int nw = gridDim.x * GEMV_WAVES;
     const int w = blockIdx.x * GEMV_WAVES + wave;
-    ActCopy<> ac;
+    ActCopy<GEMV_WAVES, AB> ac;
     act_load(ac, q, dx, sx, M, K);
 
     const int nb = K >> 8;
@@ -857,7 +858,7 @@ static_assert(Q6S_SEG * 210 + 16 <= Q6S_SLOT, "segment fits a slot");
 
 // LDS bytes of the staged activation plane of M tokens: int8 values, f32
 // per-32 scales, int16 per-16 sums.
-__host__ __device__ constexpr int q6s_act_bytes(int M, int K)
+__host__ __device__ constexpr int64_t q6s_act_bytes(int64_t M, int64_t K)
 {
     return M * K + M * (K / 32) * 4 + M * (K / 16) * 2;
 }
@@ -1144,11 +1145,24 @@ hipError_t q4k_stream(const uint8_t *W, const uint8_t *W2, int N1, const int8_t 
 
 } // namespace
 
-// The persistent stream takes up to 8 tokens with rows of up to 6 passes
-// whose activation plane fits its LDS copy.
+// The persistent streams take up to 8 tokens whose activation plane fits
+// their LDS copy, with rows of up to 6 passes of 7 blocks (Q4_K) or 3 of 8
+// (Q5_K).
 bool q4k_stream_fits(int64_t M, int64_t K)
 {
     if (M < 1 || M > 8 || K > GEMV_STREAM_NP_MAX * 7 * 256)
+        return false;
+    return M * K * 5 / 4 <= stream_act_bytes(M <= 4 ? 4 : 8);
+}
+
+bool q6k_stream_fits(int64_t M, int64_t K)
+{
+    return M >= 1 && M <= 16 && K >= 256 && q6s_act_bytes(M, K) <= Q6S_ACT_MAX;
+}
+
+bool q5k_stream_fits(int64_t M, int64_t K)
+{
+    if (M < 1 || M > 8 || K > 3 * 8 * 256)
         return false;
     return M * K * 5 / 4 <= stream_act_bytes(M <= 4 ? 4 : 8);
 }
@@ -1182,21 +1196,22 @@ hipError_t launch_gemv_q5k(const uint8_t *W, const int8_t *q, const float *d,
                            hipStream_t st)
 {
     // persistent stream up to 3 passes of 8 blocks (at 4 passes and more the
-    // row-grid kernel measured faster for Q5_K)
-    if (M <= 2 && K <= 3 * 8 * 256 && (int64_t)M * K * 5 / 4 <= GEMV_ACT_LDS) {
+    // row-grid kernel measured faster for Q5_K) and 8 tokens whose plane fits
+    // the LDS copy
+    if (q5k_stream_fits(M, K)) {
         const int nwg = max(1, min((N + GEMV_WAVES - 1) / GEMV_WAVES, GEMV_STREAM_WGS));
         const dim3 grid(nwg), block(64 * GEMV_WAVES);
-        if (K <= 2 * 8 * 256) {
-            if (M == 1)
-                launch(gemv_q5k_stream_kernel<1, 2, GEMV_STREAM_D>, grid, block, 0, st, W, q, d, s, M, N, K, out);
+        auto go = [&](auto mt) {
+            constexpr int MT = decltype(mt)::value;
+            if (K <= 2 * 8 * 256)
+                launch(gemv_q5k_stream_kernel<MT, 2, GEMV_STREAM_D>, grid, block, 0, st, W, q, d, s, M, N, K, out);
             else
-                launch(gemv_q5k_stream_kernel<2, 2, GEMV_STREAM_D>, grid, block, 0, st, W, q, d, s, M, N, K, out);
-        } else {
-            if (M == 1)
-                launch(gemv_q5k_stream_kernel<1, 3, GEMV_STREAM_D>, grid, block, 0, st, W, q, d, s, M, N, K, out);
-            else
-                launch(gemv_q5k_stream_kernel<2, 3, GEMV_STREAM_D>, grid, block, 0, st, W, q, d, s, M, N, K, out);
-        }
+                launch(gemv_q5k_stream_kernel<MT, 3, GEMV_STREAM_D>, grid, block, 0, st, W, q, d, s, M, N, K, out);
+        };
+        if (M <= 1) go(std::integral_constant<int, 1>{});
+        else if (M <= 2) go(std::integral_constant<int, 2>{});
+        else if (M <= 4) go(std::integral_constant<int, 4>{});
+        else go(std::integral_constant<int, 8>{});
         return hipGetLastError();
     }
     if (M <= 1) return gemv_q5k_mt<1>(W, q, d, s, M, N, K, out, st);
@@ -1206,28 +1221,34 @@ hipError_t launch_gemv_q5k(const uint8_t *W, const int8_t *q, const float *d,
     return gemv_q5k_mt<16>(W, q, d, s, M, N, K, out, st);
 }
 
-hipError_t launch_gemv_q4k_ffn(const uint8_t *Wg, const uint8_t *Wu, const int8_t *q, const float *d,
-                               const float *s, int M, int N, int K, int8_t *qo, float *do_, float *so,
-                               float *y, hipStream_t st)
+hipError_t launch_ffn_q4k_two_pass(const uint8_t *Wg, const uint8_t *Wu, const int8_t *q, const float *d,
+                                   const float *s, int M, int N, int K, int8_t *qo, float *do_, float *so,
+                                   float *y, bool gemv, hipStream_t st)
 {
-    // g and u in the stream's workspace, then the SwiGLU quantizer. Where
-    // the persistent stream takes the plane, both matrices run as one stream
-    // of 2N rows. (A single kernel with the SwiGLU in its epilogue, each
-    // workgroup owning one 32-value block of y, measured slower than these
-    // launches at every M <= 8 on 18944 x 3584: its N / 32 equal work units
-    // leave a tail, and each wavefront streams its rows without the
-    // persistent kernel's pipelining.)
-    WsLease ws((size_t)2 * M * N * sizeof(float), st);
+    // Where the persistent stream takes the plane, both matrices run as one
+    // stream of 2N rows. (A single GEMV kernel with the SwiGLU in its
+    // epilogue, each workgroup owning one 32-value block of y, measured
+    // slower than these launches at every M <= 8 on 18944 x 3584: its N / 32
+    // equal work units leave a tail, and each wavefront streams its rows
+    // without the persistent kernel's pipelining.)
+    WsLease ws((size_t)2 * M * N * sizeof(float), st, WS_FFN);
     if (ws.err != hipSuccess)
         return ws.err;
     float *g = static_cast<float *>(ws.ptr), *u = g + (int64_t)M * N;
     hipError_t e;
-    if (q4k_stream_fits(M, K)) {
+    if (gemv && q4k_stream_fits(M, K)) {
         e = launch_gemv_q4k_pair(Wg, Wu, q, d, s, M, N, K, g, u, st);
     } else {
-        e = launch_gemv_q4k(Wg, q, d, s, M, N, K, g, st);
+        auto mm = [&](const uint8_t *W, float *o) {
+            if (gemv)
+                return launch_gemv_q4k(W, q, d, s, M, N, K, o, st);
+            if (M <= GEMM_SMALL_M_Q4K)
+                return launch_gemm_q4k_small(W, q, d, s, M, N, K, o, st);
+            return launch_gemm_q4k(W, q, d, s, M, N, K, o, st);
+        };
+        e = mm(Wg, g);
         if (e == hipSuccess)
-            e = launch_gemv_q4k(Wu, q, d, s, M, N, K, u, st);
+            e = mm(Wu, u);
     }
     if (e == hipSuccess)
         e = launch_swiglu_quantize(g, u, M, N, N, N, qo, do_, so, y, st);

@@ -228,8 +228,10 @@ int ffn(const void *Wg, const void *Wu, const int8_t *q, const float *d, const f
     const auto *Wgb = static_cast<const uint8_t *>(Wg);
     const auto *Wub = static_cast<const uint8_t *>(Wu);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const hipError_t e = gemv ? mq::launch_gemv_q4k_ffn(Wgb, Wub, q, d, s, (int)M, (int)N, (int)K, qo, do_, so, y, st)
-                              : mq::launch_gemm_q4k_ffn(Wgb, Wub, q, d, s, (int)M, (int)N, (int)K, qo, do_, so, y, st);
+    const hipError_t e =
+        gemv || M <= FFN_TWO_PASS_MAX_M
+            ? mq::launch_ffn_q4k_two_pass(Wgb, Wub, q, d, s, (int)M, (int)N, (int)K, qo, do_, so, y, gemv, st)
+            : mq::launch_gemm_q4k_ffn(Wgb, Wub, q, d, s, (int)M, (int)N, (int)K, qo, do_, so, y, st);
     return launched(e, fn);
 }
 

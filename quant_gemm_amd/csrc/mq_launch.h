@@ -40,34 +40,57 @@ inline void launch(F kernel, dim3 grid, dim3 block, uint32_t lds, hipStream_t st
 // FFN GEMV's.
 constexpr int GEMV_MAX_M = 16;
 constexpr int FFN_GEMV_MAX_M = 8;
-// MQ_PATH_AUTO: GEMV or GEMM, at the crossovers measured on MI355X (weights
-// streamed from HBM). The GEMV's cost grows with M (its dot products are
-// VALU work per token) while the small-M GEMM's stays near its launch floor
-// (~28 us for Q4_K, ~48 us for Q6_K at K = 18944): Q4_K gains from the GEMV
-// while the matmul is small (M*N*K up to about 2.6e8), Q6_K up to 4 tokens.
-// Where the persistent Q4_K stream takes the tokens (q4k_stream_fits) it
-// keeps the lead up to 8 tokens on the 7B matrices (M = 8 at 18944 x 3584:
-// 25.3 against 30.5 us; at 14336 x 4096: 23.9 against 31.0 us).
+// MQ_PATH_AUTO: GEMV or GEMM, at the crossovers measured on MI355X (GPU time
+// per call, weights streamed from HBM). The GEMV's cost grows with M (its dot
+// products are VALU work per token) while the 32-token GEMM stays near its
+// floor (16-25 us for Q4_K at K = 3584..8192). Where the persistent stream
+// takes the tokens (q4k_stream_fits / q5k_stream_fits) the GEMV keeps the lead
+// while M*N*K stays below about 4.2e8 for Q4_K (at 18944 x 3584: M = 6 20.7
+// against 24.7 us, M = 8 a tie; at 14336 x 4096, M = 8: 23.4 against 21.3)
+// and through 8 tokens of the 7B shapes for Q5_K (18944 x 3584, M = 8: 23.3
+// against 30.3 us). Otherwise the row-grid GEMV serves while M*N*K <= 2.6e8
+// (Q4_K; 8192 x 8192, M = 4: 28.9 against 24.1 us) or 3.3e8 (Q5_K, whose
+// GEMM is slower: M = 4 26.4 against 28.2 us). Q6_K runs the GEMV for
+// M <= 4, and up to 8 tokens where its LDS ring kernel takes the plane while
+// M*N*K <= 5.5e8 (18944 x 3584, M = 8: 33.5 against 42.5 us; the down
+// projection's K = 18944 leaves the ring kernel at M = 2, and its register
+// kernel loses from M = 6: 55.2 against 46.4 us).
 bool q4k_stream_fits(int64_t M, int64_t K);
+bool q5k_stream_fits(int64_t M, int64_t K);
+bool q6k_stream_fits(int64_t M, int64_t K);
 inline bool gemv_auto(bool q6, int64_t M, int64_t N, int64_t K)
 {
-    if (q6)
-        return M <= 4;
     const double mnk = (double)M * (double)N * (double)K;
-    return M <= 2 || (q4k_stream_fits(M, K) && mnk <= 5.5e8) || (M <= GEMV_MAX_M && mnk <= 2.6e8);
+    if (q6)
+        return M <= 4 || (M <= 8 && q6k_stream_fits(M, K) && mnk <= 5.5e8);
+    return M <= 2 || (q4k_stream_fits(M, K) && mnk <= 4.2e8) || (M <= GEMV_MAX_M && mnk <= 2.6e8);
 }
-// Q5_K: its GEMV keeps the lead over the 32-token GEMM a little longer
-// (M = 4 at 18944 x 3584: 32.7 against 38.0 us).
 inline bool gemv_auto_q5k(int64_t M, int64_t N, int64_t K)
 {
-    return M <= 2 || (M <= GEMV_MAX_M && (double)M * (double)N * (double)K <= 3.3e8);
+    const double mnk = (double)M * (double)N * (double)K;
+    return M <= 2 || (q5k_stream_fits(M, K) && mnk <= 5.5e8) || (M <= GEMV_MAX_M && mnk <= 3.3e8);
 }
 constexpr int FFN_AUTO_M = 8;
+// Above FFN_AUTO_M the FFN runs its two GEMMs and the SwiGLU quantizer as
+// separate passes up to this token count, and the one-launch GEMM beyond.
+// GPU time at 18944 x 3584: the one-launch GEMM's 128-token tiles cost about
+// the same from 9 to 128 tokens (112-118 us); two passes took 51.5 us at
+// M = 9, 80.1 at 64, 113.7 at 128; at 192 they were even (193 against 195)
+// and at 256 and 3314 the one-launch GEMM was as fast or faster (197
+// against 203, 1859 both) and keeps g and u out of memory.
+#ifndef FFN_TWO_PASS_MAX_M
+#define FFN_TWO_PASS_MAX_M 128
+#endif
 // The GEMMs run their small-M configuration (32-token tiles) up to these
-// token counts, measured crossovers against the 128-token tiles.
-constexpr int GEMM_SMALL_M_Q4K = 96;
+// token counts: crossovers against the 128-token tiles by GPU time per call.
+// Q4_K 18944 x 3584: M = 64 35.8 against 47.6 us, M = 80 56.2 against 49.0;
+// Q5_K: M = 64 49.2 against 58.0, M = 80 63.0 against 59.3; Q6_K 3584 x
+// 18944: M = 32 42.8 against 70.3, M = 48 72.6 against 71.2. (Rows of 3584
+// favour the small tiles longer: Q4_K 3584 x 3584 at M = 128 23.4 against
+// 25.0 us.)
+constexpr int GEMM_SMALL_M_Q4K = 64;
 constexpr int GEMM_SMALL_M_Q6K = 32;
-constexpr int GEMM_SMALL_M_Q5K = 96;
+constexpr int GEMM_SMALL_M_Q5K = 64;
 
 hipError_t launch_quantize(const float *x, int64_t M, int64_t K, int64_t ldx,
                            int8_t *q, float *d, float *s, hipStream_t st);
@@ -113,9 +136,12 @@ hipError_t launch_gemm_q4k_ffn(const uint8_t *Wg, const uint8_t *Wu, const int8_
 // length K.
 hipError_t launch_gemv_q4k_pair(const uint8_t *Wg, const uint8_t *Wu, const int8_t *q, const float *d,
                                 const float *s, int M, int N, int K, float *g, float *u, hipStream_t st);
-hipError_t launch_gemv_q4k_ffn(const uint8_t *Wg, const uint8_t *Wu, const int8_t *q, const float *d,
-                               const float *s, int M, int N, int K, int8_t *qo, float *do_, float *so,
-                               float *y, hipStream_t st);
+// FFN up half in two passes: g and u into the stream's workspace (the GEMV
+// when gemv is set, else the GEMM of the token count), then the SwiGLU
+// quantizer. launch_gemm_q4k_ffn is the one-launch GEMM form.
+hipError_t launch_ffn_q4k_two_pass(const uint8_t *Wg, const uint8_t *Wu, const int8_t *q, const float *d,
+                                   const float *s, int M, int N, int K, int8_t *qo, float *do_, float *so,
+                                   float *y, bool gemv, hipStream_t st);
 hipError_t launch_gemm_q6k(const uint8_t *W, const int8_t *q, const float *d,
                            int M, int N, int K, float *out, hipStream_t st);
 
@@ -147,23 +173,28 @@ int gemm_splits(int tiles, int tile_elems, int pairs, int64_t M, int64_t N, int 
 hipError_t splitk_reduce(const float *part, int nsplit, int64_t n, float *out, hipStream_t st);
 
 // Workspace for the kernels a call enqueues on stream st: a device buffer
-// the library keeps per (device, stream), grown with hipMalloc when a call
-// needs more (the old one freed after st drains) and reused otherwise, so a
-// call costs no allocation. Calls on one stream run in order, so they share
-// it; other streams get their own. The lease holds a library-wide lock: keep
-// it until every kernel that reads or writes the buffer is enqueued, so that
-// no other thread grows (frees) it in between. (A stream-ordered
-// hipMallocAsync / hipFreeAsync pair per call was measured instead:
-// hipFreeAsync blocked the host until the stream drained, 0.34 ms per call
-// behind queued work.) Buffers stay allocated until the process ends.
+// the library keeps per (device, stream, role), grown with hipMalloc when a
+// call needs more (the old one freed after st drains) and reused otherwise,
+// so a call costs no allocation. Calls on one stream run in order, so they
+// share it; other streams get their own. Roles keep leases that nest apart
+// (the FFN's g | u buffer, role WS_FFN, around the split-K partial sums of
+// the GEMMs it runs, role WS_SPLIT_K). The lease holds a library-wide
+// (recursive) lock: keep it until every kernel that reads or writes the
+// buffer is enqueued, so that no other thread grows (frees) it in between.
+// (A stream-ordered hipMallocAsync / hipFreeAsync pair per call was measured
+// instead: hipFreeAsync blocked the host until the stream drained, 0.34 ms
+// per call behind queued work.) Buffers stay allocated until the process
+// ends.
+constexpr int WS_SPLIT_K = 0;
+constexpr int WS_FFN = 1;
 class WsLease {
   public:
-    WsLease(size_t bytes, hipStream_t st);
+    WsLease(size_t bytes, hipStream_t st, int role);
     void *ptr = nullptr;
     hipError_t err = hipSuccess;
 
   private:
-    std::unique_lock<std::mutex> lock_;
+    std::unique_lock<std::recursive_mutex> lock_;
 };
 
 // Runs launch(dst) once: with dst = out when nsplit == 1, else with dst a
@@ -174,7 +205,7 @@ hipError_t run_split_k(int nsplit, int64_t n, float *out, hipStream_t st, Launch
 {
     if (nsplit <= 1)
         return launch(out);
-    WsLease ws((size_t)nsplit * (size_t)n * sizeof(float), st);
+    WsLease ws((size_t)nsplit * (size_t)n * sizeof(float), st, WS_SPLIT_K);
     if (ws.err != hipSuccess)
         return ws.err;
     float *part = static_cast<float *>(ws.ptr);

@@ -12,6 +12,7 @@
 #include <cstdint>
 #include <map>
 #include <mutex>
+#include <tuple>
 #include <utility>
 
 #include "mq_device.h"
@@ -47,16 +48,16 @@ __global__ __launch_bounds__(256) void splitk_reduce4_kernel(const v4f *__restri
 
 } // namespace
 
-WsLease::WsLease(size_t bytes, hipStream_t st)
+WsLease::WsLease(size_t bytes, hipStream_t st, int role)
 {
-    static std::mutex mu;
-    static std::map<std::pair<int, hipStream_t>, std::pair<void *, size_t>> bufs;
-    lock_ = std::unique_lock<std::mutex>(mu);
+    static std::recursive_mutex mu;
+    static std::map<std::tuple<int, hipStream_t, int>, std::pair<void *, size_t>> bufs;
+    lock_ = std::unique_lock<std::recursive_mutex>(mu);
     int dev = 0;
     err = hipGetDevice(&dev);
     if (err != hipSuccess)
         return;
-    auto &slot = bufs[{dev, st}];
+    auto &slot = bufs[{dev, st, role}];
     if (slot.second < bytes) {
         if (slot.first) {
             // the old buffer's last reader is on st

@@ -195,7 +195,7 @@ def test_workspace_reuse_across_streams(dev):
 # The small-M band: token counts around the switches between the GEMV, the
 # GEMM's 32-token tiles and its 128-token tiles, for every path.
 @pytest.mark.parametrize("fmt", ["q4k", "q5k", "q6k"])
-@pytest.mark.parametrize("M", [3, 5, 9, 16, 24, 32, 33, 64, 96, 97])
+@pytest.mark.parametrize("M", [3, 5, 9, 16, 24, 32, 33, 64, 65, 96, 97])
 def test_small_m_band(dev, fmt, M):
     N, K = 700, 2560
     rng = np.random.default_rng(M * 17 + FMT_SEED[fmt])
@@ -460,9 +460,9 @@ def test_time_next_kernel(dev):
 
 
 # Row lengths served by the persistent stream kernels with 2, 3 and 6 passes
-# per row (Q4_K up to K = 10752, Q5_K up to 6144), ragged N. Q4_K streams up
-# to 8 tokens while the plane fits its LDS copy (M = 4 at K <= 5120, M = 7 at
-# K = 4096); Q5_K up to 2; the other cases run the row-grid kernels.
+# per row (Q4_K up to K = 10752, Q5_K up to 6144), ragged N. Both stream up
+# to 8 tokens while the plane fits their LDS copy (M = 4 at K <= 6144, M = 7
+# at K = 4096); the other cases run the row-grid kernels.
 @pytest.mark.parametrize("fmt,K", [("q4k", 4096), ("q4k", 5120), ("q4k", 8192), ("q4k", 10752),
                                    ("q5k", 4096), ("q5k", 5120), ("q5k", 6144)])
 @pytest.mark.parametrize("M", [1, 2, 4, 7])

@@ -143,14 +143,15 @@ def test_swiglu_quantize_edge_values(dev):
 
 # ---------------------------------------------------------------- fused FFN up half
 
-# Decode sizes whose plane fits the persistent stream run gate and up as one
-# stream plus the SwiGLU quantizer; longer rows (K > 10752) and larger planes
-# run the single fused kernel, with (K = 11008, M = 2) and without
-# (K = 12288, M = 4) its LDS copy of the plane.
+# Up to 128 tokens the FFN runs two passes (g and u into a workspace, then
+# the SwiGLU quantizer): decode sizes whose plane fits the persistent stream
+# run gate and up as one stream, longer rows (K = 11008, 12288) two GEMVs,
+# path 2 the GEMMs (32-token tiles to 64 tokens, 128-token tiles at 100).
+# Beyond 128 tokens (130, 3314) one GEMM launch with SwiGLU in its epilogue.
 FFN_CASES = [(1, 256, 1024, (1, 2)), (3, 512, 3584, (1, 2)), (8, 768, 2048, (1, 2)),
              (8, 512, 3584, (1,)), (2, 512, 11008, (1,)), (4, 256, 12288, (1,)),
-             (9, 256, 1024, (2,)), (130, 512, 3584, (2,)), (1, 18944, 3584, (1,)),
-             (3314, 18944, 3584, (2,))]
+             (9, 256, 1024, (2,)), (100, 256, 2048, (2,)), (130, 512, 3584, (2,)),
+             (1, 18944, 3584, (1,)), (3314, 18944, 3584, (2,))]
 
 
 @pytest.mark.parametrize("M,N,K,paths", FFN_CASES)
