@@ -18,9 +18,11 @@
  *     sums, and the decode FFN (mq_ffn_q4k at M <= 8) keeps g and u in
  *     2*M*N f32. The workspace is a device buffer the library keeps per
  *     (device, stream) and reuses; a call that needs more than it holds
- *     waits for that stream to drain (hipStreamSynchronize), frees it and
- *     allocates a larger one (hipMalloc, 2 MiB granules). Buffers stay
- *     allocated until the process ends. A failed allocation is
+ *     allocates a larger one (hipMalloc, at least twice the size, 2 MiB
+ *     granules) and keeps the old one, which queued kernels or a captured
+ *     graph may still read: no call frees memory or waits on the stream,
+ *     and what is kept is at most about twice the largest request. Buffers
+ *     stay allocated until the process ends. A failed allocation is
  *     MQ_ERR_LAUNCH. Calls from several host threads are safe; calls on one
  *     stream run in stream order, calls on different streams use different
  *     buffers.

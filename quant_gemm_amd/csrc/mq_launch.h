@@ -174,8 +174,9 @@ hipError_t splitk_reduce(const float *part, int nsplit, int64_t n, float *out, h
 
 // Workspace for the kernels a call enqueues on stream st: a device buffer
 // the library keeps per (device, stream, role), grown with hipMalloc when a
-// call needs more (the old one freed after st drains) and reused otherwise,
-// so a call costs no allocation. Calls on one stream run in order, so they
+// call needs more (to at least twice its size; the old buffer is kept, since
+// queued kernels or captured graphs may still use it) and reused otherwise,
+// so a call costs no allocation and never waits on the stream. Calls on one stream run in order, so they
 // share it; other streams get their own. Roles keep leases that nest apart
 // (the FFN's g | u buffer, role WS_FFN, around the split-K partial sums of
 // the GEMMs it runs, role WS_SPLIT_K). The lease holds a library-wide

@@ -59,18 +59,15 @@ WsLease::WsLease(size_t bytes, hipStream_t st, int role)
         return;
     auto &slot = bufs[{dev, st, role}];
     if (slot.second < bytes) {
-        if (slot.first) {
-            // the old buffer's last reader is on st
-            err = hipStreamSynchronize(st);
-            if (err != hipSuccess)
-                return;
-            err = hipFree(slot.first);
-            slot = {nullptr, 0};
-            if (err != hipSuccess)
-                return;
-        }
+        // Grow to at least twice the old size. The old buffer is not freed:
+        // kernels already queued (or recorded into a graph) may still use
+        // it, so it stays allocated, like the new one, until the process
+        // ends; the doubling bounds what is kept to twice the largest
+        // request.
         const size_t grain = size_t(2) << 20;
-        const size_t size = (bytes + grain - 1) / grain * grain;
+        size_t size = (bytes + grain - 1) / grain * grain;
+        if (size < 2 * slot.second)
+            size = 2 * slot.second;
         void *p = nullptr;
         err = hipMalloc(&p, size);
         if (err != hipSuccess)

@@ -192,6 +192,60 @@ def test_workspace_reuse_across_streams(dev):
         assert np.array_equal(o.cpu().numpy(), ref[i]), f"case {i}: queued result differs"
 
 
+def test_graph_replay_uses_kept_workspace(dev):
+    """Calls captured into a HIP graph keep the stream's workspace address:
+    a split-K GEMM and the two-pass FFN, warmed up on the capture stream,
+    captured, then replayed three times with eager work (including a call
+    that grows that stream's workspace) and host synchronization between
+    replays; every replay equals the eager result bit for bit."""
+    import torch
+    rng = np.random.default_rng(77)
+    M, N, K = 40, 130, 6912                       # split-K shape
+    W = synth.q4k_weights(rng, N, K)
+    q, d, s = gpu_plane(synth.activations(rng, M, K, outliers=True))
+    Wd = to_dev(W.reshape(-1))
+    Mf, Nf, Kf = 12, 512, 1024                    # two-pass FFN (GEMMs)
+    Wg, Wu = to_dev(synth.q4k_weights(rng, Nf, Kf).reshape(-1)), to_dev(synth.q4k_weights(rng, Nf, Kf).reshape(-1))
+    qf, df, sf = gpu_plane(synth.activations(rng, Mf, Kf, outliers=True))
+    big_M, big_N, big_K = 300, 700, 4608          # larger split-K workspace
+    Wb = to_dev(synth.q6k_weights(rng, big_N, big_K).reshape(-1))
+    qb, db, sb = gpu_plane(synth.activations(rng, big_M, big_K, outliers=True))
+
+    out = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    ffn_out = [torch.empty((Mf, Nf), dtype=torch.int8, device="cuda"),
+               torch.empty((Mf, Nf // 32), dtype=torch.float32, device="cuda"),
+               torch.empty((Mf, Nf // 32), dtype=torch.float32, device="cuda")]
+    ref = host(mq.matmul_q4k(Wd, q, d, s, N, K, path=mq.MQ_PATH_GEMM))
+    rq, rdd, rss = (host(t) for t in mq.ffn_q4k(Wg, Wu, qf, df, sf, Nf, Kf, path=mq.MQ_PATH_GEMM))
+
+    def work():
+        mq.matmul_q4k(Wd, q, d, s, N, K, out=out, path=mq.MQ_PATH_GEMM)
+        mq.ffn_q4k(Wg, Wu, qf, df, sf, Nf, Kf, qo=ffn_out[0], do=ffn_out[1], so=ffn_out[2], path=mq.MQ_PATH_GEMM)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        work()                                    # the workspace of `side` exists before capture
+    side.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        work()
+    for rep in range(3):
+        out.zero_()
+        for t in ffn_out:
+            t.zero_()
+        if rep == 1:
+            with torch.cuda.stream(side):        # grows the workspace of `side`
+                mq.matmul_q6k(Wb, qb, db, sb, big_N, big_K, stream=side, path=mq.MQ_PATH_GEMM)
+            side.synchronize()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(out), ref), f"replay {rep}: split-K GEMM differs"
+        assert np.array_equal(host(ffn_out[0]), rq) and np.array_equal(host(ffn_out[1]), rdd) \
+            and np.array_equal(host(ffn_out[2]), rss), f"replay {rep}: FFN plane differs"
+
+
 # The small-M band: token counts around the switches between the GEMV, the
 # GEMM's 32-token tiles and its 128-token tiles, for every path.
 @pytest.mark.parametrize("fmt", ["q4k", "q5k", "q6k"])
