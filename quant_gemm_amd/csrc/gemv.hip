@@ -847,12 +847,18 @@ __global__ __launch_bounds__(64 * GEMV_WAVES) void gemv_q6k_kernel(
 // the sums of each 16-value group) is staged in LDS once per workgroup, so
 // the only vector-memory loads in the loop are the DMAs and the waits on
 // them are exact.
-constexpr int Q6S_WAVES = 4;                  // wavefronts per workgroup
-constexpr int Q6S_D = 2;                      // ring slots per wavefront
+#ifndef Q6S_WAVES_CFG
+#define Q6S_WAVES_CFG 4
+#endif
+#ifndef Q6S_D_CFG
+#define Q6S_D_CFG 2
+#endif
+constexpr int Q6S_WAVES = Q6S_WAVES_CFG;      // wavefronts per workgroup
+constexpr int Q6S_D = Q6S_D_CFG;              // ring slots per wavefront
 constexpr int Q6S_SEG = 16;                   // blocks per segment
 constexpr int Q6S_SLOT = 4096;                // bytes per slot (16*210 + alignment, whole DMA rows)
 constexpr int Q6S_DMA = Q6S_SLOT / 1024;      // DMA instructions per segment
-constexpr int Q6S_ACT_MAX = 40 * 1024;        // LDS budget of the activation plane
+constexpr int Q6S_ACT_MAX = 48 * 1024;        // LDS budget of the activation plane (two tokens at K = 18944)
 constexpr size_t Q6S_LDS_PER_CU = 160 * 1024;  // gfx950 LDS per compute unit
 static_assert(Q6S_SEG * 210 + 16 <= Q6S_SLOT, "segment fits a slot");
 
@@ -1157,7 +1163,8 @@ bool q4k_stream_fits(int64_t M, int64_t K)
 
 bool q6k_stream_fits(int64_t M, int64_t K)
 {
-    return M >= 1 && M <= 16 && K >= 256 && q6s_act_bytes(M, K) <= Q6S_ACT_MAX;
+    return M >= 1 && M <= 16 && K >= 256 && q6s_act_bytes(M, K) <= Q6S_ACT_MAX &&
+           q6s_act_bytes(M, K) + (int64_t)Q6S_WAVES * Q6S_D * Q6S_SLOT <= (int64_t)Q6S_LDS_PER_CU;
 }
 
 bool q5k_stream_fits(int64_t M, int64_t K)
@@ -1258,7 +1265,7 @@ hipError_t launch_ffn_q4k_two_pass(const uint8_t *Wg, const uint8_t *Wu, const i
 hipError_t launch_gemv_q6k(const uint8_t *W, const int8_t *q, const float *d,
                            int M, int N, int K, float *out, hipStream_t st)
 {
-    if (q6s_act_bytes(M, K) <= Q6S_ACT_MAX) {
+    if (q6k_stream_fits(M, K)) {
         // as many workgroups as fit on the chip at once (LDS-limited)
         const int n_cu = device_cu_count();
         const size_t lds = (size_t)q6s_act_bytes(M, K) + (size_t)Q6S_WAVES * Q6S_D * Q6S_SLOT;

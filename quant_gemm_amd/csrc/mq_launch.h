@@ -53,7 +53,7 @@ constexpr int FFN_GEMV_MAX_M = 8;
 // GEMM is slower: M = 4 26.4 against 28.2 us). Q6_K runs the GEMV for
 // M <= 4, and up to 8 tokens where its LDS ring kernel takes the plane while
 // M*N*K <= 5.5e8 (18944 x 3584, M = 8: 33.5 against 42.5 us; the down
-// projection's K = 18944 leaves the ring kernel at M = 2, and its register
+// projection's K = 18944 leaves the ring kernel at M = 3, and its register
 // kernel loses from M = 6: 55.2 against 46.4 us).
 bool q4k_stream_fits(int64_t M, int64_t K);
 bool q5k_stream_fits(int64_t M, int64_t K);

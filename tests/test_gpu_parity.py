@@ -465,7 +465,8 @@ def test_full_size_workloads(dev, name):
 # Long rows (K >= 8192): the GEMVs give each wavefront one row and stream it
 # in double-buffered batches; ragged N and several token counts.
 @pytest.mark.parametrize("fmt", ["q4k", "q5k", "q6k"])
-@pytest.mark.parametrize("M,N,K", [(1, 300, 18944), (3, 77, 8192), (8, 129, 18944), (16, 40, 10240)])
+@pytest.mark.parametrize("M,N,K", [(1, 300, 18944), (2, 300, 18944), (3, 77, 8192), (8, 129, 18944),
+                                   (16, 40, 10240)])
 def test_long_rows_gemv(dev, fmt, M, N, K):
     rng = np.random.default_rng(M * 131 + N + K + FMT_SEED[fmt])
     W = synth.weights(fmt, rng, N, K)
