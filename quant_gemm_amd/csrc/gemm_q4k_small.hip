@@ -2,10 +2,10 @@
 //
 // At a few to a few dozen tokens (a speculative-decoding verify batch, a
 // short prompt) the 128-token tiles of the main configuration are mostly
-// empty rows. This build of the same kernel gives a workgroup 32 tokens x
-// 256 weight rows, its four wavefronts side by side along the rows (each 32
-// tokens x 64 rows, 1 x 2 MFMA tiles of 32 x 32), and relies on split-K to
-// fill the chip. Everything else (staging, arithmetic, epilogue, split-K
+// empty rows. This instantiation of the same kernel source gives a
+// workgroup 32 tokens x 256 weight rows, its four wavefronts side by side
+// along the rows (each 32 tokens x 64 rows, 1 x 2 MFMA tiles of 32 x 32),
+// and relies on split-K to fill the chip. Everything else (staging, arithmetic, epilogue, split-K
 // reduction) is the main kernel's.
 #define MQ_Q4K_TM 1
 #define MQ_Q4K_TN 2

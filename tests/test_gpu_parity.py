@@ -262,7 +262,7 @@ def test_small_m_band(dev, fmt, M):
     for path in paths:
         check_close(host(run_matmul(fmt, W, q, d, s, N, K, path=path)), ref, f"{fmt} M={M} path {path}")
 
-def test_config0_exact_workload(dev):
+def test_tiny_q4k_workload_exact(dev):
     case = synth.case_by_name("tiny_q4k")
     W = case.make_weights()
     x = case.make_activations()
@@ -270,7 +270,7 @@ def test_config0_exact_workload(dev):
     rq, rd, _ = oracle.quantize_act(x)
     ref = oracle.matmul_q4k(W, rq, rd, case.N, case.K)
     for p in (mq.MQ_PATH_GEMV, mq.MQ_PATH_GEMM, mq.MQ_PATH_AUTO):
-        check_close(host(run_matmul("q4k", W, q, d, s, case.N, case.K, path=p)), ref, f"cfg0 path={p}")
+        check_close(host(run_matmul("q4k", W, q, d, s, case.N, case.K, path=p)), ref, f"tiny_q4k path={p}")
 
 
 # ---------------------------------------------------------------- position probes

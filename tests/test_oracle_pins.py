@@ -39,7 +39,7 @@ def _rel_err(a, b):
 # ---------------------------------------------------------------- brute force
 
 @pytest.mark.parametrize("fmt", ["q4k", "q6k"])
-def test_oracle_matches_bruteforce_config0_shape(fmt):
+def test_oracle_matches_bruteforce_tiny_shape(fmt):
     case = synth.case_by_name("tiny_q4k")
     W = (case.make_weights() if fmt == "q4k"
          else synth.q6k_weights(np.random.default_rng(7), case.N, case.K))
