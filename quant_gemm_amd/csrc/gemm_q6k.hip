@@ -314,14 +314,15 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_q6k_kernel(
     constexpr bool X = std::is_same<Src, Planes>::value;
     __shared__ ActStage A0, A1;
     __shared__ WgtStage B;
-    // blockIdx = split * tiles + tile_n * tiles_m + tile_m; split s of nsplit
+    // blockIdx = split * tiles + tile (tile_order maps tile to tile_m and
+    // tile_n); split s of nsplit
     // covers the super-blocks [s*P/nsplit, (s+1)*P/nsplit) of P = K/256 and,
     // when nsplit > 1, writes its partial sums to out + s*M*N.
     const int tiles = gridDim.x / nsplit;
     const int split = blockIdx.x / tiles;
     const int tile = blockIdx.x - split * tiles;
-    const int tile_m = tile % tiles_m;
-    const int tile_n = tile / tiles_m;
+    int tile_m, tile_n;
+    tile_order(tile, tiles_m, tiles / tiles_m, tile_m, tile_n);
     const int pairs = K >> 8;
     const int st_begin = 2 * (int)((int64_t)split * pairs / nsplit);
     const int st_end = 2 * (int)((int64_t)(split + 1) * pairs / nsplit);
