@@ -592,7 +592,10 @@ __global__ __launch_bounds__(64 * GEMV_WAVES) void gemv_q5k_kernel(
 // while a row is reduced and stored; blocks past a row's end are clamped and
 // masked, and nothing is loaded past the wavefront's last row.
 template <int MT, int NP, int D>
-__global__ __launch_bounds__(64 * GEMV_WAVES) void gemv_q5k_stream_kernel(
+#ifndef Q5S_WAVES
+#define Q5S_WAVES GEMV_WAVES
+#endif
+__global__ __launch_bounds__(64 * Q5S_WAVES) void gemv_q5k_stream_kernel(
     const uint8_t *__restrict__ W, const int8_t *__restrict__ q,
     const float *__restrict__ dx, const float *__restrict__ sx, int M, int N,
     int K, float *__restrict__ out)
@@ -601,9 +604,9 @@ __global__ __launch_bounds__(64 * GEMV_WAVES) void gemv_q5k_stream_kernel(
     __shared__ v4i act[AB / 16];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int nw = gridDim.x * GEMV_WAVES;
-    const int w = blockIdx.x * GEMV_WAVES + wave;
-    ActCopy<GEMV_WAVES, AB> ac;
+    const int nw = gridDim.x * Q5S_WAVES;
+    const int w = blockIdx.x * Q5S_WAVES + wave;
+    ActCopy<Q5S_WAVES, AB> ac;
     act_load(ac, q, dx, sx, M, K);
 
     const int nb = K >> 8;
@@ -1206,8 +1209,8 @@ hipError_t launch_gemv_q5k(const uint8_t *W, const int8_t *q, const float *d,
     // row-grid kernel measured faster for Q5_K) and 8 tokens whose plane fits
     // the LDS copy
     if (q5k_stream_fits(M, K)) {
-        const int nwg = max(1, min((N + GEMV_WAVES - 1) / GEMV_WAVES, GEMV_STREAM_WGS));
-        const dim3 grid(nwg), block(64 * GEMV_WAVES);
+        const int nwg = max(1, min((N + Q5S_WAVES - 1) / Q5S_WAVES, GEMV_STREAM_WGS));
+        const dim3 grid(nwg), block(64 * Q5S_WAVES);
         auto go = [&](auto mt) {
             constexpr int MT = decltype(mt)::value;
             if (K <= 2 * 8 * 256)
