@@ -22,6 +22,7 @@ CPU oracle timed on a bounded sample of the same GEMM.
   python bench.py [--steps K] [--warmup W] [--no-cpu]
   python bench.py --all                  # per-matrix table of every workload
   python bench.py --copy-calibration     # plain copy kernel (counter scale)
+  python bench.py --ceilings             # read-stream and MFMA/VALU ceiling probes
 """
 from __future__ import annotations
 
@@ -519,6 +520,74 @@ def run_copy_calibration(args):
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": args.steps}))
 
 
+def run_ceilings(args):
+    """The hardware ceilings the kernels are judged against, from the probes
+    in libmq_probes.so (GPU time per launch, queued behind busy work):
+      * read stream: the best of grid-stride register loads (4, 8 or 16 in
+        flight per lane) and an LDS-DMA ring (2, 4 or 8 slots per wavefront)
+        over 1024-8192 workgroups, for byte counts of the decode matrices
+        (Q4_K 18944 x 3584, Q6_K 3584 x 18944, the Q6_K output head) and
+        1 GiB, each read from rotating copies in a 2 GiB pool;
+      * int8 MFMA with k f32 VALU operations per int32 result (k = 0: the
+        MFMAs alone; 3: convert, scale product, fma, as the GEMM epilogue)."""
+    import ctypes
+    import numpy as np
+    import torch
+
+    from quant_gemm_amd import build as mq_build
+    if not os.path.exists(mq_build.PROBES_LIB):
+        raise RuntimeError(f"{mq_build.PROBES_LIB} is not built (python -m quant_gemm_amd.build)")
+    P = ctypes.CDLL(mq_build.PROBES_LIB)
+    P.mqp_read.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                           ctypes.c_void_p, ctypes.c_void_p]
+    P.mqp_read.restype = ctypes.c_int
+    P.mqp_mix.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    P.mqp_mix.restype = ctypes.c_int
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    sink = torch.zeros(16, dtype=torch.int32, device="cuda")
+    pool_bytes = 2 << 30
+    pool = torch.empty(pool_bytes, dtype=torch.uint8, device="cuda")
+
+    def check(rc):
+        if rc != 0:
+            raise RuntimeError(f"probe launch failed: hipError {rc}")
+
+    sizes = [("Q4_K 18944 x 3584", 18944 * 14 * 144), ("Q6_K 3584 x 18944", 3584 * 74 * 210),
+             ("Q6_K head 152064 x 3584", 152064 * 14 * 210), ("1 GiB", 1 << 30)]
+    for name, nbytes in sizes:
+        copies = max(2, pool_bytes // nbytes)
+        ptr = lambda i: ctypes.c_void_p(pool.data_ptr() + (i % copies) * nbytes)
+        reps = max(20, 2 * copies)
+        best = None
+        for kind, depths in ((0, (4, 8, 16)), (1, (2, 4, 8))):
+            for depth in depths:
+                for grid in (1024, 2048, 4096, 8192):
+                    fn = lambda i: check(P.mqp_read(kind, depth, ptr(i), nbytes, grid, ctypes.c_void_p(sink.data_ptr()), st))
+                    us = _time_rotating(fn, copies, reps)
+                    if best is None or us < best[0]:
+                        best = (us, kind, depth, grid)
+        _, kind, depth, grid = best
+        fn = lambda i: check(P.mqp_read(kind, depth, ptr(i), nbytes, grid, ctypes.c_void_p(sink.data_ptr()), st))
+        us = float(np.median([_time_rotating(fn, copies, reps) for _ in range(3)]))
+        row = {"probe": "read", "case": name, "bytes": nbytes, "us": round(us, 2),
+               "GBs": round(nbytes / (us * 1e-6) / 1e9, 1), "frac_hbm": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 3),
+               "best": {"pattern": ["register loads", "LDS-DMA ring"][kind], "depth": depth, "workgroups": grid}}
+        print(json.dumps(row), flush=True)
+    del pool
+    torch.cuda.empty_cache()
+
+    grid, iters = 2048, 1000
+    out = torch.zeros(grid * 256, dtype=torch.float32, device="cuda")
+    ops = grid * 4 * iters * 4 * 2 * 32 * 32 * 32
+    for k in (0, 2, 3, 4):
+        fn = lambda i: check(P.mqp_mix(k, iters, grid, ctypes.c_void_p(out.data_ptr()), st))
+        us = float(np.median([_time_rotating(fn, 1, 5) for _ in range(3)]))
+        tops = ops / (us * 1e-6) / 1e12
+        row = {"probe": "int8 MFMA + k f32 VALU ops per result", "k": k, "us": round(us, 1),
+               "TOPS": round(tops, 1), "frac_int8_peak": round(tops / INT8_PEAK_TOPS, 3)}
+        print(json.dumps(row), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -528,6 +597,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--all", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--ceilings", action="store_true", help="read-stream and MFMA/VALU probes")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus}: this benchmark measures one GPU only; the multi-GPU "
@@ -535,6 +605,8 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         run_copy_calibration(args)
+    elif args.ceilings:
+        run_ceilings(args)
     elif args.all:
         run_all(args)
     else:

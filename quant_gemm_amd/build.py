@@ -79,13 +79,35 @@ def build(verbose: bool = False) -> str:
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")
+    build_probes(verbose)
     return LIB
+
+
+PROBES_SRC = os.path.join(HERE, "probes", "probes.hip")
+PROBES_LIB = os.path.join(HERE, "libmq_probes.so")
+
+
+def build_probes(verbose: bool = False) -> str:
+    """libmq_probes.so: the ceiling probes bench.py --ceilings measures (a
+    separate library; nothing of it is linked into libmq.so)."""
+    tl = torch_lib_dir()
+    tmp = PROBES_LIB + ".tmp"
+    cmd = [HIPCC, *HIP_FLAGS, "-shared", PROBES_SRC, "-o", tmp, f"-L{tl}", "-l:libamdhip64.so",
+           f"-Wl,-rpath,{tl}"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, PROBES_LIB)
+    if verbose:
+        print(f"built {PROBES_LIB}")
+    return PROBES_LIB
 
 
 def clean() -> None:
     shutil.rmtree(os.path.join(ROOT, "_build"), ignore_errors=True)
-    if os.path.exists(LIB):
-        os.remove(LIB)
+    for lib in (LIB, PROBES_LIB):
+        if os.path.exists(lib):
+            os.remove(lib)
 
 
 if __name__ == "__main__":

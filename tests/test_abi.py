@@ -257,3 +257,22 @@ def test_error_is_cleared_by_next_call(L):
 def test_plane_entry_validation(L, call, status, needle):
     assert call(L) == status
     assert needle in L.mq_last_error().decode()
+
+
+def test_probe_library_exports_and_rejects_bad_arguments():
+    """libmq_probes.so (the ceiling probes of bench.py --ceilings) exports its
+    two entry points; malformed arguments return hipErrorInvalidValue (1)
+    before any HIP call, so this runs without a GPU."""
+    import ctypes
+    from quant_gemm_amd import build as mq_build
+    assert os.path.exists(mq_build.PROBES_LIB), "build() also builds libmq_probes.so"
+    P = ctypes.CDLL(mq_build.PROBES_LIB)
+    P.mqp_read.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                           ctypes.c_void_p, ctypes.c_void_p]
+    P.mqp_mix.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    dummy = ctypes.c_void_p(0x1000)
+    assert P.mqp_read(0, 4, dummy, 1000, 64, dummy, None) == 1        # not a multiple of 1024
+    assert P.mqp_read(0, 4, None, 1024, 64, dummy, None) == 1         # no source
+    assert P.mqp_read(0, 4, dummy, 1024, 0, dummy, None) == 1         # empty grid
+    assert P.mqp_mix(3, 0, 64, dummy, None) == 1                      # no iterations
+    assert P.mqp_mix(3, 10, 64, None, None) == 1                      # no sink
