@@ -114,13 +114,20 @@ __global__ __launch_bounds__(256) void mix(int iters, float *sink)
         b.x += i;
         if constexpr (K == 0) {
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
-                chain[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, chain[t], 0, 0, 0);
+            for (int t = 0; t < 4; ++t) {
+                v4i bt = b;
+                bt.y += t;
+                chain[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, bt, chain[t], 0, 0, 0);
+            }
         } else {
+            // distinct operands per tile, so that the four MFMAs stay four
             v16i I[4];
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
-                I[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, v16i{}, 0, 0, 0);
+            for (int t = 0; t < 4; ++t) {
+                v4i bt = b;
+                bt.y += t;
+                I[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, bt, v16i{}, 0, 0, 0);
+            }
             // a per-tile factor that changes every iteration times a
             // per-element one: one distinct scale product per result, as
             // d_x[token] * (d*sc)[row] in the GEMM epilogue
