@@ -147,9 +147,14 @@ int mq_swiglu_quantize(const float *g, const float *u, int64_t M, int64_t K,
  * Small M runs the weight-streaming GEMV, larger M the int8 MFMA GEMM (the
  * CUDA dispatch splits decode from prefill by token count: minfer Support
  * Matrix, "CUDA notes"). MQ_PATH_AUTO switches at crossovers measured on
- * MI355X: Q4_K runs the GEMV for M <= 2, and up to 16 tokens while
- * M*N*K <= 2.6e8; Q6_K for M <= 4. The GEMM uses 32-token tiles up to
- * M = 96 (Q4_K) / 32 (Q6_K) and 128-token tiles above. The GEMV serves up to
+ * MI355X (GPU time per call): Q4_K runs the GEMV for M <= 2; up to 8 tokens
+ * where its persistent stream takes them (rows of K <= 10752 and a plane of
+ * at most 32 KB, 40 KB above 4 tokens) while M*N*K <= 4.2e8; otherwise up
+ * to 16 tokens while
+ * M*N*K <= 2.6e8. Q5_K likewise (rows of K <= 6144; 5.5e8 and 3.3e8). Q6_K
+ * runs it for M <= 4, and up to 8 tokens where its LDS ring kernel takes the
+ * plane while M*N*K <= 5.5e8. The GEMM uses 32-token tiles up to M = 64
+ * (Q4_K, Q5_K) / 32 (Q6_K) and 128-token tiles above. The GEMV serves up to
  * mq_gemv_max_m() tokens when forced.
  * W as described above; q, d, s from mq_quantize_act (s is required).
  */
@@ -263,7 +268,7 @@ int mq_dsc_q4k(const void *W, int64_t N, int64_t K, float *fw, float *fm,
  * Q4_K matmul reading the quants from W and the factors from the
  * decoded-scale planes (no block header decoded per tile): the same result
  * and contract as mq_matmul_q4k, always on the GEMM (32-token tiles up to
- * M = 96). fw, fm as built by mq_dsc_q4k from this W; s is required.
+ * M = 64). fw, fm as built by mq_dsc_q4k from this W; s is required.
  */
 int mq_matmul_q4k_dsc(const void *W, const float *fw, const float *fm,
                       const int8_t *q, const float *d, const float *s,
