@@ -150,8 +150,8 @@ int mq_swiglu_quantize(const float *g, const float *u, int64_t M, int64_t K,
  * MI355X (GPU time per call): Q4_K runs the GEMV for M <= 2; up to 8 tokens
  * where its persistent stream takes them (rows of K <= 10752 and a plane of
  * at most 32 KB, 40 KB above 4 tokens) while M*N*K <= 4.2e8; otherwise up
- * to 16 tokens while
- * M*N*K <= 2.6e8. Q5_K likewise (rows of K <= 6144; 5.5e8 and 3.3e8). Q6_K
+ * to 16 tokens while M*N*K <= 2.6e8. Q5_K likewise (rows of K <= 6144;
+ * 5.5e8 and 3.3e8). Q6_K
  * runs it for M <= 4, and up to 8 tokens where its LDS ring kernel takes the
  * plane while M*N*K <= 5.5e8. The GEMM uses 32-token tiles up to M = 64
  * (Q4_K, Q5_K) / 32 (Q6_K) and 128-token tiles above. The GEMV serves up to
