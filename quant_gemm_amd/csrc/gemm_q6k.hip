@@ -9,10 +9,16 @@
 // lo = p & 63 in [0, 63] and hi = p >> 6 in [-64, 64], both int8. Two
 // v_mfma_i32_32x32x32_i8 per 32-value block (one per limb) give
 //     J = 64 * I_hi + I_lo = sum_k sc_k * (q_k - 32) * x_k
-// exactly in int32 (|J| <= 32 * 4096 * 127 < 2^31), and the f32 epilogue
-// per token t, row n and block is  acc += d_x[t] * d[n] * J:  4 VALU
-// operations (combine, convert, scale, add) per 32 values instead of two
-// scaled groups of 16.
+// exactly in int32 (|J| <= 32 * 4096 * 127 < 2^31). The result is
+//     out[t, n] = sum over super-blocks s of d[n, s] * sum_b d_x[t, b] * J_b,
+// and d changes only once per 256 values, so each accumulator is kept in
+// units of its row's current d: acc' += d_x[t] * J per 32 values (combine,
+// convert, fma: 3 VALU operations), and at each super-block whose d is
+// nonzero acc' is multiplied by d_old / d_new once (16 operations per row
+// tile per 256 values); the stored result is acc' * d. A super-block with
+// d = 0 contributes nothing: its limbs are written as zeros and the scale
+// is kept. Each rescale rounds twice (the quotient and the product), at
+// most 2 * K/256 * 2^-24 relative on the running sum.
 //
 // Tiling and staging follow the Q4_K kernel: a 256-thread workgroup computes
 // 128 tokens x 128 rows as 4 wavefronts of 32 tokens x 128 rows (1 x 4 MFMA
@@ -218,14 +224,17 @@ __device__ __forceinline__ void store_raw(WgtStage &w, ActStage &a, const Raw<tr
 {
     const int tid = threadIdx.x;
     const int row = tid >> 1, hh = tid & 1;
+    // a row past N (which reads the last row) and a super-block with d = 0
+    // get zero limbs and d = 0 (the accumulator scale is then kept)
+    const bool ok = n0 + row < N && p.dw != 0.0f;
+    const v4i z = {0, 0, 0, 0};
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        *reinterpret_cast<v4i *>(w.lo + 16 * slot8(row, 2 * r + hh)) = p.lo[r];
-        *reinterpret_cast<v4i *>(w.hi + 16 * slot8(row, 2 * r + hh)) = p.hi[r];
+        *reinterpret_cast<v4i *>(w.lo + 16 * slot8(row, 2 * r + hh)) = ok ? p.lo[r] : z;
+        *reinterpret_cast<v4i *>(w.hi + 16 * slot8(row, 2 * r + hh)) = ok ? p.hi[r] : z;
     }
-    // a row past N reads the last row's limbs; its d of 0 cancels them
     if (hh == 0)
-        w.dw[row] = n0 + row < N ? p.dw : 0.0f;
+        w.dw[row] = ok ? p.dw : 0.0f;
     store_act_scales(a, p.ds, M, t0);
 }
 
@@ -234,7 +243,8 @@ __device__ __forceinline__ void store_raw(WgtStage &w, ActStage &a, const Raw<fa
 {
     const int tid = threadIdx.x;
     const int row = tid >> 1, hh = tid & 1;
-    const bool rok = n0 + row < N;
+    // rows past N and super-blocks with d = 0 (either sign) get zero limbs
+    const bool rok = n0 + row < N && (p.dbits & 0x7fffu) != 0;
     uint32_t l0[4], l1[4], h[4], sc[2];
     realign<4>(p.w0, p.sh, l0);
     realign<4>(p.w1, p.sh, l1);
@@ -262,19 +272,32 @@ __device__ __forceinline__ void store_raw(WgtStage &w, ActStage &a, const Raw<fa
     }
     // every thread consumes its loaded values (only some store them), so no
     // load into these registers is left pending into the next step
-    const float dwv = rok ? f16_bits_to_f32(p.dbits) : 0.0f;
+    const float dwv = rok ? f16_bits_to_f32(p.dbits) : 0.0f;   // 0: limbs zeroed, scale kept
     if (hh == 0)
         w.dw[row] = dwv;
     store_act_scales(a, p.ds, M, t0);
 }
 
+// FIRST: the step opens a super-block, so each row tile moves its
+// accumulator to the new d (cur[b]: the d the accumulator is counted in).
+template <bool FIRST>
 __device__ __forceinline__ void compute_step(const ActStage &a, const WgtStage &w,
-                                             v16f (&acc)[TN], int wm, int wn, int lr, int lh)
+                                             v16f (&acc)[TN], float (&cur)[TN], int wm, int wn, int lr,
+                                             int lh)
 {
-    float dwv[TN];
+    if constexpr (FIRST) {
 #pragma unroll
-    for (int b = 0; b < TN; ++b)
-        dwv[b] = w.dw[(wn * TN + b) * 32 + lr];
+        for (int b = 0; b < TN; ++b) {
+            const float dn = w.dw[(wn * TN + b) * 32 + lr];
+            if (dn != 0.0f) {
+                const float f = cur[b] / dn;
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    acc[b][v] *= f;
+                cur[b] = dn;
+            }
+        }
+    }
 #pragma unroll 1
     for (int j = 0; j < BK / 32; ++j) {
         const int tr = wm * 32 + lr;
@@ -298,7 +321,7 @@ __device__ __forceinline__ void compute_step(const ActStage &a, const WgtStage &
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int J = (ih[v] << 6) + il[v];
-                acc[b][v] = fmaf((float)J, dv[v] * dwv[b], acc[b][v]);
+                acc[b][v] = fmaf((float)J, dv[v], acc[b][v]);
             }
         }
     }
@@ -335,11 +358,14 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_q6k_kernel(
     const int lr = lane & 31, lh = lane >> 5;
 
     v16f acc[TN];
+    float cur[TN];
 #pragma unroll
-    for (int b = 0; b < TN; ++b)
+    for (int b = 0; b < TN; ++b) {
+        cur[b] = 1.0f;
 #pragma unroll
         for (int v = 0; v < 16; ++v)
             acc[b][v] = 0.0f;
+    }
 
     // The step range is even (whole super-blocks): steps alternate the
     // activation buffers A0, A1.
@@ -354,7 +380,7 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_q6k_kernel(
         // of them then has no DMA in flight to wait for
         load_raw(p, W, dx, M, N, K, t0, n0, st + 1);
         issue_act(A1, q, M, K, t0, st + 1, wave, lane);
-        compute_step(A0, B, acc, wm, wn, lr, lh);
+        compute_step<true>(A0, B, acc, cur, wm, wn, lr, lh);
         __syncthreads();                      // limb planes of step st consumed
         wait_vm<0>();
         store_raw(B, A1, p, M, N, t0, n0);
@@ -364,7 +390,7 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_q6k_kernel(
             load_raw(p, W, dx, M, N, K, t0, n0, st + 2);
             issue_act(A0, q, M, K, t0, st + 2, wave, lane);
         }
-        compute_step(A1, B, acc, wm, wn, lr, lh);
+        compute_step<false>(A1, B, acc, cur, wm, wn, lr, lh);
         __syncthreads();
         if (more) {
             wait_vm<0>();
@@ -381,7 +407,7 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_q6k_kernel(
             for (int v = 0; v < 16; ++v) {
                 const int t = t0 + wm * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
                 if (t < M)
-                    dst[(int64_t)t * N + n] = acc[b][v];
+                    dst[(int64_t)t * N + n] = acc[b][v] * cur[b];
             }
         }
     }

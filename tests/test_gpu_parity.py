@@ -434,6 +434,41 @@ def test_wide_scale_range(dev, fmt):
         for t in range(got.shape[0]):
             check_close(got[t], ref[rows][t], f"{fmt} path {path} row {t}")
 
+def test_q6k_zero_d_superblocks(dev):
+    """Q6_K super-blocks with d = +0 or -0 among nonzero ones: they add
+    nothing, whatever their quants and scales (the GEMMs keep their
+    accumulators in units of the row's current d and zero such blocks'
+    limbs). Covers a row whose first super-blocks are zero, one whose last
+    ones are, one that is zero throughout, and the expansion planes."""
+    rng = np.random.default_rng(14)
+    N, K, M = 70, 2048, 130
+    W = synth.q6k_weights(rng, N, K).reshape(N, K // 256, 210)
+    zero = rng.random((N, K // 256)) < 0.3
+    zero[0, :3] = True
+    zero[1, -2:] = True
+    zero[2, :] = True
+    zero[3, :] = False
+    neg = rng.random((N, K // 256)) < 0.5
+    W[:, :, 208][zero] = 0
+    W[:, :, 209][zero] = np.where(neg[zero], 0x80, 0x00)
+    W = W.reshape(N, -1)
+    x = synth.activations(rng, M, K, outliers=True)
+    rq, rd, _ = oracle.quantize_act(x)
+    ref = oracle_mm("q6k", W, rq, rd, N, K)
+    assert np.all(ref[:, 2] == 0.0)
+    q, d, s = gpu_plane(x)
+    got = host(run_matmul("q6k", W, q, d, s, N, K, path=mq.MQ_PATH_GEMM))
+    check_close(got, ref, "q6k GEMM, zero-d super-blocks")
+    assert np.all(got[:, 2] == 0.0)
+    Wd = to_dev(W.reshape(-1))
+    lo, hi, dw = mq.expand_q6k(Wd, N, K)
+    gx = host(mq.matmul_q6k_x(lo, hi, dw, q, d, N, K))
+    assert np.array_equal(gx, got), "planes and raw blocks: the same result bit for bit"
+    q8, d8, s8 = gpu_plane(x[:8])
+    gv = host(run_matmul("q6k", W, q8, d8, s8, N, K, path=mq.MQ_PATH_GEMV))
+    check_close(gv, ref[:8], "q6k GEMV, zero-d super-blocks")
+
+
 # ---------------------------------------------------------------- full-size workloads
 
 _SAMPLE_TOKENS = [0, 1, 2, 63, 64, 127, 128, 129, 511, 1000, 2047, 2048, 3199, 3200, 3201, 3250, 3312, 3313]
