@@ -295,67 +295,152 @@ template <int HF>
 __device__ __forceinline__ void compute_step(const Stage &s, v16f (&acc)[TM][TN], int wm, int wn,
                                              int lr, int lh)
 {
-#pragma unroll 1
-    for (int cl = 0; cl < 2; ++cl) {
-        v4i raw[TN];
-#pragma unroll
-        for (int b = 0; b < TN; ++b) {
-            const int r = (wn * TN + b) * 32 + lr;
-            raw[b] = *reinterpret_cast<const v4i *>(s.qs + 16 * q_slot(r, 2 * cl + lh));
-        }
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int j = 2 * cl + h;            // sub-block within the step
-            v4i bf[TN], af[TM];
+    if constexpr (!Q5 && TM == 1 && TN == 4) {
+        // The main configuration rolls its int8 MFMAs under the epilogue: two
+        // 32x32 tiles are in flight, and each tile's MFMA for the sub-block is
+        // issued as soon as the epilogue before it has read its register
+        // buffer; the next sub-block's activation fragment, weight factors
+        // and (at the chunk change) quant chunks are read from LDS while the
+        // current epilogue runs. The nibbles are unpacked right before each
+        // MFMA. The arithmetic per output is unchanged (same products, same
+        // order): measured 4% faster than issuing a sub-block's four MFMAs
+        // together. Each stage is pinned by a scheduling barrier.
+        const int tr = wm * 32 + lr;
+        const int tl0 = wm * 32 + 4 * lh;
+        auto ld_raw = [&](int cl, v4i (&raw)[TN]) {
 #pragma unroll
             for (int b = 0; b < TN; ++b)
-                bf[b] = h ? ((raw[b] >> 4) & 0x0f0f0f0f) : (raw[b] & 0x0f0f0f0f);
-            if constexpr (Q5) {
-                // Q5_K: this lane's 16 high-bit bytes (positions 16 lh.. of
-                // the row's sub-blocks), read per sub-block to keep registers
-                // free; bit 4 HF + j of every byte rotated to bit 4
-                const int rot = (4 * HF + j + 28) & 31;
+                raw[b] = *reinterpret_cast<const v4i *>(s.qs + 16 * q_slot((wn * TN + b) * 32 + lr, 2 * cl + lh));
+        };
+        auto ld_dv = [&](int j, float (&dv)[16]) {
 #pragma unroll
-                for (int b = 0; b < TN; ++b) {
-                    const v4i hq = *reinterpret_cast<const volatile v4i *>(
-                        s.qh + 16 * h_slot((wn * TN + b) * 32 + lr, lh));
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        bf[b][e] |= (int)(__builtin_rotateright32((uint32_t)hq[e], rot) & 0x10101010u);
-                }
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const float4 d4 = *reinterpret_cast<const float4 *>(&s.dx[j][tl0 + 8 * g4]);
+                dv[4 * g4] = d4.x;
+                dv[4 * g4 + 1] = d4.y;
+                dv[4 * g4 + 2] = d4.z;
+                dv[4 * g4 + 3] = d4.w;
             }
-#pragma unroll
-            for (int a = 0; a < TM; ++a) {
-                const int r = (wm * TM + a) * 32 + lr;
-                af[a] = *reinterpret_cast<const v4i *>(s.a + 16 * a_slot(r, 2 * j + lh));
-            }
-            v16i I[TM][TN];
-            // raised wave priority while the MFMAs issue, so that they are
-            // not queued behind the other wavefront's epilogue (measured +1.5%)
-            __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-            for (int a = 0; a < TM; ++a)
-#pragma unroll
-                for (int b = 0; b < TN; ++b)
-                    I[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[a], bf[b], v16i{}, 0, 0, 0);
-            __builtin_amdgcn_s_setprio(0);
-            float fw[TN];
+        };
+        auto ld_fw = [&](int j, float (&fw)[TN]) {
 #pragma unroll
             for (int b = 0; b < TN; ++b)
                 fw[b] = s.fw[j][(wn * TN + b) * 32 + lr];
+        };
+        // tile b's nibbles for sub-block parity h (low / high half of its chunk)
+        auto nib = [&](const v4i (&r)[TN], int h, int b) {
+            return h ? ((r[b] >> 4) & 0x0f0f0f0f) : (r[b] & 0x0f0f0f0f);
+        };
+        auto epi = [&](int b, const v16i &I, const float (&dv)[16], float f) {
 #pragma unroll
-            for (int a = 0; a < TM; ++a) {
+            for (int v = 0; v < 16; ++v)
+                acc[0][b][v] = fmaf((float)I[v], dv[v] * f, acc[0][b][v]);
+        };
+        v4i raw[TN];
+        ld_raw(0, raw);
+        v4i af = *reinterpret_cast<const v4i *>(s.a + 16 * a_slot(tr, lh));
+        float dv[16], fw[TN];
+        ld_fw(0, fw);
+        v16i X = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, nib(raw, 0, 0), v16i{}, 0, 0, 0);
+        v16i Y = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, nib(raw, 0, 1), v16i{}, 0, 0, 0);
 #pragma unroll
-                for (int g4 = 0; g4 < 4; ++g4) {
-                    const int tl = (wm * TM + a) * 32 + 8 * g4 + 4 * lh;
-                    const float4 d4 = *reinterpret_cast<const float4 *>(&s.dx[j][tl]);
-                    const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+        for (int j = 0; j < 4; ++j) {
+            const int h = j & 1;
+            v4i af_n = af, raw_n[TN];
+            float fw_n[TN];
+            ld_dv(j, dv);
+            if (j < 3) {
+                af_n = *reinterpret_cast<const v4i *>(s.a + 16 * a_slot(tr, 2 * (j + 1) + lh));
+                ld_fw(j + 1, fw_n);
+                if (j == 1)
+                    ld_raw(1, raw_n);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            epi(0, X, dv, fw[0]);
+            X = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, nib(raw, h, 2), v16i{}, 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            epi(1, Y, dv, fw[1]);
+            Y = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, nib(raw, h, 3), v16i{}, 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            epi(2, X, dv, fw[2]);
+            if (j < 3)   // the next sub-block: high nibbles of this chunk, or the next chunk
+                X = __builtin_amdgcn_mfma_i32_32x32x32_i8(af_n, nib(j == 1 ? raw_n : raw, h ^ 1, 0), v16i{}, 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            epi(3, Y, dv, fw[3]);
+            if (j < 3) {
+                Y = __builtin_amdgcn_mfma_i32_32x32x32_i8(af_n, nib(j == 1 ? raw_n : raw, h ^ 1, 1), v16i{}, 0, 0, 0);
+                af = af_n;
 #pragma unroll
+                for (int b = 0; b < TN; ++b) {
+                    fw[b] = fw_n[b];
+                    if (j == 1)
+                        raw[b] = raw_n[b];
+                }
+            }
+        }
+    } else {
+    #pragma unroll 1
+        for (int cl = 0; cl < 2; ++cl) {
+            v4i raw[TN];
+    #pragma unroll
+            for (int b = 0; b < TN; ++b) {
+                const int r = (wn * TN + b) * 32 + lr;
+                raw[b] = *reinterpret_cast<const v4i *>(s.qs + 16 * q_slot(r, 2 * cl + lh));
+            }
+    #pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int j = 2 * cl + h;            // sub-block within the step
+                v4i bf[TN], af[TM];
+    #pragma unroll
+                for (int b = 0; b < TN; ++b)
+                    bf[b] = h ? ((raw[b] >> 4) & 0x0f0f0f0f) : (raw[b] & 0x0f0f0f0f);
+                if constexpr (Q5) {
+                    // Q5_K: this lane's 16 high-bit bytes (positions 16 lh.. of
+                    // the row's sub-blocks), read per sub-block to keep registers
+                    // free; bit 4 HF + j of every byte rotated to bit 4
+                    const int rot = (4 * HF + j + 28) & 31;
+    #pragma unroll
                     for (int b = 0; b < TN; ++b) {
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const int v = 4 * g4 + r;
-                            acc[a][b][v] = fmaf((float)I[a][b][v], dv[r] * fw[b], acc[a][b][v]);
+                        const v4i hq = *reinterpret_cast<const volatile v4i *>(
+                            s.qh + 16 * h_slot((wn * TN + b) * 32 + lr, lh));
+    #pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            bf[b][e] |= (int)(__builtin_rotateright32((uint32_t)hq[e], rot) & 0x10101010u);
+                    }
+                }
+    #pragma unroll
+                for (int a = 0; a < TM; ++a) {
+                    const int r = (wm * TM + a) * 32 + lr;
+                    af[a] = *reinterpret_cast<const v4i *>(s.a + 16 * a_slot(r, 2 * j + lh));
+                }
+                v16i I[TM][TN];
+                // raised wave priority while the MFMAs issue, so that they are
+                // not queued behind the other wavefront's epilogue (measured +1.5%)
+                __builtin_amdgcn_s_setprio(1);
+    #pragma unroll
+                for (int a = 0; a < TM; ++a)
+    #pragma unroll
+                    for (int b = 0; b < TN; ++b)
+                        I[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[a], bf[b], v16i{}, 0, 0, 0);
+                __builtin_amdgcn_s_setprio(0);
+                float fw[TN];
+    #pragma unroll
+                for (int b = 0; b < TN; ++b)
+                    fw[b] = s.fw[j][(wn * TN + b) * 32 + lr];
+    #pragma unroll
+                for (int a = 0; a < TM; ++a) {
+    #pragma unroll
+                    for (int g4 = 0; g4 < 4; ++g4) {
+                        const int tl = (wm * TM + a) * 32 + 8 * g4 + 4 * lh;
+                        const float4 d4 = *reinterpret_cast<const float4 *>(&s.dx[j][tl]);
+                        const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+    #pragma unroll
+                        for (int b = 0; b < TN; ++b) {
+    #pragma unroll
+                            for (int r = 0; r < 4; ++r) {
+                                const int v = 4 * g4 + r;
+                                acc[a][b][v] = fmaf((float)I[a][b][v], dv[r] * fw[b], acc[a][b][v]);
+                            }
                         }
                     }
                 }
