@@ -11,14 +11,15 @@ decode GEMV rotates through enough weight copies (>= 1 GiB) that the 256 MB
 last-level cache cannot hold them, so its weight bytes come from HBM.
 
 Prints one JSON line: value = int8 ops of the whole step (2*M*N*K of both
-matmuls) per second, in TOPS, from two events around the K timed steps;
-"roofline" for the dominant kernel (the GEMM, MFMA-bound) and
-"decode_roofline" for the GEMV (HBM-bound), both from a second, instrumented
-pass over the same K steps: HIP events that the library records at each
+matmuls) per second, in TOPS, from the median of 21 windows of exactly K
+steps, each between two events (p10 / p90 beside it), after a warm-up of at
+least 0.5 s; "roofline" for the dominant kernel (the GEMM, MFMA-bound) and
+"decode_roofline" for the GEMV (HBM-bound), both from a second,
+instrumented pass over K steps: HIP events that the library records at each
 kernel's own dispatch start and end (mq_time_next_kernel, the quantity a
 kernel trace reports), with the events recorded around each call beside them
-("avg_us_call_bracket", which adds the launch gap); "cpu_baseline" = the
-CPU oracle timed on a bounded sample of the same GEMM.
+("avg_us_call_bracket", which adds the launch gap); "cpu_baseline" = the CPU
+oracle timed on the whole prefill GEMM (median of 3) and on one thread.
 
   python bench.py [--steps K] [--warmup W] [--no-cpu]
   python bench.py --all                  # per-matrix table of every workload
@@ -41,6 +42,8 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 INT8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA, published
 ROTATE_BYTES = 1 << 30       # weight copies for HBM-bound kernels
+WARMUP_S = 0.5               # warm-up of the contract run, at least
+WINDOWS = 21                 # timed windows of K steps each
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
     "gemm_q4k": "quant_gemm_amd/csrc/gemm_q4k.hip",
@@ -89,27 +92,41 @@ def q6k_gemv_bytes(M, N, K):
     return N * (K // 256) * 210 + M * (K + 4 * (K // 32)) + 4 * M * N
 
 
-def cpu_baseline(W, x, case, target_s):
-    """The oracle, as it is, on the first tokens of the prefill GEMM."""
+def cpu_baseline(W, x, case):
+    """The oracle, as it is, on the whole prefill GEMM: one warm-up run and
+    the median of three timed runs on all its OpenMP threads, plus the rate
+    of one thread on the first 128 tokens."""
     import numpy as np
     import oracle
     oracle.lib()
     threads = oracle.max_threads()
     q, d, _ = oracle.quantize_act(x)
-    ntok = 2
-    t0 = time.perf_counter()
-    oracle.matmul_q4k(W, q, d, case.N, case.K, tokens=np.arange(ntok))
-    t = time.perf_counter() - t0
-    ntok = int(max(2, min(case.M, ntok * target_s / max(t, 1e-6))))
-    t0 = time.perf_counter()
-    oracle.matmul_q4k(W, q, d, case.N, case.K, tokens=np.arange(ntok))
-    t = time.perf_counter() - t0
-    macs = ntok * case.N * case.K
+
+    def timed(tokens=None):
+        t0 = time.perf_counter()
+        oracle.matmul_q4k(W, q, d, case.N, case.K, tokens=tokens)
+        return time.perf_counter() - t0
+
+    warm = timed()
+    runs = [timed() for _ in range(3 if warm < 20.0 else 1)]
+    t = float(np.median(runs))
+    macs = case.M * case.N * case.K
+    ntok1 = min(128, case.M)
+    oracle.set_threads(1)
+    try:
+        t1 = timed(np.arange(ntok1))
+    finally:
+        oracle.set_threads(threads)
+    macs1 = ntok1 * case.N * case.K
     return {
-        "value": 2 * macs / t / 1e12, "unit": "TOPS", "cores": threads, "kind": "oracle",
-        "sample": (f"Q4_K matmul of tokens 0..{ntok - 1} of the M={case.M} prefill "
-                   f"(N={case.N}, K={case.K}): {macs:.3g} MACs in {t:.2f} s on {threads} "
-                   "OpenMP threads (plain C, integer group dots, f64 combination)"),
+        "value": round(2 * macs / t / 1e12, 4), "unit": "TOPS", "cores": threads, "kind": "oracle",
+        "host_cpus": os.cpu_count(),
+        "sample": (f"the whole Q4_K matmul of the M={case.M} prefill (N={case.N}, K={case.K}, "
+                   f"{macs:.3g} MACs): median of {len(runs)} runs after one warm-up, "
+                   f"{t:.2f} s each ({', '.join(f'{r:.2f}' for r in runs)} s) on {threads} OpenMP threads "
+                   "(plain C, integer group dots, f64 combination)"),
+        "one_thread": {"value": round(2 * macs1 / t1 / 1e12, 5), "unit": "TOPS", "cores": 1,
+                       "sample": f"tokens 0..{ntok1 - 1} of the same matmul, {t1:.2f} s"},
     }
 
 
@@ -200,22 +217,33 @@ def run_contract(args):
         mq.matmul_q4k(Wd[i % copies], qd, dd, sd, dec.N, dec.K, out=outd)
         if ev: ev[4].record()
 
-    log(f"[bench] warmup {args.warmup} steps")
-    for i in range(args.warmup):
-        step(i)
+    # Warm-up: the --warmup steps, continued until at least WARMUP_S seconds
+    # of steps have run, so that clocks and caches have settled.
+    log(f"[bench] warmup: {args.warmup} steps, at least {WARMUP_S} s")
+    t0 = time.perf_counter()
+    warm = 0
+    while warm < args.warmup or time.perf_counter() - t0 < WARMUP_S:
+        step(warm)
+        warm += 1
+        if warm % 8 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
-    # The timed region: exactly K steps and nothing else (no per-call events,
-    # whose marker packets would add GPU time to each step).
-    log(f"[bench] timing {args.steps} steps")
+    # The timed region: WINDOWS windows of exactly K steps each, every one
+    # between a synchronize and two events with nothing else in it (no
+    # per-call events, whose marker packets would add GPU time to each step).
+    log(f"[bench] timing {WINDOWS} windows of {args.steps} steps")
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record()
-    for i in range(args.steps):
-        step(i)
-    t_end.record()
-    torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
+    win_ms = []
+    for _ in range(WINDOWS):
+        torch.cuda.synchronize()
+        t_start.record()
+        for i in range(args.steps):
+            step(i)
+        t_end.record()
+        torch.cuda.synchronize()
+        win_ms.append(t_start.elapsed_time(t_end))
+    win_step = np.array(win_ms) / args.steps
     # A second pass over the same steps, instrumented: events around each call
     # and the kernels' own dispatch-boundary events (the roofline figures).
     log(f"[bench] per-kernel timing pass, {args.steps} steps")
@@ -235,8 +263,9 @@ def run_contract(args):
 
     ops_pre = pre.ops
     ops_dec = dec.ops
-    ms_step = total_ms / args.steps
+    ms_step = float(np.median(win_step))
     value = (ops_pre + ops_dec) / (ms_step * 1e-3) / 1e12
+    instr_ms_step = float(sum(v.mean() for v in per.values()))
 
     # roofline figures from the kernels' own durations (dispatch-boundary
     # events); the per-call event brackets are reported beside them
@@ -255,6 +284,11 @@ def run_contract(args):
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "ms_per_step_p10": round(float(np.percentile(win_step, 10)), 4),
+        "ms_per_step_p90": round(float(np.percentile(win_step, 90)), 4),
+        "timing": (f"median over {WINDOWS} windows of {args.steps} steps (events around each window); "
+                   f"warm-up {warm} steps, {WARMUP_S} s or more"),
+        "instrumented_ms_per_step": round(instr_ms_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -288,7 +322,7 @@ def run_contract(args):
     }
     if not args.no_cpu:
         log("[bench] CPU oracle baseline")
-        res["cpu_baseline"] = cpu_baseline(Wp_np, xp_np, pre, args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(Wp_np, xp_np, pre)
     print(json.dumps(res), flush=True)
 
 
@@ -604,7 +638,6 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--all", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--ceilings", action="store_true", help="read-stream and MFMA/VALU probes")

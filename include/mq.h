@@ -13,19 +13,25 @@
  *   - Pointers are device pointers owned by the caller. The calls enqueue
  *     kernels on `stream` (a hipStream_t passed as void*, NULL = the null
  *     stream) and return; nothing synchronizes. Inputs are read-only; outputs
- *     are overwritten. Two paths use a workspace: a GEMM with too few
- *     output tiles to fill the device splits K into nsplit*M*N f32 partial
- *     sums, and the decode FFN (mq_ffn_q4k at M <= 8) keeps g and u in
- *     2*M*N f32. The workspace is a device buffer the library keeps per
- *     (device, stream) and reuses; a call that needs more than it holds
- *     allocates a larger one (hipMalloc, at least twice the size, 2 MiB
- *     granules) and keeps the old one, which queued kernels or a captured
- *     graph may still read: no call frees memory or waits on the stream,
- *     and what is kept is at most about twice the largest request. Buffers
- *     stay allocated until the process ends. A failed allocation is
- *     MQ_ERR_LAUNCH. Calls from several host threads are safe; calls on one
- *     stream run in stream order, calls on different streams use different
- *     buffers.
+ *     are overwritten. The library never allocates or frees device memory
+ *     and keeps no buffers between calls: the buffers belong to the caller,
+ *     as they belong to the allocator and not to the kernels on the pages
+ *     (minfer Compute Graph Design, §1.4 Core invariants).
+ *   - Workspace. Two plans use scratch memory: a GEMM with too few output
+ *     tiles to fill the device splits K into nsplit [M][N] f32 planes of
+ *     partial sums (added in a fixed order, so results do not depend on
+ *     scheduling), and the fused FFN's two-pass form keeps g and u. The
+ *     *_ws entry points take that memory from the caller (ws, ws_bytes);
+ *     mq_matmul_workspace / mq_ffn_q4k_workspace give the bytes a call
+ *     with the same arguments needs (0 when its plan uses none). ws == NULL
+ *     (with ws_bytes == 0) selects the workspace-free plan: GEMMs never
+ *     split K, and the FFN runs its one-launch GEMM. A non-NULL ws must be
+ *     16-byte aligned and hold at least the bytes the query gives, else the
+ *     call fails with MQ_ERR_WORKSPACE and launches nothing. The entry
+ *     points without a ws argument take the workspace-free plan. The
+ *     workspace is read and written only by the kernels of the call that
+ *     receives it: calls in flight at the same time need distinct
+ *     workspaces (calls in order on one stream may share one).
  *   - Arguments are validated on the host before any HIP call. A failed
  *     check returns a nonzero mq_status and nothing is launched; the
  *     calling thread's mq_last_error() then names the argument and its value.
@@ -59,7 +65,13 @@
  *   out  f32  [M][N]     token-major output (minfer Compute Graph Design,
  *                        §7.1: activations and outputs are token-major)
  *
- * Alignment: W, q, d and s must be 16-byte aligned; x and out 4-byte aligned.
+ * Alignment: q, d and s must be 16-byte aligned; x and out 4-byte aligned.
+ * W: 16-byte aligned for Q4_K and Q5_K, whose block fields are read as
+ * 16-byte pieces (their rows are multiples of 16 bytes, so every row of an
+ * aligned matrix is aligned too); 4-byte aligned for Q6_K, whose 210-byte
+ * blocks fall on 2-byte boundaries within a row anyway and are read
+ * through aligned dwords (so a slice from any even-length row offset is
+ * accepted).
  */
 #ifndef MQ_H
 #define MQ_H
@@ -70,7 +82,7 @@
 extern "C" {
 #endif
 
-#define MQ_ABI_VERSION 3
+#define MQ_ABI_VERSION 4
 
 typedef enum {
     MQ_OK = 0,
@@ -79,8 +91,12 @@ typedef enum {
     MQ_ERR_ALIGN = 3,       /* a pointer is not aligned as required */
     MQ_ERR_UNSUPPORTED = 4, /* the current device is not gfx950 */
     MQ_ERR_DEVICE = 5,      /* a HIP runtime query failed */
-    MQ_ERR_LAUNCH = 6       /* the kernel launch failed */
+    MQ_ERR_LAUNCH = 6,      /* the kernel launch failed */
+    MQ_ERR_WORKSPACE = 7    /* the workspace is smaller than the call needs */
 } mq_status;
+
+/* Weight formats, for mq_matmul_workspace. */
+enum { MQ_FMT_Q4K = 0, MQ_FMT_Q5K = 1, MQ_FMT_Q6K = 2 };
 
 /* Kernel path selectors for the *_ex entry points. */
 enum { MQ_PATH_AUTO = 0, MQ_PATH_GEMV = 1, MQ_PATH_GEMM = 2 };
@@ -157,6 +173,8 @@ int mq_swiglu_quantize(const float *g, const float *u, int64_t M, int64_t K,
  * (Q4_K, Q5_K) / 32 (Q6_K) and 128-token tiles above. The GEMV serves up to
  * mq_gemv_max_m() tokens when forced.
  * W as described above; q, d, s from mq_quantize_act (s is required).
+ * Workspace-free plan: the GEMM never splits K (mq_matmul_q4k_ws, given a
+ * workspace, may).
  */
 int mq_matmul_q4k(const void *W, const int8_t *q, const float *d,
                   const float *s, int64_t M, int64_t N, int64_t K,
@@ -186,7 +204,7 @@ int mq_matmul_q5k(const void *W, const int8_t *q, const float *d,
  * As mq_matmul_q4k / mq_matmul_q5k / mq_matmul_q6k with the kernel chosen by `path`
  * (MQ_PATH_AUTO, MQ_PATH_GEMV, MQ_PATH_GEMM). MQ_PATH_GEMV requires
  * M <= mq_gemv_max_m() (M <= 8 for mq_ffn_q4k_ex). Both paths meet the same contract; tests use this
- * to check each path on the same inputs.
+ * to check each path on the same inputs. Workspace-free plan.
  */
 int mq_matmul_q4k_ex(const void *W, const int8_t *q, const float *d,
                      const float *s, int64_t M, int64_t N, int64_t K,
@@ -197,6 +215,30 @@ int mq_matmul_q5k_ex(const void *W, const int8_t *q, const float *d,
 int mq_matmul_q6k_ex(const void *W, const int8_t *q, const float *d,
                      const float *s, int64_t M, int64_t N, int64_t K,
                      float *out, void *stream, int path);
+
+/*
+ * The matmuls with a caller workspace (see the conventions above): the
+ * same result and contract, and the full plan, which may split K over the
+ * workspace when the output has too few tiles to fill the device.
+ * mq_matmul_workspace writes to *bytes the workspace a matmul of format fmt
+ * (MQ_FMT_Q4K / Q5K / Q6K) with these M, N, K and path needs: 0 when its
+ * plan splits nothing, else nsplit * M * N * 4. It validates M, N, K and
+ * path as the matmul does.
+ */
+int mq_matmul_workspace(int fmt, int64_t M, int64_t N, int64_t K, int path,
+                        int64_t *bytes);
+int mq_matmul_q4k_ws(const void *W, const int8_t *q, const float *d,
+                     const float *s, int64_t M, int64_t N, int64_t K,
+                     float *out, void *ws, int64_t ws_bytes, void *stream,
+                     int path);
+int mq_matmul_q5k_ws(const void *W, const int8_t *q, const float *d,
+                     const float *s, int64_t M, int64_t N, int64_t K,
+                     float *out, void *ws, int64_t ws_bytes, void *stream,
+                     int path);
+int mq_matmul_q6k_ws(const void *W, const int8_t *q, const float *d,
+                     const float *s, int64_t M, int64_t N, int64_t K,
+                     float *out, void *ws, int64_t ws_bytes, void *stream,
+                     int path);
 
 /*
  * Fused FFN up half: the gate and up projections and SwiGLU in one call,
@@ -211,14 +253,19 @@ int mq_matmul_q6k_ex(const void *W, const int8_t *q, const float *d,
  *       what mq_quantize_act would write for y);
  *   y  optional f32 [M][N], written when not NULL.
  * Wg and Wu are N rows of K each (Q4_K layout); N is a positive multiple of
- * 256 (it is the down projection's K). Above 128 tokens one GEMM launch
- * does it all: its tiles pair 64 gate rows with the same 64 up rows and
- * apply SwiGLU and the quantizer in their epilogue. Up to 128 tokens it
- * runs in two passes: g and u into the stream's workspace (see the
- * conventions above), then the SwiGLU quantizer. The first pass is the
- * GEMV up to 8 tokens under MQ_PATH_AUTO (both matrices as one persistent
- * stream where the plane fits it) and the GEMMs above; MQ_PATH_GEMV forces
- * the GEMV (M <= 8), MQ_PATH_GEMM the GEMMs.
+ * 256 (it is the down projection's K).
+ * Plans. mq_ffn_q4k_ws with a workspace: up to 128 tokens in two passes,
+ * g and u into the workspace (2*M*N f32, followed by the split-K planes of
+ * the GEMMs when they split), then the SwiGLU quantizer. The first pass is
+ * the GEMV up to 8 tokens under MQ_PATH_AUTO (both matrices as one
+ * persistent stream where the plane fits it) and the GEMMs above;
+ * MQ_PATH_GEMV forces the GEMV (M <= 8), MQ_PATH_GEMM the GEMMs. Above 128
+ * tokens, and at every M without a workspace (mq_ffn_q4k, mq_ffn_q4k_ex,
+ * or ws == NULL), one GEMM launch does it all: its tiles pair 64 gate rows
+ * with the same 64 up rows and apply SwiGLU and the quantizer in their
+ * epilogue. MQ_PATH_GEMV without a workspace is MQ_ERR_WORKSPACE.
+ * mq_ffn_q4k_workspace gives the bytes of the two-pass form (0 where the
+ * one-launch GEMM runs); it validates M, N, K and path as the call does.
  * Alignment as for the matmuls; qo, do_, so and y 16-byte aligned.
  */
 int mq_ffn_q4k(const void *Wg, const void *Wu, const int8_t *q, const float *d,
@@ -227,6 +274,11 @@ int mq_ffn_q4k(const void *Wg, const void *Wu, const int8_t *q, const float *d,
 int mq_ffn_q4k_ex(const void *Wg, const void *Wu, const int8_t *q, const float *d,
                   const float *s, int64_t M, int64_t N, int64_t K, int8_t *qo,
                   float *do_, float *so, float *y, void *stream, int path);
+int mq_ffn_q4k_workspace(int64_t M, int64_t N, int64_t K, int path, int64_t *bytes);
+int mq_ffn_q4k_ws(const void *Wg, const void *Wu, const int8_t *q, const float *d,
+                  const float *s, int64_t M, int64_t N, int64_t K, int8_t *qo,
+                  float *do_, float *so, float *y, void *ws, int64_t ws_bytes,
+                  void *stream, int path);
 
 /*
  * Registration-time weight planes for the prefill GEMM. The pages build
@@ -241,7 +293,8 @@ int mq_ffn_q4k_ex(const void *Wg, const void *Wu, const int8_t *q, const float *
  * mq_expand_q6k: W (Q6_K, N rows of K) -> lo, hi int8 [N][K] and dw f32
  * [N][K/256]: for every weight p = sc_g * (q - 32) (g its 16-value group,
  * p in -4064..4096) is lo + 64 * hi with lo in 0..63, hi in -64..64; dw is
- * each super-block's d. Exact. W, lo, hi, dw 16-byte aligned.
+ * each super-block's d. Exact. W 4-byte aligned; lo, hi, dw 16-byte
+ * aligned.
  */
 int mq_expand_q6k(const void *W, int64_t N, int64_t K, int8_t *lo, int8_t *hi,
                   float *dw, void *stream);
@@ -251,10 +304,13 @@ int mq_expand_q6k(const void *W, int64_t N, int64_t K, int8_t *lo, int8_t *hi,
  * mq_matmul_q6k on the blocks they were built from (f32, within its
  * tolerance), always on the int8 MFMA GEMM (32-token tiles up to M = 32).
  * lo, hi 16-byte aligned, dw 4-byte aligned; q, d, out as for the matmuls.
+ * ws / ws_bytes as for mq_matmul_q6k_ws with MQ_PATH_GEMM (the same split
+ * of K; NULL = no split).
  */
 int mq_matmul_q6k_x(const int8_t *lo, const int8_t *hi, const float *dw,
                     const int8_t *q, const float *d, int64_t M, int64_t N,
-                    int64_t K, float *out, void *stream);
+                    int64_t K, float *out, void *ws, int64_t ws_bytes,
+                    void *stream);
 
 /*
  * mq_dsc_q4k: W (Q4_K, N rows of K) -> fw, fm f32 [N][K/32] with
@@ -269,10 +325,12 @@ int mq_dsc_q4k(const void *W, int64_t N, int64_t K, float *fw, float *fm,
  * decoded-scale planes (no block header decoded per tile): the same result
  * and contract as mq_matmul_q4k, always on the GEMM (32-token tiles up to
  * M = 64). fw, fm as built by mq_dsc_q4k from this W; s is required.
+ * ws / ws_bytes as for mq_matmul_q4k_ws with MQ_PATH_GEMM.
  */
 int mq_matmul_q4k_dsc(const void *W, const float *fw, const float *fm,
                       const int8_t *q, const float *d, const float *s,
-                      int64_t M, int64_t N, int64_t K, float *out, void *stream);
+                      int64_t M, int64_t N, int64_t K, float *out, void *ws,
+                      int64_t ws_bytes, void *stream);
 
 /*
  * Measurement hook. The next matmul call of the calling thread (mq_matmul_*,
@@ -282,7 +340,8 @@ int mq_matmul_q4k_dsc(const void *W, const float *fw, const float *fm,
  * hipEventElapsedTime gives the kernel's duration without the launch gap an
  * event recorded before the call would include. A split-K GEMM's reduction
  * kernel is not covered. The request is consumed by that call, and dropped
- * by any other mq_* call in between. Always returns MQ_OK.
+ * by any other mq_* call in between that launches kernels (the workspace
+ * queries leave it). Always returns MQ_OK.
  */
 int mq_time_next_kernel(void *start_event, void *stop_event);
 

@@ -660,29 +660,42 @@ __global__ __launch_bounds__(NTHR, MQ_Q4K_OCC) void gemm_q4k_kernel(
 
 } // namespace
 
+namespace {
+// K ranges of a launch (see gemm_splits); tiles of BM x BN outputs
+int nsplit_for(int M, int N, int K)
+{
+    const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    return gemm_splits(tiles, BM * BN, K >> 8, M, N, K, Q4K_SLOT_OPS);
+}
+} // namespace
+
 #if MQ_Q5K && defined(MQ_Q4K_SMALL)
+int splits_gemm_q5k_small(int M, int N, int K) { return nsplit_for(M, N, K); }
 hipError_t launch_gemm_q5k_small(const uint8_t *W, const int8_t *q, const float *d,
                                  const float *s, int M, int N, int K, float *out,
-                                 hipStream_t st)
+                                 const Ws &ws, hipStream_t st)
 #elif MQ_Q5K
+int splits_gemm_q5k(int M, int N, int K) { return nsplit_for(M, N, K); }
 hipError_t launch_gemm_q5k(const uint8_t *W, const int8_t *q, const float *d,
                            const float *s, int M, int N, int K, float *out,
-                           hipStream_t st)
+                           const Ws &ws, hipStream_t st)
 #elif defined(MQ_Q4K_SMALL)
+int splits_gemm_q4k_small(int M, int N, int K) { return nsplit_for(M, N, K); }
 hipError_t launch_gemm_q4k_small(const uint8_t *W, const int8_t *q, const float *d,
                                  const float *s, int M, int N, int K, float *out,
-                                 hipStream_t st)
+                                 const Ws &ws, hipStream_t st)
 #else
+int splits_gemm_q4k(int M, int N, int K) { return nsplit_for(M, N, K); }
 hipError_t launch_gemm_q4k(const uint8_t *W, const int8_t *q, const float *d,
                            const float *s, int M, int N, int K, float *out,
-                           hipStream_t st)
+                           const Ws &ws, hipStream_t st)
 #endif
 {
     const int tiles_m = (M + BM - 1) / BM;
     const int tiles_n = (N + BN - 1) / BN;
     const int tiles = tiles_m * tiles_n;
-    const int nsplit = gemm_splits(tiles, BM * BN, K >> 8, M, N, K, Q4K_SLOT_OPS);
-    return run_split_k(nsplit, (int64_t)M * N, out, st, [&](float *dst) {
+    const int nsplit = ws.ptr ? nsplit_for(M, N, K) : 1;
+    return run_split_k(nsplit, (int64_t)M * N, out, ws, st, [&](float *dst) {
         launch(gemm_q4k_kernel<false, false>, dim3((unsigned)(tiles * nsplit)), dim3(NTHR), 0, st, 
             W, nullptr, Dsc{nullptr, nullptr}, q, d, s, M, N, K, tiles_m, nsplit, dst, nullptr, nullptr, nullptr);
         return hipGetLastError();
@@ -693,18 +706,18 @@ hipError_t launch_gemm_q4k(const uint8_t *W, const int8_t *q, const float *d,
 #ifdef MQ_Q4K_SMALL
 hipError_t launch_gemm_q4k_dsc_small(const uint8_t *W, const float *fw, const float *fm, const int8_t *q,
                                      const float *d, const float *s, int M, int N, int K, float *out,
-                                     hipStream_t st)
+                                     const Ws &ws, hipStream_t st)
 #else
 hipError_t launch_gemm_q4k_dsc(const uint8_t *W, const float *fw, const float *fm, const int8_t *q,
                                const float *d, const float *s, int M, int N, int K, float *out,
-                               hipStream_t st)
+                               const Ws &ws, hipStream_t st)
 #endif
 {
     const int tiles_m = (M + BM - 1) / BM;
     const int tiles_n = (N + BN - 1) / BN;
     const int tiles = tiles_m * tiles_n;
-    const int nsplit = gemm_splits(tiles, BM * BN, K >> 8, M, N, K, Q4K_SLOT_OPS);
-    return run_split_k(nsplit, (int64_t)M * N, out, st, [&](float *dst) {
+    const int nsplit = ws.ptr ? nsplit_for(M, N, K) : 1;
+    return run_split_k(nsplit, (int64_t)M * N, out, ws, st, [&](float *dst) {
         launch(gemm_q4k_kernel<false, true>, dim3((unsigned)(tiles * nsplit)), dim3(NTHR), 0, st, 
             W, nullptr, Dsc{fw, fm}, q, d, s, M, N, K, tiles_m, nsplit, dst, nullptr, nullptr, nullptr);
         return hipGetLastError();

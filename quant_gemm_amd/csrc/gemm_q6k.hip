@@ -62,8 +62,6 @@ constexpr int NWAVES = WM * WN;
 constexpr int NTHR = 64 * NWAVES;
 // int8 ops per second of one resident workgroup, for the split-K choice
 constexpr double Q6K_SLOT_OPS = 0.6e12;
-// the same split choice for the expansion planes, so both give one result
-constexpr double Q6K_X_SLOT_OPS = Q6K_SLOT_OPS;
 constexpr int A_CHUNKS = BM * BK / 16;      // 16-byte activation chunks per step
 static_assert(A_CHUNKS % (64 * NWAVES) == 0, "DMA split");
 static_assert(NTHR == 2 * BN && NTHR >= BM, "one thread per (row, half) and per token");
@@ -474,19 +472,31 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_q6k_kernel(
 
 } // namespace
 
+namespace {
+// K ranges of a launch (see gemm_splits); tiles of BM x BN outputs. The
+// expansion-plane GEMM takes the same choice, so both give one result.
+int nsplit_for(int M, int N, int K)
+{
+    const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    return gemm_splits(tiles, BM * BN, K >> 8, M, N, K, Q6K_SLOT_OPS);
+}
+} // namespace
+
 #ifdef MQ_Q6K_SMALL
+int splits_gemm_q6k_small(int M, int N, int K) { return nsplit_for(M, N, K); }
 hipError_t launch_gemm_q6k_small(const uint8_t *W, const int8_t *q, const float *d,
-                                 int M, int N, int K, float *out, hipStream_t st)
+                                 int M, int N, int K, float *out, const Ws &ws, hipStream_t st)
 #else
+int splits_gemm_q6k(int M, int N, int K) { return nsplit_for(M, N, K); }
 hipError_t launch_gemm_q6k(const uint8_t *W, const int8_t *q, const float *d,
-                           int M, int N, int K, float *out, hipStream_t st)
+                           int M, int N, int K, float *out, const Ws &ws, hipStream_t st)
 #endif
 {
     const int tiles_m = (M + BM - 1) / BM;
     const int tiles_n = (N + BN - 1) / BN;
     const int tiles = tiles_m * tiles_n;
-    const int nsplit = gemm_splits(tiles, BM * BN, K >> 8, M, N, K, Q6K_SLOT_OPS);
-    return run_split_k(nsplit, (int64_t)M * N, out, st, [&](float *dst) {
+    const int nsplit = ws.ptr ? nsplit_for(M, N, K) : 1;
+    return run_split_k(nsplit, (int64_t)M * N, out, ws, st, [&](float *dst) {
         launch(gemm_q6k_kernel<const uint8_t *>, dim3((unsigned)(tiles * nsplit)), dim3(NTHR), 0, st, W, q, d, M, N, K, tiles_m,
                                                                                  nsplit, dst);
         return hipGetLastError();
@@ -495,18 +505,19 @@ hipError_t launch_gemm_q6k(const uint8_t *W, const int8_t *q, const float *d,
 
 #ifdef MQ_Q6K_SMALL
 hipError_t launch_gemm_q6k_x_small(const int8_t *lo, const int8_t *hi, const float *dw, const int8_t *q,
-                                   const float *d, int M, int N, int K, float *out, hipStream_t st)
+                                   const float *d, int M, int N, int K, float *out, const Ws &ws,
+                                   hipStream_t st)
 #else
 hipError_t launch_gemm_q6k_x(const int8_t *lo, const int8_t *hi, const float *dw, const int8_t *q,
-                             const float *d, int M, int N, int K, float *out, hipStream_t st)
+                             const float *d, int M, int N, int K, float *out, const Ws &ws, hipStream_t st)
 #endif
 {
     const int tiles_m = (M + BM - 1) / BM;
     const int tiles_n = (N + BN - 1) / BN;
     const int tiles = tiles_m * tiles_n;
-    const int nsplit = gemm_splits(tiles, BM * BN, K >> 8, M, N, K, Q6K_X_SLOT_OPS);
+    const int nsplit = ws.ptr ? nsplit_for(M, N, K) : 1;
     const Planes E{lo, hi, dw};
-    return run_split_k(nsplit, (int64_t)M * N, out, st, [&](float *dst) {
+    return run_split_k(nsplit, (int64_t)M * N, out, ws, st, [&](float *dst) {
         launch(gemm_q6k_kernel<Planes>, dim3((unsigned)(tiles * nsplit)), dim3(NTHR), 0, st, E, q, d, M, N, K, tiles_m,
                                                                                  nsplit, dst);
         return hipGetLastError();

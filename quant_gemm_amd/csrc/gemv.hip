@@ -915,13 +915,14 @@ __global__ __launch_bounds__(64 * Q6S_WAVES) void gemv_q6k_stream_kernel(
     auto issue = [&](int it) {
         const int ic = min(it, nitems - 1);
         const int ri = ic / nseg, seg = ic - ri * nseg;
-        const int64_t rs = (int64_t)(w + ri * nw) * rowb + (int64_t)seg * (Q6S_SEG * 210);
+        const uintptr_t ab = reinterpret_cast<uintptr_t>(W) + (uintptr_t)((int64_t)(w + ri * nw) * rowb +
+                                                                          (int64_t)seg * (Q6S_SEG * 210));
         const int nbytes = min(Q6S_SEG, nb - seg * Q6S_SEG) * 210;
-        const int64_t c0 = rs >> 4, c1 = (rs + nbytes - 1) >> 4;
+        const uintptr_t c0 = ab >> 4, c1 = (ab + nbytes - 1) >> 4;
         uint8_t *slot = ring + (it % Q6S_D) * Q6S_SLOT;
 #pragma unroll
         for (int i = 0; i < Q6S_DMA; ++i)
-            dma16(W + 16 * min(c0 + 64 * i + lane, c1), slot + 1024 * i);
+            dma16(reinterpret_cast<const uint8_t *>(16 * min(c0 + 64 * i + lane, c1)), slot + 1024 * i);
     };
 
     // Activation plane -> LDS: all loads first (one memory latency), with the
@@ -975,8 +976,9 @@ __global__ __launch_bounds__(64 * Q6S_WAVES) void gemv_q6k_stream_kernel(
         const int blk = seg * Q6S_SEG + bl;
         if (blk < nb) {
             const uint8_t *sl = ring + (it % Q6S_D) * Q6S_SLOT;
-            const int64_t rs = (int64_t)n * rowb + (int64_t)seg * (Q6S_SEG * 210);
-            const int p = (int)(rs & 15) + 210 * bl;    // this block in the slot
+            const uintptr_t ab = reinterpret_cast<uintptr_t>(W) + (uintptr_t)((int64_t)n * rowb +
+                                                                              (int64_t)seg * (Q6S_SEG * 210));
+            const int p = (int)(ab & 15) + 210 * bl;    // this block in the slot
             uint32_t l0[4], l1[4], h[4], sc[2], dw[1];
             lds_dwords_a2<4>(sl, p + 64 * g + 16 * hh, l0);
             lds_dwords_a2<4>(sl, p + 64 * g + 32 + 16 * hh, l1);
@@ -1231,9 +1233,21 @@ hipError_t launch_gemv_q5k(const uint8_t *W, const int8_t *q, const float *d,
     return gemv_q5k_mt<16>(W, q, d, s, M, N, K, out, st);
 }
 
+// The GEMMs of the two-pass FFN: the configuration of the token count.
+static int ffn_gemm_splits(int M, int N, int K)
+{
+    return M <= GEMM_SMALL_M_Q4K ? splits_gemm_q4k_small(M, N, K) : splits_gemm_q4k(M, N, K);
+}
+
+size_t ffn_two_pass_bytes(int M, int N, int K, bool gemv)
+{
+    const size_t gu = (size_t)2 * M * N * sizeof(float);
+    return gemv ? gu : gu + split_bytes(ffn_gemm_splits(M, N, K), M, N);
+}
+
 hipError_t launch_ffn_q4k_two_pass(const uint8_t *Wg, const uint8_t *Wu, const int8_t *q, const float *d,
                                    const float *s, int M, int N, int K, int8_t *qo, float *do_, float *so,
-                                   float *y, bool gemv, hipStream_t st)
+                                   float *y, bool gemv, const Ws &ws, hipStream_t st)
 {
     // Where the persistent stream takes the plane, both matrices run as one
     // stream of 2N rows. (A single GEMV kernel with the SwiGLU in its
@@ -1241,10 +1255,13 @@ hipError_t launch_ffn_q4k_two_pass(const uint8_t *Wg, const uint8_t *Wu, const i
     // slower than these launches at every M <= 8 on 18944 x 3584: its N / 32
     // equal work units leave a tail, and each wavefront streams its rows
     // without the persistent kernel's pipelining.)
-    WsLease ws((size_t)2 * M * N * sizeof(float), st, WS_FFN);
-    if (ws.err != hipSuccess)
-        return ws.err;
+    // Workspace: g [M][N], u [M][N], then the GEMMs' split-K planes (the two
+    // GEMMs run one after the other on st and reuse them).
+    if (!ws.ptr || ws.bytes < ffn_two_pass_bytes(M, N, K, gemv))
+        return hipErrorInvalidValue;
     float *g = static_cast<float *>(ws.ptr), *u = g + (int64_t)M * N;
+    const size_t gu = (size_t)2 * M * N * sizeof(float);
+    const Ws split{static_cast<uint8_t *>(ws.ptr) + gu, ws.bytes - gu};
     hipError_t e;
     if (gemv && q4k_stream_fits(M, K)) {
         e = launch_gemv_q4k_pair(Wg, Wu, q, d, s, M, N, K, g, u, st);
@@ -1253,8 +1270,8 @@ hipError_t launch_ffn_q4k_two_pass(const uint8_t *Wg, const uint8_t *Wu, const i
             if (gemv)
                 return launch_gemv_q4k(W, q, d, s, M, N, K, o, st);
             if (M <= GEMM_SMALL_M_Q4K)
-                return launch_gemm_q4k_small(W, q, d, s, M, N, K, o, st);
-            return launch_gemm_q4k(W, q, d, s, M, N, K, o, st);
+                return launch_gemm_q4k_small(W, q, d, s, M, N, K, o, split, st);
+            return launch_gemm_q4k(W, q, d, s, M, N, K, o, split, st);
         };
         e = mm(Wg, g);
         if (e == hipSuccess)

@@ -26,8 +26,9 @@ namespace {
 
 thread_local char g_err[512];
 
-// Entry points that launch no matmul kernel drop a pending timing request,
-// so it can only ever attach to the matmul call that follows it.
+// Entry points that launch kernels other than a matmul's drop a pending
+// timing request, so it can only ever attach to the matmul call that follows
+// it (the workspace queries launch nothing and leave it).
 void drop_timing() { mq::kernel_events() = mq::KernelEvents{}; }
 
 int fail(int status, const char *fmt, ...)
@@ -91,18 +92,16 @@ int check_K(int64_t K, const char *fn)
     return MQ_OK;
 }
 
-enum class Fmt { Q4K, Q5K, Q6K };
+enum class Fmt { Q4K = MQ_FMT_Q4K, Q5K = MQ_FMT_Q5K, Q6K = MQ_FMT_Q6K };
 
-int matmul(Fmt fmt, const void *W, const int8_t *q, const float *d, const float *s,
-           int64_t M, int64_t N, int64_t K, float *out, void *stream, int path)
+const char *fmt_fn(Fmt fmt)
 {
-    const bool q6 = fmt == Fmt::Q6K;
-    const char *fn = q6 ? "mq_matmul_q6k" : fmt == Fmt::Q5K ? "mq_matmul_q5k" : "mq_matmul_q4k";
-    if (!W) return fail(MQ_ERR_INVALID_ARG, "%s: W is NULL", fn);
-    if (!q) return fail(MQ_ERR_INVALID_ARG, "%s: q is NULL", fn);
-    if (!d) return fail(MQ_ERR_INVALID_ARG, "%s: d is NULL", fn);
-    if (!q6 && !s) return fail(MQ_ERR_INVALID_ARG, "%s: s is NULL (the min term needs it)", fn);
-    if (!out) return fail(MQ_ERR_INVALID_ARG, "%s: out is NULL", fn);
+    return fmt == Fmt::Q6K ? "mq_matmul_q6k" : fmt == Fmt::Q5K ? "mq_matmul_q5k" : "mq_matmul_q4k";
+}
+
+// Shape and path checks shared by a matmul and its workspace query.
+int check_matmul_shape(const char *fn, int64_t M, int64_t N, int64_t K, int path)
+{
     if (M <= 0) return fail(MQ_ERR_INVALID_ARG, "%s: M=%lld must be positive", fn, (long long)M);
     if (N <= 0) return fail(MQ_ERR_INVALID_ARG, "%s: N=%lld must be positive", fn, (long long)N);
     if (int rc = check_K(K, fn)) return rc;
@@ -114,42 +113,109 @@ int matmul(Fmt fmt, const void *W, const int8_t *q, const float *d, const float 
     if (path == MQ_PATH_GEMV && M > mq::GEMV_MAX_M)
         return fail(MQ_ERR_INVALID_ARG, "%s: path=MQ_PATH_GEMV needs M <= %d, got M=%lld", fn,
                     mq::GEMV_MAX_M, (long long)M);
-    if (!aligned(W, 16)) return fail(MQ_ERR_ALIGN, "%s: W=%p is not 16-byte aligned", fn, W);
-    if (!aligned(q, 16)) return fail(MQ_ERR_ALIGN, "%s: q=%p is not 16-byte aligned", fn, (const void *)q);
-    if (!aligned(d, 16)) return fail(MQ_ERR_ALIGN, "%s: d=%p is not 16-byte aligned", fn, (const void *)d);
-    if (s && !aligned(s, 16)) return fail(MQ_ERR_ALIGN, "%s: s=%p is not 16-byte aligned", fn, (const void *)s);
-    if (!aligned(out, 4)) return fail(MQ_ERR_ALIGN, "%s: out=%p is not 4-byte aligned", fn, (const void *)out);
     // grid sizes must fit the launch limits
     const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
     if (tiles > kMaxDim)
         return fail(MQ_ERR_SHAPE, "%s: M=%lld x N=%lld needs too many tiles", fn, (long long)M, (long long)N);
-    if (int rc = check_device()) return rc;
+    return MQ_OK;
+}
 
+// The kernel a matmul runs: the GEMV, or the GEMM in its small-M or its
+// main configuration.
+enum class Kern { GEMV, GEMM_SMALL, GEMM };
+
+Kern matmul_kernel(Fmt fmt, int64_t M, int64_t N, int64_t K, int path)
+{
+    const bool q6 = fmt == Fmt::Q6K;
     const bool gemv = path == MQ_PATH_GEMV ||
                       (path == MQ_PATH_AUTO && (fmt == Fmt::Q5K ? mq::gemv_auto_q5k(M, N, K)
                                                                 : mq::gemv_auto(q6, M, N, K)));
+    if (gemv)
+        return Kern::GEMV;
+    const int small = q6 ? mq::GEMM_SMALL_M_Q6K : fmt == Fmt::Q5K ? mq::GEMM_SMALL_M_Q5K : mq::GEMM_SMALL_M_Q4K;
+    return M <= small ? Kern::GEMM_SMALL : Kern::GEMM;
+}
+
+// Workspace bytes of the full plan of a GEMM configuration (0 = none).
+size_t gemm_ws_bytes(Fmt fmt, Kern kern, int64_t M, int64_t N, int64_t K)
+{
+    const int m = (int)M, n = (int)N, k = (int)K;
+    int s = 1;
+    if (kern == Kern::GEMM_SMALL)
+        s = fmt == Fmt::Q6K ? mq::splits_gemm_q6k_small(m, n, k)
+          : fmt == Fmt::Q5K ? mq::splits_gemm_q5k_small(m, n, k) : mq::splits_gemm_q4k_small(m, n, k);
+    else if (kern == Kern::GEMM)
+        s = fmt == Fmt::Q6K ? mq::splits_gemm_q6k(m, n, k)
+          : fmt == Fmt::Q5K ? mq::splits_gemm_q5k(m, n, k) : mq::splits_gemm_q4k(m, n, k);
+    return mq::split_bytes(s, M, N);
+}
+
+// The caller's workspace argument: NULL (with ws_bytes 0) selects the
+// workspace-free plan; otherwise it must be 16-byte aligned and hold
+// `need` bytes.
+int check_ws(const char *fn, const void *ws, int64_t ws_bytes, size_t need)
+{
+    if (ws_bytes < 0)
+        return fail(MQ_ERR_INVALID_ARG, "%s: ws_bytes=%lld is negative", fn, (long long)ws_bytes);
+    if (!ws) {
+        if (ws_bytes != 0)
+            return fail(MQ_ERR_INVALID_ARG, "%s: ws is NULL but ws_bytes=%lld", fn, (long long)ws_bytes);
+        return MQ_OK;
+    }
+    if (!aligned(ws, 16)) return fail(MQ_ERR_ALIGN, "%s: ws=%p is not 16-byte aligned", fn, ws);
+    if ((uint64_t)ws_bytes < (uint64_t)need)
+        return fail(MQ_ERR_WORKSPACE, "%s: the workspace holds %lld bytes, this call needs %llu", fn,
+                    (long long)ws_bytes, (unsigned long long)need);
+    return MQ_OK;
+}
+
+int matmul(Fmt fmt, const void *W, const int8_t *q, const float *d, const float *s,
+           int64_t M, int64_t N, int64_t K, float *out, void *ws, int64_t ws_bytes, void *stream, int path)
+{
+    const bool q6 = fmt == Fmt::Q6K;
+    const char *fn = fmt_fn(fmt);
+    if (!W) return fail(MQ_ERR_INVALID_ARG, "%s: W is NULL", fn);
+    if (!q) return fail(MQ_ERR_INVALID_ARG, "%s: q is NULL", fn);
+    if (!d) return fail(MQ_ERR_INVALID_ARG, "%s: d is NULL", fn);
+    if (!q6 && !s) return fail(MQ_ERR_INVALID_ARG, "%s: s is NULL (the min term needs it)", fn);
+    if (!out) return fail(MQ_ERR_INVALID_ARG, "%s: out is NULL", fn);
+    if (int rc = check_matmul_shape(fn, M, N, K, path)) return rc;
+    // Q4_K / Q5_K blocks are read as 16-byte pieces (their rows are whole
+    // multiples of 16 bytes); Q6_K blocks are 2-byte aligned within a row
+    // and read through aligned dwords, so W needs 4 bytes.
+    if (!aligned(W, q6 ? 4 : 16))
+        return fail(MQ_ERR_ALIGN, "%s: W=%p is not %d-byte aligned", fn, W, q6 ? 4 : 16);
+    if (!aligned(q, 16)) return fail(MQ_ERR_ALIGN, "%s: q=%p is not 16-byte aligned", fn, (const void *)q);
+    if (!aligned(d, 16)) return fail(MQ_ERR_ALIGN, "%s: d=%p is not 16-byte aligned", fn, (const void *)d);
+    if (s && !aligned(s, 16)) return fail(MQ_ERR_ALIGN, "%s: s=%p is not 16-byte aligned", fn, (const void *)s);
+    if (!aligned(out, 4)) return fail(MQ_ERR_ALIGN, "%s: out=%p is not 4-byte aligned", fn, (const void *)out);
+    const Kern kern = matmul_kernel(fmt, M, N, K, path);
+    if (int rc = check_ws(fn, ws, ws_bytes, ws ? gemm_ws_bytes(fmt, kern, M, N, K) : 0)) return rc;
+    if (int rc = check_device()) return rc;
+
     const auto *Wb = static_cast<const uint8_t *>(W);
     hipStream_t st = static_cast<hipStream_t>(stream);
+    const mq::Ws w{ws, (size_t)ws_bytes};
     const int m = (int)M, n = (int)N, k = (int)K;
     hipError_t e;
-    if (q6 && gemv)
+    if (q6 && kern == Kern::GEMV)
         e = mq::launch_gemv_q6k(Wb, q, d, m, n, k, out, st);
-    else if (q6 && m <= mq::GEMM_SMALL_M_Q6K)
-        e = mq::launch_gemm_q6k_small(Wb, q, d, m, n, k, out, st);
+    else if (q6 && kern == Kern::GEMM_SMALL)
+        e = mq::launch_gemm_q6k_small(Wb, q, d, m, n, k, out, w, st);
     else if (q6)
-        e = mq::launch_gemm_q6k(Wb, q, d, m, n, k, out, st);
-    else if (fmt == Fmt::Q5K && gemv)
+        e = mq::launch_gemm_q6k(Wb, q, d, m, n, k, out, w, st);
+    else if (fmt == Fmt::Q5K && kern == Kern::GEMV)
         e = mq::launch_gemv_q5k(Wb, q, d, s, m, n, k, out, st);
-    else if (fmt == Fmt::Q5K && m <= mq::GEMM_SMALL_M_Q5K)
-        e = mq::launch_gemm_q5k_small(Wb, q, d, s, m, n, k, out, st);
+    else if (fmt == Fmt::Q5K && kern == Kern::GEMM_SMALL)
+        e = mq::launch_gemm_q5k_small(Wb, q, d, s, m, n, k, out, w, st);
     else if (fmt == Fmt::Q5K)
-        e = mq::launch_gemm_q5k(Wb, q, d, s, m, n, k, out, st);
-    else if (gemv)
+        e = mq::launch_gemm_q5k(Wb, q, d, s, m, n, k, out, w, st);
+    else if (kern == Kern::GEMV)
         e = mq::launch_gemv_q4k(Wb, q, d, s, m, n, k, out, st);
-    else if (m <= mq::GEMM_SMALL_M_Q4K)
-        e = mq::launch_gemm_q4k_small(Wb, q, d, s, m, n, k, out, st);
+    else if (kern == Kern::GEMM_SMALL)
+        e = mq::launch_gemm_q4k_small(Wb, q, d, s, m, n, k, out, w, st);
     else
-        e = mq::launch_gemm_q4k(Wb, q, d, s, m, n, k, out, st);
+        e = mq::launch_gemm_q4k(Wb, q, d, s, m, n, k, out, w, st);
     return launched(e, fn);
 }
 
@@ -175,7 +241,7 @@ int check_gemm_shape(const char *fn, const int8_t *q, const float *d, float *out
 }
 
 // Shared checks of a plane builder reading N rows of K.
-int check_planes(const char *fn, const void *W, int64_t N, int64_t K)
+int check_planes(const char *fn, const void *W, int64_t N, int64_t K, int align)
 {
     if (!W) return fail(MQ_ERR_INVALID_ARG, "%s: W is NULL", fn);
     if (N <= 0) return fail(MQ_ERR_INVALID_ARG, "%s: N=%lld must be positive", fn, (long long)N);
@@ -183,22 +249,13 @@ int check_planes(const char *fn, const void *W, int64_t N, int64_t K)
     if (N > kMaxRows) return fail(MQ_ERR_SHAPE, "%s: N=%lld exceeds %lld", fn, (long long)N, (long long)kMaxRows);
     if (N * (K / 256) > kMaxDim * 4)
         return fail(MQ_ERR_SHAPE, "%s: N=%lld x K=%lld has too many blocks", fn, (long long)N, (long long)K);
-    if (!aligned(W, 16)) return fail(MQ_ERR_ALIGN, "%s: W=%p is not 16-byte aligned", fn, W);
+    if (!aligned(W, align)) return fail(MQ_ERR_ALIGN, "%s: W=%p is not %d-byte aligned", fn, W, align);
     return MQ_OK;
 }
 
-int ffn(const void *Wg, const void *Wu, const int8_t *q, const float *d, const float *s, int64_t M,
-        int64_t N, int64_t K, int8_t *qo, float *do_, float *so, float *y, void *stream, int path)
+// Shape and path checks shared by the fused FFN and its workspace query.
+int check_ffn_shape(const char *fn, int64_t M, int64_t N, int64_t K, int path)
 {
-    const char *fn = "mq_ffn_q4k";
-    if (!Wg) return fail(MQ_ERR_INVALID_ARG, "%s: Wg is NULL", fn);
-    if (!Wu) return fail(MQ_ERR_INVALID_ARG, "%s: Wu is NULL", fn);
-    if (!q) return fail(MQ_ERR_INVALID_ARG, "%s: q is NULL", fn);
-    if (!d) return fail(MQ_ERR_INVALID_ARG, "%s: d is NULL", fn);
-    if (!s) return fail(MQ_ERR_INVALID_ARG, "%s: s is NULL (the Q4_K min term needs it)", fn);
-    if (!qo) return fail(MQ_ERR_INVALID_ARG, "%s: qo is NULL", fn);
-    if (!do_) return fail(MQ_ERR_INVALID_ARG, "%s: do_ is NULL", fn);
-    if (!so) return fail(MQ_ERR_INVALID_ARG, "%s: so is NULL", fn);
     if (M <= 0) return fail(MQ_ERR_INVALID_ARG, "%s: M=%lld must be positive", fn, (long long)M);
     if (N <= 0 || N % 256 != 0)
         return fail(MQ_ERR_SHAPE, "%s: N=%lld must be a positive multiple of 256", fn, (long long)N);
@@ -211,6 +268,42 @@ int ffn(const void *Wg, const void *Wu, const int8_t *q, const float *d, const f
     if (path == MQ_PATH_GEMV && M > mq::FFN_GEMV_MAX_M)
         return fail(MQ_ERR_INVALID_ARG, "%s: path=MQ_PATH_GEMV needs M <= %d, got M=%lld", fn,
                     mq::FFN_GEMV_MAX_M, (long long)M);
+    const int64_t tiles = ((M + 127) / 128) * (N / 64);
+    if (tiles > kMaxDim)
+        return fail(MQ_ERR_SHAPE, "%s: M=%lld x N=%lld needs too many tiles", fn, (long long)M, (long long)N);
+    return MQ_OK;
+}
+
+// The fused FFN's plan. With a workspace: the GEMV pass (path GEMV, or AUTO
+// up to FFN_AUTO_M tokens) or the two GEMMs (up to FFN_TWO_PASS_MAX_M
+// tokens) write g and u, then the SwiGLU quantizer; above that the
+// one-launch GEMM. Without one: the one-launch GEMM at every M (path GEMV
+// needs the workspace).
+struct FfnPlan {
+    bool two_pass, gemv;
+    size_t bytes;   // workspace of the two-pass form
+};
+FfnPlan ffn_plan(int64_t M, int64_t N, int64_t K, int path)
+{
+    const bool gemv = path == MQ_PATH_GEMV || (path == MQ_PATH_AUTO && M <= mq::FFN_AUTO_M);
+    const bool two_pass = gemv || M <= FFN_TWO_PASS_MAX_M;
+    return {two_pass, gemv, two_pass ? mq::ffn_two_pass_bytes((int)M, (int)N, (int)K, gemv) : 0};
+}
+
+int ffn(const void *Wg, const void *Wu, const int8_t *q, const float *d, const float *s, int64_t M,
+        int64_t N, int64_t K, int8_t *qo, float *do_, float *so, float *y, void *ws, int64_t ws_bytes,
+        void *stream, int path)
+{
+    const char *fn = "mq_ffn_q4k";
+    if (!Wg) return fail(MQ_ERR_INVALID_ARG, "%s: Wg is NULL", fn);
+    if (!Wu) return fail(MQ_ERR_INVALID_ARG, "%s: Wu is NULL", fn);
+    if (!q) return fail(MQ_ERR_INVALID_ARG, "%s: q is NULL", fn);
+    if (!d) return fail(MQ_ERR_INVALID_ARG, "%s: d is NULL", fn);
+    if (!s) return fail(MQ_ERR_INVALID_ARG, "%s: s is NULL (the Q4_K min term needs it)", fn);
+    if (!qo) return fail(MQ_ERR_INVALID_ARG, "%s: qo is NULL", fn);
+    if (!do_) return fail(MQ_ERR_INVALID_ARG, "%s: do_ is NULL", fn);
+    if (!so) return fail(MQ_ERR_INVALID_ARG, "%s: so is NULL", fn);
+    if (int rc = check_ffn_shape(fn, M, N, K, path)) return rc;
     if (!aligned(Wg, 16)) return fail(MQ_ERR_ALIGN, "%s: Wg=%p is not 16-byte aligned", fn, Wg);
     if (!aligned(Wu, 16)) return fail(MQ_ERR_ALIGN, "%s: Wu=%p is not 16-byte aligned", fn, Wu);
     if (!aligned(q, 16)) return fail(MQ_ERR_ALIGN, "%s: q=%p is not 16-byte aligned", fn, (const void *)q);
@@ -220,17 +313,19 @@ int ffn(const void *Wg, const void *Wu, const int8_t *q, const float *d, const f
     if (!aligned(do_, 16)) return fail(MQ_ERR_ALIGN, "%s: do_=%p is not 16-byte aligned", fn, (const void *)do_);
     if (!aligned(so, 16)) return fail(MQ_ERR_ALIGN, "%s: so=%p is not 16-byte aligned", fn, (const void *)so);
     if (y && !aligned(y, 16)) return fail(MQ_ERR_ALIGN, "%s: y=%p is not 16-byte aligned", fn, (const void *)y);
-    const int64_t tiles = ((M + 127) / 128) * (N / 64);
-    if (tiles > kMaxDim)
-        return fail(MQ_ERR_SHAPE, "%s: M=%lld x N=%lld needs too many tiles", fn, (long long)M, (long long)N);
+    const FfnPlan plan = ffn_plan(M, N, K, path);
+    if (!ws && path == MQ_PATH_GEMV)
+        return fail(MQ_ERR_WORKSPACE, "%s: path=MQ_PATH_GEMV needs a workspace of %llu bytes (ws is NULL)", fn,
+                    (unsigned long long)plan.bytes);
+    if (int rc = check_ws(fn, ws, ws_bytes, ws ? plan.bytes : 0)) return rc;
     if (int rc = check_device()) return rc;
-    const bool gemv = path == MQ_PATH_GEMV || (path == MQ_PATH_AUTO && M <= mq::FFN_AUTO_M);
     const auto *Wgb = static_cast<const uint8_t *>(Wg);
     const auto *Wub = static_cast<const uint8_t *>(Wu);
     hipStream_t st = static_cast<hipStream_t>(stream);
     const hipError_t e =
-        gemv || M <= FFN_TWO_PASS_MAX_M
-            ? mq::launch_ffn_q4k_two_pass(Wgb, Wub, q, d, s, (int)M, (int)N, (int)K, qo, do_, so, y, gemv, st)
+        ws && plan.two_pass
+            ? mq::launch_ffn_q4k_two_pass(Wgb, Wub, q, d, s, (int)M, (int)N, (int)K, qo, do_, so, y, plan.gemv,
+                                          mq::Ws{ws, (size_t)ws_bytes}, st)
             : mq::launch_gemm_q4k_ffn(Wgb, Wub, q, d, s, (int)M, (int)N, (int)K, qo, do_, so, y, st);
     return launched(e, fn);
 }
@@ -325,60 +420,112 @@ int mq_swiglu_quantize(const float *g, const float *u, int64_t M, int64_t K, int
                                                static_cast<hipStream_t>(stream)), fn);
 }
 
+int mq_matmul_workspace(int fmt, int64_t M, int64_t N, int64_t K, int path, int64_t *bytes)
+{
+    g_err[0] = '\0';
+    if (!bytes) return fail(MQ_ERR_INVALID_ARG, "mq_matmul_workspace: bytes is NULL");
+    *bytes = 0;
+    if (fmt != MQ_FMT_Q4K && fmt != MQ_FMT_Q5K && fmt != MQ_FMT_Q6K)
+        return fail(MQ_ERR_INVALID_ARG, "mq_matmul_workspace: fmt=%d is not MQ_FMT_Q4K/Q5K/Q6K", fmt);
+    const Fmt f = static_cast<Fmt>(fmt);
+    if (int rc = check_matmul_shape(fmt_fn(f), M, N, K, path)) return rc;
+    *bytes = (int64_t)gemm_ws_bytes(f, matmul_kernel(f, M, N, K, path), M, N, K);
+    return MQ_OK;
+}
+
+int mq_ffn_q4k_workspace(int64_t M, int64_t N, int64_t K, int path, int64_t *bytes)
+{
+    g_err[0] = '\0';
+    if (!bytes) return fail(MQ_ERR_INVALID_ARG, "mq_ffn_q4k_workspace: bytes is NULL");
+    *bytes = 0;
+    if (int rc = check_ffn_shape("mq_ffn_q4k", M, N, K, path)) return rc;
+    *bytes = (int64_t)ffn_plan(M, N, K, path).bytes;
+    return MQ_OK;
+}
+
 int mq_matmul_q4k(const void *W, const int8_t *q, const float *d, const float *s, int64_t M,
                   int64_t N, int64_t K, float *out, void *stream)
 {
     g_err[0] = '\0';
-    return matmul(Fmt::Q4K, W, q, d, s, M, N, K, out, stream, MQ_PATH_AUTO);
+    return matmul(Fmt::Q4K, W, q, d, s, M, N, K, out, nullptr, 0, stream, MQ_PATH_AUTO);
 }
 
 int mq_matmul_q5k(const void *W, const int8_t *q, const float *d, const float *s, int64_t M,
                   int64_t N, int64_t K, float *out, void *stream)
 {
     g_err[0] = '\0';
-    return matmul(Fmt::Q5K, W, q, d, s, M, N, K, out, stream, MQ_PATH_AUTO);
-}
-
-int mq_matmul_q5k_ex(const void *W, const int8_t *q, const float *d, const float *s, int64_t M,
-                     int64_t N, int64_t K, float *out, void *stream, int path)
-{
-    g_err[0] = '\0';
-    return matmul(Fmt::Q5K, W, q, d, s, M, N, K, out, stream, path);
+    return matmul(Fmt::Q5K, W, q, d, s, M, N, K, out, nullptr, 0, stream, MQ_PATH_AUTO);
 }
 
 int mq_matmul_q6k(const void *W, const int8_t *q, const float *d, const float *s, int64_t M,
                   int64_t N, int64_t K, float *out, void *stream)
 {
     g_err[0] = '\0';
-    return matmul(Fmt::Q6K, W, q, d, s, M, N, K, out, stream, MQ_PATH_AUTO);
+    return matmul(Fmt::Q6K, W, q, d, s, M, N, K, out, nullptr, 0, stream, MQ_PATH_AUTO);
 }
 
 int mq_matmul_q4k_ex(const void *W, const int8_t *q, const float *d, const float *s, int64_t M,
                      int64_t N, int64_t K, float *out, void *stream, int path)
 {
     g_err[0] = '\0';
-    return matmul(Fmt::Q4K, W, q, d, s, M, N, K, out, stream, path);
+    return matmul(Fmt::Q4K, W, q, d, s, M, N, K, out, nullptr, 0, stream, path);
+}
+
+int mq_matmul_q5k_ex(const void *W, const int8_t *q, const float *d, const float *s, int64_t M,
+                     int64_t N, int64_t K, float *out, void *stream, int path)
+{
+    g_err[0] = '\0';
+    return matmul(Fmt::Q5K, W, q, d, s, M, N, K, out, nullptr, 0, stream, path);
 }
 
 int mq_matmul_q6k_ex(const void *W, const int8_t *q, const float *d, const float *s, int64_t M,
                      int64_t N, int64_t K, float *out, void *stream, int path)
 {
     g_err[0] = '\0';
-    return matmul(Fmt::Q6K, W, q, d, s, M, N, K, out, stream, path);
+    return matmul(Fmt::Q6K, W, q, d, s, M, N, K, out, nullptr, 0, stream, path);
+}
+
+int mq_matmul_q4k_ws(const void *W, const int8_t *q, const float *d, const float *s, int64_t M,
+                     int64_t N, int64_t K, float *out, void *ws, int64_t ws_bytes, void *stream, int path)
+{
+    g_err[0] = '\0';
+    return matmul(Fmt::Q4K, W, q, d, s, M, N, K, out, ws, ws_bytes, stream, path);
+}
+
+int mq_matmul_q5k_ws(const void *W, const int8_t *q, const float *d, const float *s, int64_t M,
+                     int64_t N, int64_t K, float *out, void *ws, int64_t ws_bytes, void *stream, int path)
+{
+    g_err[0] = '\0';
+    return matmul(Fmt::Q5K, W, q, d, s, M, N, K, out, ws, ws_bytes, stream, path);
+}
+
+int mq_matmul_q6k_ws(const void *W, const int8_t *q, const float *d, const float *s, int64_t M,
+                     int64_t N, int64_t K, float *out, void *ws, int64_t ws_bytes, void *stream, int path)
+{
+    g_err[0] = '\0';
+    return matmul(Fmt::Q6K, W, q, d, s, M, N, K, out, ws, ws_bytes, stream, path);
 }
 
 int mq_ffn_q4k(const void *Wg, const void *Wu, const int8_t *q, const float *d, const float *s, int64_t M,
                int64_t N, int64_t K, int8_t *qo, float *do_, float *so, float *y, void *stream)
 {
     g_err[0] = '\0';
-    return ffn(Wg, Wu, q, d, s, M, N, K, qo, do_, so, y, stream, MQ_PATH_AUTO);
+    return ffn(Wg, Wu, q, d, s, M, N, K, qo, do_, so, y, nullptr, 0, stream, MQ_PATH_AUTO);
 }
 
 int mq_ffn_q4k_ex(const void *Wg, const void *Wu, const int8_t *q, const float *d, const float *s, int64_t M,
                   int64_t N, int64_t K, int8_t *qo, float *do_, float *so, float *y, void *stream, int path)
 {
     g_err[0] = '\0';
-    return ffn(Wg, Wu, q, d, s, M, N, K, qo, do_, so, y, stream, path);
+    return ffn(Wg, Wu, q, d, s, M, N, K, qo, do_, so, y, nullptr, 0, stream, path);
+}
+
+int mq_ffn_q4k_ws(const void *Wg, const void *Wu, const int8_t *q, const float *d, const float *s, int64_t M,
+                  int64_t N, int64_t K, int8_t *qo, float *do_, float *so, float *y, void *ws, int64_t ws_bytes,
+                  void *stream, int path)
+{
+    g_err[0] = '\0';
+    return ffn(Wg, Wu, q, d, s, M, N, K, qo, do_, so, y, ws, ws_bytes, stream, path);
 }
 
 int mq_expand_q6k(const void *W, int64_t N, int64_t K, int8_t *lo, int8_t *hi, float *dw, void *stream)
@@ -386,7 +533,7 @@ int mq_expand_q6k(const void *W, int64_t N, int64_t K, int8_t *lo, int8_t *hi, f
     g_err[0] = '\0';
     drop_timing();
     const char *fn = "mq_expand_q6k";
-    if (int rc = check_planes(fn, W, N, K)) return rc;
+    if (int rc = check_planes(fn, W, N, K, 4)) return rc;
     if (!lo) return fail(MQ_ERR_INVALID_ARG, "%s: lo is NULL", fn);
     if (!hi) return fail(MQ_ERR_INVALID_ARG, "%s: hi is NULL", fn);
     if (!dw) return fail(MQ_ERR_INVALID_ARG, "%s: dw is NULL", fn);
@@ -399,7 +546,7 @@ int mq_expand_q6k(const void *W, int64_t N, int64_t K, int8_t *lo, int8_t *hi, f
 }
 
 int mq_matmul_q6k_x(const int8_t *lo, const int8_t *hi, const float *dw, const int8_t *q, const float *d,
-                    int64_t M, int64_t N, int64_t K, float *out, void *stream)
+                    int64_t M, int64_t N, int64_t K, float *out, void *ws, int64_t ws_bytes, void *stream)
 {
     g_err[0] = '\0';
     const char *fn = "mq_matmul_q6k_x";
@@ -410,11 +557,14 @@ int mq_matmul_q6k_x(const int8_t *lo, const int8_t *hi, const float *dw, const i
     if (!aligned(lo, 16)) return fail(MQ_ERR_ALIGN, "%s: lo=%p is not 16-byte aligned", fn, (const void *)lo);
     if (!aligned(hi, 16)) return fail(MQ_ERR_ALIGN, "%s: hi=%p is not 16-byte aligned", fn, (const void *)hi);
     if (!aligned(dw, 4)) return fail(MQ_ERR_ALIGN, "%s: dw=%p is not 4-byte aligned", fn, (const void *)dw);
+    const Kern kern = M <= mq::GEMM_SMALL_M_Q6K ? Kern::GEMM_SMALL : Kern::GEMM;
+    if (int rc = check_ws(fn, ws, ws_bytes, ws ? gemm_ws_bytes(Fmt::Q6K, kern, M, N, K) : 0)) return rc;
     if (int rc = check_device()) return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
+    const mq::Ws w{ws, (size_t)ws_bytes};
     const int m = (int)M, n = (int)N, k = (int)K;
-    const hipError_t e = m <= mq::GEMM_SMALL_M_Q6K ? mq::launch_gemm_q6k_x_small(lo, hi, dw, q, d, m, n, k, out, st)
-                                                   : mq::launch_gemm_q6k_x(lo, hi, dw, q, d, m, n, k, out, st);
+    const hipError_t e = kern == Kern::GEMM_SMALL ? mq::launch_gemm_q6k_x_small(lo, hi, dw, q, d, m, n, k, out, w, st)
+                                                  : mq::launch_gemm_q6k_x(lo, hi, dw, q, d, m, n, k, out, w, st);
     return launched(e, fn);
 }
 
@@ -423,7 +573,7 @@ int mq_dsc_q4k(const void *W, int64_t N, int64_t K, float *fw, float *fm, void *
     g_err[0] = '\0';
     drop_timing();
     const char *fn = "mq_dsc_q4k";
-    if (int rc = check_planes(fn, W, N, K)) return rc;
+    if (int rc = check_planes(fn, W, N, K, 16)) return rc;
     if (!fw) return fail(MQ_ERR_INVALID_ARG, "%s: fw is NULL", fn);
     if (!fm) return fail(MQ_ERR_INVALID_ARG, "%s: fm is NULL", fn);
     if (!aligned(fw, 16)) return fail(MQ_ERR_ALIGN, "%s: fw=%p is not 16-byte aligned", fn, (void *)fw);
@@ -434,7 +584,8 @@ int mq_dsc_q4k(const void *W, int64_t N, int64_t K, float *fw, float *fm, void *
 }
 
 int mq_matmul_q4k_dsc(const void *W, const float *fw, const float *fm, const int8_t *q, const float *d,
-                      const float *s, int64_t M, int64_t N, int64_t K, float *out, void *stream)
+                      const float *s, int64_t M, int64_t N, int64_t K, float *out, void *ws, int64_t ws_bytes,
+                      void *stream)
 {
     g_err[0] = '\0';
     const char *fn = "mq_matmul_q4k_dsc";
@@ -447,13 +598,16 @@ int mq_matmul_q4k_dsc(const void *W, const float *fw, const float *fm, const int
     if (!aligned(fw, 16)) return fail(MQ_ERR_ALIGN, "%s: fw=%p is not 16-byte aligned", fn, (const void *)fw);
     if (!aligned(fm, 16)) return fail(MQ_ERR_ALIGN, "%s: fm=%p is not 16-byte aligned", fn, (const void *)fm);
     if (!aligned(s, 16)) return fail(MQ_ERR_ALIGN, "%s: s=%p is not 16-byte aligned", fn, (const void *)s);
+    const Kern kern = M <= mq::GEMM_SMALL_M_Q4K ? Kern::GEMM_SMALL : Kern::GEMM;
+    if (int rc = check_ws(fn, ws, ws_bytes, ws ? gemm_ws_bytes(Fmt::Q4K, kern, M, N, K) : 0)) return rc;
     if (int rc = check_device()) return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
+    const mq::Ws w{ws, (size_t)ws_bytes};
     const auto *Wb = static_cast<const uint8_t *>(W);
     const int m = (int)M, n = (int)N, k = (int)K;
-    const hipError_t e = m <= mq::GEMM_SMALL_M_Q4K
-                             ? mq::launch_gemm_q4k_dsc_small(Wb, fw, fm, q, d, s, m, n, k, out, st)
-                             : mq::launch_gemm_q4k_dsc(Wb, fw, fm, q, d, s, m, n, k, out, st);
+    const hipError_t e = kern == Kern::GEMM_SMALL
+                             ? mq::launch_gemm_q4k_dsc_small(Wb, fw, fm, q, d, s, m, n, k, out, w, st)
+                             : mq::launch_gemm_q4k_dsc(Wb, fw, fm, q, d, s, m, n, k, out, w, st);
     return launched(e, fn);
 }
 

@@ -7,7 +7,6 @@
 #include <stdint.h>
 
 #include <cstddef>
-#include <mutex>
 
 namespace mq {
 
@@ -109,23 +108,31 @@ hipError_t launch_rmsnorm_quantize(const float *x, const float *w, int64_t M, in
 hipError_t launch_swiglu_quantize(const float *g, const float *u, int64_t M, int64_t K, int64_t ldg,
                                   int64_t ldu, int8_t *q, float *d, float *s, float *y, hipStream_t st);
 
+// The caller's device workspace for one call: split-K partial sums and the
+// two-pass FFN's g and u. ptr == nullptr means none was given; the
+// launchers then take their workspace-free plan (no split of K).
+struct Ws {
+    void *ptr = nullptr;
+    size_t bytes = 0;
+};
+
 hipError_t launch_gemm_q4k(const uint8_t *W, const int8_t *q, const float *d,
                            const float *s, int M, int N, int K, float *out,
-                           hipStream_t st);
+                           const Ws &ws, hipStream_t st);
 // Small-M configuration of the Q4_K GEMM (32 tokens x 256 rows per workgroup).
 hipError_t launch_gemm_q4k_small(const uint8_t *W, const int8_t *q, const float *d,
                                  const float *s, int M, int N, int K, float *out,
-                                 hipStream_t st);
+                                 const Ws &ws, hipStream_t st);
 // Small-M configuration of the Q6_K GEMM (32 tokens x 128 rows per workgroup).
 hipError_t launch_gemm_q6k_small(const uint8_t *W, const int8_t *q, const float *d,
-                                 int M, int N, int K, float *out, hipStream_t st);
+                                 int M, int N, int K, float *out, const Ws &ws, hipStream_t st);
 hipError_t launch_gemm_q5k(const uint8_t *W, const int8_t *q, const float *d,
                            const float *s, int M, int N, int K, float *out,
-                           hipStream_t st);
+                           const Ws &ws, hipStream_t st);
 // Small-M configuration of the Q5_K GEMM (32 tokens x 128 rows per workgroup).
 hipError_t launch_gemm_q5k_small(const uint8_t *W, const int8_t *q, const float *d,
                                  const float *s, int M, int N, int K, float *out,
-                                 hipStream_t st);
+                                 const Ws &ws, hipStream_t st);
 hipError_t launch_gemm_q4k_ffn(const uint8_t *Wg, const uint8_t *Wu, const int8_t *q, const float *d,
                                const float *s, int M, int N, int K, int8_t *qo, float *do_, float *so,
                                float *y, hipStream_t st);
@@ -136,30 +143,35 @@ hipError_t launch_gemm_q4k_ffn(const uint8_t *Wg, const uint8_t *Wu, const int8_
 // length K.
 hipError_t launch_gemv_q4k_pair(const uint8_t *Wg, const uint8_t *Wu, const int8_t *q, const float *d,
                                 const float *s, int M, int N, int K, float *g, float *u, hipStream_t st);
-// FFN up half in two passes: g and u into the stream's workspace (the GEMV
-// when gemv is set, else the GEMM of the token count), then the SwiGLU
-// quantizer. launch_gemm_q4k_ffn is the one-launch GEMM form.
+// FFN up half in two passes: g and u into the caller's workspace (the GEMV
+// when gemv is set, else the GEMM of the token count, whose split-K planes
+// follow g and u in the workspace), then the SwiGLU quantizer.
+// launch_gemm_q4k_ffn is the one-launch GEMM form. ffn_two_pass_bytes is
+// the workspace it needs.
+size_t ffn_two_pass_bytes(int M, int N, int K, bool gemv);
 hipError_t launch_ffn_q4k_two_pass(const uint8_t *Wg, const uint8_t *Wu, const int8_t *q, const float *d,
                                    const float *s, int M, int N, int K, int8_t *qo, float *do_, float *so,
-                                   float *y, bool gemv, hipStream_t st);
+                                   float *y, bool gemv, const Ws &ws, hipStream_t st);
 hipError_t launch_gemm_q6k(const uint8_t *W, const int8_t *q, const float *d,
-                           int M, int N, int K, float *out, hipStream_t st);
+                           int M, int N, int K, float *out, const Ws &ws, hipStream_t st);
 
 // Registration-time planes (Q6_K expansion, Q4_K decoded scales) and the
-// GEMMs that read them.
+// GEMMs that read them (the split choice of the raw-block GEMM of the same
+// configuration).
 hipError_t launch_expand_q6k(const uint8_t *W, int64_t N, int64_t K, int8_t *lo, int8_t *hi, float *dw,
                              hipStream_t st);
 hipError_t launch_dsc_q4k(const uint8_t *W, int64_t N, int64_t K, float *fw, float *fm, hipStream_t st);
 hipError_t launch_gemm_q6k_x(const int8_t *lo, const int8_t *hi, const float *dw, const int8_t *q,
-                             const float *d, int M, int N, int K, float *out, hipStream_t st);
+                             const float *d, int M, int N, int K, float *out, const Ws &ws, hipStream_t st);
 hipError_t launch_gemm_q6k_x_small(const int8_t *lo, const int8_t *hi, const float *dw, const int8_t *q,
-                                   const float *d, int M, int N, int K, float *out, hipStream_t st);
+                                   const float *d, int M, int N, int K, float *out, const Ws &ws,
+                                   hipStream_t st);
 hipError_t launch_gemm_q4k_dsc(const uint8_t *W, const float *fw, const float *fm, const int8_t *q,
                                const float *d, const float *s, int M, int N, int K, float *out,
-                               hipStream_t st);
+                               const Ws &ws, hipStream_t st);
 hipError_t launch_gemm_q4k_dsc_small(const uint8_t *W, const float *fw, const float *fm, const int8_t *q,
                                      const float *d, const float *s, int M, int N, int K, float *out,
-                                     hipStream_t st);
+                                     const Ws &ws, hipStream_t st);
 
 // Compute units of the current device (cached per device).
 int device_cu_count();
@@ -172,48 +184,39 @@ int gemm_splits(int tiles, int tile_elems, int pairs, int64_t M, int64_t N, int 
 // out[i] = sum over s = 0..nsplit-1, in that order, of part[s * n + i].
 hipError_t splitk_reduce(const float *part, int nsplit, int64_t n, float *out, hipStream_t st);
 
-// Workspace for the kernels a call enqueues on stream st: a device buffer
-// the library keeps per (device, stream, role), grown with hipMalloc when a
-// call needs more (to at least twice its size; the old buffer is kept, since
-// queued kernels or captured graphs may still use it) and reused otherwise,
-// so a call costs no allocation and never waits on the stream. Calls on one stream run in order, so they
-// share it; other streams get their own. Roles keep leases that nest apart
-// (the FFN's g | u buffer, role WS_FFN, around the split-K partial sums of
-// the GEMMs it runs, role WS_SPLIT_K). The lease holds a library-wide
-// (recursive) lock: keep it until every kernel that reads or writes the
-// buffer is enqueued, so that no other thread grows (frees) it in between.
-// (A stream-ordered hipMallocAsync / hipFreeAsync pair per call was measured
-// instead: hipFreeAsync blocked the host until the stream drained, 0.34 ms
-// per call behind queued work.) Buffers stay allocated until the process
-// ends.
-constexpr int WS_SPLIT_K = 0;
-constexpr int WS_FFN = 1;
-class WsLease {
-  public:
-    WsLease(size_t bytes, hipStream_t st, int role);
-    void *ptr = nullptr;
-    hipError_t err = hipSuccess;
+// Number of K ranges each GEMM configuration cuts a launch of M x N x K
+// into when it is given a workspace (1 = no split); the launchers below use
+// the same choice, so a caller can size the workspace before the call.
+int splits_gemm_q4k(int M, int N, int K);
+int splits_gemm_q4k_small(int M, int N, int K);
+int splits_gemm_q5k(int M, int N, int K);
+int splits_gemm_q5k_small(int M, int N, int K);
+int splits_gemm_q6k(int M, int N, int K);
+int splits_gemm_q6k_small(int M, int N, int K);
 
-  private:
-    std::unique_lock<std::recursive_mutex> lock_;
-};
-
-// Runs launch(dst) once: with dst = out when nsplit == 1, else with dst a
-// workspace of nsplit [M][N] f32 planes (n = M*N elements each) leased on st,
-// followed by the reduction into out.
+// Runs launch(dst) once: with dst = out when nsplit == 1, else with dst the
+// caller's workspace holding nsplit [M][N] f32 planes (n = M*N elements
+// each), followed by the reduction into out. A workspace too small for the
+// planes is hipErrorInvalidValue (the C ABI checks the size before it gets
+// here).
 template <class Launch>
-hipError_t run_split_k(int nsplit, int64_t n, float *out, hipStream_t st, Launch &&launch)
+hipError_t run_split_k(int nsplit, int64_t n, float *out, const Ws &ws, hipStream_t st, Launch &&launch)
 {
     if (nsplit <= 1)
         return launch(out);
-    WsLease ws((size_t)nsplit * (size_t)n * sizeof(float), st, WS_SPLIT_K);
-    if (ws.err != hipSuccess)
-        return ws.err;
+    if (!ws.ptr || ws.bytes < (size_t)nsplit * (size_t)n * sizeof(float))
+        return hipErrorInvalidValue;
     float *part = static_cast<float *>(ws.ptr);
     hipError_t e = launch(part);
     if (e == hipSuccess)
         e = splitk_reduce(part, nsplit, n, out, st);
     return e;
+}
+
+// Workspace bytes of a split-K GEMM (0 when it does not split).
+inline size_t split_bytes(int nsplit, int64_t M, int64_t N)
+{
+    return nsplit > 1 ? (size_t)nsplit * (size_t)M * (size_t)N * sizeof(float) : 0;
 }
 
 } // namespace mq

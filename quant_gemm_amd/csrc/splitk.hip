@@ -4,16 +4,12 @@
 // A GEMM whose tile count is small against the workgroups the chip holds at
 // once (2 per CU for both GEMM kernels) leaves CUs idle or ends on a partial
 // wave of tiles. Cutting K into S ranges multiplies the workgroups by S; each
-// range writes f32 partial sums to its own [M][N] plane of a stream-ordered
+// range writes f32 partial sums to its own [M][N] plane of the caller's
 // workspace, and splitk_reduce adds the S planes in order s = 0..S-1, so the
 // result does not depend on scheduling.
 #include <atomic>
 #include <cmath>
 #include <cstdint>
-#include <map>
-#include <mutex>
-#include <tuple>
-#include <utility>
 
 #include "mq_device.h"
 #include "mq_launch.h"
@@ -47,35 +43,6 @@ __global__ __launch_bounds__(256) void splitk_reduce4_kernel(const v4f *__restri
 }
 
 } // namespace
-
-WsLease::WsLease(size_t bytes, hipStream_t st, int role)
-{
-    static std::recursive_mutex mu;
-    static std::map<std::tuple<int, hipStream_t, int>, std::pair<void *, size_t>> bufs;
-    lock_ = std::unique_lock<std::recursive_mutex>(mu);
-    int dev = 0;
-    err = hipGetDevice(&dev);
-    if (err != hipSuccess)
-        return;
-    auto &slot = bufs[{dev, st, role}];
-    if (slot.second < bytes) {
-        // Grow to at least twice the old size. The old buffer is not freed:
-        // kernels already queued (or recorded into a graph) may still use
-        // it, so it stays allocated, like the new one, until the process
-        // ends; the doubling bounds what is kept to twice the largest
-        // request.
-        const size_t grain = size_t(2) << 20;
-        size_t size = (bytes + grain - 1) / grain * grain;
-        if (size < 2 * slot.second)
-            size = 2 * slot.second;
-        void *p = nullptr;
-        err = hipMalloc(&p, size);
-        if (err != hipSuccess)
-            return;
-        slot = {p, size};
-    }
-    ptr = slot.first;
-}
 
 int device_cu_count()
 {

@@ -149,6 +149,10 @@ WORKLOAD_GROUPS = {
         _c("layer_up", "q4k", 3314, 18944, 3584, True, 1004, 3, 2),
         _c("layer_down", "q6k", 3314, 3584, 18944, True, 1004, 4, 3),
         _c("output_head", "q6k", 1, 152064, 3584, True, 1004, 5, 4)],
+    # One GPU's share of the ffn_up matrix when its rows are split over 8
+    # GPUs (N / 8 = 2368 rows each), decode and prefill
+    "shard8": [_c("q4k_decode_ffn_up_n2368", "q4k", 1, 2368, 3584, False, 1006, 0, 0),
+               _c("q4k_prefill_ffn_up_n2368", "q4k", 3314, 2368, 3584, True, 1006, 1, 1)],
     # Q5_K at the ffn_up shape, decode and prefill
     "q5k": [_c("q5k_decode_ffn_up", "q5k", 1, 18944, 3584, False, 1005, 0, 0),
             _c("q5k_prefill_ffn_up", "q5k", 3314, 18944, 3584, True, 1005, 0, 1)],

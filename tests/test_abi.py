@@ -15,7 +15,7 @@ import quant_gemm_amd as mq
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "mq.h")
 
-OK, INVALID, SHAPE, ALIGN = 0, 1, 2, 3
+OK, INVALID, SHAPE, ALIGN, WORKSPACE = 0, 1, 2, 3, 7
 P = 0x7f0000000000          # a 256-byte aligned fake device address
 
 
@@ -240,19 +240,23 @@ def test_error_is_cleared_by_next_call(L):
     (lambda L: L.mq_expand_q6k(P, 8, 256, None, P, P, None), INVALID, "lo is NULL"),
     (lambda L: L.mq_expand_q6k(P, 8, 256, P, P + 4, P, None), ALIGN, "hi="),
     (lambda L: L.mq_expand_q6k(P, 8, 256, P, P, P + 8, None), ALIGN, "dw="),
-    (lambda L: L.mq_matmul_q6k_x(P, P, None, P, P, 4, 8, 256, P, None), INVALID, "dw is NULL"),
-    (lambda L: L.mq_matmul_q6k_x(P, P, P, P, P, 0, 8, 256, P, None), INVALID, "M=0"),
-    (lambda L: L.mq_matmul_q6k_x(P, P, P, P, P, 4, 8, 512 + 64, P, None), SHAPE, "K=576"),
-    (lambda L: L.mq_matmul_q6k_x(P + 8, P, P, P, P, 4, 8, 256, P, None), ALIGN, "lo="),
-    (lambda L: L.mq_matmul_q6k_x(P, P, P, P + 4, P, 4, 8, 256, P, None), ALIGN, "q="),
+    (lambda L: L.mq_matmul_q6k_x(P, P, None, P, P, 4, 8, 256, P, None, 0, None), INVALID, "dw is NULL"),
+    (lambda L: L.mq_matmul_q6k_x(P, P, P, P, P, 0, 8, 256, P, None, 0, None), INVALID, "M=0"),
+    (lambda L: L.mq_matmul_q6k_x(P, P, P, P, P, 4, 8, 512 + 64, P, None, 0, None), SHAPE, "K=576"),
+    (lambda L: L.mq_matmul_q6k_x(P + 8, P, P, P, P, 4, 8, 256, P, None, 0, None), ALIGN, "lo="),
+    (lambda L: L.mq_matmul_q6k_x(P, P, P, P + 4, P, 4, 8, 256, P, None, 0, None), ALIGN, "q="),
     (lambda L: L.mq_dsc_q4k(P, 8, 256, None, P, None), INVALID, "fw is NULL"),
     (lambda L: L.mq_dsc_q4k(P + 4, 8, 256, P, P, None), ALIGN, "W="),
     (lambda L: L.mq_dsc_q4k(P, 8, 256, P, P + 4, None), ALIGN, "fm="),
-    (lambda L: L.mq_matmul_q4k_dsc(P, P, P, P, P, None, 4, 8, 256, P, None), INVALID, "s is NULL"),
-    (lambda L: L.mq_matmul_q4k_dsc(P, None, P, P, P, P, 4, 8, 256, P, None), INVALID, "fw is NULL"),
-    (lambda L: L.mq_matmul_q4k_dsc(P, P, P, P, P, P, 4, -2, 256, P, None), INVALID, "N=-2"),
-    (lambda L: L.mq_matmul_q4k_dsc(P, P, P + 8, P, P, P, 4, 8, 256, P, None), ALIGN, "fm="),
-    (lambda L: L.mq_matmul_q4k_dsc(P, P, P, P, P, P, 4, 8, 256, P + 2, None), ALIGN, "out="),
+    (lambda L: L.mq_matmul_q4k_dsc(P, P, P, P, P, None, 4, 8, 256, P, None, 0, None), INVALID, "s is NULL"),
+    (lambda L: L.mq_matmul_q4k_dsc(P, None, P, P, P, P, 4, 8, 256, P, None, 0, None), INVALID, "fw is NULL"),
+    (lambda L: L.mq_matmul_q4k_dsc(P, P, P, P, P, P, 4, -2, 256, P, None, 0, None), INVALID, "N=-2"),
+    (lambda L: L.mq_matmul_q4k_dsc(P, P, P + 8, P, P, P, 4, 8, 256, P, None, 0, None), ALIGN, "fm="),
+    (lambda L: L.mq_matmul_q4k_dsc(P, P, P, P, P, P, 4, 8, 256, P + 2, None, 0, None), ALIGN, "out="),
+    (lambda L: L.mq_expand_q6k(P + 2, 8, 256, P, P, P, None), ALIGN, "W="),
+    (lambda L: L.mq_matmul_q6k_x(P, P, P, P, P, 4, 8, 256, P, None, 16, None), INVALID, "ws is NULL"),
+    (lambda L: L.mq_matmul_q4k_dsc(P, P, P, P, P, P, 4, 8, 256, P, P + 8, 64, None), ALIGN, "ws="),
+    (lambda L: L.mq_matmul_q6k_x(P, P, P, P, P, 512, 3584, 18944, P, P, 4096, None), WORKSPACE, "needs"),
 ])
 def test_plane_entry_validation(L, call, status, needle):
     assert call(L) == status
@@ -276,3 +280,89 @@ def test_probe_library_exports_and_rejects_bad_arguments():
     assert P.mqp_read(0, 4, dummy, 1024, 0, dummy, None) == 1         # empty grid
     assert P.mqp_mix(3, 0, 64, dummy, None) == 1                      # no iterations
     assert P.mqp_mix(3, 10, 64, None, None) == 1                      # no sink
+
+
+# ---------------------------------------------------------------- caller-owned workspace
+
+import ctypes  # noqa: E402
+
+
+def _ws_bytes(L, fmt, M, N, K, path=0):
+    n = ctypes.c_int64(-1)
+    assert L.mq_matmul_workspace(fmt, M, N, K, path, ctypes.byref(n)) == OK
+    return n.value
+
+
+def test_workspace_query_matches_the_split_planes(L):
+    """The query is nsplit * M * N * 4 bytes for a GEMM that splits K (a
+    whole number of [M][N] f32 planes, 2..16 of them), 0 for the GEMV and
+    for GEMMs with enough tiles (the 3314-token FFN shapes)."""
+    for fmt, M, N, K in ((mq.MQ_FMT_Q6K, 512, 3584, 18944), (mq.MQ_FMT_Q4K, 64, 18944, 3584),
+                         (mq.MQ_FMT_Q5K, 16, 18944, 3584), (mq.MQ_FMT_Q6K, 16, 3584, 18944)):
+        b = _ws_bytes(L, fmt, M, N, K, path=mq.MQ_PATH_GEMM)
+        plane = M * N * 4
+        assert b % plane == 0 and 2 <= b // plane <= 16, (fmt, M, N, K, b)
+    assert _ws_bytes(L, mq.MQ_FMT_Q4K, 3314, 18944, 3584) == 0
+    assert _ws_bytes(L, mq.MQ_FMT_Q4K, 1, 18944, 3584) == 0          # GEMV
+    assert _ws_bytes(L, mq.MQ_FMT_Q6K, 1, 3584, 18944) == 0
+
+
+def test_workspace_query_validates_like_the_call(L):
+    n = ctypes.c_int64(-1)
+    assert L.mq_matmul_workspace(3, 4, 8, 256, 0, ctypes.byref(n)) == INVALID
+    assert "fmt=3" in L.mq_last_error().decode()
+    assert L.mq_matmul_workspace(mq.MQ_FMT_Q4K, 4, 8, 300, 0, ctypes.byref(n)) == SHAPE
+    assert "mq_matmul_q4k" in L.mq_last_error().decode() and "K=300" in L.mq_last_error().decode()
+    assert L.mq_matmul_workspace(mq.MQ_FMT_Q6K, 4, 8, 256, 0, None) == INVALID
+    assert L.mq_ffn_q4k_workspace(4, 100, 256, 0, ctypes.byref(n)) == SHAPE
+    assert L.mq_ffn_q4k_workspace(9, 256, 256, mq.MQ_PATH_GEMV, ctypes.byref(n)) == INVALID
+
+
+def test_ffn_workspace_query(L):
+    """The two-pass FFN keeps g and u (2 * M * N f32) in the workspace, plus
+    the GEMMs' split planes above the GEMV band; the one-launch GEMM (above
+    128 tokens) needs none."""
+    n = ctypes.c_int64(-1)
+    assert L.mq_ffn_q4k_workspace(1, 18944, 3584, 0, ctypes.byref(n)) == OK
+    assert n.value == 2 * 1 * 18944 * 4
+    assert L.mq_ffn_q4k_workspace(64, 18944, 3584, 0, ctypes.byref(n)) == OK
+    gu = 2 * 64 * 18944 * 4
+    assert n.value >= gu and (n.value - gu) % (64 * 18944 * 4) == 0
+    assert L.mq_ffn_q4k_workspace(3314, 18944, 3584, 0, ctypes.byref(n)) == OK and n.value == 0
+
+
+@pytest.mark.parametrize("fn,fmt,s", [("mq_matmul_q4k_ws", mq.MQ_FMT_Q4K, P),
+                                      ("mq_matmul_q5k_ws", mq.MQ_FMT_Q5K, P),
+                                      ("mq_matmul_q6k_ws", mq.MQ_FMT_Q6K, None)])
+def test_matmul_workspace_errors(L, fn, fmt, s):
+    """A workspace smaller than the query is MQ_ERR_WORKSPACE naming both
+    sizes; ws NULL with a size, a negative size or a misaligned ws are
+    argument errors. All fail before any HIP call."""
+    f = getattr(L, fn)
+    M, N, K = 512, 3584, 18944
+    need = _ws_bytes(L, fmt, M, N, K, path=mq.MQ_PATH_GEMM)
+    assert need > 0
+    assert f(P, P, P, s, M, N, K, P, P, need - 16, None, mq.MQ_PATH_GEMM) == WORKSPACE
+    msg = L.mq_last_error().decode()
+    assert str(need) in msg and str(need - 16) in msg
+    assert f(P, P, P, s, M, N, K, P, None, 64, None, 0) == INVALID
+    assert f(P, P, P, s, M, N, K, P, P, -1, None, 0) == INVALID
+    assert f(P, P, P, s, M, N, K, P, P + 4, need, None, 0) == ALIGN
+    assert "ws=" in L.mq_last_error().decode()
+
+
+def test_ffn_gemv_path_needs_a_workspace(L):
+    rc = L.mq_ffn_q4k_ex(P, P, P, P, P, 1, 256, 256, P, P, P, None, None, mq.MQ_PATH_GEMV)
+    assert rc == WORKSPACE and "needs a workspace" in L.mq_last_error().decode()
+    rc = L.mq_ffn_q4k_ws(P, P, P, P, P, 1, 256, 256, P, P, P, None, P, 8, None, mq.MQ_PATH_GEMV)
+    assert rc == WORKSPACE
+
+
+def test_q6k_weights_need_only_4_byte_alignment(L):
+    """Q6_K W is accepted at 4-byte alignment (a row slice of a matrix whose
+    rows are 4 bytes mod 16); the call below then stops at the misaligned
+    output, after W passed. Q4_K / Q5_K keep 16 bytes."""
+    assert _q6k(L, W=P + 4, out=P + 2) == ALIGN
+    assert "out=" in L.mq_last_error().decode()
+    assert _q6k(L, W=P + 2) == ALIGN and "4-byte" in L.mq_last_error().decode()
+    assert _q4k(L, W=P + 4) == ALIGN and "16-byte" in L.mq_last_error().decode()

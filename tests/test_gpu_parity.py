@@ -162,10 +162,11 @@ def test_split_k_shapes(dev, fmt, M, N, K):
 
 
 def test_workspace_reuse_across_streams(dev):
-    """Split-K GEMMs keep their partial sums in the stream's workspace, which
-    grows when a call needs more: calls queued back to back on two streams
-    (no host synchronization in between), small, large and small again,
-    give the bits the same calls give one at a time."""
+    """Split-K GEMMs keep their partial sums in the workspace the caller
+    gives each call (here torch's allocator on the call's stream): calls
+    queued back to back on two streams (no host synchronization in
+    between), small, large and small again, give the bits the same calls
+    give one at a time."""
     import torch
     cases = []
     for fmt, M, N, K in [("q4k", 40, 130, 6912), ("q6k", 300, 700, 4608), ("q4k", 64, 2000, 3584),
@@ -174,6 +175,9 @@ def test_workspace_reuse_across_streams(dev):
         W = synth.weights(fmt, rng, N, K)
         q, d, s = gpu_plane(synth.activations(rng, M, K, outliers=True))
         cases.append((fmt, to_dev(W.reshape(-1)), q, d, s, N, K))
+    fmt_code = {"q4k": mq.MQ_FMT_Q4K, "q6k": mq.MQ_FMT_Q6K}
+    for c in cases:
+        assert mq.matmul_workspace(fmt_code[c[0]], c[2].shape[0], c[5], c[6], mq.MQ_PATH_GEMM) > 0, c[0]
     mm = {"q4k": lambda W, q, d, s, N, K, st: mq.matmul_q4k(W, q, d, s, N, K, stream=st, path=mq.MQ_PATH_GEMM),
           "q6k": lambda W, q, d, s, N, K, st: mq.matmul_q6k(W, q, d, s, N, K, stream=st, path=mq.MQ_PATH_GEMM)}
     ref = [host(mm[c[0]](*c[1:], None)) for c in cases]
@@ -192,12 +196,46 @@ def test_workspace_reuse_across_streams(dev):
         assert np.array_equal(o.cpu().numpy(), ref[i]), f"case {i}: queued result differs"
 
 
-def test_graph_replay_uses_kept_workspace(dev):
-    """Calls captured into a HIP graph keep the stream's workspace address:
-    a split-K GEMM and the two-pass FFN, warmed up on the capture stream,
-    captured, then replayed three times with eager work (including a call
-    that grows that stream's workspace) and host synchronization between
-    replays; every replay equals the eager result bit for bit."""
+def test_workspace_free_plan_matches(dev):
+    """Without a workspace the GEMMs do not split K and the FFN runs its
+    one-launch GEMM; both meet the bar against the oracle, and the split
+    plan's result against the unsplit one."""
+    rng = np.random.default_rng(91)
+    for fmt, M, N, K in [("q4k", 40, 130, 6912), ("q6k", 300, 700, 4608), ("q5k", 24, 300, 5120)]:
+        W = synth.weights(fmt, rng, N, K)
+        x = synth.activations(rng, M, K, outliers=True)
+        rq, rd, _ = oracle.quantize_act(x)
+        q, d, s = gpu_plane(x)
+        Wd = to_dev(W.reshape(-1))
+        sp = None if fmt == "q6k" else s
+        ref = oracle_mm(fmt, W, rq, rd, N, K)
+        free = host(GPU_MM[fmt](Wd, q, d, sp, N, K, path=mq.MQ_PATH_GEMM, workspace=False))
+        split = host(GPU_MM[fmt](Wd, q, d, sp, N, K, path=mq.MQ_PATH_GEMM))
+        check_close(free, ref, f"{fmt} M={M} workspace-free")
+        check_close(split, ref, f"{fmt} M={M} split")
+    from oracle import producers
+    M, N, K = 5, 512, 1024
+    Wg, Wu = synth.q4k_weights(rng, N, K), synth.q4k_weights(rng, N, K)
+    x = synth.activations(rng, M, K, outliers=True)
+    rq, rd, _ = oracle.quantize_act(x)
+    q, d, s = gpu_plane(x)
+    _, _, _, ry = producers.ffn_q4k(Wg, Wu, rq, rd, N, K)
+    import torch
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    fq, fd, _, y = mq.ffn_q4k(to_dev(Wg.reshape(-1)), to_dev(Wu.reshape(-1)), q, d, s, N, K, y=y, workspace=False)
+    check_close(host(y), ry, "ffn workspace-free")
+    cq, cd, _ = oracle.quantize_act(host(y))
+    assert np.array_equal(host(fq), cq) and np.array_equal(host(fd), cd)
+
+
+def test_graph_capture_on_fresh_stream(dev):
+    """A split-K GEMM and the two-pass FFN captured into a HIP graph on a
+    stream no call has used before (their workspaces come from the graph's
+    own memory pool during capture). Each of three replays runs on the
+    capture stream with eager split-K GEMMs queued right behind it on the
+    same stream, with no host synchronization in between; the replay's
+    outputs and the eager ones each equal their one-at-a-time results bit
+    for bit. Eager work and synchronizations separate the replays."""
     import torch
     rng = np.random.default_rng(77)
     M, N, K = 40, 130, 6912                       # split-K shape
@@ -207,9 +245,12 @@ def test_graph_replay_uses_kept_workspace(dev):
     Mf, Nf, Kf = 12, 512, 1024                    # two-pass FFN (GEMMs)
     Wg, Wu = to_dev(synth.q4k_weights(rng, Nf, Kf).reshape(-1)), to_dev(synth.q4k_weights(rng, Nf, Kf).reshape(-1))
     qf, df, sf = gpu_plane(synth.activations(rng, Mf, Kf, outliers=True))
-    big_M, big_N, big_K = 300, 700, 4608          # larger split-K workspace
+    big_M, big_N, big_K = 300, 700, 4608          # eager split-K work on the capture stream
     Wb = to_dev(synth.q6k_weights(rng, big_N, big_K).reshape(-1))
     qb, db, sb = gpu_plane(synth.activations(rng, big_M, big_K, outliers=True))
+    assert mq.matmul_workspace(mq.MQ_FMT_Q4K, M, N, K, mq.MQ_PATH_GEMM) > 0
+    assert mq.matmul_workspace(mq.MQ_FMT_Q6K, big_M, big_N, big_K, mq.MQ_PATH_GEMM) > 0
+    assert mq.ffn_q4k_workspace(Mf, Nf, Kf, mq.MQ_PATH_GEMM) > 2 * Mf * Nf * 4
 
     out = torch.empty((M, N), dtype=torch.float32, device="cuda")
     ffn_out = [torch.empty((Mf, Nf), dtype=torch.int8, device="cuda"),
@@ -217,33 +258,30 @@ def test_graph_replay_uses_kept_workspace(dev):
                torch.empty((Mf, Nf // 32), dtype=torch.float32, device="cuda")]
     ref = host(mq.matmul_q4k(Wd, q, d, s, N, K, path=mq.MQ_PATH_GEMM))
     rq, rdd, rss = (host(t) for t in mq.ffn_q4k(Wg, Wu, qf, df, sf, Nf, Kf, path=mq.MQ_PATH_GEMM))
+    big_ref = host(mq.matmul_q6k(Wb, qb, db, sb, big_N, big_K, path=mq.MQ_PATH_GEMM))
 
-    def work():
-        mq.matmul_q4k(Wd, q, d, s, N, K, out=out, path=mq.MQ_PATH_GEMM)
-        mq.ffn_q4k(Wg, Wu, qf, df, sf, Nf, Kf, qo=ffn_out[0], do=ffn_out[1], so=ffn_out[2], path=mq.MQ_PATH_GEMM)
-
-    side = torch.cuda.Stream()
+    side = torch.cuda.Stream()                    # never used before the capture
     side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        work()                                    # the workspace of `side` exists before capture
-    side.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=side):
-        work()
+        mq.matmul_q4k(Wd, q, d, s, N, K, out=out, path=mq.MQ_PATH_GEMM)
+        mq.ffn_q4k(Wg, Wu, qf, df, sf, Nf, Kf, qo=ffn_out[0], do=ffn_out[1], so=ffn_out[2], path=mq.MQ_PATH_GEMM)
     for rep in range(3):
         out.zero_()
         for t in ffn_out:
             t.zero_()
-        if rep == 1:
-            with torch.cuda.stream(side):        # grows the workspace of `side`
-                mq.matmul_q6k(Wb, qb, db, sb, big_N, big_K, stream=side, path=mq.MQ_PATH_GEMM)
-            side.synchronize()
         torch.cuda.synchronize()
-        g.replay()
+        eager = []
+        with torch.cuda.stream(side):
+            g.replay()
+            for _ in range(2):                    # queued behind the replay, no sync
+                eager.append(mq.matmul_q6k(Wb, qb, db, sb, big_N, big_K, stream=side, path=mq.MQ_PATH_GEMM))
         torch.cuda.synchronize()
         assert np.array_equal(host(out), ref), f"replay {rep}: split-K GEMM differs"
         assert np.array_equal(host(ffn_out[0]), rq) and np.array_equal(host(ffn_out[1]), rdd) \
             and np.array_equal(host(ffn_out[2]), rss), f"replay {rep}: FFN plane differs"
+        for e in eager:
+            assert np.array_equal(host(e), big_ref), f"replay {rep}: eager split-K GEMM differs"
 
 
 # The small-M band: token counts around the switches between the GEMV, the
@@ -469,6 +507,74 @@ def test_q6k_zero_d_superblocks(dev):
     check_close(gv, ref[:8], "q6k GEMV, zero-d super-blocks")
 
 
+# ---------------------------------------------------------------- signed block scales
+
+def _negate_scales(fmt, W, rng, frac=0.5):
+    """Flip the f16 sign bit of d (and dmin for Q4_K / Q5_K) in a random half
+    of the blocks, independently: GGML's quantizers may store a negative d,
+    and the kernels rescale by it."""
+    W = W.copy()
+    blk = {"q4k": 144, "q5k": 176, "q6k": 210}[fmt]
+    b = W.reshape(-1, blk)
+    n = b.shape[0]
+    if fmt == "q6k":
+        b[rng.random(n) < frac, 209] ^= 0x80
+    else:
+        b[rng.random(n) < frac, 1] ^= 0x80
+        b[rng.random(n) < frac, 3] ^= 0x80
+    return W
+
+
+@pytest.mark.parametrize("fmt", ["q4k", "q5k", "q6k"])
+@pytest.mark.parametrize("M", [1, 4, 40, 200])
+def test_signed_block_scales(dev, fmt, M):
+    """Mixed-sign nonzero d and dmin: every path against the oracle."""
+    N, K = 300, 2560
+    rng = np.random.default_rng(4242 + M + FMT_SEED[fmt])
+    W = _negate_scales(fmt, synth.weights(fmt, rng, N, K), rng)
+    hdr = W.reshape(-1, {"q4k": 144, "q5k": 176, "q6k": 210}[fmt])
+    sign = hdr[:, 209] if fmt == "q6k" else hdr[:, 1]
+    assert (sign & 0x80).any() and not (sign & 0x80).all()
+    x = synth.activations(rng, M, K, outliers=True)
+    rq, rd, _ = oracle.quantize_act(x)
+    q, d, s = gpu_plane(x)
+    ref = oracle_mm(fmt, W, rq, rd, N, K)
+    paths = [mq.MQ_PATH_AUTO, mq.MQ_PATH_GEMM] + ([mq.MQ_PATH_GEMV] if M <= mq.gemv_max_m() else [])
+    for p in paths:
+        check_close(host(run_matmul(fmt, W, q, d, s, N, K, path=p)), ref, f"{fmt} M={M} signed d, path {p}")
+
+
+# ---------------------------------------------------------------- Q6_K rows at 4-byte alignment
+
+@pytest.mark.parametrize("M", [1, 2, 8, 40, 300])
+def test_q6k_weights_at_4_byte_offsets(dev, M):
+    """A Q6_K matrix that starts one row into a larger one: rows of K = 3584
+    are 2940 bytes, so row r starts 12, 8, 4, 0 bytes past a 16-byte
+    boundary for r = 1, 2, 3, 4. Every path (the LDS-ring GEMV, the register
+    GEMV, both GEMM tiles) and the expansion planes of the slice against the
+    oracle on the same rows."""
+    import torch
+    N, K = 131, 3584
+    rng = np.random.default_rng(515 + M)
+    Wfull = synth.q6k_weights(rng, N + 4, K)
+    x = synth.activations(rng, M, K, outliers=True)
+    rq, rd, _ = oracle.quantize_act(x)
+    q, d, s = gpu_plane(x)
+    Wd = to_dev(Wfull.reshape(-1))
+    rowb = Wfull.shape[1]
+    for r0 in (1, 2, 3):
+        Wsl = Wd[r0 * rowb:(r0 + N) * rowb]
+        assert Wsl.data_ptr() % 16 == 16 - 4 * r0 and Wsl.data_ptr() % 4 == 0
+        ref = oracle_mm("q6k", np.ascontiguousarray(Wfull[r0:r0 + N]), rq, rd, N, K)
+        paths = [mq.MQ_PATH_AUTO, mq.MQ_PATH_GEMM] + ([mq.MQ_PATH_GEMV] if M <= mq.gemv_max_m() else [])
+        for p in paths:
+            got = host(mq.matmul_q6k(Wsl, q, d, None, N, K, path=p))
+            check_close(got, ref, f"q6k slice at row {r0} M={M} path {p}")
+        lo, hi, dw = mq.expand_q6k(Wsl, N, K)
+        check_close(host(mq.matmul_q6k_x(lo, hi, dw, q, d, N, K)), ref, f"q6k_x slice at row {r0} M={M}")
+    del torch
+
+
 # ---------------------------------------------------------------- full-size workloads
 
 _SAMPLE_TOKENS = [0, 1, 2, 63, 64, 127, 128, 129, 511, 1000, 2047, 2048, 3199, 3200, 3201, 3250, 3312, 3313]
@@ -477,6 +583,11 @@ _SAMPLE_TOKENS = [0, 1, 2, 63, 64, 127, 128, 129, 511, 1000, 2047, 2048, 3199, 3
 def _tokens_for(M):
     t = sorted({x for x in _SAMPLE_TOKENS if x < M} | {M - 1})
     return np.array(t, dtype=np.int64)
+
+
+# Workloads compared over every output (the oracle takes a few seconds for
+# each on the host cores); the others on the sampled token rows.
+_FULL_COMPARE = {"q4k_prefill_ffn_up", "layer_down", "q4k_prefill_ffn_up_n2368"}
 
 
 @pytest.mark.parametrize("name", [c.name for _, c in synth.all_cases()])
@@ -489,7 +600,7 @@ def test_full_size_workloads(dev, name):
     rq, rd, rs = oracle.quantize_act(x)
     assert np.array_equal(host(q), rq) and np.array_equal(host(d), rd) and np.array_equal(host(s), rs)
     out_t = run_matmul(case.fmt, W, q, d, s, case.N, case.K)
-    toks = None if case.M <= 8 else _tokens_for(case.M)
+    toks = None if case.M <= 8 or name in _FULL_COMPARE else _tokens_for(case.M)
     ref = oracle_mm(case.fmt, W, rq, rd, case.N, case.K, tokens=toks)
     out = host(out_t)
     got = out if toks is None else out[toks]

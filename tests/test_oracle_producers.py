@@ -157,3 +157,47 @@ def test_plane_is_quantizer_of_producer_output(which):
     # |y - d*q| <= d/2 (plus the division's rounding) in every block
     dq = (q.astype(np.float64).reshape(9, -1, 32) * d.astype(np.float64)[:, :, None]).reshape(9, 512)
     assert np.all(np.abs(y - dq) <= np.repeat(d, 32, axis=1) * (0.5 + 2 ** -16))
+
+
+# ---------------------------------------------------------------- fused FFN composition
+
+def _const_q4k_rows(N, K, value):
+    """N rows of K Q4_K weights that all dequantize to the integer `value`
+    exactly: value >= 0 through d = 1, sc = value, q4 = 1, dmin = 0;
+    value < 0 through the min term alone (q4 = 0, dmin = 1, m = -value)."""
+    from blocks import q4k_pack
+    if value >= 0:
+        blk = q4k_pack(1.0, 0.0, [value] * 8, [0] * 8, np.ones(256, np.int64))
+    else:
+        blk = q4k_pack(1.0, 1.0, [1] * 8, [-value] * 8, np.zeros(256, np.int64))
+    return np.tile(blk, (N, K // 256)).reshape(N, (K // 256) * 144)
+
+
+@pytest.mark.parametrize("gate,up", [(-30, 1), (2, -3), (5, 7)])
+def test_ffn_applies_silu_to_the_gate_matrix(gate, up):
+    """FusedFFN is SwiGLU(gate, up) = SiLU(x Wg^T) * (x Wu^T) (minfer Compute
+    Graph Design, "The Op vocabulary"). Token 0's plane is q = (127, -126, 0,
+    ...) with d = 1 (so its activation sum is 1) and token 1 is all zero:
+    with Wg and Wu dequantizing to the constants `gate` and `up`, g = gate and
+    u = up exactly, so y = SiLU(gate) * up from the logistic function alone.
+    SiLU is not symmetric in its arguments, so a composition that swaps the
+    two matrices gives SiLU(up) * gate, far from it (gate = -30, up = 1:
+    -2.8e-12 against -21.9)."""
+    N, K = 256, 512                    # N is the down projection's K: whole 32-blocks
+    Wg, Wu = _const_q4k_rows(N, K, gate), _const_q4k_rows(N, K, up)
+    x = np.zeros((2, K), np.float32)
+    x[0, 0], x[0, 1] = 127.0, -126.0
+    q, d, _ = oracle.quantize_act(x)
+    assert q[0, 0] == 127 and q[0, 1] == -126 and d[0, 0] == 1.0 and not q[1].any()
+    qo, do, so, y = producers.ffn_q4k(Wg, Wu, q, d, N, K)
+    silu = lambda v: v / (1.0 + math.exp(-v))
+    want = silu(gate) * up
+    swapped = silu(up) * gate
+    assert np.allclose(y[0], want, rtol=1e-6, atol=0.0), (y[0], want)
+    assert abs(want - swapped) > 1e-3 * max(abs(want), abs(swapped))
+    assert not np.allclose(y[0], swapped, rtol=1e-3, atol=0.0)
+    assert np.all(y[1] == 0.0)
+    # the plane of a constant row: every q is +-127 and d = |y| / 127
+    assert np.all(qo[0] == (127 if want > 0 else -127)) and not qo[1].any()
+    assert np.array_equal(do[0], np.full(N // 32, np.float32(abs(y[0, 0])) / np.float32(127)))
+    assert not do[1].any() and not so[1].any()
