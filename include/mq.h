@@ -333,6 +333,27 @@ int mq_matmul_q4k_dsc(const void *W, const float *fw, const float *fm,
                       int64_t ws_bytes, void *stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the Q6_K
+ * matmul with the full plan of mq_matmul_q6k_ws (MQ_PATH_AUTO), its split-K
+ * partial sums kept in a static device array of the library instead of a
+ * caller workspace. The array holds MQ_STATIC_SCRATCH_BYTES (32 MiB); each
+ * GPU the library runs on holds its own copy until the process ends, and its
+ * address is looked up once per device on the first call there that needs
+ * it. A call whose plan needs more (mq_matmul_workspace with MQ_FMT_Q6K and
+ * MQ_PATH_AUTO gives the size; e.g. 3314 x 3584 x 18944 needs about 95 MB)
+ * fails with MQ_ERR_WORKSPACE before anything is launched. The call
+ * allocates nothing. All calls on one GPU share its array, which keeps the
+ * last call's partial sums (every call overwrites what it reads): calls
+ * that overlap in time on one GPU, on any streams, race and give wrong
+ * results. Same arguments, result and alignment rules as mq_matmul_q6k.
+ */
+#define MQ_STATIC_SCRATCH_BYTES (32u << 20)
+int mq_matmul_q6k_static(const void *W, const int8_t *q, const float *d,
+                         const float *s, int64_t M, int64_t N, int64_t K,
+                         float *out, void *stream);
+
+/*
  * Measurement hook. The next matmul call of the calling thread (mq_matmul_*,
  * mq_ffn_q4k*) launches its main kernel with hipExtLaunchKernel, which
  * records start_event and stop_event (hipEvent_t, created by the caller;

@@ -56,6 +56,7 @@ SIGNATURES = {
     "mq_matmul_q5k_ws": (_MATMUL_WS_ARGS, _I),
     "mq_matmul_q6k_ws": (_MATMUL_WS_ARGS, _I),
     "mq_matmul_workspace": ([_I, _I64, _I64, _I64, _I, ctypes.POINTER(_I64)], _I),
+    "mq_matmul_q6k_static": (_MATMUL_ARGS, _I),
     "mq_expand_q6k": ([_P, _I64, _I64, _P, _P, _P, _P], _I),
     "mq_matmul_q6k_x": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _I64, _P], _I),
     "mq_dsc_q4k": ([_P, _I64, _I64, _P, _P, _P], _I),
@@ -324,6 +325,23 @@ def matmul_q5k(W, q, d, s, N, K, out=None, stream=None, path=MQ_PATH_AUTO, works
 def matmul_q6k(W, q, d, s, N, K, out=None, stream=None, path=MQ_PATH_AUTO, workspace=True):
     """out [M, N] f32 = Q6_K weights W (N rows of K) times the activation plane (q, d); s unused."""
     return _matmul(MQ_FMT_Q6K, W, q, d, s, N, K, out, stream, path, workspace)
+
+
+STATIC_SCRATCH_BYTES = 32 << 20
+
+
+def matmul_q6k_static(W, q, d, N, K, out=None, stream=None):
+    """matmul_q6k without any allocation: split-K partial sums in the
+    library's static device array (STATIC_SCRATCH_BYTES per GPU). Calls that
+    overlap in time on one GPU race; a plan needing more raises
+    MQError(MQ_ERR_WORKSPACE)."""
+    L = load()
+    _weights("W", W, N, K, Q6K_BLOCK_BYTES)
+    M = _plane(q, d, None, K, s_required=False)
+    out = _out(out, M, N, q.device)
+    _check(L.mq_matmul_q6k_static(W.data_ptr(), q.data_ptr(), d.data_ptr(), None, M, N, K, out.data_ptr(),
+                                  _stream(stream)))
+    return out
 
 
 def expand_q6k(W, N, K, lo=None, hi=None, dw=None, stream=None):

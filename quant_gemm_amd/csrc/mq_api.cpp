@@ -10,6 +10,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/mq.h"
 #include "mq_launch.h"
@@ -330,6 +331,39 @@ int ffn(const void *Wg, const void *Wu, const int8_t *q, const float *d, const f
     return launched(e, fn);
 }
 
+// The split-K workspace of mq_matmul_q6k_static: a file-scope device array,
+// one copy per GPU the library runs on, held until the process ends. In host
+// code `scratch` names a host-side stand-in, not the device memory: kernels
+// get the address hipGetSymbolAddress returns for the current device, taken
+// once per device (scratch_ptr) and used everywhere instead of the name.
+constexpr size_t kScratchBytes = MQ_STATIC_SCRATCH_BYTES;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+// The current device's copy of `scratch` (nullptr and a message on failure).
+int scratch_ptr(const char *fn, void **out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return fail(MQ_ERR_DEVICE, "%s: hipGetDevice failed: %s", fn, hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(MQ_ERR_DEVICE, "%s: device ordinal %d out of range", fn, dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(MQ_ERR_DEVICE, "%s: hipGetSymbolAddress(scratch) on device %d failed: %s", fn, dev,
+                        hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return MQ_OK;
+}
+
 } // namespace
 
 extern "C" {
@@ -609,6 +643,26 @@ int mq_matmul_q4k_dsc(const void *W, const float *fw, const float *fm, const int
                              ? mq::launch_gemm_q4k_dsc_small(Wb, fw, fm, q, d, s, m, n, k, out, w, st)
                              : mq::launch_gemm_q4k_dsc(Wb, fw, fm, q, d, s, m, n, k, out, w, st);
     return launched(e, fn);
+}
+
+int mq_matmul_q6k_static(const void *W, const int8_t *q, const float *d, const float *s, int64_t M,
+                         int64_t N, int64_t K, float *out, void *stream)
+{
+    g_err[0] = '\0';
+    const char *fn = "mq_matmul_q6k_static";
+    // the checks of the call, then the size of the plan against the array
+    if (int rc = check_matmul_shape(fn, M, N, K, MQ_PATH_AUTO)) return rc;
+    const size_t need = gemm_ws_bytes(Fmt::Q6K, matmul_kernel(Fmt::Q6K, M, N, K, MQ_PATH_AUTO), M, N, K);
+    if (need > kScratchBytes)
+        return fail(MQ_ERR_WORKSPACE, "%s: M=%lld N=%lld K=%lld needs %llu bytes of scratch; the static array "
+                    "holds %llu (use mq_matmul_q6k_ws)", fn, (long long)M, (long long)N, (long long)K,
+                    (unsigned long long)need, (unsigned long long)kScratchBytes);
+    void *ws = nullptr;
+    if (need > 0) {
+        if (int rc = check_device()) return rc;
+        if (int rc = scratch_ptr(fn, &ws)) return rc;
+    }
+    return matmul(Fmt::Q6K, W, q, d, s, M, N, K, out, ws, ws ? (int64_t)kScratchBytes : 0, stream, MQ_PATH_AUTO);
 }
 
 int mq_time_next_kernel(void *start_event, void *stop_event)
