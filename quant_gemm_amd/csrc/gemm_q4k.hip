@@ -118,22 +118,12 @@ struct alignas(16) Stage {
 // the same accuracy as one f32 multiply-add per sub-block. A record holds,
 // for one token or row, the limbs of the step's 4 sub-blocks as bf16 pairs:
 // part 0 = {x1 j0j1, x1 j2j3, x2 j0j1, x2 j2j3}, part 1 = {x3 j0j1, x3 j2j3, 0, 0}.
-__device__ __forceinline__ uint32_t bf16_bits(float x)
-{
-    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x);
-}
-
 __device__ __forceinline__ void limbs4(const float (&x)[4], uint4 &r0, uint4 &r1)
 {
     uint32_t h[4], m[4], l[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        h[j] = bf16_bits(x[j]);
-        const float r = x[j] - __builtin_bit_cast(float, h[j] << 16);
-        m[j] = bf16_bits(r);
-        const float rr = r - __builtin_bit_cast(float, m[j] << 16);
-        l[j] = bf16_bits(rr);
-    }
+    for (int j = 0; j < 4; ++j)
+        bf16_limbs3(x[j], h[j], m[j], l[j]);
     r0 = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), m[0] | (m[1] << 16), m[2] | (m[3] << 16));
     r1 = make_uint4(l[0] | (l[1] << 16), l[2] | (l[3] << 16), 0u, 0u);
 }

@@ -50,6 +50,25 @@ __device__ __forceinline__ float wave_sum(float v)
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
+// bf16 bits (round to nearest even) of x.
+__device__ __forceinline__ uint32_t bf16_bits(float x)
+{
+    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x);
+}
+
+// Three bf16 limbs of x: x = x1 + x2 + x3 up to 2^-27 relative, each limb
+// the nearest bf16 of what the previous ones left. Products of limbs are
+// exact in the f32 accumulation of the bf16 matrix cores, so a sum of the
+// limb products other than the smallest ones carries an f32 product's
+// accuracy.
+__device__ __forceinline__ void bf16_limbs3(float x, uint32_t &x1, uint32_t &x2, uint32_t &x3)
+{
+    x1 = bf16_bits(x);
+    const float r = x - __builtin_bit_cast(float, x1 << 16);
+    x2 = bf16_bits(r);
+    x3 = bf16_bits(r - __builtin_bit_cast(float, x2 << 16));
+}
+
 // The 4*n bytes at a 2-byte aligned address p, as n dwords, using only
 // aligned dword loads. When p is 2 mod 4 the loads also cover the 2 bytes
 // before p and the 2 bytes after p + 4n: callers keep [p - 2, p + 4n + 2)
