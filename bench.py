@@ -620,16 +620,23 @@ def run_ceilings(args):
     del pool
     torch.cuda.empty_cache()
 
-    grid, iters = 2048, 1000
-    out = torch.zeros(grid * 256, dtype=torch.float32, device="cuda")
-    ops = grid * 4 * iters * 4 * 2 * 32 * 32 * 32
-    for k in (0, 2, 3, 4):
-        fn = lambda i: check(P.mqp_mix(k, iters, grid, ctypes.c_void_p(out.data_ptr()), st))
-        us = float(np.median([_time_rotating(fn, 1, 5) for _ in range(3)]))
-        tops = ops / (us * 1e-6) / 1e12
-        row = {"probe": "int8 MFMA + k f32 VALU ops per result", "k": k, "us": round(us, 1),
-               "TOPS": round(tops, 1), "frac_int8_peak": round(tops / INT8_PEAK_TOPS, 3)}
-        print(json.dumps(row), flush=True)
+    # 2048 workgroups: many wavefronts per SIMD; 512: two per SIMD, the
+    # occupancy of the GEMMs. The fp8 kinds count the same int8-equivalent
+    # work per MFMA (one 32 x 32 x 32 sub-block product).
+    iters = 1000
+    names = {0: "int8 MFMA alone", 2: "int8 MFMA + cvt, fma", 3: "int8 MFMA + cvt, mul, fma",
+             4: "int8 MFMA + cvt, mul, mul, fma", 10: "fp8 MFMA alone", 11: "fp8 MFMA + fma",
+             12: "fp8 MFMA + mul, fma"}
+    for grid in (2048, 512):
+        out = torch.zeros(grid * 256, dtype=torch.float32, device="cuda")
+        ops = grid * 4 * iters * 4 * 2 * 32 * 32 * 32
+        for k in (0, 2, 3, 4, 10, 11, 12):
+            fn = lambda i: check(P.mqp_mix(k, iters, grid, ctypes.c_void_p(out.data_ptr()), st))
+            us = float(np.median([_time_rotating(fn, 1, 5) for _ in range(3)]))
+            tops = ops / (us * 1e-6) / 1e12
+            row = {"probe": "MFMA + VALU ops per result", "kind": names[k], "k": k, "workgroups": grid,
+                   "us": round(us, 1), "TOPS": round(tops, 1), "frac_int8_peak": round(tops / INT8_PEAK_TOPS, 3)}
+            print(json.dumps(row), flush=True)
 
 
 def main():

@@ -1236,7 +1236,7 @@ hipError_t launch_gemv_q5k(const uint8_t *W, const int8_t *q, const float *d,
 // The GEMMs of the two-pass FFN: the configuration of the token count.
 static int ffn_gemm_splits(int M, int N, int K)
 {
-    return M <= GEMM_SMALL_M_Q4K ? splits_gemm_q4k_small(M, N, K) : splits_gemm_q4k_f8(M, N, K);
+    return M <= GEMM_SMALL_M_Q4K ? splits_gemm_q4k_small(M, N, K) : splits_gemm_q4k(M, N, K);
 }
 
 size_t ffn_two_pass_bytes(int M, int N, int K, bool gemv)
@@ -1271,7 +1271,7 @@ hipError_t launch_ffn_q4k_two_pass(const uint8_t *Wg, const uint8_t *Wu, const i
                 return launch_gemv_q4k(W, q, d, s, M, N, K, o, st);
             if (M <= GEMM_SMALL_M_Q4K)
                 return launch_gemm_q4k_small(W, q, d, s, M, N, K, o, split, st);
-            return launch_gemm_q4k_f8(W, q, d, s, M, N, K, o, split, st);
+            return launch_gemm_q4k(W, q, d, s, M, N, K, o, split, st);
         };
         e = mm(Wg, g);
         if (e == hipSuccess)

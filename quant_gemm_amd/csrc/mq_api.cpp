@@ -147,7 +147,7 @@ size_t gemm_ws_bytes(Fmt fmt, Kern kern, int64_t M, int64_t N, int64_t K)
           : fmt == Fmt::Q5K ? mq::splits_gemm_q5k_small(m, n, k) : mq::splits_gemm_q4k_small(m, n, k);
     else if (kern == Kern::GEMM)
         s = fmt == Fmt::Q6K ? mq::splits_gemm_q6k(m, n, k)
-          : fmt == Fmt::Q5K ? mq::splits_gemm_q5k(m, n, k) : mq::splits_gemm_q4k_f8(m, n, k);
+          : fmt == Fmt::Q5K ? mq::splits_gemm_q5k(m, n, k) : mq::splits_gemm_q4k(m, n, k);
     return mq::split_bytes(s, M, N);
 }
 
@@ -216,7 +216,7 @@ int matmul(Fmt fmt, const void *W, const int8_t *q, const float *d, const float 
     else if (kern == Kern::GEMM_SMALL)
         e = mq::launch_gemm_q4k_small(Wb, q, d, s, m, n, k, out, w, st);
     else
-        e = mq::launch_gemm_q4k_f8(Wb, q, d, s, m, n, k, out, w, st);
+        e = mq::launch_gemm_q4k(Wb, q, d, s, m, n, k, out, w, st);
     return launched(e, fn);
 }
 

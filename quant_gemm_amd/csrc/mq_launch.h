@@ -119,11 +119,6 @@ struct Ws {
 hipError_t launch_gemm_q4k(const uint8_t *W, const int8_t *q, const float *d,
                            const float *s, int M, int N, int K, float *out,
                            const Ws &ws, hipStream_t st);
-// The 128-token Q4_K GEMM on the fp8 matrix cores (exact sub-block dots as
-// f32, scale products on the bf16 matrix cores): the prefill default.
-hipError_t launch_gemm_q4k_f8(const uint8_t *W, const int8_t *q, const float *d,
-                              const float *s, int M, int N, int K, float *out,
-                              const Ws &ws, hipStream_t st);
 // Small-M configuration of the Q4_K GEMM (32 tokens x 256 rows per workgroup).
 hipError_t launch_gemm_q4k_small(const uint8_t *W, const int8_t *q, const float *d,
                                  const float *s, int M, int N, int K, float *out,
@@ -193,7 +188,6 @@ hipError_t splitk_reduce(const float *part, int nsplit, int64_t n, float *out, h
 // into when it is given a workspace (1 = no split); the launchers below use
 // the same choice, so a caller can size the workspace before the call.
 int splits_gemm_q4k(int M, int N, int K);
-int splits_gemm_q4k_f8(int M, int N, int K);
 int splits_gemm_q4k_small(int M, int N, int K);
 int splits_gemm_q5k(int M, int N, int K);
 int splits_gemm_q5k_small(int M, int N, int K);

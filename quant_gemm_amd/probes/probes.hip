@@ -16,8 +16,11 @@
 //       iteration per wavefront) with k f32 VALU operations per int32
 //       result: k = 0 chains the MFMAs only; k = 2 converts and adds
 //       (cvt, fma); k = 3 also forms a scale product (cvt, mul, fma), as
-//       the GEMM epilogue does; k = 4 one more multiply. sink holds
-//       grid * 256 floats.
+//       the GEMM epilogue does; k = 4 one more multiply. k = 10, 11, 12:
+//       the scaled fp8 MFMA (v_mfma_scale_f32_32x32x64_f8f6f4, one
+//       32-value sub-block's exact dot as an f32 from two base-16 digits
+//       of the activation) chained, or followed by fma, or by scale
+//       product and fma. sink holds grid * 256 floats.
 // Both return the hipError_t of the launch.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -25,6 +28,7 @@
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
@@ -94,9 +98,68 @@ __global__ __launch_bounds__(256) void read_lds(const v4i *__restrict__ src, int
         sink[0] = fold;
 }
 
+// K = 0, 2, 3, 4: int8 32x32x32 MFMAs, each int32 result followed by K f32
+// VALU operations (0: the MFMAs alone, chained). K = 10, 11, 12: the scaled
+// fp8 32x32x64 MFMA that gives one 32-value sub-block's dot as an f32 (two
+// base-16 digits of the activation against the same quants), followed by 0
+// (chained), 1 (fma) or 2 (scale product, fma) VALU operations per result.
 template <int K>
 __global__ __launch_bounds__(256) void mix(int iters, float *sink)
 {
+    if constexpr (K >= 10) {
+        v8i a8 = {(int)threadIdx.x & 0x07070707, 1, 2, 3, 4, 5, 6, 7};
+        v8i b8 = {3, 2, 1, (int)threadIdx.x & 0x07070707, 4, 5, 6, 7};
+        float scale[16];
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+            scale[v] = 1.0f + v * 1e-3f;
+        float f = 1e-3f * threadIdx.x;
+        v16f acc[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+            acc[t] = v16f{};
+        for (int i = 0; i < iters; ++i) {
+            b8.x += i & 0x0101;
+            if constexpr (K == 10) {
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    v8i bt = b8;
+                    bt.y += t;
+                    acc[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, bt, acc[t], 0, 0, 0, 140, 0, 136);
+                }
+            } else {
+                v16f I[4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    v8i bt = b8;
+                    bt.y += t;
+                    I[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, bt, v16f{}, 0, 0, 0, 140, 0, 136);
+                }
+                float rowf[4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    rowf[t] = f * (1.0f + 1e-3f * t);
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        if constexpr (K == 11)
+                            acc[t][v] = __builtin_fmaf(I[t][v], rowf[t], acc[t][v]);
+                        else
+                            acc[t][v] = __builtin_fmaf(I[t][v], rowf[t] * scale[v], acc[t][v]);
+                    }
+                f += 1e-7f;
+            }
+        }
+        float s = 0.0f;
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                s += acc[t][v];
+        sink[(int64_t)blockIdx.x * 256 + threadIdx.x] = s;
+        return;
+    } else {
     v4i a = {(int)threadIdx.x, 1, 2, 3}, b = {3, 2, 1, (int)threadIdx.x};
     float scale[16];
 #pragma unroll
@@ -157,6 +220,7 @@ __global__ __launch_bounds__(256) void mix(int iters, float *sink)
         for (int v = 0; v < 16; ++v)
             s += acc[t][v] + (float)chain[t][v];
     sink[(int64_t)blockIdx.x * 256 + threadIdx.x] = s;
+    }
 }
 
 } // namespace
@@ -195,6 +259,9 @@ extern "C" int mqp_mix(int k, int iters, int grid, float *sink, void *stream)
     else if (k == 2) mix<2><<<grid, 256, 0, st>>>(iters, sink);
     else if (k == 3) mix<3><<<grid, 256, 0, st>>>(iters, sink);
     else if (k == 4) mix<4><<<grid, 256, 0, st>>>(iters, sink);
+    else if (k == 10) mix<10><<<grid, 256, 0, st>>>(iters, sink);
+    else if (k == 11) mix<11><<<grid, 256, 0, st>>>(iters, sink);
+    else if (k == 12) mix<12><<<grid, 256, 0, st>>>(iters, sink);
     else return (int)hipErrorInvalidValue;
     return (int)hipGetLastError();
 }

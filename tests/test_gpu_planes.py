@@ -95,12 +95,7 @@ def test_matmul_q4k_dsc(dev, M, N, K):
     rq, rd, _ = oracle.quantize_act(x)
     check_close(got, oracle.matmul_q4k(W, rq, rd, N, K), f"q4k_dsc M={M} N={N} K={K}")
     raw = host(mq.matmul_q4k(Wd, q, d, s, N, K, path=mq.MQ_PATH_GEMM))
-    if M <= 64:
-        # both on the int8 kernel's 32-token tiles: same factors, same order
-        assert np.array_equal(got, raw), "the raw-block GEMM's result bit for bit"
-    else:
-        # the raw-block GEMM of 128-token tiles runs on the fp8 matrix cores
-        check_close(got, raw.astype(np.float64), f"q4k_dsc against the raw-block GEMM M={M}")
+    assert np.array_equal(got, raw), "same factors, same order: the raw-block GEMM's result bit for bit"
 
 
 _SAMPLE = [0, 1, 63, 64, 127, 128, 129, 511, 1000, 2047, 2048, 3199, 3200, 3250, 3312, 3313]
