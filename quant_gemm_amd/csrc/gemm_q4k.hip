@@ -586,22 +586,24 @@ __global__ __launch_bounds__(NTHR, MQ_Q4K_OCC) void gemm_q4k_kernel(
 #pragma unroll
             for (int v = 0; v < 16; ++v)
                 amax[v] = half_max(amax[v]);
-            float db[16], qf[16];
+            float db[16], rdb[16], qf[16];
             bool slow = false;
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                db[v] = amax[v] / 127.0f;
+                db[v] = q_scale(amax[v]);
+                rdb[v] = q_recip(db[v]);
                 const bool zero = db[v] == 0.0f;
-                const float t = y[v] * (zero ? 0.0f : 1.0f / db[v]);
-                slow |= !zero && (db[v] < 0x1p-100f || q_near_half(t));
-                qf[v] = q_clamp_round(t);
+                const float t = y[v] * rdb[v];
+                const float r = __builtin_rintf(t);
+                slow |= !zero && (db[v] < 0x1p-100f || q_near_half(t, r));
+                qf[v] = fminf(fmaxf(r, -127.0f), 127.0f);
             }
             if (__any(slow)) {
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const bool zero = db[v] == 0.0f;
-                    const float t = y[v] * (zero ? 0.0f : 1.0f / db[v]);
-                    if (!zero && (db[v] < 0x1p-100f || q_near_half(t)))
+                    const float t = y[v] * rdb[v];
+                    if (!zero && (db[v] < 0x1p-100f || q_near_half(t, __builtin_rintf(t))))
                         qf[v] = q_clamp_round(y[v] / db[v]);
                 }
             }

@@ -7,14 +7,15 @@
 // The pages call for activations quantized on the fly, once per activation,
 // with per-block sums (minfer Support Matrix, "Supported Quantization
 // Formats"; minfer Compute Graph Design, §9.3 Execution dispatch); the
-// rounding rule is the reading stated in mq.h. Every step is one IEEE f32
-// operation (correctly rounded division, no contraction, no denormal flush),
-// so the plane is bit-exact against a host evaluation of the same rule.
+// rounding rule is the reading stated in mq.h. The plane equals, bit for
+// bit, a host evaluation of the rule in IEEE f32 (correctly rounded
+// division, no contraction, no denormal flush); quant_core.h gives the
+// argument for the cheaper forms the kernels evaluate.
 //
 // HBM-bound: 4 B read and 1 + 8/32 B written per element. A lane owns 4
-// consecutive values of each of QA_ITEMS blocks (16-byte loads, 4-byte
-// stores); 8 lanes own a 32-value block and combine amax and sum(q) with
-// cross-lane swizzles (quant_core.h).
+// consecutive values of each of a few blocks (16-byte loads, 4-byte stores);
+// 8 lanes own a 32-value block and combine amax and sum(q) with DPP moves
+// (quant_core.h).
 #include "mq_device.h"
 #include "mq_launch.h"
 #include "quant_core.h"
@@ -31,13 +32,13 @@ __device__ __forceinline__ int quant1(float v, float db, float rdb, bool zero)
     if (zero)
         return 0;
     const float t = v * rdb;
-    return (int)q_clamp_round(db < 0x1p-100f || q_near_half(t) ? v / db : t);
+    return (int)q_clamp_round(db < 0x1p-100f || q_near_half(t, __builtin_rintf(t)) ? v / db : t);
 }
 
-// Vector path: x 16-byte aligned and ldx % 4 == 0. A workgroup covers
-// QA_ITEMS * 1024 consecutive values of one token row: QA_ITEMS float4 per
-// thread, 8 threads per 32-value block, all loads issued first.
-constexpr int QA_ITEMS = 4;
+// Strided rows (x 16-byte aligned, ldx % 4 == 0, ldx > K): a workgroup
+// covers QA_ITEMS * 1024 consecutive values of one token row: QA_ITEMS
+// float4 per thread, 8 threads per 32-value block, all loads issued first.
+constexpr int QA_ITEMS = 2;
 
 __global__ __launch_bounds__(256) void quantize_act_v4(
     const float *__restrict__ x, int K, int chunks, int64_t ldx, int8_t *__restrict__ q,
@@ -52,7 +53,7 @@ __global__ __launch_bounds__(256) void quantize_act_v4(
 #pragma unroll
     for (int i = 0; i < QA_ITEMS; ++i) {
         const int k = (c * QA_ITEMS + i) * 1024 + 4 * threadIdx.x;
-        v[i] = *reinterpret_cast<const float4 *>(xr + (k < K ? k : K - 4));   // in range; not stored past K
+        v[i] = ld_stream_f4(xr + (k < K ? k : K - 4));   // in range; not stored past K
     }
     uint32_t qp[QA_ITEMS];
     float db[QA_ITEMS], sb[QA_ITEMS];
@@ -73,67 +74,44 @@ __global__ __launch_bounds__(256) void quantize_act_v4(
 
 // Contiguous rows (ldx == K, x 16-byte aligned): the plane is one flat
 // sequence of nblk = M*K/32 blocks, and so are q (32 bytes per block), d and
-// s. A persistent grid walks units of 32*NC blocks (unit u: blocks
-// 32*NC*u .. 32*NC*u + 32*NC - 1; 8-lane group g of the workgroup takes
-// block 32*NC*u + 32*c + g of its chunk c), with the next unit's loads in
-// flight while a unit is quantized and stored. Against one workgroup per
-// row chunk (quantize_act_v4), measured by GPU time on MI355X: 3314 x 3584
-// 19.6 -> 15.2 us, 512 x 18944 15.6 -> 12.8 us, one token 3.2 -> 2.7 us;
-// but 3314 x 18944 (251 MB) 60.9 -> 66.0 us, so planes of more than 128 MB
-// of input keep the row-chunk grid (many waves of workgroups already
-// overlap there). 1, 2 and 4 blocks per group and unit and 1024, 2048 and
-// 4096 workgroups were measured; 2 and 1024 were best up to 128 MB.
-#ifndef QA_STREAM_NC
-#define QA_STREAM_NC 2
-#endif
-#ifndef QA_STREAM_WGS
-#define QA_STREAM_WGS 1024
-#endif
-constexpr int64_t QA_STREAM_MAX_BYTES = int64_t(128) << 20;
+// s. Workgroup b takes blocks 32*QA_FLAT_NC*b .. + 32*QA_FLAT_NC - 1
+// (8-lane group g of it block 32*QA_FLAT_NC*b + 32*c + g of its chunk c), so
+// no workgroup idles on a row's tail. Measured on MI355X, kernel time with
+// the input cold in HBM: 3314 x 3584 12.5 us, 512 x 18944 10.6 us,
+// 3314 x 18944 69 us; a kernel that moves the same bytes in the same pattern
+// with no arithmetic takes 12.2, 10.1 and 72 us. Persistent grids (1024 to
+// 4096 workgroups, the next unit's loads in flight), 1, 2 and 4 blocks per
+// group and 2 or 4 units per workgroup were measured too and were no
+// faster.
+constexpr int QA_FLAT_NC = 2;
 
-template <int NC>
-__global__ __launch_bounds__(256) void quantize_act_stream(
+__global__ __launch_bounds__(256) void quantize_act_flat(
     const float *__restrict__ x, int64_t nblk, int8_t *__restrict__ q, float *__restrict__ d,
     float *__restrict__ s)
 {
     const int g = threadIdx.x >> 3;
     const int li = threadIdx.x & 7;
-    const int64_t per = 32 * NC;
-    const int64_t nunits = (nblk + per - 1) / per;
-    auto load = [&](float4 (&v)[NC], int64_t u) {
+    const int64_t base = (int64_t)blockIdx.x * (32 * QA_FLAT_NC) + g;
+    float4 v[QA_FLAT_NC];
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            const int64_t B = u * per + 32 * c + g;
-            const int64_t Bc = B < nblk ? B : nblk - 1;   // in range; not stored past nblk
-            const v4f t = __builtin_nontemporal_load(reinterpret_cast<const v4f *>(x + 32 * Bc + 4 * li));
-            v[c] = make_float4(t[0], t[1], t[2], t[3]);
-        }
-    };
-    float4 cur[NC], nxt[NC];
-    int64_t u = blockIdx.x;
-    if (u < nunits)
-        load(cur, u);
-    for (; u < nunits; u += gridDim.x) {
-        const int64_t un = u + gridDim.x;
-        if (un < nunits)                          // workgroup-uniform
-            load(nxt, un);
-        uint32_t qp[NC];
-        float db[NC], sb[NC];
-        quant_chunks<NC>(cur, qp, db, sb);
+    for (int c = 0; c < QA_FLAT_NC; ++c) {
+        const int64_t B = base + 32 * c;
+        const int64_t Bc = B < nblk ? B : nblk - 1;   // in range; not stored past nblk
+        v[c] = ld_stream_f4(x + 32 * Bc + 4 * li);
+    }
+    uint32_t qp[QA_FLAT_NC];
+    float db[QA_FLAT_NC], sb[QA_FLAT_NC];
+    quant_chunks<QA_FLAT_NC>(v, qp, db, sb);
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            const int64_t B = u * per + 32 * c + g;
-            if (B < nblk) {                       // whole 8-lane groups
-                *reinterpret_cast<uint32_t *>(q + 32 * B + 4 * li) = qp[c];
-                if (li == 0) {
-                    d[B] = db[c];
-                    s[B] = sb[c];
-                }
+    for (int c = 0; c < QA_FLAT_NC; ++c) {
+        const int64_t B = base + 32 * c;
+        if (B < nblk) {                           // whole 8-lane groups
+            *reinterpret_cast<uint32_t *>(q + 32 * B + 4 * li) = qp[c];
+            if (li == 0) {
+                d[B] = db[c];
+                s[B] = sb[c];
             }
         }
-#pragma unroll
-        for (int c = 0; c < NC; ++c)
-            cur[c] = nxt[c];
     }
 }
 
@@ -175,11 +153,10 @@ hipError_t launch_quantize(const float *x, int64_t M, int64_t K, int64_t ldx,
                            int8_t *q, float *d, float *s, hipStream_t st)
 {
     const bool vec = (reinterpret_cast<uintptr_t>(x) % 16 == 0) && (ldx % 4 == 0);
-    if (vec && ldx == K && M * K * 4 <= QA_STREAM_MAX_BYTES) {
+    if (vec && ldx == K) {
         const int64_t nblk = M * (K / 32);
-        const int64_t nunits = (nblk + 32 * QA_STREAM_NC - 1) / (32 * QA_STREAM_NC);
-        const int64_t grid = nunits < QA_STREAM_WGS ? nunits : QA_STREAM_WGS;
-        quantize_act_stream<QA_STREAM_NC><<<dim3((unsigned)grid), dim3(256), 0, st>>>(x, nblk, q, d, s);
+        const int64_t grid = (nblk + 32 * QA_FLAT_NC - 1) / (32 * QA_FLAT_NC);
+        quantize_act_flat<<<dim3((unsigned)grid), dim3(256), 0, st>>>(x, nblk, q, d, s);
     } else if (vec) {
         const int chunks = (int)((K + QA_ITEMS * 1024 - 1) / (QA_ITEMS * 1024));
         quantize_act_v4<<<dim3((unsigned)(M * chunks)), dim3(256), 0, st>>>(x, (int)K, chunks, ldx, q, d, s);

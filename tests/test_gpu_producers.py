@@ -55,7 +55,8 @@ def assert_plane_of(q, d, s, y, what):
 
 
 RMS_SHAPES = [(1, 256, None), (7, 3584, None), (64, 1024, 1100), (33, 18944, None),
-              (3314, 3584, None), (5, 8192, 8196), (2, 9216, None)]
+              (3314, 3584, None), (5, 8192, 8196), (2, 9216, None), (300, 1024, 1028),
+              (256, 3840, None), (257, 4096, None), (301, 768, None)]
 
 
 @pytest.mark.parametrize("M,K,ldx", RMS_SHAPES)
@@ -70,6 +71,56 @@ def test_rmsnorm_quantize_bit_exact(dev, M, K, ldx, eps):
     assert np.array_equal(y, ry), f"y differs in {np.count_nonzero(y != ry)} elements"
     assert np.array_equal(q, rq) and np.array_equal(d, rd) and np.array_equal(s, rs)
     assert np.array_equal(q2, q) and np.array_equal(d2, d) and np.array_equal(s2, s)
+
+
+def _rows_near_scale_boundary(rng, M, K, eps):
+    """Rows whose exact sum of squares puts r = f32(1/sqrt(ss/K + eps)) on the
+    midpoint between two f32 values, to within about 2^-70 of ss: a sum of
+    squares that is off by a few f64 ulps rounds r the other way. A random
+    body is completed by three entries that take up the remainder."""
+    import math
+    eps64 = float(np.float32(eps))
+    x = np.empty((M, K), np.float32)
+    for t in range(M):
+        r0 = np.float32(rng.uniform(0.3, 3.0))
+        m = (float(r0) + float(np.nextafter(r0, np.float32(np.inf)))) / 2
+        target = K * (1.0 / (m * m) - eps64)
+        row = (rng.standard_normal(K) * 0.5 * math.sqrt(target / K)).astype(np.float32)
+        pos = rng.choice(K, 3, replace=False)
+        row[pos] = 0
+        rest = target - math.fsum((row.astype(np.float64) ** 2).tolist())
+        for p in pos:
+            if rest <= 0:
+                break
+            a = np.float32(math.sqrt(rest))
+            while float(a) ** 2 > rest:
+                a = np.nextafter(a, np.float32(0))
+            row[p] = a if rng.random() < 0.5 else -a
+            rest -= float(a) ** 2
+        x[t] = row
+    return x
+
+
+@pytest.mark.parametrize("M,K", [(27, 256), (300, 256), (27, 3584), (300, 3584), (9, 8192)])
+@pytest.mark.parametrize("eps", [1e-6, 0.0])
+def test_rmsnorm_scale_on_rounding_boundary(dev, M, K, eps):
+    """Where r sits on an f32 rounding boundary only an exactly rounded sum of
+    squares gives the oracle's r: the kernels' certified fast sum must notice
+    and take the exact one."""
+    import math
+    rng = np.random.default_rng(M * 7 + K + int(eps == 0))
+    x = _rows_near_scale_boundary(rng, M, K, eps)
+    w = (1.0 + 0.3 * rng.standard_normal(K)).astype(np.float32)
+    e64 = float(np.float32(eps))
+    for t in range(M):                       # the construction holds: the rows are hard
+        ss = math.fsum((x[t].astype(np.float64) ** 2).tolist())
+        lo, hi = ss * (1 - 2.0 ** -46), ss * (1 + 2.0 ** -46)
+        assert np.float32(1 / math.sqrt(lo / K + e64)) != np.float32(1 / math.sqrt(hi / K + e64))
+    print(f"[producers] rmsnorm boundary rows M={M} K={K} eps={eps}", flush=True)
+    q, d, s, y, q2, d2, s2 = gpu_rms(x, w, eps)
+    rq, rd, rs, ry = producers.rmsnorm_quantize(x, w, eps)
+    assert np.array_equal(y, ry), f"y differs in rows {np.nonzero((y != ry).any(axis=1))[0]}"
+    assert np.array_equal(q, rq) and np.array_equal(d, rd) and np.array_equal(s, rs)
 
 
 def test_rmsnorm_quantize_edge_rows(dev):
