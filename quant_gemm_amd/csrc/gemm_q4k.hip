@@ -527,7 +527,7 @@ __global__ __launch_bounds__(NTHR, MQ_Q4K_OCC) void gemm_q4k_kernel(
     const int n0 = tile_n * (FFN ? BN / 2 : BN);
     const WRows rows{W, W2, n0, N, (int64_t)(K >> 8) * BLK_BYTES};
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: DMA bases in SGPRs
     const int wm = wave % WM, wn = wave / WM;
     const int lr = lane & 31, lh = lane >> 5;
 

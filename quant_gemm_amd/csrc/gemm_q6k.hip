@@ -29,12 +29,11 @@
 // with aligned dword loads realigned in registers): the limb planes use one
 // buffer, written between two barriers.
 //
-// Expansion planes (X): the same kernel reads the two limbs and d from
-// planes built once at registration (mq_expand_q6k) instead of decoding
-// the raw blocks on every tile, as the pages' q6_K expansion planes do
-// (minfer Features, "GPU — CUDA"). The per-step decode then reduces to two
-// 16-byte loads per limb chunk, passed through registers into the same LDS
-// layout.
+// Expansion planes: a second kernel reads the two limbs and d from planes
+// built once at registration (mq_expand_q6k) instead of decoding the raw
+// blocks on every tile, as the pages' q6_K expansion planes do (minfer
+// Features, "GPU — CUDA"). With nothing to decode it stages everything by
+// DMA into double-buffered 64-value steps (see "planes GEMM" below).
 //
 // MFMA operand layout (32x32x32): lane l supplies row (l % 32) of A and
 // column (l % 32) of B, 16 consecutive K values from 16 * (l / 32) each;
@@ -96,7 +95,7 @@ __device__ __forceinline__ void issue_act(ActStage &s, const int8_t *__restrict_
     }
 }
 
-// Expansion planes of the weights (X): limbs lo / hi [N][K], d [N][K/256].
+// Expansion planes of the weights: limbs lo / hi [N][K], d [N][K/256].
 struct Planes {
     const int8_t *lo, *hi;
     const float *dw;
@@ -107,21 +106,12 @@ struct Planes {
 // fields start 2 bytes into a dword when the block does; the aligned dwords
 // covering them are kept as loaded and realigned only after the step's
 // compute, so the loads stay in flight during it.
-template <bool X>
 struct Raw {
     uint32_t w0[5], w1[5], wh[5], ws[3];
     uint32_t sh;                             // 0 or 2: byte offset of the fields in their dwords
     uint32_t dbits;
     float4 ds;                               // 4 activation scales of token tid (tid < BM)
 };
-// X: the thread's four 16-byte chunks c = 2r + hh of each limb plane
-template <>
-struct Raw<true> {
-    v4i lo[4], hi[4];
-    float dw;
-    float4 ds;
-};
-
 template <int n>
 __device__ __forceinline__ void load_dw(const uint8_t *p, uint32_t (&w)[n + 1], uint32_t sh)
 {
@@ -142,24 +132,7 @@ __device__ __forceinline__ void realign(const uint32_t (&w)[n + 1], uint32_t sh,
         o[i] = __builtin_amdgcn_alignbyte(w[i + 1], w[i], sh);
 }
 
-__device__ __forceinline__ void load_raw(Raw<true> &p, const Planes &E, const float *__restrict__ dx,
-                                         int M, int N, int K, int t0, int n0, int st)
-{
-    const int tid = threadIdx.x;
-    const int row = tid >> 1, hh = tid & 1;
-    const int64_t n = min(n0 + row, N - 1);
-    const int64_t base = n * K + (int64_t)st * BK + 16 * hh;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        p.lo[r] = *reinterpret_cast<const v4i *>(E.lo + base + 32 * r);
-        p.hi[r] = *reinterpret_cast<const v4i *>(E.hi + base + 32 * r);
-    }
-    p.dw = E.dw[n * (K >> 8) + (st >> 1)];
-    const int t = min(t0 + (tid & (BM - 1)), M - 1);
-    p.ds = *reinterpret_cast<const float4 *>(dx + (int64_t)t * (K >> 5) + (st * BK >> 5));
-}
-
-__device__ __forceinline__ void load_raw(Raw<false> &p, const uint8_t *__restrict__ W,
+__device__ __forceinline__ void load_raw(Raw &p, const uint8_t *__restrict__ W,
                                          const float *__restrict__ dx, int M, int N, int K,
                                          int t0, int n0, int st)
 {
@@ -217,26 +190,7 @@ __device__ __forceinline__ void store_act_scales(ActStage &a, const float4 &ds, 
     }
 }
 
-__device__ __forceinline__ void store_raw(WgtStage &w, ActStage &a, const Raw<true> &p, int M, int N,
-                                          int t0, int n0)
-{
-    const int tid = threadIdx.x;
-    const int row = tid >> 1, hh = tid & 1;
-    // a row past N (which reads the last row) and a super-block with d = 0
-    // get zero limbs and d = 0 (the accumulator scale is then kept)
-    const bool ok = n0 + row < N && p.dw != 0.0f;
-    const v4i z = {0, 0, 0, 0};
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        *reinterpret_cast<v4i *>(w.lo + 16 * slot8(row, 2 * r + hh)) = ok ? p.lo[r] : z;
-        *reinterpret_cast<v4i *>(w.hi + 16 * slot8(row, 2 * r + hh)) = ok ? p.hi[r] : z;
-    }
-    if (hh == 0)
-        w.dw[row] = ok ? p.dw : 0.0f;
-    store_act_scales(a, p.ds, M, t0);
-}
-
-__device__ __forceinline__ void store_raw(WgtStage &w, ActStage &a, const Raw<false> &p, int M, int N,
+__device__ __forceinline__ void store_raw(WgtStage &w, ActStage &a, const Raw &p, int M, int N,
                                           int t0, int n0)
 {
     const int tid = threadIdx.x;
@@ -302,8 +256,12 @@ __device__ __forceinline__ void compute_step(const ActStage &a, const WgtStage &
         // first tile before the last tile's epilogue: at the step's last
         // sub-block that product repeats tile 0 of the same sub-block and is not
         // used (1 of the step's 16 MFMA pairs), so that every sub-block runs the
-        // same schedule; the stages are pinned by scheduling barriers (measured
-        // 3% faster than each tile's MFMAs followed at once by its epilogue).
+        // same rolled loop body; the stages are pinned by scheduling barriers
+        // (measured 3% faster than each tile's MFMAs followed at once by its
+        // epilogue). Skipping that pair, by a branch or by peeling the last
+        // sub-block, takes the kernel past 256 registers (99 to 119 spilled),
+        // and the MFMA pipe is not what bounds it. The expansion-plane kernel
+        // below has no such pair.
         const int tr = wm * 32 + lr;
         auto mm = [&](int j, int b, const v4i &afx, v16i &il, v16i &ih) {
             const int r = (wn * TN + b) * 32 + lr;
@@ -384,14 +342,11 @@ __device__ __forceinline__ void compute_step(const ActStage &a, const WgtStage &
     }
 }
 
-// Src: the raw blocks (const uint8_t *) or the expansion planes (Planes).
-template <class Src>
 __global__ __launch_bounds__(NTHR, 2) void gemm_q6k_kernel(
-    const Src W, const int8_t *__restrict__ q,
+    const uint8_t *__restrict__ W, const int8_t *__restrict__ q,
     const float *__restrict__ dx, int M, int N, int K, int tiles_m, int nsplit,
     float *__restrict__ out)
 {
-    constexpr bool X = std::is_same<Src, Planes>::value;
     __shared__ ActStage A0, A1;
     __shared__ WgtStage B;
     // blockIdx = split * tiles + tile (tile_order maps tile to tile_m and
@@ -410,7 +365,7 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_q6k_kernel(
     const int t0 = tile_m * BM;
     const int n0 = tile_n * BN;
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: DMA bases in SGPRs
     const int wm = wave % WM, wn = wave / WM;
     const int lr = lane & 31, lh = lane >> 5;
 
@@ -426,7 +381,7 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_q6k_kernel(
 
     // The step range is even (whole super-blocks): steps alternate the
     // activation buffers A0, A1.
-    Raw<X> p;
+    Raw p;
     issue_act(A0, q, M, K, t0, st_begin, wave, lane);
     load_raw(p, W, dx, M, N, K, t0, n0, st_begin);
     wait_vm<0>();
@@ -453,6 +408,268 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_q6k_kernel(
             wait_vm<0>();
             store_raw(B, A0, p, M, N, t0, n0);
             __syncthreads();
+        }
+    }
+
+#pragma unroll
+    for (int b = 0; b < TN; ++b) {
+        const int n = n0 + (wn * TN + b) * 32 + lr;
+        if (n < N) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int t = t0 + wm * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
+                if (t < M)
+                    dst[(int64_t)t * N + n] = acc[b][v] * cur[b];
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------- planes GEMM
+// The expansion planes need no decoding, so their GEMM stages everything by
+// global->LDS DMA (the pages stage the W_exp planes with asynchronous
+// copies: minfer Features, "GPU — CUDA"): K moves in steps of 64 values
+// through two stages, each holding the step's activation tile, both limb
+// tiles, the activation scales and (at super-block starts) the rows' d.
+// While the wavefronts compute on one stage the DMA fills the other, with
+// one barrier per step. The planes hold the limbs of a super-block with
+// d = 0 as they are; in a super-block where one of its rows has d = 0, a
+// wavefront zeroes those rows' limbs in the stage before it reads them
+// (every wavefront that reads a row zeroes it itself, so no barrier is
+// needed), as the raw-block kernel writes them.
+//
+// LDS rows are 64 bytes (4 chunks of 16); chunk c of row r sits in slot
+// 4 r + (c ^ ((r >> 2) & 3)), so the 16 rows one MFMA operand read touches
+// in a cycle fall in distinct banks.
+constexpr int XBK = 64;
+constexpr int XSUB = XBK / 32;               // 32-value sub-blocks per step
+struct alignas(16) XStage {
+    int8_t a[BM * XBK];
+    int8_t lo[BN * XBK];
+    int8_t hi[BN * XBK];
+    float dx[XSUB][BM];
+    float dw[BN];
+};
+
+__device__ __forceinline__ int slot4(int r, int c) { return r * 4 + (c ^ ((r >> 2) & 3)); }
+
+// The DMA of a stage: 64-lane instructions i = wave + NWAVES * ii over each
+// array; every lane keeps the source address of its share of each array
+// for step 0 (the step adds 64 values, 2 activation scales and, every 4
+// steps, 1 super-block).
+constexpr int XA_I = BM * 4 / 64;            // activation tile: 16-byte chunks / 64
+constexpr int XW_I = BN * 4 / 64;            // one limb tile
+constexpr int XD_I = XSUB * BM / 64;         // activation scales (dwords)
+constexpr int XE_I = BN / 64;                // rows' d (dwords)
+static_assert(XA_I * 64 == BM * 4 && XW_I * 64 == BN * 4 && XD_I * 64 == XSUB * BM && XE_I * 64 == BN,
+              "whole DMA instructions");
+template <int I>
+constexpr int per_wave() { return (I + NWAVES - 1) / NWAVES; }
+
+struct XSrc {
+    const int8_t *a[per_wave<XA_I>()];
+    const int8_t *lo[per_wave<XW_I>()];
+    const int8_t *hi[per_wave<XW_I>()];
+    const float *dx[per_wave<XD_I>()];
+    const float *dw[per_wave<XE_I>()];
+};
+
+__device__ __forceinline__ XSrc x_src(const Planes &E, const int8_t *__restrict__ q, const float *__restrict__ dx,
+                                      int M, int N, int K, int t0, int n0, int wave, int lane)
+{
+    XSrc S;
+    auto chunk = [&](int i, int &r, int &c) {
+        const int p = 64 * i + lane;
+        r = p >> 2;
+        c = (p & 3) ^ ((r >> 2) & 3);
+    };
+#pragma unroll
+    for (int ii = 0; ii < per_wave<XA_I>(); ++ii) {
+        int r, c;
+        chunk(wave + NWAVES * ii, r, c);
+        S.a[ii] = q + (int64_t)min(t0 + r, M - 1) * K + 16 * c;
+    }
+#pragma unroll
+    for (int ii = 0; ii < per_wave<XW_I>(); ++ii) {
+        int r, c;
+        chunk(wave + NWAVES * ii, r, c);
+        const int64_t o = (int64_t)min(n0 + r, N - 1) * K + 16 * c;
+        S.lo[ii] = E.lo + o;
+        S.hi[ii] = E.hi + o;
+    }
+#pragma unroll
+    for (int ii = 0; ii < per_wave<XD_I>(); ++ii) {
+        const int p = 64 * (wave + NWAVES * ii) + lane;
+        S.dx[ii] = dx + (int64_t)min(t0 + p % BM, M - 1) * (K >> 5) + p / BM;
+    }
+#pragma unroll
+    for (int ii = 0; ii < per_wave<XE_I>(); ++ii) {
+        const int r = 64 * (wave + NWAVES * ii) + lane;
+        S.dw[ii] = E.dw + (int64_t)min(n0 + r, N - 1) * (K >> 8);
+    }
+    return S;
+}
+
+__device__ __forceinline__ void x_issue(XStage &S, const XSrc &src, int st, int wave)
+{
+    const int64_t k0 = (int64_t)st * XBK;
+#pragma unroll
+    for (int ii = 0; ii < per_wave<XA_I>(); ++ii) {
+        const int i = wave + NWAVES * ii;
+        if (XA_I % NWAVES == 0 || i < XA_I)  // wavefront-uniform
+            dma16(src.a[ii] + k0, S.a + 1024 * i);
+    }
+#pragma unroll
+    for (int ii = 0; ii < per_wave<XW_I>(); ++ii) {
+        const int i = wave + NWAVES * ii;
+        if (XW_I % NWAVES == 0 || i < XW_I) {
+            dma16(src.lo[ii] + k0, S.lo + 1024 * i);
+            dma16(src.hi[ii] + k0, S.hi + 1024 * i);
+        }
+    }
+#pragma unroll
+    for (int ii = 0; ii < per_wave<XD_I>(); ++ii) {
+        const int i = wave + NWAVES * ii;
+        if (XD_I % NWAVES == 0 || i < XD_I)
+            dma4(src.dx[ii] + XSUB * st, &S.dx[0][0] + 64 * i);
+    }
+    if ((st & 3) == 0) {                     // a super-block starts: the rows' d
+#pragma unroll
+        for (int ii = 0; ii < per_wave<XE_I>(); ++ii) {
+            const int i = wave + NWAVES * ii;
+            if (XE_I % NWAVES == 0 || i < XE_I)
+                dma4(src.dw[ii] + (st >> 2), S.dw + 64 * i);
+        }
+    }
+}
+
+// One step on a stage: for each sub-block, each tile's two limb MFMAs and
+// then its epilogue (combine the limbs, convert, fma with the activation
+// scale). The sub-block loop stays rolled, which keeps the MFMA results of
+// one tile at a time in registers.
+__device__ __forceinline__ void x_compute(const XStage &S, v16f (&acc)[TN], int wm, int wn, int lr, int lh)
+{
+    const int tr = wm * 32 + lr;
+#pragma unroll 1
+    for (int j = 0; j < XSUB; ++j) {
+        const v4i af = *reinterpret_cast<const v4i *>(S.a + 16 * slot4(tr, 2 * j + lh));
+        float dv[16];
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+            const float4 d4 = *reinterpret_cast<const float4 *>(&S.dx[j][wm * 32 + 8 * g4 + 4 * lh]);
+            dv[4 * g4 + 0] = d4.x;
+            dv[4 * g4 + 1] = d4.y;
+            dv[4 * g4 + 2] = d4.z;
+            dv[4 * g4 + 3] = d4.w;
+        }
+#pragma unroll
+        for (int b = 0; b < TN; ++b) {
+            const int r = (wn * TN + b) * 32 + lr;
+            const v4i lo = *reinterpret_cast<const v4i *>(S.lo + 16 * slot4(r, 2 * j + lh));
+            const v4i hi = *reinterpret_cast<const v4i *>(S.hi + 16 * slot4(r, 2 * j + lh));
+            const v16i il = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, lo, v16i{}, 0, 0, 0);
+            const v16i ih = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, hi, v16i{}, 0, 0, 0);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int J = (ih[v] << 6) + il[v];
+                acc[b][v] = fmaf((float)J, dv[v], acc[b][v]);
+            }
+        }
+    }
+}
+
+// A step: wait for this stage's DMA (own, then everyone's through the
+// barrier, which also ends every wavefront's reads of the other stage),
+// start the next step's DMA into the other stage, then compute. FIRST: the
+// step opens a super-block, so each row tile moves its accumulator to the
+// new d (cur[b]: the d the accumulator is counted in).
+template <bool FIRST>
+__device__ __forceinline__ void x_step(XStage &S, XStage &Snext, const XSrc &src, int st, int st_end,
+                                       v16f (&acc)[TN], float (&cur)[TN], bool (&zr)[TN], bool &mask, int wave,
+                                       int wm, int wn, int lr, int lh)
+{
+    wait_vm<0>();
+    __syncthreads();
+    if (st + 1 < st_end)
+        x_issue(Snext, src, st + 1, wave);
+    if constexpr (FIRST) {
+        bool any = false;
+#pragma unroll
+        for (int b = 0; b < TN; ++b) {
+            const float dn = S.dw[(wn * TN + b) * 32 + lr];
+            zr[b] = dn == 0.0f;
+            any |= zr[b];
+            if (dn != 0.0f) {
+                const float f = cur[b] / dn;
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    acc[b][v] *= f;
+                cur[b] = dn;
+            }
+        }
+        mask = __any(any);
+    }
+    if (mask) {                              // rare: zero the limbs this lane reads of rows with d = 0
+        const v4i z = {0, 0, 0, 0};
+#pragma unroll
+        for (int b = 0; b < TN; ++b) {
+            if (zr[b]) {
+                const int r = (wn * TN + b) * 32 + lr;
+#pragma unroll
+                for (int j = 0; j < XSUB; ++j) {
+                    *reinterpret_cast<v4i *>(S.lo + 16 * slot4(r, 2 * j + lh)) = z;
+                    *reinterpret_cast<v4i *>(S.hi + 16 * slot4(r, 2 * j + lh)) = z;
+                }
+            }
+        }
+    }
+    x_compute(S, acc, wm, wn, lr, lh);
+}
+
+__global__ __launch_bounds__(NTHR, 2) void gemm_q6k_planes_kernel(
+    const Planes E, const int8_t *__restrict__ q, const float *__restrict__ dx, int M, int N, int K,
+    int tiles_m, int nsplit, float *__restrict__ out)
+{
+    __shared__ XStage S0, S1;
+    const int tiles = gridDim.x / nsplit;
+    const int split = blockIdx.x / tiles;
+    const int tile = blockIdx.x - split * tiles;
+    int tile_m, tile_n;
+    tile_order(tile, tiles_m, tiles / tiles_m, tile_m, tile_n);
+    const int sbs = K >> 8;                  // super-blocks; 4 steps each
+    const int st_begin = 4 * (int)((int64_t)split * sbs / nsplit);
+    const int st_end = 4 * (int)((int64_t)(split + 1) * sbs / nsplit);
+    float *dst = out + (int64_t)split * M * N;
+    const int t0 = tile_m * BM;
+    const int n0 = tile_n * BN;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: DMA bases in SGPRs
+    const int wm = wave % WM, wn = wave / WM;
+    const int lr = lane & 31, lh = lane >> 5;
+
+    v16f acc[TN];
+    float cur[TN];
+    bool zr[TN];
+    bool mask = false;
+#pragma unroll
+    for (int b = 0; b < TN; ++b) {
+        cur[b] = 1.0f;
+        zr[b] = false;
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+            acc[b][v] = 0.0f;
+    }
+    const XSrc src = x_src(E, q, dx, M, N, K, t0, n0, wave, lane);
+    if (st_begin < st_end)
+        x_issue(S0, src, st_begin, wave);
+#pragma unroll 1
+    for (int st = st_begin; st < st_end; st += 4) {   // whole super-blocks: stages S0, S1, S0, S1
+        x_step<true>(S0, S1, src, st, st_end, acc, cur, zr, mask, wave, wm, wn, lr, lh);
+        x_step<false>(S1, S0, src, st + 1, st_end, acc, cur, zr, mask, wave, wm, wn, lr, lh);
+#pragma unroll 1
+        for (int k = 2; k < 4; k += 2) {          // rolled: one copy of the S0, S1 pair
+            x_step<false>(S0, S1, src, st + k, st_end, acc, cur, zr, mask, wave, wm, wn, lr, lh);
+            x_step<false>(S1, S0, src, st + k + 1, st_end, acc, cur, zr, mask, wave, wm, wn, lr, lh);
         }
     }
 
@@ -497,7 +714,7 @@ hipError_t launch_gemm_q6k(const uint8_t *W, const int8_t *q, const float *d,
     const int tiles = tiles_m * tiles_n;
     const int nsplit = ws.ptr ? nsplit_for(M, N, K) : 1;
     return run_split_k(nsplit, (int64_t)M * N, out, ws, st, [&](float *dst) {
-        launch(gemm_q6k_kernel<const uint8_t *>, dim3((unsigned)(tiles * nsplit)), dim3(NTHR), 0, st, W, q, d, M, N, K, tiles_m,
+        launch(gemm_q6k_kernel, dim3((unsigned)(tiles * nsplit)), dim3(NTHR), 0, st, W, q, d, M, N, K, tiles_m,
                                                                                  nsplit, dst);
         return hipGetLastError();
     });
@@ -518,8 +735,8 @@ hipError_t launch_gemm_q6k_x(const int8_t *lo, const int8_t *hi, const float *dw
     const int nsplit = ws.ptr ? nsplit_for(M, N, K) : 1;
     const Planes E{lo, hi, dw};
     return run_split_k(nsplit, (int64_t)M * N, out, ws, st, [&](float *dst) {
-        launch(gemm_q6k_kernel<Planes>, dim3((unsigned)(tiles * nsplit)), dim3(NTHR), 0, st, E, q, d, M, N, K, tiles_m,
-                                                                                 nsplit, dst);
+        launch(gemm_q6k_planes_kernel, dim3((unsigned)(tiles * nsplit)), dim3(NTHR), 0, st, E, q, d, M, N, K, tiles_m,
+               nsplit, dst);
         return hipGetLastError();
     });
 }

@@ -120,6 +120,23 @@ __device__ __forceinline__ void dma16(const void *src, const void *lds_dst)
                  : "memory");
 }
 
+// One 4-byte global->LDS DMA per lane (global_load_lds_dword): lane L's
+// dword lands at LDS byte address lds_dst + 4 * L (lds_dst wave-uniform and
+// 4-byte aligned, src 4-byte aligned). As dma16 otherwise.
+__device__ __forceinline__ void dma4(const void *src, const void *lds_dst)
+{
+    const uint32_t base = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)lds_dst);
+    uint32_t saved;
+    asm volatile("s_mov_b32 %0, m0\n\t"
+                 "s_mov_b32 m0, %2\n\t"
+                 "global_load_lds_dword %1, off\n\t"
+                 "s_mov_b32 m0, %0"
+                 : "=&s"(saved)
+                 : "v"(src), "s"(base)
+                 : "memory");
+}
+
 // Tile order of the GEMMs. Workgroups are handed to the 8 XCDs in turn
 // (workgroup b to XCD b % 8), and each XCD has its own L2. b is renumbered
 // so that each XCD walks one contiguous range of the tile sequence, and the
