@@ -65,8 +65,9 @@ constexpr int A_CHUNKS = BM * BK / 16;      // 16-byte activation chunks per ste
 static_assert(A_CHUNKS % (64 * NWAVES) == 0, "DMA split");
 static_assert(NTHR == 2 * BN && NTHR >= BM, "one thread per (row, half) and per token");
 
-// LDS. 16-byte chunk c of row r sits in slot r*8 + (c ^ (r & 7)) in the
-// activation tiles and in both limb planes.
+// LDS. 16-byte chunk c of row r sits in slot r*8 + (c ^ ((r >> 1) & 7)) in
+// the activation tiles and in both limb planes: sixteen consecutive 128-byte
+// rows reading one chunk fall in sixteen different 4-bank groups.
 struct alignas(16) ActStage {
     int8_t a[A_CHUNKS * 16];
     float dx[BK / 32][BM];
@@ -77,7 +78,7 @@ struct alignas(16) WgtStage {
     float dw[BN];                            // d of the row's super-block
 };
 
-__device__ __forceinline__ int slot8(int r, int c) { return r * 8 + (c ^ (r & 7)); }
+__device__ __forceinline__ int slot8(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }
 
 // Activation tile of step st by DMA; rows past M read the last valid row.
 __device__ __forceinline__ void issue_act(ActStage &s, const int8_t *__restrict__ q, int M,
@@ -89,7 +90,7 @@ __device__ __forceinline__ void issue_act(ActStage &s, const int8_t *__restrict_
         const int i = wave * (A_CHUNKS / 64 / NWAVES) + ii;
         const int p = 64 * i + lane;
         const int r = p >> 3;
-        const int c = (p & 7) ^ (r & 7);
+        const int c = (p & 7) ^ ((r >> 1) & 7);
         const int t = min(t0 + r, M - 1);
         dma16(q + (int64_t)t * K + k0 + 16 * c, s.a + 1024 * i);
     }
