@@ -354,10 +354,11 @@ int mq_matmul_q6k_static(const void *W, const int8_t *q, const float *d,
                          float *out, void *stream);
 
 /*
- * Measurement hook. The next matmul call of the calling thread (mq_matmul_*,
- * mq_ffn_q4k*) launches its main kernel with hipExtLaunchKernel, which
- * records start_event and stop_event (hipEvent_t, created by the caller;
- * either may be NULL) at that kernel's own dispatch start and end, so
+ * Measurement hook. The next matmul or quantizer call of the calling thread
+ * (mq_matmul_*, mq_ffn_q4k*, mq_quantize_act) launches its main kernel with
+ * hipExtLaunchKernel, which records start_event and stop_event (hipEvent_t,
+ * created by the caller; either may be NULL) at that kernel's own dispatch
+ * start and end, so
  * hipEventElapsedTime gives the kernel's duration without the launch gap an
  * event recorded before the call would include. A split-K GEMM's reduction
  * kernel is not covered. The request is consumed by that call, and dropped

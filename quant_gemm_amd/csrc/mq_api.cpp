@@ -27,9 +27,9 @@ namespace {
 
 thread_local char g_err[512];
 
-// Entry points that launch kernels other than a matmul's drop a pending
-// timing request, so it can only ever attach to the matmul call that follows
-// it (the workspace queries launch nothing and leave it).
+// Entry points whose kernels the timing hook does not cover drop a pending
+// timing request, so it can only ever attach to the matmul or quantizer call
+// that follows it (the workspace queries launch nothing and leave it).
 void drop_timing() { mq::kernel_events() = mq::KernelEvents{}; }
 
 int fail(int status, const char *fmt, ...)
@@ -372,7 +372,6 @@ int mq_quantize_act(const float *x, int64_t M, int64_t K, int64_t ldx, int8_t *q
                     float *d, float *s, void *stream)
 {
     g_err[0] = '\0';
-    drop_timing();
     const char *fn = "mq_quantize_act";
     if (!x) return fail(MQ_ERR_INVALID_ARG, "%s: x is NULL", fn);
     if (!q) return fail(MQ_ERR_INVALID_ARG, "%s: q is NULL", fn);

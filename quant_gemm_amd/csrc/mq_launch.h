@@ -11,9 +11,9 @@
 namespace mq {
 
 // Kernel-boundary timing (mq_time_next_kernel): when a pair of events is set
-// for the calling thread, the next matmul kernel launched through launch()
-// records them at its own dispatch start and end (hipExtLaunchKernel) and
-// the pair is cleared. Defined in mq_api.cpp.
+// for the calling thread, the next matmul or quantizer kernel launched
+// through launch() records them at its own dispatch start and end
+// (hipExtLaunchKernel) and the pair is cleared. Defined in mq_api.cpp.
 struct KernelEvents {
     hipEvent_t start = nullptr, stop = nullptr;
 };

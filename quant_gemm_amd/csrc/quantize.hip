@@ -156,15 +156,15 @@ hipError_t launch_quantize(const float *x, int64_t M, int64_t K, int64_t ldx,
     if (vec && ldx == K) {
         const int64_t nblk = M * (K / 32);
         const int64_t grid = (nblk + 32 * QA_FLAT_NC - 1) / (32 * QA_FLAT_NC);
-        quantize_act_flat<<<dim3((unsigned)grid), dim3(256), 0, st>>>(x, nblk, q, d, s);
+        launch(quantize_act_flat, dim3((unsigned)grid), dim3(256), 0, st, x, nblk, q, d, s);
     } else if (vec) {
         const int chunks = (int)((K + QA_ITEMS * 1024 - 1) / (QA_ITEMS * 1024));
-        quantize_act_v4<<<dim3((unsigned)(M * chunks)), dim3(256), 0, st>>>(x, (int)K, chunks, ldx, q, d, s);
+        launch(quantize_act_v4, dim3((unsigned)(M * chunks)), dim3(256), 0, st, x, (int)K, chunks, ldx, q, d, s);
     } else {
         const int64_t nbk = K / 32;
         const int64_t nblk = M * nbk;
         const int64_t grid = (nblk * 32 + 255) / 256;
-        quantize_act_v1<<<dim3((unsigned)grid), dim3(256), 0, st>>>(x, nblk, nbk, K, ldx, q, d, s);
+        launch(quantize_act_v1, dim3((unsigned)grid), dim3(256), 0, st, x, nblk, nbk, K, ldx, q, d, s);
     }
     return hipGetLastError();
 }

@@ -656,7 +656,21 @@ def test_time_next_kernel(dev):
         ms2 = ctypes.c_float()
         assert lib.hipEventElapsedTime(ctypes.byref(ms2), ev[0], ev[1]) == 0
         assert ms2.value == ms.value
-    for e in ev:
+    # the quantizer is covered too, also with events that skip the
+    # system-scope fence (hipEventDisableSystemFence, as bench.py uses)
+    evf = [ctypes.c_void_p(), ctypes.c_void_p()]
+    for e in evf:
+        assert lib.hipEventCreateWithFlags(ctypes.byref(e), 0x20000000) == 0
+    x = synth.activations(rng, 300, K, outliers=True)
+    q0, d0, s0 = (host(t) for t in gpu_plane(x))
+    for pair in (ev, evf):
+        mq.time_next_kernel(pair[0].value, pair[1].value)
+        q1, d1, s1 = (host(t) for t in gpu_plane(x))
+        ms = ctypes.c_float()
+        assert lib.hipEventElapsedTime(ctypes.byref(ms), pair[0], pair[1]) == 0
+        assert 0.0 < ms.value < 100.0, ms.value
+        assert np.array_equal(q1, q0) and np.array_equal(d1, d0) and np.array_equal(s1, s0)
+    for e in ev + evf:
         lib.hipEventDestroy(e)
 
 
