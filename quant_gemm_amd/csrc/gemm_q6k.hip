@@ -544,17 +544,24 @@ __device__ __forceinline__ void x_issue(XStage &S, const XSrc &src, int st, int 
     }
 }
 
-// One step on a stage: for each sub-block, each tile's two limb MFMAs and
-// then its epilogue (combine the limbs, convert, fma with the activation
-// scale). The sub-block loop stays rolled, which keeps the MFMA results of
-// one tile at a time in registers.
+// One step on a stage: for each sub-block, each tile's two limb MFMAs, then
+// (while they run) the next tile's limb reads from LDS, then the tile's
+// epilogue (combine the limbs, convert, fma with the activation scale). The
+// sub-block loop stays rolled, which keeps the MFMA results of one tile at
+// a time in registers (164 VGPRs, three workgroups per CU). The empty asm
+// statements hold each epilogue in its place: without them the compiler
+// moves every epilogue of the step behind all its MFMAs (251 VGPRs).
+// Measured on MI355X: the read-ahead cuts the wait cycles by a quarter,
+// about 2% of the kernel's time.
 __device__ __forceinline__ void x_compute(const XStage &S, v16f (&acc)[TN], int wm, int wn, int lr, int lh)
 {
     const int tr = wm * 32 + lr;
-#pragma unroll 1
-    for (int j = 0; j < XSUB; ++j) {
-        const v4i af = *reinterpret_cast<const v4i *>(S.a + 16 * slot4(tr, 2 * j + lh));
-        float dv[16];
+    auto ld_w = [&](int j, int b, v4i &lo, v4i &hi) {
+        const int r = (wn * TN + b) * 32 + lr;
+        lo = *reinterpret_cast<const v4i *>(S.lo + 16 * slot4(r, 2 * j + lh));
+        hi = *reinterpret_cast<const v4i *>(S.hi + 16 * slot4(r, 2 * j + lh));
+    };
+    auto ld_dv = [&](int j, float (&dv)[16]) {
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
             const float4 d4 = *reinterpret_cast<const float4 *>(&S.dx[j][wm * 32 + 8 * g4 + 4 * lh]);
@@ -563,18 +570,32 @@ __device__ __forceinline__ void x_compute(const XStage &S, v16f (&acc)[TN], int 
             dv[4 * g4 + 2] = d4.z;
             dv[4 * g4 + 3] = d4.w;
         }
+    };
+    v4i lo, hi;
+    ld_w(0, 0, lo, hi);
+#pragma unroll 1
+    for (int j = 0; j < XSUB; ++j) {
+        const v4i af = *reinterpret_cast<const v4i *>(S.a + 16 * slot4(tr, 2 * j + lh));
+        float dv[16];
+        ld_dv(j, dv);
 #pragma unroll
         for (int b = 0; b < TN; ++b) {
-            const int r = (wn * TN + b) * 32 + lr;
-            const v4i lo = *reinterpret_cast<const v4i *>(S.lo + 16 * slot4(r, 2 * j + lh));
-            const v4i hi = *reinterpret_cast<const v4i *>(S.hi + 16 * slot4(r, 2 * j + lh));
             const v16i il = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, lo, v16i{}, 0, 0, 0);
             const v16i ih = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, hi, v16i{}, 0, 0, 0);
+            if (b + 1 < TN)
+                ld_w(j, b + 1, lo, hi);
+            else if (j + 1 < XSUB)
+                ld_w(j + 1, 0, lo, hi);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int J = (ih[v] << 6) + il[v];
                 acc[b][v] = fmaf((float)J, dv[v], acc[b][v]);
             }
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                asm volatile("" : "+v"(acc[b][v]));
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 }
