@@ -608,7 +608,11 @@ def run_ceilings(args):
         (Q4_K 18944 x 3584, Q6_K 3584 x 18944, the Q6_K output head) and
         1 GiB, each read from rotating copies in a 2 GiB pool;
       * int8 MFMA with k f32 VALU operations per int32 result (k = 0: the
-        MFMAs alone; 3: convert, scale product, fma, as the GEMM epilogue)."""
+        MFMAs alone; 3: convert, scale product, fma, as the GEMM epilogue);
+      * the GEMM's sub-block step with operands from LDS on the f16 matrix
+        cores (scale folded into the weights, one fma per result; with the
+        weights and then the activations also converted in registers)
+        against the same step on the int8 matrix cores."""
     import ctypes
     import numpy as np
     import torch
@@ -661,11 +665,13 @@ def run_ceilings(args):
     iters = 1000
     names = {0: "int8 MFMA alone", 2: "int8 MFMA + cvt, fma", 3: "int8 MFMA + cvt, mul, fma",
              4: "int8 MFMA + cvt, mul, mul, fma", 10: "fp8 MFMA alone", 11: "fp8 MFMA + fma",
-             12: "fp8 MFMA + mul, fma"}
+             12: "fp8 MFMA + mul, fma", 20: "LDS step: f16 MFMA pair alone", 21: "LDS step: f16 MFMA pair + fma",
+             22: "LDS step: f16 + fma, weights converted", 23: "LDS step: f16 + fma, weights and activations converted",
+             30: "LDS step: int8 MFMA + unpack, cvt, mul, fma"}
     for grid in (2048, 512):
         out = torch.zeros(grid * 256, dtype=torch.float32, device="cuda")
         ops = grid * 4 * iters * 4 * 2 * 32 * 32 * 32
-        for k in (0, 2, 3, 4, 10, 11, 12):
+        for k in (0, 2, 3, 4, 10, 11, 12, 20, 21, 22, 23, 30):
             fn = lambda i: check(P.mqp_mix(k, iters, grid, ctypes.c_void_p(out.data_ptr()), st))
             us = float(np.median([_time_rotating(fn, 1, 5) for _ in range(3)]))
             tops = ops / (us * 1e-6) / 1e12

@@ -20,7 +20,19 @@
 //       the scaled fp8 MFMA (v_mfma_scale_f32_32x32x64_f8f6f4, one
 //       32-value sub-block's exact dot as an f32 from two base-16 digits
 //       of the activation) chained, or followed by fma, or by scale
-//       product and fma. sink holds grid * 256 floats.
+//       product and fma. k = 20..23, 30: a sub-block step of the GEMM
+//       inner loop with its operands read from LDS (4 tiles of 32 x 32 per
+//       wavefront, one 32-value sub-block per iteration):
+//         20: two chained v_mfma_f32_32x32x16_f16 per tile (the f16 route,
+//             6-bit scale folded into the weights: sc * q is exact in f16);
+//         21: 20 plus one fma per result (J times the activation scale);
+//         22: 21 with the weights converted from raw nibbles in registers
+//             (mask, then v_cvt_scalef32_pk_f16_fp8: the nibble is an e4m3
+//             code q * 2^-9, scaled by sc * 2^9 to sc * q exactly);
+//         23: 22 with the activations converted from int8 in registers;
+//         30: the int8 route for comparison: nibble unpack, one
+//             v_mfma_i32_32x32x32_i8 per tile, then cvt, mul, fma.
+//       sink holds grid * 256 floats.
 // Both return the hipError_t of the launch.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -31,6 +43,8 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 
 constexpr int MAGIC = 0x5a5a1234;
 
@@ -223,6 +237,135 @@ __global__ __launch_bounds__(256) void mix(int iters, float *sink)
     }
 }
 
+// Two e4m3 codes (bytes 2 hi, 2 hi + 1 of w) as an f16 pair, times s.
+__device__ __forceinline__ uint32_t e4m3x2_to_f16(uint32_t w, float s, bool hi)
+{
+    const v2h r = hi ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, s, true)
+                     : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, s, false);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// Four int8 as two exact f16 pairs: x + 128 under the exponent of 1024,
+// then 1152 subtracted.
+__device__ __forceinline__ void i8x4_to_f16(uint32_t w, uint32_t &h01, uint32_t &h23)
+{
+    const uint32_t u = w ^ 0x80808080u;
+    const v2h c = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+    h01 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(v2h, __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u)) + c);
+    h23 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(v2h, __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u)) + c);
+}
+
+// LDS-fed inner-loop mixes (k = 20..23, 30; see the header). The 64 KB of
+// LDS hold arbitrary data; every index is masked into it.
+template <int K>
+__global__ __launch_bounds__(256, 2) void mix_lds(int iters, float *sink)
+{
+    __shared__ v4i lds[4096];
+    const int tid = threadIdx.x, lane = tid & 63;
+    for (int i = tid; i < 4096; i += 256)
+        lds[i] = v4i{i * 0x01030507, i * 0x0b0d1113, i ^ 0x5a5a5a5a, i * 7};
+    __syncthreads();
+    const float *ldf = reinterpret_cast<const float *>(lds);
+    v16f acc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+        acc[t] = v16f{};
+    v4i raw[4];
+    float sc = 2.0f, f = 1e-3f;
+    for (int i = 0; i < iters; ++i) {
+        const int base = ((i & 15) * 64 + lane) & 1023;
+        const v4i ai = lds[base];
+        float dv[16];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int o = 4 * (2048 + ((((i & 7) * 64 + lane) * 4 + 256 * g) & 1023));
+            const float4 d4 = *reinterpret_cast<const float4 *>(ldf + o);
+            dv[4 * g] = d4.x;
+            dv[4 * g + 1] = d4.y;
+            dv[4 * g + 2] = d4.z;
+            dv[4 * g + 3] = d4.w;
+        }
+        const bool hi = i & 1;
+        if (!hi) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                raw[t] = lds[(base + 128 * (t + 1)) & 4095];
+        }
+        if constexpr (K == 30) {
+            v16i I[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const v4i b = hi ? ((raw[t] >> 4) & 0x0f0f0f0f) : (raw[t] & 0x0f0f0f0f);
+                I[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ai, b, v16i{}, 0, 0, 0);
+            }
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const float fw = f * (1.0f + 1e-3f * t);
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    acc[t][v] = __builtin_fmaf((float)I[t][v], dv[v] * fw, acc[t][v]);
+            }
+            f += 1e-7f;
+            continue;
+        } else {
+            v8h a0, a1;
+            if constexpr (K >= 23) {
+                uint32_t ah[8];
+                i8x4_to_f16(ai.x, ah[0], ah[1]);
+                i8x4_to_f16(ai.y, ah[2], ah[3]);
+                i8x4_to_f16(ai.z, ah[4], ah[5]);
+                i8x4_to_f16(ai.w, ah[6], ah[7]);
+                a0 = __builtin_bit_cast(v8h, v4i{(int)ah[0], (int)ah[1], (int)ah[2], (int)ah[3]});
+                a1 = __builtin_bit_cast(v8h, v4i{(int)ah[4], (int)ah[5], (int)ah[6], (int)ah[7]});
+            } else {
+                a0 = __builtin_bit_cast(v8h, ai);
+                a1 = __builtin_bit_cast(v8h, lds[base + 1024]);
+            }
+            v16f J[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                v8h b0, b1;
+                if constexpr (K >= 22) {
+                    uint32_t w[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        w[e] = hi ? (((uint32_t)raw[t][e] >> 4) & 0x0f0f0f0fu) : ((uint32_t)raw[t][e] & 0x0f0f0f0fu);
+                    const float s = sc + t;
+                    b0 = __builtin_bit_cast(v8h, v4i{(int)e4m3x2_to_f16(w[0], s, false), (int)e4m3x2_to_f16(w[0], s, true),
+                                                     (int)e4m3x2_to_f16(w[1], s, false), (int)e4m3x2_to_f16(w[1], s, true)});
+                    b1 = __builtin_bit_cast(v8h, v4i{(int)e4m3x2_to_f16(w[2], s, false), (int)e4m3x2_to_f16(w[2], s, true),
+                                                     (int)e4m3x2_to_f16(w[3], s, false), (int)e4m3x2_to_f16(w[3], s, true)});
+                } else {
+                    b0 = __builtin_bit_cast(v8h, lds[(base + 128 * (t + 5)) & 4095]);
+                    b1 = __builtin_bit_cast(v8h, lds[(base + 128 * (t + 9)) & 4095]);
+                }
+                if constexpr (K == 20) {
+                    acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b0, acc[t], 0, 0, 0);
+                    acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b1, acc[t], 0, 0, 0);
+                } else {
+                    J[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b0, v16f{}, 0, 0, 0);
+                    J[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b1, J[t], 0, 0, 0);
+                }
+            }
+            if constexpr (K >= 21) {
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v)
+                        acc[t][v] = __builtin_fmaf(J[t][v], dv[v], acc[t][v]);
+            }
+            sc += 1.0f;
+        }
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+            s += acc[t][v];
+    sink[(int64_t)blockIdx.x * 256 + tid] = s;
+}
+
 } // namespace
 
 extern "C" int mqp_read(int kind, int depth, const void *src, int64_t bytes, int grid, int *sink,
@@ -262,6 +405,11 @@ extern "C" int mqp_mix(int k, int iters, int grid, float *sink, void *stream)
     else if (k == 10) mix<10><<<grid, 256, 0, st>>>(iters, sink);
     else if (k == 11) mix<11><<<grid, 256, 0, st>>>(iters, sink);
     else if (k == 12) mix<12><<<grid, 256, 0, st>>>(iters, sink);
+    else if (k == 20) mix_lds<20><<<grid, 256, 0, st>>>(iters, sink);
+    else if (k == 21) mix_lds<21><<<grid, 256, 0, st>>>(iters, sink);
+    else if (k == 22) mix_lds<22><<<grid, 256, 0, st>>>(iters, sink);
+    else if (k == 23) mix_lds<23><<<grid, 256, 0, st>>>(iters, sink);
+    else if (k == 30) mix_lds<30><<<grid, 256, 0, st>>>(iters, sink);
     else return (int)hipErrorInvalidValue;
     return (int)hipGetLastError();
 }
