@@ -47,6 +47,7 @@ INT8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA, published
 ROTATE_BYTES = 1 << 30       # weight copies for HBM-bound kernels
 WARMUP_S = 0.5               # warm-up of the contract run, at least
 WINDOWS = 21                 # timed windows of K steps each
+REWARM_S = 0.1               # plain steps queued right before each measured pass
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
     "gemm_q4k": "quant_gemm_amd/csrc/gemm_q4k.hip",
@@ -227,6 +228,12 @@ def run_contract(args):
         mq.matmul_q4k(Wd[i % copies], qd, dd, sd, dec.N, dec.K, out=outd)
         if ev: ev[4].record()
 
+    # Every event of the measured passes is created now: creating them
+    # between passes would leave the GPU idle long enough for its clocks to
+    # drop, and the first launches after that run slow.
+    kclocks = [KernelClock(args.steps) for _ in names]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+
     # Warm-up: the --warmup steps, continued until at least WARMUP_S seconds
     # of steps have run, so that clocks and caches have settled.
     log(f"[bench] warmup: {args.warmup} steps, at least {WARMUP_S} s")
@@ -254,13 +261,21 @@ def run_contract(args):
         torch.cuda.synchronize()
         win_ms.append(t_start.elapsed_time(t_end))
     win_step = np.array(win_ms) / args.steps
+    # Each measured pass below is queued right behind REWARM_S seconds of
+    # plain steps, with no synchronization in between, so that it starts on
+    # a busy GPU at the clocks of the timed windows.
+    rewarm_steps = max(1, int(REWARM_S / (float(np.median(win_step)) * 1e-3)))
+
+    def rewarm():
+        for i in range(rewarm_steps):
+            step(i)
+
     # A second pass over the same steps, instrumented: the GEMM (even steps)
     # and the GEMV (odd steps) record fence-free events at their own dispatch
     # start and end (the roofline figures). One timed kernel per step keeps
     # the instrumentation's own cost small; the pass is timed as a whole like
     # a window, so that its time per step shows that cost.
     log(f"[bench] per-kernel timing pass, {args.steps} steps")
-    kclocks = [KernelClock(args.steps) for _ in names]
     timed = {n: [] for n in names}
 
     def instrumented_pass(which):
@@ -272,11 +287,13 @@ def run_contract(args):
             step(i, kc=armed)
 
     torch.cuda.synchronize()
+    rewarm()
     t_start.record()
     instrumented_pass((1, 3))
     t_end.record()
     torch.cuda.synchronize()
     instr_ms_step = t_start.elapsed_time(t_end) / args.steps
+    rewarm()
     instrumented_pass((0, 2))        # the two quantizers, in a pass of their own
     torch.cuda.synchronize()
     kernel_us = {n: np.array([kc.us(i) for i in timed[n]]) for n, kc in zip(names, kclocks)}
@@ -284,8 +301,7 @@ def run_contract(args):
         kc.close()
     # A third pass: events recorded around each call (kernel plus the launch
     # gap after the preceding one), kept apart from the kernel figures.
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
+    rewarm()
     for i in range(args.steps):
         step(i, ev=evs[i])
     torch.cuda.synchronize()
