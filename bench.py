@@ -528,7 +528,11 @@ def run_planes(dev):
         if c.fmt == "q6k":
             lo, hi, dw = mq.expand_q6k(W, c.N, c.K)
             build = lambda i: mq.expand_q6k(W, c.N, c.K, lo, hi, dw)
-            raw = lambda i: mq.matmul_q6k(W, q, d, None, c.N, c.K, out=out, path=mq.MQ_PATH_GEMM)
+            # the raw-block GEMM: a workspace of the split-K part only (the
+            # full one would expand W per call)
+            ws = torch.empty(max(16, mq.matmul_split_workspace(mq.MQ_FMT_Q6K, c.M, c.N, c.K, mq.MQ_PATH_GEMM)),
+                             dtype=torch.uint8, device=dev)
+            raw = lambda i: mq.matmul_q6k(W, q, d, None, c.N, c.K, out=out, path=mq.MQ_PATH_GEMM, workspace=ws)
             planes = lambda i: mq.matmul_q6k_x(lo, hi, dw, q, d, c.N, c.K, out=out)
             kind, plane_bytes = "q6k expansion (lo, hi, d)", 2 * lo.numel() + 4 * dw.numel()
         else:

@@ -17,17 +17,24 @@
  *     and keeps no buffers between calls: the buffers belong to the caller,
  *     as they belong to the allocator and not to the kernels on the pages
  *     (minfer Compute Graph Design, §1.4 Core invariants).
- *   - Workspace. Two plans use scratch memory: a GEMM with too few output
+ *   - Workspace. Three plans use scratch memory: a GEMM with too few output
  *     tiles to fill the device splits K into nsplit [M][N] f32 planes of
  *     partial sums (added in a fixed order, so results do not depend on
- *     scheduling), and the fused FFN's two-pass form keeps g and u. The
+ *     scheduling); a Q6_K GEMM of at least 1024 tokens (on matrices of at
+ *     most 2^28 weights) first expands W into the limb planes of
+ *     mq_expand_q6k there, decoding each block once per call instead of
+ *     once per token tile, with the same result bit for bit; and the fused
+ *     FFN's two-pass form keeps g and u. The
  *     *_ws entry points take that memory from the caller (ws, ws_bytes);
  *     mq_matmul_workspace / mq_ffn_q4k_workspace give the bytes a call
  *     with the same arguments needs (0 when its plan uses none). ws == NULL
  *     (with ws_bytes == 0) selects the workspace-free plan: GEMMs never
  *     split K, and the FFN runs its one-launch GEMM. A non-NULL ws must be
  *     16-byte aligned and hold at least the bytes the query gives, else the
- *     call fails with MQ_ERR_WORKSPACE and launches nothing. The entry
+ *     call fails with MQ_ERR_WORKSPACE and launches nothing; the one
+ *     exception is a Q6_K GEMM that would expand W, which with at least
+ *     the split-K part (the query's figure less the planes) runs on the raw
+ *     blocks instead, with the same result. The entry
  *     points without a ws argument take the workspace-free plan. The
  *     workspace is read and written only by the kernels of the call that
  *     receives it: calls in flight at the same time need distinct
@@ -82,7 +89,7 @@
 extern "C" {
 #endif
 
-#define MQ_ABI_VERSION 4
+#define MQ_ABI_VERSION 5
 
 typedef enum {
     MQ_OK = 0,
@@ -221,10 +228,17 @@ int mq_matmul_q6k_ex(const void *W, const int8_t *q, const float *d,
  * same result and contract, and the full plan, which may split K over the
  * workspace when the output has too few tiles to fill the device.
  * mq_matmul_workspace writes to *bytes the workspace a matmul of format fmt
- * (MQ_FMT_Q4K / Q5K / Q6K) with these M, N, K and path needs: 0 when its
- * plan splits nothing, else nsplit * M * N * 4. It validates M, N, K and
- * path as the matmul does.
+ * (MQ_FMT_Q4K / Q5K / Q6K) with these M, N, K and path needs: nsplit * M *
+ * N * 4 (0 when the plan splits nothing), plus, for a Q6_K GEMM that
+ * expands W (M >= MQ_Q6K_EXPAND_MIN_M on a matrix of at most
+ * MQ_Q6K_EXPAND_MAX_WEIGHTS weights), its planes: 2 * N * K + 4 * N * K /
+ * 256 bytes (each part rounded up to 256). It validates M, N, K and path as
+ * the matmul does. Measured on MI355X (3584 x 18944): the expansion plan
+ * takes 354 / 614 / 964 us at M = 1024 / 2048 / 3314 against 393 / 734 /
+ * 1221 us on the raw blocks.
  */
+#define MQ_Q6K_EXPAND_MIN_M 1024
+#define MQ_Q6K_EXPAND_MAX_WEIGHTS (1ll << 28)
 int mq_matmul_workspace(int fmt, int64_t M, int64_t N, int64_t K, int path,
                         int64_t *bytes);
 int mq_matmul_q4k_ws(const void *W, const int8_t *q, const float *d,
@@ -335,14 +349,15 @@ int mq_matmul_q4k_dsc(const void *W, const float *fw, const float *fm,
 /*
  * For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the Q6_K
- * matmul with the full plan of mq_matmul_q6k_ws (MQ_PATH_AUTO), its split-K
- * partial sums kept in a static device array of the library instead of a
- * caller workspace. The array holds MQ_STATIC_SCRATCH_BYTES (32 MiB); each
+ * matmul of mq_matmul_q6k_ws (MQ_PATH_AUTO) with its split-K partial sums
+ * kept in a static device array of the library instead of a caller
+ * workspace; it never takes the expansion plan, so it needs nsplit * M * N
+ * * 4 bytes (mq_matmul_workspace's figure without the planes) and gives the
+ * same result. The array holds MQ_STATIC_SCRATCH_BYTES (32 MiB); each
  * GPU the library runs on holds its own copy until the process ends, and its
  * address is looked up once per device on the first call there that needs
- * it. A call whose plan needs more (mq_matmul_workspace with MQ_FMT_Q6K and
- * MQ_PATH_AUTO gives the size; e.g. 3314 x 3584 x 18944 needs about 95 MB)
- * fails with MQ_ERR_WORKSPACE before anything is launched. The call
+ * it. A call whose split-K plan needs more (e.g. 3314 x 3584 x 18944 needs
+ * about 95 MB) fails with MQ_ERR_WORKSPACE before anything is launched. The call
  * allocates nothing. All calls on one GPU share its array, which keeps the
  * last call's partial sums (every call overwrites what it reads): calls
  * that overlap in time on one GPU, on any streams, race and give wrong

@@ -26,7 +26,7 @@ MQ_FMT_Q4K, MQ_FMT_Q5K, MQ_FMT_Q6K = 0, 1, 2
 STATUS_NAMES = {0: "MQ_OK", 1: "MQ_ERR_INVALID_ARG", 2: "MQ_ERR_SHAPE",
                 3: "MQ_ERR_ALIGN", 4: "MQ_ERR_UNSUPPORTED", 5: "MQ_ERR_DEVICE",
                 6: "MQ_ERR_LAUNCH", 7: "MQ_ERR_WORKSPACE"}
-ABI_VERSION = 4
+ABI_VERSION = 5
 Q4K_BLOCK_BYTES = 144
 Q5K_BLOCK_BYTES = 176
 Q6K_BLOCK_BYTES = 210
@@ -199,6 +199,31 @@ def matmul_workspace(fmt, M, N, K, path=MQ_PATH_AUTO) -> int:
     n = ctypes.c_int64()
     _check(load().mq_matmul_workspace(fmt, M, N, K, path, ctypes.byref(n)))
     return n.value
+
+
+# A Q6_K GEMM of at least Q6K_EXPAND_MIN_M tokens on a matrix of at most
+# Q6K_EXPAND_MAX_WEIGHTS weights, given its full workspace, expands W there
+# (mq.h: MQ_Q6K_EXPAND_MIN_M, MQ_Q6K_EXPAND_MAX_WEIGHTS).
+Q6K_EXPAND_MIN_M = 1024
+Q6K_EXPAND_MAX_WEIGHTS = 1 << 28
+
+
+def q6k_expansion_bytes(N, K) -> int:
+    """Bytes the expansion planes of an N x K Q6_K matrix take in a
+    workspace (lo, hi and d, each rounded up to 256)."""
+    r = lambda v: (v + 255) // 256 * 256
+    return 2 * r(N * K) + r(N * (K // 256) * 4)
+
+
+def matmul_split_workspace(fmt, M, N, K, path=MQ_PATH_AUTO) -> int:
+    """Bytes of the split-K part of a matmul's workspace: the query's figure,
+    less the expansion planes where the call would expand W. A workspace of
+    this size runs a Q6_K GEMM on the raw blocks, with the same result."""
+    full = matmul_workspace(fmt, M, N, K, path)
+    if (fmt == MQ_FMT_Q6K and path != MQ_PATH_GEMV and M >= Q6K_EXPAND_MIN_M
+            and N * K <= Q6K_EXPAND_MAX_WEIGHTS):
+        return full - q6k_expansion_bytes(N, K)
+    return full
 
 
 def ffn_q4k_workspace(M, N, K, path=MQ_PATH_AUTO) -> int:

@@ -137,8 +137,9 @@ Kern matmul_kernel(Fmt fmt, int64_t M, int64_t N, int64_t K, int path)
     return M <= small ? Kern::GEMM_SMALL : Kern::GEMM;
 }
 
-// Workspace bytes of the full plan of a GEMM configuration (0 = none).
-size_t gemm_ws_bytes(Fmt fmt, Kern kern, int64_t M, int64_t N, int64_t K)
+// Workspace bytes of the split-K partial sums of a GEMM configuration (0 =
+// it does not split).
+size_t split_ws_bytes(Fmt fmt, Kern kern, int64_t M, int64_t N, int64_t K)
 {
     const int m = (int)M, n = (int)N, k = (int)K;
     int s = 1;
@@ -149,6 +150,33 @@ size_t gemm_ws_bytes(Fmt fmt, Kern kern, int64_t M, int64_t N, int64_t K)
         s = fmt == Fmt::Q6K ? mq::splits_gemm_q6k(m, n, k)
           : fmt == Fmt::Q5K ? mq::splits_gemm_q5k(m, n, k) : mq::splits_gemm_q4k(m, n, k);
     return mq::split_bytes(s, M, N);
+}
+
+// The Q6_K expansion plan: a GEMM of at least MQ_Q6K_EXPAND_MIN_M tokens,
+// given the full workspace, expands W there into the limb planes lo, hi
+// [N][K] and d [N][K/256] (then the split-K sums) and runs the
+// expansion-plane GEMM: each block decoded once per call instead of once
+// per token tile, the same result bit for bit. Measured on MI355X at
+// 3584 x 18944: M = 3314 964 us against 1221 us on the raw blocks, M = 1024
+// 354 against 393 us; at M = 512 the 54 us expansion about cancels the
+// gain (220 against 226 us). Matrices of more than MQ_Q6K_EXPAND_MAX_WEIGHTS
+// weights keep the raw blocks (their planes would pass 512 MB).
+bool q6k_expands(Fmt fmt, Kern kern, int64_t M, int64_t N, int64_t K)
+{
+    return fmt == Fmt::Q6K && kern == Kern::GEMM && M >= MQ_Q6K_EXPAND_MIN_M &&
+           N * K <= MQ_Q6K_EXPAND_MAX_WEIGHTS;
+}
+constexpr size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+size_t q6k_planes_bytes(int64_t N, int64_t K)
+{
+    return 2 * round256((size_t)N * (size_t)K) + round256((size_t)N * (size_t)(K / 256) * sizeof(float));
+}
+
+// Workspace bytes of the full plan of a GEMM configuration (0 = none).
+size_t gemm_ws_bytes(Fmt fmt, Kern kern, int64_t M, int64_t N, int64_t K)
+{
+    const size_t split = split_ws_bytes(fmt, kern, M, N, K);
+    return q6k_expands(fmt, kern, M, N, K) ? q6k_planes_bytes(N, K) + split : split;
 }
 
 // The caller's workspace argument: NULL (with ws_bytes 0) selects the
@@ -170,8 +198,11 @@ int check_ws(const char *fn, const void *ws, int64_t ws_bytes, size_t need)
     return MQ_OK;
 }
 
+// expand: the call may take the Q6_K expansion plan (the static-array entry
+// point keeps the split-K plan of the raw-block GEMM).
 int matmul(Fmt fmt, const void *W, const int8_t *q, const float *d, const float *s,
-           int64_t M, int64_t N, int64_t K, float *out, void *ws, int64_t ws_bytes, void *stream, int path)
+           int64_t M, int64_t N, int64_t K, float *out, void *ws, int64_t ws_bytes, void *stream, int path,
+           bool expand = true)
 {
     const bool q6 = fmt == Fmt::Q6K;
     const char *fn = fmt_fn(fmt);
@@ -191,7 +222,11 @@ int matmul(Fmt fmt, const void *W, const int8_t *q, const float *d, const float 
     if (s && !aligned(s, 16)) return fail(MQ_ERR_ALIGN, "%s: s=%p is not 16-byte aligned", fn, (const void *)s);
     if (!aligned(out, 4)) return fail(MQ_ERR_ALIGN, "%s: out=%p is not 4-byte aligned", fn, (const void *)out);
     const Kern kern = matmul_kernel(fmt, M, N, K, path);
-    if (int rc = check_ws(fn, ws, ws_bytes, ws ? gemm_ws_bytes(fmt, kern, M, N, K) : 0)) return rc;
+    // the split-K part is required; the full plan's bytes also enable the
+    // Q6_K expansion
+    if (int rc = check_ws(fn, ws, ws_bytes, ws ? split_ws_bytes(fmt, kern, M, N, K) : 0)) return rc;
+    const bool x = expand && ws && q6k_expands(fmt, kern, M, N, K) &&
+                   (uint64_t)ws_bytes >= (uint64_t)gemm_ws_bytes(fmt, kern, M, N, K);
     if (int rc = check_device()) return rc;
 
     const auto *Wb = static_cast<const uint8_t *>(W);
@@ -199,7 +234,19 @@ int matmul(Fmt fmt, const void *W, const int8_t *q, const float *d, const float 
     const mq::Ws w{ws, (size_t)ws_bytes};
     const int m = (int)M, n = (int)N, k = (int)K;
     hipError_t e;
-    if (q6 && kern == Kern::GEMV)
+    if (x) {
+        // expand W into the workspace, then the expansion-plane GEMM with its
+        // split-K sums after the planes (the expansion launches without the
+        // timing hook, which stays for the GEMM)
+        auto *lo = static_cast<int8_t *>(ws);
+        int8_t *hi = lo + round256((size_t)N * (size_t)K);
+        auto *dw = reinterpret_cast<float *>(hi + round256((size_t)N * (size_t)K));
+        const size_t pb = q6k_planes_bytes(N, K);
+        e = mq::launch_expand_q6k(Wb, N, K, lo, hi, dw, st);
+        if (e == hipSuccess)
+            e = mq::launch_gemm_q6k_x(lo, hi, dw, q, d, m, n, k, out,
+                                      mq::Ws{static_cast<uint8_t *>(ws) + pb, (size_t)ws_bytes - pb}, st);
+    } else if (q6 && kern == Kern::GEMV)
         e = mq::launch_gemv_q6k(Wb, q, d, m, n, k, out, st);
     else if (q6 && kern == Kern::GEMM_SMALL)
         e = mq::launch_gemm_q6k_small(Wb, q, d, m, n, k, out, w, st);
@@ -591,7 +638,7 @@ int mq_matmul_q6k_x(const int8_t *lo, const int8_t *hi, const float *dw, const i
     if (!aligned(hi, 16)) return fail(MQ_ERR_ALIGN, "%s: hi=%p is not 16-byte aligned", fn, (const void *)hi);
     if (!aligned(dw, 4)) return fail(MQ_ERR_ALIGN, "%s: dw=%p is not 4-byte aligned", fn, (const void *)dw);
     const Kern kern = M <= mq::GEMM_SMALL_M_Q6K ? Kern::GEMM_SMALL : Kern::GEMM;
-    if (int rc = check_ws(fn, ws, ws_bytes, ws ? gemm_ws_bytes(Fmt::Q6K, kern, M, N, K) : 0)) return rc;
+    if (int rc = check_ws(fn, ws, ws_bytes, ws ? split_ws_bytes(Fmt::Q6K, kern, M, N, K) : 0)) return rc;
     if (int rc = check_device()) return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
     const mq::Ws w{ws, (size_t)ws_bytes};
@@ -632,7 +679,7 @@ int mq_matmul_q4k_dsc(const void *W, const float *fw, const float *fm, const int
     if (!aligned(fm, 16)) return fail(MQ_ERR_ALIGN, "%s: fm=%p is not 16-byte aligned", fn, (const void *)fm);
     if (!aligned(s, 16)) return fail(MQ_ERR_ALIGN, "%s: s=%p is not 16-byte aligned", fn, (const void *)s);
     const Kern kern = M <= mq::GEMM_SMALL_M_Q4K ? Kern::GEMM_SMALL : Kern::GEMM;
-    if (int rc = check_ws(fn, ws, ws_bytes, ws ? gemm_ws_bytes(Fmt::Q4K, kern, M, N, K) : 0)) return rc;
+    if (int rc = check_ws(fn, ws, ws_bytes, ws ? split_ws_bytes(Fmt::Q4K, kern, M, N, K) : 0)) return rc;
     if (int rc = check_device()) return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
     const mq::Ws w{ws, (size_t)ws_bytes};
@@ -651,7 +698,7 @@ int mq_matmul_q6k_static(const void *W, const int8_t *q, const float *d, const f
     const char *fn = "mq_matmul_q6k_static";
     // the checks of the call, then the size of the plan against the array
     if (int rc = check_matmul_shape(fn, M, N, K, MQ_PATH_AUTO)) return rc;
-    const size_t need = gemm_ws_bytes(Fmt::Q6K, matmul_kernel(Fmt::Q6K, M, N, K, MQ_PATH_AUTO), M, N, K);
+    const size_t need = split_ws_bytes(Fmt::Q6K, matmul_kernel(Fmt::Q6K, M, N, K, MQ_PATH_AUTO), M, N, K);
     if (need > kScratchBytes)
         return fail(MQ_ERR_WORKSPACE, "%s: M=%lld N=%lld K=%lld needs %llu bytes of scratch; the static array "
                     "holds %llu (use mq_matmul_q6k_ws)", fn, (long long)M, (long long)N, (long long)K,
@@ -661,7 +708,8 @@ int mq_matmul_q6k_static(const void *W, const int8_t *q, const float *d, const f
         if (int rc = check_device()) return rc;
         if (int rc = scratch_ptr(fn, &ws)) return rc;
     }
-    return matmul(Fmt::Q6K, W, q, d, s, M, N, K, out, ws, ws ? (int64_t)kScratchBytes : 0, stream, MQ_PATH_AUTO);
+    return matmul(Fmt::Q6K, W, q, d, s, M, N, K, out, ws, ws ? (int64_t)kScratchBytes : 0, stream, MQ_PATH_AUTO,
+                  false);
 }
 
 int mq_time_next_kernel(void *start_event, void *stop_event)

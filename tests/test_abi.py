@@ -47,6 +47,8 @@ def test_abi_version_and_constants(L):
     assert L.mq_gemv_max_m() >= 1
     hdr = open(HEADER).read()
     assert f"#define MQ_ABI_VERSION {mq.ABI_VERSION}" in hdr
+    assert f"#define MQ_Q6K_EXPAND_MIN_M {mq.Q6K_EXPAND_MIN_M}" in hdr
+    assert mq.Q6K_EXPAND_MAX_WEIGHTS == 1 << 28 and "#define MQ_Q6K_EXPAND_MAX_WEIGHTS (1ll << 28)" in hdr
 
 
 def _q4k(L, W=P, q=P, d=P, s=P, M=4, N=8, K=256, out=P, path=0):
@@ -305,6 +307,25 @@ def test_workspace_query_matches_the_split_planes(L):
     assert _ws_bytes(L, mq.MQ_FMT_Q4K, 3314, 18944, 3584) == 0
     assert _ws_bytes(L, mq.MQ_FMT_Q4K, 1, 18944, 3584) == 0          # GEMV
     assert _ws_bytes(L, mq.MQ_FMT_Q6K, 1, 3584, 18944) == 0
+
+
+def test_workspace_query_q6k_expansion(L):
+    """A Q6_K GEMM of at least 1024 tokens on a matrix of at most 2^28
+    weights also keeps W's expansion planes in its workspace: the query is
+    the planes plus a whole number of split-K [M][N] f32 planes. Below 1024
+    tokens, on larger matrices and on the GEMV there are no planes."""
+    for M, N, K in ((3314, 3584, 18944), (1024, 300, 4608), (1100, 3584, 3584)):
+        b = _ws_bytes(L, mq.MQ_FMT_Q6K, M, N, K, path=mq.MQ_PATH_GEMM)
+        split = b - mq.q6k_expansion_bytes(N, K)
+        assert split == mq.matmul_split_workspace(mq.MQ_FMT_Q6K, M, N, K, mq.MQ_PATH_GEMM)
+        assert split >= 0 and split % (M * N * 4) == 0 and split // (M * N * 4) in (0,) + tuple(range(2, 17)), \
+            (M, N, K, b)
+    for M, N, K in ((1023, 300, 4608), (3314, 152064, 3584), (512, 3584, 18944)):
+        b = _ws_bytes(L, mq.MQ_FMT_Q6K, M, N, K, path=mq.MQ_PATH_GEMM)
+        assert b % (M * N * 4) == 0, (M, N, K, b)
+        assert b == mq.matmul_split_workspace(mq.MQ_FMT_Q6K, M, N, K, mq.MQ_PATH_GEMM)
+    # Q4_K and Q5_K never expand
+    assert _ws_bytes(L, mq.MQ_FMT_Q4K, 3314, 18944, 3584) == 0
 
 
 def test_workspace_query_validates_like_the_call(L):

@@ -6,7 +6,10 @@ through the C ABI.
   * mq_matmul_q6k_x and mq_matmul_q4k_dsc meet the matmul bar against the
     raw-block oracle (max|d| <= 1e-4 max|oracle|), for small shapes, split-K
     shapes and the full-size workloads (sampled token rows), and agree
-    bitwise with the raw-block GEMM where the arithmetic is the same.
+    bitwise with the raw-block GEMM where the arithmetic is the same;
+  * a Q6_K matmul of at least 1024 tokens given its full workspace expands
+    W there and runs the expansion-plane GEMM: bitwise the raw-block GEMM's
+    result with the split-K workspace alone.
 """
 import numpy as np
 import pytest
@@ -121,3 +124,44 @@ def test_full_size_planes(dev, name):
     rq, rd, _ = oracle.quantize_act(x)
     rel = check_close(out[toks], mm(W, rq, rd, case.N, case.K, tokens=toks), name)
     print(f"[planes] {name}: max|d|/max|ref| = {rel:.2e}", flush=True)
+
+
+def test_q6k_matmul_expansion_plan(dev):
+    """mq_matmul_q6k_ws at M >= 1024 with the full workspace (the query's
+    bytes) expands W into it and runs the expansion-plane GEMM; with only
+    the split-K part it runs the raw-block GEMM. Same splits, same limbs,
+    same order: the same bits, and the oracle's result within the bar. The
+    weights carry super-blocks with d = +0 and -0 (zeroed limbs) and with a
+    negative d (the accumulators' rescale by a signed factor)."""
+    import torch
+    rng = np.random.default_rng(1100)
+    M, N, K = 1100, 300, 4608
+    W = synth.q6k_weights(rng, N, K).reshape(N, K // 256, 210)
+    zero = rng.random((N, K // 256)) < 0.1
+    zero[0, :] = True
+    W[:, :, 208][zero] = 0
+    W[:, :, 209][zero] = np.where(rng.random(zero.sum()) < 0.5, 0x80, 0x00)
+    neg = (rng.random((N, K // 256)) < 0.3) & ~zero
+    W[:, :, 209][neg] ^= 0x80
+    W = W.reshape(N, -1)
+    x = synth.activations(rng, M, K, outliers=True)
+    q, d, s = _plane(x)
+    Wd = to_dev(W.reshape(-1))
+    full = mq.matmul_workspace(mq.MQ_FMT_Q6K, M, N, K, mq.MQ_PATH_GEMM)
+    split = mq.matmul_split_workspace(mq.MQ_FMT_Q6K, M, N, K, mq.MQ_PATH_GEMM)
+    assert full == split + mq.q6k_expansion_bytes(N, K)
+    assert split > 0, "this shape splits K"
+    print(f"[planes] expansion plan M={M} N={N} K={K}: workspace {full} bytes, split part {split}", flush=True)
+    ws_full = torch.empty(full, dtype=torch.uint8, device="cuda")
+    ws_split = torch.empty(split, dtype=torch.uint8, device="cuda")
+    got = host(mq.matmul_q6k(Wd, q, d, None, N, K, path=mq.MQ_PATH_GEMM, workspace=ws_full))
+    raw = host(mq.matmul_q6k(Wd, q, d, None, N, K, path=mq.MQ_PATH_GEMM, workspace=ws_split))
+    assert np.array_equal(got, raw), "expansion plan and raw blocks: the same result bit for bit"
+    assert np.all(got[:, 0] == 0.0)
+    toks = np.array(sorted({0, 1, 127, 128, 511, 512, 1023, 1024, M - 1}))
+    rq, rd, _ = oracle.quantize_act(x)
+    check_close(got[toks], oracle.matmul_q6k(W, rq, rd, N, K, tokens=toks), "q6k expansion plan")
+    with pytest.raises(mq.MQError) as e:
+        mq.matmul_q6k(Wd, q, d, None, N, K, path=mq.MQ_PATH_GEMM,
+                      workspace=torch.empty(split - 256, dtype=torch.uint8, device="cuda"))
+    assert e.value.status == 7

@@ -52,7 +52,9 @@ def test_static_scratch_matches_caller_workspace(dev):
 def test_static_scratch_rejects_plans_beyond_it(dev):
     import torch
     M, N, K = 3314, 3584, 18944
-    need = mq.matmul_workspace(mq.MQ_FMT_Q6K, M, N, K)
+    # the static array never holds expansion planes: the call needs the
+    # split-K part of the query's figure
+    need = mq.matmul_split_workspace(mq.MQ_FMT_Q6K, M, N, K)
     assert need > mq.STATIC_SCRATCH_BYTES
     Wd = torch.zeros(N * (K // 256) * 210, dtype=torch.uint8, device="cuda")
     q = torch.zeros((M, K), dtype=torch.int8, device="cuda")
