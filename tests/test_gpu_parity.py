@@ -690,3 +690,29 @@ def test_stream_pass_counts(dev, fmt, K, M):
     q, d, s = gpu_plane(x)
     ref = oracle_mm(fmt, W, rq, rd, N, K)
     check_close(host(run_matmul(fmt, W, q, d, s, N, K, path=mq.MQ_PATH_GEMV)), ref, f"{fmt} M={M} K={K}")
+
+
+# One token on long Q6_K rows (K >= 8192: the LDS ring kernel where its
+# plane fits, the row kernel beyond), ragged row counts, one row, rows of
+# 36 blocks (not a whole number of the ring's 16-block segments), and
+# super-blocks with d = +0, -0 and negative d.
+@pytest.mark.parametrize("N,K", [(1, 8192), (37, 9216), (333, 12800), (1000, 18944), (70, 65536)])
+def test_q6k_gemv_long_rows(dev, N, K):
+    rng = np.random.default_rng(N * 13 + K)
+    W = synth.q6k_weights(rng, N, K).reshape(N, K // 256, 210)
+    zero = rng.random((N, K // 256)) < 0.1
+    W[:, :, 208][zero] = 0
+    W[:, :, 209][zero] = np.where(rng.random(zero.sum()) < 0.5, 0x80, 0x00)
+    neg = (rng.random((N, K // 256)) < 0.3) & ~zero
+    W[:, :, 209][neg] ^= 0x80
+    W = W.reshape(N, -1)
+    x = synth.activations(rng, 1, K, outliers=True)
+    print(f"[q6k long rows] M=1 N={N} K={K}", flush=True)
+    rq, rd, _ = oracle.quantize_act(x)
+    ref = oracle_mm("q6k", W, rq, rd, N, K)
+    q, d, s = gpu_plane(x)
+    for path in (mq.MQ_PATH_AUTO, mq.MQ_PATH_GEMV):
+        got = host(run_matmul("q6k", W, q, d, s, N, K, path=path))
+        check_close(got, ref, f"q6k long rows N={N} K={K} path {path}")
+        again = host(run_matmul("q6k", W, q, d, s, N, K, path=path))
+        assert np.array_equal(got, again), "bitwise repeatable"
