@@ -28,6 +28,7 @@ around each call ("avg_us_call_bracket", which adds the launch gap).
   python bench.py --all                  # per-matrix table of every workload
   python bench.py --copy-calibration     # plain copy kernel (counter scale)
   python bench.py --ceilings             # read-stream and MFMA/VALU ceiling probes
+  python bench.py --case NAME --steps K  # one workload's matmul K times (profiling target)
 """
 from __future__ import annotations
 
@@ -607,6 +608,35 @@ def run_producers(dev):
         torch.cuda.empty_cache()
 
 
+def run_case(args):
+    """One named workload's matmul, K times through the library's default
+    full plan (a workspace from the query), after one warm-up call: a
+    profiling target (rocprofv3 -- python3 bench.py --case NAME). Prints
+    the GPU time per call, queued behind busy work."""
+    import numpy as np
+    import torch
+
+    import quant_gemm_amd as mq
+    from quant_gemm_amd import synth
+
+    mq.load()
+    dev = torch.device("cuda:0")
+    case = synth.case_by_name(args.case)
+    W = torch.from_numpy(case.make_weights().reshape(-1)).to(dev)
+    x = torch.from_numpy(case.make_activations()).to(dev)
+    q, d, s = mq.quantize_act(x)
+    mm = {"q4k": mq.matmul_q4k, "q5k": mq.matmul_q5k, "q6k": mq.matmul_q6k}[case.fmt]
+    out = torch.empty((case.M, case.N), dtype=torch.float32, device=dev)
+    fmt = {"q4k": mq.MQ_FMT_Q4K, "q5k": mq.MQ_FMT_Q5K, "q6k": mq.MQ_FMT_Q6K}[case.fmt]
+    ws = torch.empty(max(1, mq.matmul_workspace(fmt, case.M, case.N, case.K)), dtype=torch.uint8, device=dev)
+    fn = lambda i: mm(W, q, d, s, case.N, case.K, out=out, workspace=ws)
+    fn(0)
+    us = _time_rotating(fn, 1, args.steps)
+    print(json.dumps({"case": case.name, "fmt": case.fmt, "M": case.M, "N": case.N, "K": case.K,
+                      "calls": args.steps, "us": round(us, 2), "TOPS": round(case.ops / (us * 1e-6) / 1e12, 2)}),
+          flush=True)
+
+
 def run_copy_calibration(args):
     """A plain device copy of known size, to scale FETCH_SIZE / WRITE_SIZE."""
     import torch
@@ -709,6 +739,7 @@ def main():
     ap.add_argument("--all", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--ceilings", action="store_true", help="read-stream and MFMA/VALU probes")
+    ap.add_argument("--case", help="time one named workload's matmul (a profiling target)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus}: this benchmark measures one GPU only; the multi-GPU "
@@ -718,6 +749,8 @@ def main():
         run_copy_calibration(args)
     elif args.ceilings:
         run_ceilings(args)
+    elif args.case:
+        run_case(args)
     elif args.all:
         run_all(args)
     else:
