@@ -662,7 +662,11 @@ def run_ceilings(args):
       * the GEMM's sub-block step with operands from LDS on the f16 matrix
         cores (scale folded into the weights, one fma per result; with the
         weights and then the activations also converted in registers)
-        against the same step on the int8 matrix cores."""
+        against the same step on the int8 matrix cores;
+      * the VALU issue rate per SIMD at 1, 2 and 4 wavefronts per SIMD, for
+        f32 epilogue mixes alone and beside independent MFMAs, with the
+        shader clock each wavefront ran at.
+    --part read|mix|valu runs one of the three groups."""
     import ctypes
     import numpy as np
     import torch
@@ -676,6 +680,9 @@ def run_ceilings(args):
     P.mqp_read.restype = ctypes.c_int
     P.mqp_mix.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     P.mqp_mix.restype = ctypes.c_int
+    P.mqp_valu.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    P.mqp_valu.restype = ctypes.c_int
+    parts = ("read", "mix", "valu") if not args.part else (args.part,)
     st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     sink = torch.zeros(16, dtype=torch.int32, device="cuda")
     pool_bytes = 2 << 30
@@ -687,7 +694,7 @@ def run_ceilings(args):
 
     sizes = [("Q4_K 18944 x 3584", 18944 * 14 * 144), ("Q6_K 3584 x 18944", 3584 * 74 * 210),
              ("Q6_K head 152064 x 3584", 152064 * 14 * 210), ("1 GiB", 1 << 30)]
-    for name, nbytes in sizes:
+    for name, nbytes in sizes if "read" in parts else ():
         copies = max(2, pool_bytes // nbytes)
         ptr = lambda i: ctypes.c_void_p(pool.data_ptr() + (i % copies) * nbytes)
         reps = max(20, 2 * copies)
@@ -718,7 +725,7 @@ def run_ceilings(args):
              12: "fp8 MFMA + mul, fma", 20: "LDS step: f16 MFMA pair alone", 21: "LDS step: f16 MFMA pair + fma",
              22: "LDS step: f16 + fma, weights converted", 23: "LDS step: f16 + fma, weights and activations converted",
              30: "LDS step: int8 MFMA + unpack, cvt, mul, fma"}
-    for grid in (2048, 512):
+    for grid in (2048, 512) if "mix" in parts else ():
         out = torch.zeros(grid * 256, dtype=torch.float32, device="cuda")
         ops = grid * 4 * iters * 4 * 2 * 32 * 32 * 32
         for k in (0, 2, 3, 4, 10, 11, 12, 20, 21, 22, 23, 30):
@@ -727,6 +734,32 @@ def run_ceilings(args):
             tops = ops / (us * 1e-6) / 1e12
             row = {"probe": "MFMA + VALU ops per result", "kind": names[k], "k": k, "workgroups": grid,
                    "us": round(us, 1), "TOPS": round(tops, 1), "frac_int8_peak": round(tops / INT8_PEAK_TOPS, 3)}
+            print(json.dumps(row), flush=True)
+
+    # VALU issue rate. Per iteration and wavefront the probe loops issue
+    # (counted in their gfx950 code): k = 0: 15 fma + 2 add; 1: 16 cvt,
+    # 16 integer add, 16 fma, 1 add; 2: 14 mul, 16 fma, 1 add; 3 and 7-9:
+    # 16 cvt, 15 mul, 16 fma, 16 integer add, 1 add, plus the MFMAs of 7-9.
+    # 256 workgroups of 4 wavefronts put one wavefront on each of the 1024
+    # SIMDs; 512 two, 1024 four.
+    vnames = {0: "fma", 1: "cvt, fma", 2: "mul, fma", 3: "cvt, mul, fma (the GEMM epilogue)",
+              7: "epilogue mix + 1 int8 MFMA", 8: "epilogue mix + 2 int8 MFMA", 9: "epilogue mix + 1 bf16 MFMA"}
+    per_iter = {0: 17, 1: 49, 2: 31, 3: 64, 7: 64, 8: 64, 9: 64}
+    viters = 20000
+    for k in (0, 1, 2, 3, 7, 8, 9) if "valu" in parts else ():
+        for wps in (1, 2, 4):
+            grid = 256 * wps
+            out = torch.zeros(grid * 256, dtype=torch.float32, device="cuda")
+            cyc = torch.zeros(grid * 4, dtype=torch.int64, device="cuda")
+            fn = lambda i: check(P.mqp_valu(k, viters, grid, ctypes.c_void_p(out.data_ptr()),
+                                            ctypes.c_void_p(cyc.data_ptr()), st))
+            us = float(np.median([_time_rotating(fn, 1, 3) for _ in range(3)]))
+            wave_cycles = cyc.double().mean().item()
+            n = per_iter[k] * viters            # VALU instructions per wavefront
+            row = {"probe": "VALU issue", "kind": vnames[k], "k": k, "waves_per_simd": wps,
+                   "us": round(us, 1), "clock_GHz": round(wave_cycles / (us * 1e3), 3),
+                   "valu_per_ns_per_simd": round(n * wps / (us * 1e3), 3),
+                   "cycles_per_valu_per_wave": round(wave_cycles / n, 2)}
             print(json.dumps(row), flush=True)
 
 
@@ -740,6 +773,7 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--ceilings", action="store_true", help="read-stream and MFMA/VALU probes")
     ap.add_argument("--case", help="time one named workload's matmul (a profiling target)")
+    ap.add_argument("--part", choices=("read", "mix", "valu"), help="with --ceilings: one probe group")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus}: this benchmark measures one GPU only; the multi-GPU "

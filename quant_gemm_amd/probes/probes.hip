@@ -33,7 +33,19 @@
 //         30: the int8 route for comparison: nibble unpack, one
 //             v_mfma_i32_32x32x32_i8 per tile, then cvt, mul, fma.
 //       sink holds grid * 256 floats.
-// Both return the hipError_t of the launch.
+//   mqp_valu(k, iters, grid, sink, cycles, stream)
+//       the VALU issue rate: per iteration 16 independent f32 results per
+//       lane, updated by
+//         k = 0: fma;  1: convert (from an int counter) and fma;
+//         2: scale product and fma;  3: convert, scale product and fma (the
+//         GEMM epilogue, plus the counter's integer add);
+//         7, 8: 3 plus one or two independent v_mfma_i32_32x32x32_i8;
+//         9: 3 plus one independent v_mfma_f32_32x32x16_bf16.
+//       Workgroups of 256 threads; each wavefront writes the shader clocks
+//       it ran (s_memtime) to cycles[wavefront], so clock and issue cycles
+//       per instruction follow from the launch time. sink holds grid * 256
+//       floats, cycles grid * 4 int64.
+// All return the hipError_t of the launch.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -45,6 +57,7 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 constexpr int MAGIC = 0x5a5a1234;
 
@@ -366,6 +379,60 @@ __global__ __launch_bounds__(256, 2) void mix_lds(int iters, float *sink)
     sink[(int64_t)blockIdx.x * 256 + tid] = s;
 }
 
+// VALU issue-rate probe (see the header). The MFMAs of k = 7..9 take no
+// VALU result, so they add matrix-core work without adding dependencies.
+template <int K>
+__global__ __launch_bounds__(256) void valu_rate(int iters, float s0, float *sink, long long *cycles)
+{
+    const long long c0 = clock64();
+    const int tid = blockIdx.x * 256 + threadIdx.x;
+    float acc[16], x[16];
+    int xi[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+        acc[v] = tid * 1e-7f + v;
+        x[v] = 1.0f + v * 1e-3f;
+        xi[v] = tid + v * 977;
+    }
+    v16i mi = {};
+    v16f mf = {};
+    const v4i ma = {tid, tid * 3, tid ^ 5, 7}, mb = {tid * 5, 11, tid, 13};
+    float s = s0;   // a launch argument, so that no product folds away
+    for (int i = 0; i < iters; ++i) {
+        if constexpr (K == 7 || K == 8) {
+#pragma unroll
+            for (int m = 0; m < K - 6; ++m)
+                mi = __builtin_amdgcn_mfma_i32_32x32x32_i8(ma, mb, mi, 0, 0, 0);
+        }
+        if constexpr (K == 9)
+            mf = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, ma), __builtin_bit_cast(v8bf, mb), mf,
+                                                         0, 0, 0);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            if constexpr (K == 0) {
+                acc[v] = __builtin_fmaf(x[v], s, acc[v]);
+            } else if constexpr (K == 1) {
+                acc[v] = __builtin_fmaf((float)xi[v], s, acc[v]);
+                xi[v] += 1;
+            } else if constexpr (K == 2) {
+                acc[v] = __builtin_fmaf(x[v], s * x[15 - v], acc[v]);
+            } else {
+                acc[v] = __builtin_fmaf((float)xi[v], s * x[15 - v], acc[v]);
+                xi[v] += 1;
+            }
+        }
+        s += 1e-9f;
+    }
+    float r = 0.0f;
+#pragma unroll
+    for (int v = 0; v < 16; ++v)
+        r += acc[v] + (float)xi[v] + (float)mi[v] + mf[v];
+    sink[tid] = r;
+    const long long c1 = clock64();
+    if ((threadIdx.x & 63) == 0)
+        cycles[tid >> 6] = c1 - c0;
+}
+
 } // namespace
 
 extern "C" int mqp_read(int kind, int depth, const void *src, int64_t bytes, int grid, int *sink,
@@ -410,6 +477,22 @@ extern "C" int mqp_mix(int k, int iters, int grid, float *sink, void *stream)
     else if (k == 22) mix_lds<22><<<grid, 256, 0, st>>>(iters, sink);
     else if (k == 23) mix_lds<23><<<grid, 256, 0, st>>>(iters, sink);
     else if (k == 30) mix_lds<30><<<grid, 256, 0, st>>>(iters, sink);
+    else return (int)hipErrorInvalidValue;
+    return (int)hipGetLastError();
+}
+
+extern "C" int mqp_valu(int k, int iters, int grid, float *sink, long long *cycles, void *stream)
+{
+    if (iters <= 0 || grid <= 0 || !sink || !cycles)
+        return (int)hipErrorInvalidValue;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (k == 0) valu_rate<0><<<grid, 256, 0, st>>>(iters, 1.0f, sink, cycles);
+    else if (k == 1) valu_rate<1><<<grid, 256, 0, st>>>(iters, 1.0f, sink, cycles);
+    else if (k == 2) valu_rate<2><<<grid, 256, 0, st>>>(iters, 1.0f, sink, cycles);
+    else if (k == 3) valu_rate<3><<<grid, 256, 0, st>>>(iters, 1.0f, sink, cycles);
+    else if (k == 7) valu_rate<7><<<grid, 256, 0, st>>>(iters, 1.0f, sink, cycles);
+    else if (k == 8) valu_rate<8><<<grid, 256, 0, st>>>(iters, 1.0f, sink, cycles);
+    else if (k == 9) valu_rate<9><<<grid, 256, 0, st>>>(iters, 1.0f, sink, cycles);
     else return (int)hipErrorInvalidValue;
     return (int)hipGetLastError();
 }
