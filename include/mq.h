@@ -20,7 +20,7 @@
  *   - Workspace. Three plans use scratch memory: a GEMM with too few output
  *     tiles to fill the device splits K into nsplit [M][N] f32 planes of
  *     partial sums (added in a fixed order, so results do not depend on
- *     scheduling); a Q6_K GEMM of at least 1024 tokens (on matrices of at
+ *     scheduling); a Q6_K GEMM of at least 512 tokens (on matrices of at
  *     most 2^28 weights) first expands W into the limb planes of
  *     mq_expand_q6k there, decoding each block once per call instead of
  *     once per token tile, with the same result bit for bit; and the fused
@@ -89,7 +89,7 @@
 extern "C" {
 #endif
 
-#define MQ_ABI_VERSION 5
+#define MQ_ABI_VERSION 6
 
 typedef enum {
     MQ_OK = 0,
@@ -233,11 +233,12 @@ int mq_matmul_q6k_ex(const void *W, const int8_t *q, const float *d,
  * expands W (M >= MQ_Q6K_EXPAND_MIN_M on a matrix of at most
  * MQ_Q6K_EXPAND_MAX_WEIGHTS weights), its planes: 2 * N * K + 4 * N * K /
  * 256 bytes (each part rounded up to 256). It validates M, N, K and path as
- * the matmul does. Measured on MI355X (3584 x 18944): the expansion plan
- * takes 354 / 614 / 964 us at M = 1024 / 2048 / 3314 against 393 / 734 /
- * 1221 us on the raw blocks.
+ * the matmul does. Measured on MI355X (3584 x 18944; the expansion itself
+ * 42 us): the expansion plan takes 206 / 264 / 328 us at M = 512 / 768 /
+ * 1024 against 227 / 298 / 393 us on the raw blocks, and breaks even near
+ * M = 384.
  */
-#define MQ_Q6K_EXPAND_MIN_M 1024
+#define MQ_Q6K_EXPAND_MIN_M 512
 #define MQ_Q6K_EXPAND_MAX_WEIGHTS (1ll << 28)
 int mq_matmul_workspace(int fmt, int64_t M, int64_t N, int64_t K, int path,
                         int64_t *bytes);

@@ -26,7 +26,7 @@ MQ_FMT_Q4K, MQ_FMT_Q5K, MQ_FMT_Q6K = 0, 1, 2
 STATUS_NAMES = {0: "MQ_OK", 1: "MQ_ERR_INVALID_ARG", 2: "MQ_ERR_SHAPE",
                 3: "MQ_ERR_ALIGN", 4: "MQ_ERR_UNSUPPORTED", 5: "MQ_ERR_DEVICE",
                 6: "MQ_ERR_LAUNCH", 7: "MQ_ERR_WORKSPACE"}
-ABI_VERSION = 5
+ABI_VERSION = 6
 Q4K_BLOCK_BYTES = 144
 Q5K_BLOCK_BYTES = 176
 Q6K_BLOCK_BYTES = 210
@@ -204,7 +204,7 @@ def matmul_workspace(fmt, M, N, K, path=MQ_PATH_AUTO) -> int:
 # A Q6_K GEMM of at least Q6K_EXPAND_MIN_M tokens on a matrix of at most
 # Q6K_EXPAND_MAX_WEIGHTS weights, given its full workspace, expands W there
 # (mq.h: MQ_Q6K_EXPAND_MIN_M, MQ_Q6K_EXPAND_MAX_WEIGHTS).
-Q6K_EXPAND_MIN_M = 1024
+Q6K_EXPAND_MIN_M = 512
 Q6K_EXPAND_MAX_WEIGHTS = 1 << 28
 
 

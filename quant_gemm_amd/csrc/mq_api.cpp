@@ -157,10 +157,11 @@ size_t split_ws_bytes(Fmt fmt, Kern kern, int64_t M, int64_t N, int64_t K)
 // [N][K] and d [N][K/256] (then the split-K sums) and runs the
 // expansion-plane GEMM: each block decoded once per call instead of once
 // per token tile, the same result bit for bit. Measured on MI355X at
-// 3584 x 18944: M = 3314 964 us against 1221 us on the raw blocks, M = 1024
-// 354 against 393 us; at M = 512 the 54 us expansion about cancels the
-// gain (220 against 226 us). Matrices of more than MQ_Q6K_EXPAND_MAX_WEIGHTS
-// weights keep the raw blocks (their planes would pass 512 MB).
+// 3584 x 18944 (the expansion 42 us): M = 512 206 against 227 us on the
+// raw blocks, M = 1024 328 against 393 us; at M = 384 the expansion about
+// cancels the gain (163 against 163 us). Matrices of more than
+// MQ_Q6K_EXPAND_MAX_WEIGHTS weights keep the raw blocks (their planes
+// would pass 512 MB).
 bool q6k_expands(Fmt fmt, Kern kern, int64_t M, int64_t N, int64_t K)
 {
     return fmt == Fmt::Q6K && kern == Kern::GEMM && M >= MQ_Q6K_EXPAND_MIN_M &&

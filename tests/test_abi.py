@@ -299,7 +299,7 @@ def test_workspace_query_matches_the_split_planes(L):
     """The query is nsplit * M * N * 4 bytes for a GEMM that splits K (a
     whole number of [M][N] f32 planes, 2..16 of them), 0 for the GEMV and
     for GEMMs with enough tiles (the 3314-token FFN shapes)."""
-    for fmt, M, N, K in ((mq.MQ_FMT_Q6K, 512, 3584, 18944), (mq.MQ_FMT_Q4K, 64, 18944, 3584),
+    for fmt, M, N, K in ((mq.MQ_FMT_Q6K, 384, 3584, 18944), (mq.MQ_FMT_Q4K, 64, 18944, 3584),
                          (mq.MQ_FMT_Q5K, 16, 18944, 3584), (mq.MQ_FMT_Q6K, 16, 3584, 18944)):
         b = _ws_bytes(L, fmt, M, N, K, path=mq.MQ_PATH_GEMM)
         plane = M * N * 4
@@ -310,17 +310,18 @@ def test_workspace_query_matches_the_split_planes(L):
 
 
 def test_workspace_query_q6k_expansion(L):
-    """A Q6_K GEMM of at least 1024 tokens on a matrix of at most 2^28
+    """A Q6_K GEMM of at least 512 tokens on a matrix of at most 2^28
     weights also keeps W's expansion planes in its workspace: the query is
-    the planes plus a whole number of split-K [M][N] f32 planes. Below 1024
+    the planes plus a whole number of split-K [M][N] f32 planes. Below 512
     tokens, on larger matrices and on the GEMV there are no planes."""
-    for M, N, K in ((3314, 3584, 18944), (1024, 300, 4608), (1100, 3584, 3584)):
+    assert mq.Q6K_EXPAND_MIN_M == 512
+    for M, N, K in ((3314, 3584, 18944), (512, 300, 4608), (1100, 3584, 3584), (512, 3584, 18944)):
         b = _ws_bytes(L, mq.MQ_FMT_Q6K, M, N, K, path=mq.MQ_PATH_GEMM)
         split = b - mq.q6k_expansion_bytes(N, K)
         assert split == mq.matmul_split_workspace(mq.MQ_FMT_Q6K, M, N, K, mq.MQ_PATH_GEMM)
         assert split >= 0 and split % (M * N * 4) == 0 and split // (M * N * 4) in (0,) + tuple(range(2, 17)), \
             (M, N, K, b)
-    for M, N, K in ((1023, 300, 4608), (3314, 152064, 3584), (512, 3584, 18944)):
+    for M, N, K in ((511, 300, 4608), (3314, 152064, 3584), (384, 3584, 18944)):
         b = _ws_bytes(L, mq.MQ_FMT_Q6K, M, N, K, path=mq.MQ_PATH_GEMM)
         assert b % (M * N * 4) == 0, (M, N, K, b)
         assert b == mq.matmul_split_workspace(mq.MQ_FMT_Q6K, M, N, K, mq.MQ_PATH_GEMM)
@@ -360,7 +361,7 @@ def test_matmul_workspace_errors(L, fn, fmt, s):
     sizes; ws NULL with a size, a negative size or a misaligned ws are
     argument errors. All fail before any HIP call."""
     f = getattr(L, fn)
-    M, N, K = 512, 3584, 18944
+    M, N, K = 384, 3584, 18944      # below the Q6_K expansion plan: the split part is all
     need = _ws_bytes(L, fmt, M, N, K, path=mq.MQ_PATH_GEMM)
     assert need > 0
     assert f(P, P, P, s, M, N, K, P, P, need - 16, None, mq.MQ_PATH_GEMM) == WORKSPACE

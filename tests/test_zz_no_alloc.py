@@ -32,15 +32,18 @@ def _host(t):
 
 
 def test_static_scratch_matches_caller_workspace(dev):
+    import torch
     # the full Q6_K M=512 down projection (split 4 ways: 29.4 MB of the
     # 32 MiB array), then a smaller split-K shape in the same array
     for seed, M, N, K in ((1002, 512, 3584, 18944), (77, 300, 700, 4608)):
-        need = mq.matmul_workspace(mq.MQ_FMT_Q6K, M, N, K)
+        # the static array holds the split-K part only (never expansion planes)
+        need = mq.matmul_split_workspace(mq.MQ_FMT_Q6K, M, N, K)
         assert 0 < need <= mq.STATIC_SCRATCH_BYTES, (M, N, K, need)
         print(f"[no-alloc] M={M} N={N} K={K} scratch {need} bytes", flush=True)
         W, Wd, rq, rd, q, d = _case(seed, M, N, K)
         got = _host(mq.matmul_q6k_static(Wd, q, d, N, K))
-        ref = _host(mq.matmul_q6k(Wd, q, d, None, N, K))        # caller workspace, same plan
+        ws = torch.empty(need, dtype=torch.uint8, device="cuda")   # caller workspace, same plan
+        ref = _host(mq.matmul_q6k(Wd, q, d, None, N, K, workspace=ws))
         assert np.array_equal(got, ref), "static scratch and caller workspace: the same bits"
         toks = np.arange(0, M, 37) if M > 64 else None
         orc = oracle.matmul_q6k(W, rq, rd, N, K, tokens=toks)
