@@ -53,6 +53,41 @@ def test_expand_q6k_bit_exact(dev, N, K):
     assert np.array_equal(host(lo), rlo) and np.array_equal(host(hi), rhi) and np.array_equal(host(dw), rdw)
 
 
+@pytest.mark.parametrize("off", [4, 8, 12])
+def test_q6k_expansion_from_4_byte_aligned_weights(dev, off):
+    """Q6_K weights need only 4-byte alignment: here W starts `off` bytes
+    into a 256-aligned buffer, so the expansion kernel stages its 16-block
+    groups with dword loads instead of 16-byte ones (45 rows of 19 blocks:
+    53 full groups and an odd tail of 7). Its planes equal the oracle's,
+    and a 512-token GEMM given its full workspace (the expansion plan)
+    equals the raw-block plan bit for bit."""
+    import torch
+    rng = np.random.default_rng(off)
+    N, K, M = 45, 4864, 512
+    W = synth.q6k_weights(rng, N, K)
+    buf = torch.zeros(W.size + off, dtype=torch.uint8, device="cuda")
+    Wd = buf[off:]
+    Wd.copy_(torch.from_numpy(W.reshape(-1)).to("cuda"))
+    assert Wd.data_ptr() % 16 == off
+    print(f"[planes] expand_q6k from W at +{off} bytes, N={N} K={K}", flush=True)
+    lo, hi, dw = mq.expand_q6k(Wd, N, K)
+    rlo, rhi, rdw = oracle.expand_q6k(W, N, K)
+    assert np.array_equal(host(lo), rlo) and np.array_equal(host(hi), rhi) and np.array_equal(host(dw), rdw)
+    x = synth.activations(rng, M, K, outliers=True)
+    q, d, s = _plane(x)
+    full = mq.matmul_workspace(mq.MQ_FMT_Q6K, M, N, K, mq.MQ_PATH_GEMM)
+    split = mq.matmul_split_workspace(mq.MQ_FMT_Q6K, M, N, K, mq.MQ_PATH_GEMM)
+    assert full == split + mq.q6k_expansion_bytes(N, K) and split > 0
+    got = host(mq.matmul_q6k(Wd, q, d, None, N, K, path=mq.MQ_PATH_GEMM,
+                             workspace=torch.empty(full, dtype=torch.uint8, device="cuda")))
+    raw = host(mq.matmul_q6k(Wd, q, d, None, N, K, path=mq.MQ_PATH_GEMM,
+                             workspace=torch.empty(split, dtype=torch.uint8, device="cuda")))
+    assert np.array_equal(got, raw), "expansion plan and raw blocks: the same result bit for bit"
+    toks = np.array([0, 1, 127, 128, 300, 511])
+    rq, rd, _ = oracle.quantize_act(x)
+    check_close(got[toks], oracle.matmul_q6k(W, rq, rd, N, K, tokens=toks), f"q6k expansion plan, W at +{off}")
+
+
 @pytest.mark.parametrize("N,K", [(1, 256), (45, 1280), (18944, 3584)])
 def test_dsc_q4k_bit_exact(dev, N, K):
     rng = np.random.default_rng(N * 7 + K)
