@@ -287,8 +287,9 @@ template <int HF>
 __device__ __forceinline__ void compute_step(const Stage &s, v16f (&acc)[TM][TN], int wm, int wn,
                                              int lr, int lh)
 {
-    if constexpr (!Q5 && TM == 1 && TN == 4) {
-        // The main configuration rolls its int8 MFMAs under the epilogue: two
+    if constexpr (TM == 1 && TN == 4) {
+        // The main configuration (Q4_K and Q5_K) rolls its int8 MFMAs under
+        // the epilogue (Q5_K measured 1016 against 1067 us without): two
         // 32x32 tiles are in flight, and each tile's MFMA for the sub-block is
         // issued as soon as the epilogue before it has read its register
         // buffer; the next sub-block's activation fragment, weight factors
@@ -319,9 +320,22 @@ __device__ __forceinline__ void compute_step(const Stage &s, v16f (&acc)[TM][TN]
             for (int b = 0; b < TN; ++b)
                 fw[b] = s.fw[j][(wn * TN + b) * 32 + lr];
         };
-        // tile b's nibbles for sub-block parity h (low / high half of its chunk)
-        auto nib = [&](const v4i (&r)[TN], int h, int b) {
-            return h ? ((r[b] >> 4) & 0x0f0f0f0f) : (r[b] & 0x0f0f0f0f);
+        // tile b's nibbles for sub-block parity h (low / high half of its
+        // chunk); for Q5_K merged with bit 4 HF + j of the lane's 16
+        // high-bit bytes of the tile, rotated to bit 4 (j the sub-block
+        // within the step; the bytes are re-read from LDS per use to stay
+        // within 256 VGPRs)
+        auto nib = [&](const v4i (&r)[TN], int h, int b, int j) {
+            v4i v = h ? ((r[b] >> 4) & 0x0f0f0f0f) : (r[b] & 0x0f0f0f0f);
+            if constexpr (Q5) {
+                const v4i hq = *reinterpret_cast<const volatile v4i *>(
+                    s.qh + 16 * h_slot((wn * TN + b) * 32 + lr, lh));
+                const int rot = (4 * HF + j + 28) & 31;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    v[e] |= (int)(__builtin_rotateright32((uint32_t)hq[e], rot) & 0x10101010u);
+            }
+            return v;
         };
         auto epi = [&](int b, const v16i &I, const float (&dv)[16], float f) {
 #pragma unroll
@@ -333,8 +347,8 @@ __device__ __forceinline__ void compute_step(const Stage &s, v16f (&acc)[TM][TN]
         v4i af = *reinterpret_cast<const v4i *>(s.a + 16 * a_slot(tr, lh));
         float dv[16], fw[TN];
         ld_fw(0, fw);
-        v16i X = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, nib(raw, 0, 0), v16i{}, 0, 0, 0);
-        v16i Y = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, nib(raw, 0, 1), v16i{}, 0, 0, 0);
+        v16i X = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, nib(raw, 0, 0, 0), v16i{}, 0, 0, 0);
+        v16i Y = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, nib(raw, 0, 1, 0), v16i{}, 0, 0, 0);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int h = j & 1;
@@ -349,18 +363,18 @@ __device__ __forceinline__ void compute_step(const Stage &s, v16f (&acc)[TM][TN]
             }
             __builtin_amdgcn_sched_barrier(0);
             epi(0, X, dv, fw[0]);
-            X = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, nib(raw, h, 2), v16i{}, 0, 0, 0);
+            X = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, nib(raw, h, 2, j), v16i{}, 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
             epi(1, Y, dv, fw[1]);
-            Y = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, nib(raw, h, 3), v16i{}, 0, 0, 0);
+            Y = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, nib(raw, h, 3, j), v16i{}, 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
             epi(2, X, dv, fw[2]);
             if (j < 3)   // the next sub-block: high nibbles of this chunk, or the next chunk
-                X = __builtin_amdgcn_mfma_i32_32x32x32_i8(af_n, nib(j == 1 ? raw_n : raw, h ^ 1, 0), v16i{}, 0, 0, 0);
+                X = __builtin_amdgcn_mfma_i32_32x32x32_i8(af_n, nib(j == 1 ? raw_n : raw, h ^ 1, 0, j + 1), v16i{}, 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
             epi(3, Y, dv, fw[3]);
             if (j < 3) {
-                Y = __builtin_amdgcn_mfma_i32_32x32x32_i8(af_n, nib(j == 1 ? raw_n : raw, h ^ 1, 1), v16i{}, 0, 0, 0);
+                Y = __builtin_amdgcn_mfma_i32_32x32x32_i8(af_n, nib(j == 1 ? raw_n : raw, h ^ 1, 1, j + 1), v16i{}, 0, 0, 0);
                 af = af_n;
 #pragma unroll
                 for (int b = 0; b < TN; ++b) {
