@@ -64,8 +64,10 @@ def log(msg):
 
 
 def source_hash(kernel: str) -> str:
+    """Hash of what a kernel is built from: its source, the shared device
+    header and the build script (its code generation flags)."""
     h = hashlib.sha256()
-    for rel in sorted({KERNEL_SOURCES[kernel], "quant_gemm_amd/csrc/mq_device.h"}):
+    for rel in sorted({KERNEL_SOURCES[kernel], "quant_gemm_amd/csrc/mq_device.h", "quant_gemm_amd/build.py"}):
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
