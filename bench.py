@@ -65,11 +65,13 @@ def log(msg):
 
 def source_hash(kernel: str) -> str:
     """Hash of what a kernel is built from: its source, the shared device
-    header and the build script (its code generation flags)."""
+    header and the compiler flags of its source file."""
+    from quant_gemm_amd import build as mq_build
     h = hashlib.sha256()
-    for rel in sorted({KERNEL_SOURCES[kernel], "quant_gemm_amd/csrc/mq_device.h", "quant_gemm_amd/build.py"}):
+    for rel in sorted({KERNEL_SOURCES[kernel], "quant_gemm_amd/csrc/mq_device.h"}):
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
+    h.update(" ".join(mq_build.kernel_flags(KERNEL_SOURCES[kernel])).encode())
     return h.hexdigest()[:16]
 
 

@@ -54,23 +54,27 @@ def torch_lib_dir() -> str:
 
 
 # Per-file code generation: the machine scheduler's max-ILP strategy for the
-# two prefill GEMM units. Measured on MI355X, same-box A/B at M=3314,
-# N=18944, K=3584: Q4_K GEMM 785 against 797 us (plain), and 1.4-1.6% for
-# its decoded-scale and fused-FFN forms; Q6_K planes GEMM 164.7 against
-# 168.0 us at M=512, N=3584, K=18944, unchanged at M=3314. Not for Q5_K (it
-# spills one more register) nor the 32-token tiles (more VGPRs).
+# Q4_K prefill GEMM unit. Measured on MI355X, same-box A/B at M=3314,
+# N=18944, K=3584: 785 against 797 us (plain), and 1.4-1.6% for its
+# decoded-scale and fused-FFN forms. Not for the Q6_K unit (its raw-block
+# GEMM ran 5-6% slower, its planes GEMM 2% faster only at M=512), Q5_K
+# (one more spilled register), the 32-token tiles (more VGPRs) or the
+# decode kernels (mixed).
 FILE_FLAGS = {
     "gemm_q4k.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
-    "gemm_q6k.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
 }
+
+
+def kernel_flags(src: str) -> list:
+    """The hipcc flags a kernel source file is compiled with."""
+    return [*HIP_FLAGS, *FILE_FLAGS.get(os.path.basename(src), [])]
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
-    extra = FILE_FLAGS.get(os.path.basename(src), [])
-    cmd = [HIPCC, *HIP_FLAGS, *extra, "-c", src, "-o", obj]
+    cmd = [HIPCC, *kernel_flags(src), "-c", src, "-o", obj]
     if src.endswith(".cpp"):
-        cmd = [HIPCC, "-x", "hip", *HIP_FLAGS, *extra, "-c", src, "-o", obj]
+        cmd = [HIPCC, "-x", "hip", *kernel_flags(src), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
