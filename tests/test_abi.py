@@ -267,7 +267,7 @@ def test_plane_entry_validation(L, call, status, needle):
 
 def test_probe_library_exports_and_rejects_bad_arguments():
     """libmq_probes.so (the ceiling probes of bench.py --ceilings) exports its
-    two entry points; malformed arguments return hipErrorInvalidValue (1)
+    three entry points; malformed arguments return hipErrorInvalidValue (1)
     before any HIP call, so this runs without a GPU."""
     import ctypes
     from quant_gemm_amd import build as mq_build
@@ -282,6 +282,23 @@ def test_probe_library_exports_and_rejects_bad_arguments():
     assert P.mqp_read(0, 4, dummy, 1024, 0, dummy, None) == 1         # empty grid
     assert P.mqp_mix(3, 0, 64, dummy, None) == 1                      # no iterations
     assert P.mqp_mix(3, 10, 64, None, None) == 1                      # no sink
+    P.mqp_valu.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                           ctypes.c_void_p]
+    assert P.mqp_valu(3, 0, 64, dummy, dummy, None) == 1              # no iterations
+    assert P.mqp_valu(3, 10, 64, None, dummy, None) == 1              # no sink
+    assert P.mqp_valu(3, 10, 64, dummy, None, None) == 1              # no clock array
+    assert P.mqp_valu(5, 10, 64, dummy, dummy, None) == 1             # no such kind
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: --gpus above 1 exits with status 2 and says
+    why, before it touches a device."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2, (r.returncode, r.stderr[-400:])
+    assert "one GPU" in r.stderr
 
 
 # ---------------------------------------------------------------- caller-owned workspace
